@@ -1,0 +1,172 @@
+// C ABI entry points: host-side validation, then one launch on the caller's stream.
+// Nothing here allocates device memory or synchronises unless KDA_DEBUG=1.
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "kda.h"
+#include "kda_internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+kda_status_t fail(kda_status_t st, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+bool debug_sync() {
+    static const bool on = [] {
+        const char* e = std::getenv("KDA_DEBUG");
+        return e && e[0] && std::strcmp(e, "0") != 0;
+    }();
+    return on;
+}
+
+kda_status_t finish(hipError_t launch, hipStream_t stream, const char* what) {
+    if (launch != hipSuccess)
+        return fail(KDA_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(launch));
+    if (debug_sync()) {
+        const hipError_t e = hipStreamSynchronize(stream);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s: kernel failed: %s", what, hipGetErrorString(e));
+    }
+    g_last_error[0] = '\0';
+    return KDA_OK;
+}
+
+// Checks shared by both entry points.  Returns KDA_OK or the first violation.
+kda_status_t check_problem(const kda_problem_t* p, const char* what) {
+    if (!p) return fail(KDA_ERR_NULL_POINTER, "%s: problem is NULL", what);
+    if (p->num_seqs < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: num_seqs = %d < 0", what, p->num_seqs);
+    if (p->total_tokens < 0)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld < 0", what, (long long)p->total_tokens);
+    if (p->num_heads < 1) return fail(KDA_ERR_BAD_SHAPE, "%s: num_heads = %d < 1", what, p->num_heads);
+    if (p->head_k < 1 || p->head_v < 1)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: head sizes %d, %d must be positive", what, p->head_k, p->head_v);
+    if (p->head_k != p->head_v)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head_k = %d != head_v = %d", what, p->head_k, p->head_v);
+    if (p->head_k != 64 && p->head_k != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head size %d (supported: 64, 128)", what, p->head_k);
+    if (p->qkv_dtype != KDA_F32 && p->qkv_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: qkv_dtype %d", what, p->qkv_dtype);
+    if (p->out_dtype != KDA_F32 && p->out_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: out_dtype %d", what, p->out_dtype);
+    if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: qk_l2norm must be 0 or 1", what);
+    // Row counts that index int32 offsets inside kernels stay well within range.
+    if (p->total_tokens > (int64_t(1) << 40) || int64_t(p->num_seqs) * p->num_heads > (int64_t(1) << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_status_string(kda_status_t s) {
+    switch (s) {
+        case KDA_OK: return "ok";
+        case KDA_ERR_NULL_POINTER: return "null pointer";
+        case KDA_ERR_BAD_SHAPE: return "bad shape";
+        case KDA_ERR_UNSUPPORTED: return "unsupported";
+        case KDA_ERR_WORKSPACE: return "workspace too small";
+        case KDA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char* kda_last_error(void) { return g_last_error; }
+
+size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t* problem) {
+    (void)problem;
+    return 0;  // the chunk kernel keeps every intermediate on chip
+}
+
+kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const int32_t* cu_seqlens,
+                           const float* initial_state, void* out, float* final_state,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+    const char* what = "kda_chunk_fwd";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    if (p->chunk_size != 0 && p->chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
+    if (workspace_bytes < kda_chunk_fwd_workspace_bytes(p))
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes,
+                    kda_chunk_fwd_workspace_bytes(p));
+    (void)workspace;
+    if (p->num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "%s: cu_seqlens is NULL", what);
+    if (p->total_tokens > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta and out are required", what);
+    if (p->total_tokens == 0 && !final_state) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    kda::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.cu_seqlens = cu_seqlens;
+    a.initial_state = initial_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.total_tokens = p->total_tokens;
+    a.num_seqs = p->num_seqs;
+    a.num_heads = p->num_heads;
+    a.head_dim = p->head_k;
+    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
+    a.out_bf16 = p->out_dtype == KDA_BF16;
+    a.scale = p->scale;
+    a.l2norm = p->qk_l2norm;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_prefill(a, s), s, what);
+}
+
+kda_status_t kda_recurrent_step(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                                const float* g, const float* beta, float* state, void* out,
+                                void* stream) {
+    const char* what = "kda_recurrent_step";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    if (p->total_tokens != p->num_seqs)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld must equal num_seqs = %d (one token each)",
+                    what, (long long)p->total_tokens, p->num_seqs);
+    if (p->num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !g || !beta || !state || !out)
+        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state and out are required", what);
+    kda::DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.state = state;
+    a.out = out;
+    a.num_seqs = p->num_seqs;
+    a.num_heads = p->num_heads;
+    a.head_dim = p->head_k;
+    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
+    a.out_bf16 = p->out_dtype == KDA_BF16;
+    a.scale = p->scale;
+    a.l2norm = p->qk_l2norm;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_decode(a, s), s, what);
+}
+
+}  // extern "C"

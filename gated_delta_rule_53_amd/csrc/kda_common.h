@@ -1,0 +1,55 @@
+// Private helpers shared by the KDA kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kda.h"
+
+namespace kda {
+
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kNormEps = 1e-6f;
+
+// bfloat16 is carried as its raw 16 bits.
+struct bf16_t {
+    uint16_t bits;
+};
+
+__device__ __forceinline__ float to_f32(float x) { return x; }
+__device__ __forceinline__ float to_f32(bf16_t x) {
+    return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
+}
+
+// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{static_cast<uint16_t>((u >> 16) | 0x40u)};
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return bf16_t{static_cast<uint16_t>(u >> 16)};
+}
+
+template <typename T>
+__device__ __forceinline__ T from_f32(float x);
+template <>
+__device__ __forceinline__ float from_f32<float>(float x) { return x; }
+template <>
+__device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Sum over the lanes of a wave64 whose lane ids differ only in the bits of `mask_lo..32`.
+__device__ __forceinline__ float wave_sum_from(float x, int first_offset) {
+    for (int off = first_offset; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// 16x16x4 fp32 MFMA.  Lane l supplies A[l%16][l/16] and B[l/16][l%16]; the
+// accumulator holds D[4*(l/16)+j][l%16] in element j.
+__device__ __forceinline__ floatx4 mfma_f32_16x16x4(float a, float b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+}  // namespace kda

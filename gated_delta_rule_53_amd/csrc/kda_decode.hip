@@ -1,0 +1,145 @@
+// KDA decode step: one token per sequence, state updated in place.
+//
+// Per (sequence, head) the step is a read-modify-write of the fp32 state
+// S[dk][dv] (the Ascend model file's decode paths update the recurrent cache in
+// place with a per-channel decay; the nnterp Kimi-Linear page gives the
+// decay-then-delta-rule order).  With S read once:
+//
+//   S_bar = diag(exp(g)) S
+//   u     = S_bar^T k_hat,   p = S_bar^T q_hat          (one sweep over S_bar)
+//   delta = beta (v - u)
+//   o     = S_new^T q_hat = p + (k_hat . q_hat) delta
+//   S_new = S_bar + k_hat delta^T                          (written back)
+//
+// so HBM sees exactly one read and one write of the state, 2*dk*dv*4 bytes
+// per (sequence, head), which bounds the kernel.
+//
+// Launch: one 256-thread workgroup per (sequence, head).  Thread (cg, rg)
+// owns value columns 4cg..4cg+3 of rows rg, rg+NRG, ...: every load and store
+// of the state is a float4, and a wave touches whole 512-byte rows.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+template <int D, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void decode_step_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
+    TOut* __restrict__ out, float scale, int l2norm) {
+    constexpr int NCG = D / 4;      // column groups of four
+    constexpr int NRG = 256 / NCG;  // row groups
+    constexpr int RPT = D / NRG;    // rows per thread
+    static_assert(NRG * NCG == 256 && RPT * NRG == D, "tiling");
+
+    const int pair = blockIdx.x;  // n * H + h; also the token row of q/k/v/g/beta
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % NCG, rg = tid / NCG;
+
+    float* S = state + static_cast<size_t>(pair) * D * D;
+
+    // Issue the state loads first; they are the bulk of the traffic.
+    floatx4 s[RPT];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+        s[i] = *reinterpret_cast<const floatx4*>(S + (rg + NRG * i) * D + 4 * cg);
+
+    __shared__ float sq[D], sk[D], se[D];
+    __shared__ float red[4][NCG][8];
+    if (tid < D) {
+        const size_t off = static_cast<size_t>(pair) * D + tid;
+        sq[tid] = to_f32(q[off]);
+        sk[tid] = to_f32(k[off]);
+        se[tid] = fast_exp2(g[off] * kLog2e);
+    }
+    __syncthreads();
+
+    // Norms and k.q, computed by every wave (no extra barrier needed).
+    float aq = 0.f, ak = 0.f, aqk = 0.f;
+#pragma unroll
+    for (int c = lane; c < D; c += 64) {
+        const float qq = sq[c], kk = sk[c];
+        aq += qq * qq;
+        ak += kk * kk;
+        aqk += qq * kk;
+    }
+    aq = wave_sum_from(aq, 1);
+    ak = wave_sum_from(ak, 1);
+    aqk = wave_sum_from(aqk, 1);
+    const float rq = (l2norm ? rsqrtf(aq + kNormEps) : 1.f) * scale;
+    const float rk = l2norm ? rsqrtf(ak + kNormEps) : 1.f;
+
+    // Decay, then the two partial contractions over this thread's rows.
+    floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + NRG * i;
+        s[i] *= se[r];
+        pu += sk[r] * s[i];
+        pp += sq[r] * s[i];
+    }
+    // Lanes of one wave that share cg differ by multiples of NCG.
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        pu[j] = wave_sum_from(pu[j], NCG);
+        pp[j] = wave_sum_from(pp[j], NCG);
+    }
+    if (lane < NCG) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            red[wave][lane][j] = pu[j];
+            red[wave][lane][4 + j] = pp[j];
+        }
+    }
+    __syncthreads();
+    floatx4 u, p;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
+        p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
+    }
+
+    const size_t voff = static_cast<size_t>(pair) * D + 4 * cg;
+    const float b = beta[pair];
+    floatx4 delta;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
+
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+        const int r = rg + NRG * i;
+        s[i] += (rk * sk[r]) * delta;
+        *reinterpret_cast<floatx4*>(S + r * D + 4 * cg) = s[i];
+    }
+    if (rg == 0) {
+        const float kq = rk * rq * aqk;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+    }
+}
+
+template <int D, typename TIn, typename TOut>
+static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads));
+    decode_step_kernel<D, TIn, TOut><<<grid, 256, 0, stream>>>(
+        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
+        a.g, a.beta, a.state, static_cast<TOut*>(a.out), a.scale, a.l2norm);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_decode_d(const DecodeArgs& a, hipStream_t stream) {
+    if (a.qkv_bf16) {
+        return a.out_bf16 ? launch_decode_t<D, bf16_t, bf16_t>(a, stream)
+                          : launch_decode_t<D, bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? launch_decode_t<D, float, bf16_t>(a, stream)
+                      : launch_decode_t<D, float, float>(a, stream);
+}
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream) {
+    return a.head_dim == 128 ? launch_decode_d<128>(a, stream) : launch_decode_d<64>(a, stream);
+}
+
+}  // namespace kda

@@ -1,0 +1,50 @@
+// Launch descriptors passed from the C ABI layer to the kernel launchers.
+// Every pointer here has already been validated on the host.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+struct DecodeArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    float* state;
+    void* out;
+    int num_seqs;
+    int num_heads;
+    int head_dim;
+    bool qkv_bf16;
+    bool out_bf16;
+    float scale;
+    int l2norm;
+};
+
+struct PrefillArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const float* g;
+    const float* beta;
+    const int32_t* cu_seqlens;
+    const float* initial_state;
+    void* out;
+    float* final_state;
+    int64_t total_tokens;
+    int num_seqs;
+    int num_heads;
+    int head_dim;
+    bool qkv_bf16;
+    bool out_bf16;
+    float scale;
+    int l2norm;
+};
+
+hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+
+}  // namespace kda

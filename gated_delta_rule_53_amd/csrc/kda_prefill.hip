@@ -1,0 +1,383 @@
+// KDA chunked prefill over packed variable-length sequences.
+//
+// The chunk algorithm is the one of the Ascend Kimi-Linear model file
+// (`_torch_chunk_kda`): per chunk of C = 64 tokens with input state S
+// (dk x dv), cumulative log-decay G[r] = sum_{s<=r} g[s] inside the chunk,
+// Gamma[r] = exp(G[r]) and normalised q, k,
+//
+//   A[r,i] = beta_r sum_c k[r,c] k[i,c] exp(G[r,c]-G[i,c])       (i < r)
+//   P[r,i] =        sum_c q[r,c] k[i,c] exp(G[r,c]-G[i,c])       (i <= r)
+//   (I + A) Delta = diag(beta) (V - (Gamma*K) S)
+//   O  = (Gamma*Q) S + P Delta
+//   S' = diag(Gamma[last]) S + (K * exp(G[last]-G))^T Delta
+//
+// Design for gfx950 (what differs from the page's listing):
+//   * One 256-thread workgroup owns one (sequence, head, 16-wide value tile).
+//     The value columns of S evolve independently, so a head's state is split
+//     over dv/16 workgroups that run the chunk chain side by side; their
+//     linear ids are congruent mod 8 so they share one XCD and its L2 for the
+//     common q/k/g reads.  Only the dv-dependent products are per tile.
+//   * Delta is computed as (I+A)^{-1} [diag(beta)(V - (Gamma*K) S)]: the WY
+//     matrices W = T Gamma K and U = T V of the listing are never formed.
+//   * (I+A)^{-1} is built blockwise: 16x16 diagonal blocks by forward
+//     substitution, off-diagonal blocks by X_RI = -X_RR sum_J L_RJ X_JI.
+//   * exp(G[r]-G[i]) is factored through the start s_B of 16-token blocks:
+//     row side k[r] exp(G[r]-G[s_R]) (<= 1), column side k[i] exp(G[s_I]-G[i])
+//     (>= 1, bounded by one block's decay) and a per-channel block factor
+//     exp(G[s_R]-G[s_I]) (<= 1).  All contractions then run on MFMA.
+//   * The state tile lives in MFMA accumulators across the whole chunk chain;
+//     a copy in LDS feeds the (Gamma*K) S and (Gamma*Q) S products.
+//   * A tail chunk is masked, not padded: rows past the sequence end read as
+//     k = q = v = g = beta = 0, which makes them no-ops.
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kC = 64;     // chunk length
+constexpr int kDVT = 16;   // value columns per workgroup
+constexpr int kSC = kC + 2;  // LDS row stride of 64x64 matrices (floats)
+
+__device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
+
+}  // namespace
+
+template <int D, typename TIn, typename TOut>
+__global__ __launch_bounds__(256) void prefill_chunk_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const float* __restrict__ g, const float* __restrict__ beta,
+    const int32_t* __restrict__ cu_seqlens, const float* initial_state, TOut* __restrict__ out,
+    float* final_state, int64_t total_tokens, int num_seqs, int num_heads, float scale,
+    int l2norm) {
+    constexpr int SD = D + 2;           // LDS row stride of [64][D] buffers (floats)
+    constexpr int NSEG = 256 / D;       // token segments per channel in the cumsum
+    constexpr int SEGLEN = kC / NSEG;
+    constexpr int CBW = D / 64;         // 16-row state blocks per wave
+
+    const int chain = blockIdx.x;
+    if (chain >= num_seqs * num_heads) return;
+    const int n = chain / num_heads, h = chain % num_heads;
+    const int col0 = blockIdx.y * kDVT;
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int l16 = lane & 15, l4 = lane >> 4;
+
+    int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1];
+    if (t0 < 0 || t1 > total_tokens || t1 < t0) t1 = t0;  // malformed: no tokens
+
+    __shared__ float sKl[kC * SD];   // k_hat[r] exp(G[r]-G[s_R]); later X = (I+A)^{-1}
+    __shared__ float sQl[kC * SD];   // q_hat[r] exp(G[r]-G[s_R]); later scratch
+    __shared__ float sKi[kC * SD];   // k_hat[r] exp(G[s_R]-G[r])
+    __shared__ float sL[kC * kSC];   // I + A
+    __shared__ float sP[kC * kSC];   // P
+    __shared__ float sS[D * kDVT];   // state tile at chunk start
+    __shared__ float sY[kC * kDVT];  // diag(beta)(V - Gamma K S), then Delta
+    __shared__ float srk[kC], srq[kC], sbeta[kC];
+    __shared__ float sB[4 * D];      // G at block starts (log2 units)
+    __shared__ float sGam[4 * D];    // exp(G[s_R])
+    __shared__ float sFL[4 * D];     // exp(G[last]-G[s_R])
+    __shared__ float sFb[6 * D];     // exp(G[s_R]-G[s_I]), I < R
+    __shared__ float sGLlog[D], sGL[D];
+    __shared__ float sCarry[NSEG * D];
+    float* sX = sKl;
+    float* sT = sQl;
+
+    const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
+
+    floatx4 Sacc[CBW];
+#pragma unroll
+    for (int b = 0; b < CBW; ++b) {
+        const int cb = wave * CBW + b;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int c = 16 * cb + 4 * l4 + j;
+            const float s = initial_state ? initial_state[head_state + c * D + col0 + l16] : 0.f;
+            Sacc[b][j] = s;
+            sS[c * kDVT + l16] = s;
+        }
+    }
+    __syncthreads();
+
+    for (int64_t cs = t0; cs < t1; cs += kC) {
+        const int L = static_cast<int>(min<int64_t>(kC, t1 - cs));
+
+        // ---- load the chunk: raw k, q and g (log2 units); beta ----
+        for (int idx = tid; idx < kC * D; idx += 256) {
+            const int r = idx / D, c = idx % D;
+            float kk = 0.f, qq = 0.f, gg = 0.f;
+            if (r < L) {
+                const size_t off = (static_cast<size_t>(cs + r) * num_heads + h) * D + c;
+                kk = to_f32(k[off]);
+                qq = to_f32(q[off]);
+                gg = g[off] * kLog2e;
+            }
+            sKl[r * SD + c] = kk;
+            sQl[r * SD + c] = qq;
+            sKi[r * SD + c] = gg;
+        }
+        if (tid < kC) sbeta[tid] = tid < L ? beta[static_cast<size_t>(cs + tid) * num_heads + h] : 0.f;
+        __syncthreads();
+
+        // ---- row norms: four lanes per row ----
+        {
+            const int r = 16 * wave + (lane >> 2), part = lane & 3;
+            float a = 0.f, b = 0.f;
+            for (int c = part; c < D; c += 4) {
+                const float kk = sKl[r * SD + c], qq = sQl[r * SD + c];
+                a += kk * kk;
+                b += qq * qq;
+            }
+            a += __shfl_xor(a, 1, 64);
+            a += __shfl_xor(a, 2, 64);
+            b += __shfl_xor(b, 1, 64);
+            b += __shfl_xor(b, 2, 64);
+            if (part == 0) {
+                srk[r] = l2norm ? rsqrtf(a + kNormEps) : 1.f;
+                srq[r] = (l2norm ? rsqrtf(b + kNormEps) : 1.f) * scale;
+            }
+        }
+
+        // ---- cumulative log-decay per channel: local prefix, then carry ----
+        const int c = tid % D, seg = tid / D;
+        float Gv[SEGLEN];
+        {
+            float acc = 0.f;
+#pragma unroll
+            for (int i = 0; i < SEGLEN; ++i) {
+                acc += sKi[(seg * SEGLEN + i) * SD + c];
+                Gv[i] = acc;
+            }
+            sCarry[seg * D + c] = acc;
+        }
+        __syncthreads();
+        {
+            float carry = 0.f;
+            for (int s = 0; s < seg; ++s) carry += sCarry[s * D + c];
+#pragma unroll
+            for (int i = 0; i < SEGLEN; ++i) Gv[i] += carry;
+#pragma unroll
+            for (int i = 0; i < SEGLEN; ++i)
+                if (((seg * SEGLEN + i) & 15) == 0) sB[((seg * SEGLEN + i) >> 4) * D + c] = Gv[i];
+            if (seg == NSEG - 1) sGLlog[c] = Gv[SEGLEN - 1];
+        }
+        __syncthreads();
+
+        // ---- scaled operands and per-channel block factors ----
+#pragma unroll
+        for (int i = 0; i < SEGLEN; ++i) {
+            const int r = seg * SEGLEN + i;
+            const float Bv = sB[(r >> 4) * D + c];
+            const float kk = sKl[r * SD + c] * srk[r];
+            const float qq = sQl[r * SD + c] * srq[r];
+            const float e = fast_exp2(Gv[i] - Bv);
+            const float einv = fast_exp2(Bv - Gv[i]);
+            sKl[r * SD + c] = kk * e;
+            sQl[r * SD + c] = qq * e;
+            sKi[r * SD + c] = kk * einv;
+        }
+        if (seg == 0) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                sGam[R * D + c] = fast_exp2(sB[R * D + c]);
+                for (int I = 0; I < R; ++I)
+                    sFb[pair_index(R, I) * D + c] = fast_exp2(sB[R * D + c] - sB[I * D + c]);
+            }
+        }
+        if (seg == NSEG - 1) {
+            const float gl = sGLlog[c];
+#pragma unroll
+            for (int R = 0; R < 4; ++R) sFL[R * D + c] = fast_exp2(gl - sB[R * D + c]);
+            sGL[c] = fast_exp2(gl);
+        }
+        __syncthreads();
+
+        // ---- Z = (Gamma K) S and Oq = (Gamma Q) S for row block R = wave ----
+        floatx4 Z = {0.f, 0.f, 0.f, 0.f}, Oq = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int R = wave, r = 16 * R + l16;
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const int cc = k0 + l4;
+                const float gam = sGam[R * D + cc];
+                const float bS = sS[cc * kDVT + l16];
+                Z = mfma_f32_16x16x4(sKl[r * SD + cc] * gam, bS, Z);
+                Oq = mfma_f32_16x16x4(sQl[r * SD + cc] * gam, bS, Oq);
+            }
+        }
+        // ---- A and P, block pairs (R, I <= R) spread over the waves ----
+        for (int pi = wave; pi < 10; pi += 4) {
+            const int R = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
+            const int I = pi - R * (R + 1) / 2;
+            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+            const int ra = 16 * R + l16, ib = 16 * I + l16;
+            for (int k0 = 0; k0 < D; k0 += 4) {
+                const int cc = k0 + l4;
+                const float fb = I < R ? sFb[pair_index(R, I) * D + cc] : 1.f;
+                const float bK = sKi[ib * SD + cc] * fb;
+                accA = mfma_f32_16x16x4(sKl[ra * SD + cc], bK, accA);
+                accP = mfma_f32_16x16x4(sQl[ra * SD + cc], bK, accP);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * l4 + j, i = ib;
+                float lv, pv;
+                if (I < R) {
+                    lv = sbeta[r] * accA[j];
+                    pv = accP[j];
+                } else {
+                    lv = i < r ? sbeta[r] * accA[j] : (i == r ? 1.f : 0.f);
+                    pv = i <= r ? accP[j] : 0.f;
+                }
+                sL[r * kSC + i] = lv;
+                sP[r * kSC + i] = pv;
+            }
+        }
+        __syncthreads();
+
+        // ---- diagonal blocks of X = (I+A)^{-1}; Y = diag(beta)(V - Z) ----
+        {
+            const int R = wave;
+            if (lane < 16) {
+                const int j = lane;
+                float x[16];
+#pragma unroll
+                for (int m = 0; m < 16; ++m) {
+                    float s = (m == j) ? 1.f : 0.f;
+#pragma unroll
+                    for (int p = 0; p < m; ++p) s -= sL[(16 * R + m) * kSC + 16 * R + p] * x[p];
+                    x[m] = s;
+                }
+#pragma unroll
+                for (int m = 0; m < 16; ++m) sX[(16 * R + m) * kSC + 16 * R + j] = x[m];
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * l4 + j;
+                float vv = 0.f;
+                if (r < L) vv = to_f32(v[(static_cast<size_t>(cs + r) * num_heads + h) * D + col0 + l16]);
+                sY[r * kDVT + l16] = sbeta[r] * (vv - Z[j]);
+            }
+        }
+        __syncthreads();
+
+        // ---- off-diagonal blocks of X, one block distance at a time ----
+#pragma unroll
+        for (int dist = 1; dist < 4; ++dist) {
+            const bool active = wave < 4 - dist;
+            const int I = wave, R = wave + dist;
+            float* T = sT + wave * 16 * 17;
+            if (active) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int J = I; J < R; ++J) {
+#pragma unroll
+                    for (int k0 = 0; k0 < 16; k0 += 4)
+                        acc = mfma_f32_16x16x4(sL[(16 * R + l16) * kSC + 16 * J + k0 + l4],
+                                               sX[(16 * J + k0 + l4) * kSC + 16 * I + l16], acc);
+                }
+#pragma unroll
+                for (int j = 0; j < 4; ++j) T[(4 * l4 + j) * 17 + l16] = acc[j];
+            }
+            __syncthreads();
+            if (active) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    acc = mfma_f32_16x16x4(sX[(16 * R + l16) * kSC + 16 * R + k0 + l4],
+                                           T[(k0 + l4) * 17 + l16], acc);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) sX[(16 * R + 4 * l4 + j) * kSC + 16 * I + l16] = -acc[j];
+            }
+            __syncthreads();
+        }
+
+        // ---- Delta = X Y for row block R = wave ----
+        floatx4 Dl = {0.f, 0.f, 0.f, 0.f};
+        {
+            const int R = wave;
+            for (int I = 0; I <= R; ++I) {
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    Dl = mfma_f32_16x16x4(sX[(16 * R + l16) * kSC + 16 * I + k0 + l4],
+                                          sY[(16 * I + k0 + l4) * kDVT + l16], Dl);
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sY[(16 * wave + 4 * l4 + j) * kDVT + l16] = Dl[j];
+        __syncthreads();
+
+        // ---- O = Oq + P Delta, written out ----
+        {
+            const int R = wave;
+            floatx4 acc = Oq;
+            for (int I = 0; I <= R; ++I) {
+#pragma unroll
+                for (int k0 = 0; k0 < 16; k0 += 4)
+                    acc = mfma_f32_16x16x4(sP[(16 * R + l16) * kSC + 16 * I + k0 + l4],
+                                           sY[(16 * I + k0 + l4) * kDVT + l16], acc);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int r = 16 * R + 4 * l4 + j;
+                if (r < L)
+                    out[(static_cast<size_t>(cs + r) * num_heads + h) * D + col0 + l16] =
+                        from_f32<TOut>(acc[j]);
+            }
+        }
+        // ---- S = diag(Gamma[last]) S + (K exp(G[last]-G))^T Delta ----
+#pragma unroll
+        for (int b = 0; b < CBW; ++b) {
+            const int cb = wave * CBW + b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) Sacc[b][j] *= sGL[16 * cb + 4 * l4 + j];
+            const int cc = 16 * cb + l16;
+            for (int r0 = 0; r0 < kC; r0 += 4) {
+                const int r = r0 + l4;
+                Sacc[b] = mfma_f32_16x16x4(sKi[r * SD + cc] * sFL[(r >> 4) * D + cc],
+                                           sY[r * kDVT + l16], Sacc[b]);
+            }
+#pragma unroll
+            for (int j = 0; j < 4; ++j) sS[(16 * cb + 4 * l4 + j) * kDVT + l16] = Sacc[b][j];
+        }
+        __syncthreads();
+    }
+
+    if (final_state) {
+#pragma unroll
+        for (int b = 0; b < CBW; ++b) {
+            const int cb = wave * CBW + b;
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                final_state[head_state + (16 * cb + 4 * l4 + j) * D + col0 + l16] = Sacc[b][j];
+        }
+    }
+}
+
+template <int D, typename TIn, typename TOut>
+static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
+    const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
+    // Round the chain count up to a multiple of 8 so that the value tiles of one
+    // chain (linear ids chain + k * grid.x) land on the same XCD.
+    const dim3 grid((chains + 7u) & ~7u, D / kDVT);
+    prefill_chunk_kernel<D, TIn, TOut><<<grid, 256, 0, stream>>>(
+        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
+        a.g, a.beta, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out), a.final_state,
+        a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
+    if (a.qkv_bf16) {
+        return a.out_bf16 ? launch_prefill_t<D, bf16_t, bf16_t>(a, stream)
+                          : launch_prefill_t<D, bf16_t, float>(a, stream);
+    }
+    return a.out_bf16 ? launch_prefill_t<D, float, bf16_t>(a, stream)
+                      : launch_prefill_t<D, float, float>(a, stream);
+}
+
+hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    return a.head_dim == 128 ? launch_prefill_d<128>(a, stream) : launch_prefill_d<64>(a, stream);
+}
+
+}  // namespace kda

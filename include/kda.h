@@ -1,0 +1,151 @@
+/*
+ * kda.h -- C ABI of the Kimi Delta Attention (KDA) core for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * KDA is a gated delta-rule recurrence whose decay is one value per key
+ * channel (the nnterp Kimi-Linear page, KDA description).  Per sequence and
+ * head, with state S[dk][dv] (rows are key channels, columns value channels):
+ *
+ *     k_hat = k / sqrt(sum(k^2) + 1e-6),  q_hat = scale * q / sqrt(sum(q^2) + 1e-6)
+ *     S     = diag(exp(g_t)) S
+ *     S     = S + beta_t k_hat (v_t - S^T k_hat)^T
+ *     o_t   = S^T q_hat
+ *
+ * The normalisation (eps inside the root), the query-only scale 1/sqrt(dk)
+ * and the read-after-update order follow the Ascend model file (its
+ * `_l2_normalize` helper and its chunked fallback `_torch_chunk_kda`).  Each
+ * kernel takes (q, k, v, g, beta, initial_state) and returns (out,
+ * final_state), the interface the nnterp page gives for the chunked prompt
+ * kernel and the token-by-token decode kernel.
+ *
+ * Conventions for every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
+ *     and densely packed, innermost dimension last.  The library allocates
+ *     nothing, keeps no state between calls and never synchronises `stream`:
+ *     work is enqueued on it and the call returns.
+ *   - Argument errors are detected on the host before anything is enqueued
+ *     and leave every output untouched.  KDA_ERR_HIP reports a failed launch.
+ *     kda_last_error() gives a human-readable detail for the calling thread.
+ *   - NaN or Inf inputs propagate into the outputs; they are not checked.
+ *   - The numeric domain of the chunked kernel: g must be finite and <= 0,
+ *     and within every aligned 16-token block the per-channel sum of g must be
+ *     >= -80 (the kernel factors exp(G_r - G_i) through the block start, and
+ *     exp(80) is near the float32 limit).  Decode has no such limit.
+ *   - Setting the environment variable KDA_DEBUG=1 makes every call wait for
+ *     its own kernels and report their errors (this synchronises the stream).
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+typedef enum kda_status {
+    KDA_OK = 0,
+    KDA_ERR_NULL_POINTER = 1, /* a required pointer is NULL                      */
+    KDA_ERR_BAD_SHAPE = 2,    /* negative or inconsistent sizes                  */
+    KDA_ERR_UNSUPPORTED = 3,  /* valid but not implemented (head size, dtype...) */
+    KDA_ERR_WORKSPACE = 4,    /* workspace smaller than the queried size         */
+    KDA_ERR_HIP = 5           /* a HIP launch or runtime call failed             */
+} kda_status_t;
+
+typedef enum kda_dtype {
+    KDA_F32 = 0,  /* IEEE binary32                              */
+    KDA_BF16 = 1  /* bfloat16 (upper 16 bits of a binary32)     */
+} kda_dtype_t;
+
+/* Problem description shared by both entry points. */
+typedef struct kda_problem {
+    int64_t total_tokens; /* T: rows of q/k/v/g/beta/out.  Prefill: == cu_seqlens[num_seqs].
+                             Decode: == num_seqs (one token per sequence).              */
+    int32_t num_seqs;     /* N >= 0.  N == 0 or T == 0 is a no-op that returns KDA_OK.    */
+    int32_t num_heads;    /* H >= 1                                                       */
+    int32_t head_k;       /* dk; 64 or 128                                                */
+    int32_t head_v;       /* dv; must equal dk                                            */
+    int32_t qkv_dtype;    /* kda_dtype_t of q, k and v                                    */
+    int32_t out_dtype;    /* kda_dtype_t of out                                           */
+    float scale;          /* multiplies q after its L2 norm; 1/sqrt(dk) by convention     */
+    int32_t qk_l2norm;    /* 1: L2-normalise q and k inside the kernel; 0: use as given   */
+    int32_t chunk_size;   /* prefill chunk length; 64 only (0 selects 64)                 */
+} kda_problem_t;
+
+/* ABI revision of the loaded library; compare with KDA_ABI_VERSION. */
+int kda_abi_version(void);
+
+/* Static text for a status code. */
+const char *kda_status_string(kda_status_t status);
+
+/* Detail of the last error raised on the calling thread ("" if none). */
+const char *kda_last_error(void);
+
+/*
+ * Bytes of device workspace kda_chunk_fwd needs for this problem (0 if none).
+ * Returns 0 as well for an invalid problem; kda_chunk_fwd then reports why.
+ */
+size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
+
+/*
+ * Chunked prefill over packed variable-length sequences.
+ *
+ * Defined by the chunk algorithm of the Ascend model file (`_torch_chunk_kda`):
+ * tokens are cut into chunks of `chunk_size` per sequence, never straddling a
+ * sequence boundary; inside a chunk the delta rule is solved as one unit
+ * lower-triangular system, and the state is carried from chunk to chunk.  The
+ * result equals the token-by-token recurrence above up to rounding.  Varlen
+ * packing follows that file's per-request loop (`_prefill_flash_kda`): the
+ * sequences are concatenated and cu_seqlens marks their boundaries; each
+ * sequence starts from its own initial state.  A tail chunk shorter than
+ * chunk_size behaves as if padded with no-op tokens (k = v = g = beta = 0).
+ *
+ *   q, k           [T, H, dk]  qkv_dtype
+ *   v              [T, H, dv]  qkv_dtype
+ *   g              [T, H, dk]  float32, log-decay per key channel (<= 0)
+ *   beta           [T, H]      float32, in [0, 1]
+ *   cu_seqlens     [N + 1]     int32 (device): 0 = cu[0] <= cu[1] <= ... <= cu[N] = T.
+ *                  Sequence n is rows cu[n] .. cu[n+1]-1.  Zero-length sequences are
+ *                  allowed (their final state is their initial state).  Entries outside
+ *                  [0, T] or decreasing pairs make that sequence empty; they never cause
+ *                  an out-of-bounds access.
+ *   initial_state  [N, H, dk, dv] float32, or NULL for zeros
+ *   out            [T, H, dv]  out_dtype (written)
+ *   final_state    [N, H, dk, dv] float32 (written), or NULL to skip.  May alias
+ *                  initial_state exactly (same pointer); partial overlap is undefined.
+ *   workspace      device buffer of at least kda_chunk_fwd_workspace_bytes(problem)
+ *                  bytes, or NULL when that is 0.  Contents need not be initialised.
+ *   stream         a hipStream_t (NULL: the default stream)
+ */
+kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const void *k,
+                           const void *v, const float *g, const float *beta,
+                           const int32_t *cu_seqlens, const float *initial_state, void *out,
+                           float *final_state, void *workspace, size_t workspace_bytes,
+                           void *stream);
+
+/*
+ * One decode step: every sequence advances by exactly one token, and its state
+ * is updated IN PLACE.  This is the token-by-token form (the nnterp page's
+ * decode kernel; the Ascend model file's decode paths update the recurrent
+ * cache in place with a per-channel decay `gk`).
+ *
+ *   q, k    [N, H, dk]  qkv_dtype     (problem->total_tokens must equal N)
+ *   v       [N, H, dv]  qkv_dtype
+ *   g       [N, H, dk]  float32
+ *   beta    [N, H]      float32
+ *   state   [N, H, dk, dv] float32, read and overwritten
+ *   out     [N, H, dv]  out_dtype (written)
+ *   stream  a hipStream_t (NULL: the default stream)
+ */
+kda_status_t kda_recurrent_step(const kda_problem_t *problem, const void *q, const void *k,
+                                const void *v, const float *g, const float *beta, float *state,
+                                void *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H_ */

@@ -1,0 +1,165 @@
+"""The C-ABI library without a GPU: load, exported symbols, argument validation.
+
+Every call here is rejected (or is a no-op) on the host before any HIP call,
+so it runs on a machine without a GPU.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_delta_rule_53_amd as kda
+from gated_delta_rule_53_amd._binding import Problem
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z0-9_]+)\s*\(", text)))
+
+
+def exported_symbols(path):
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True,
+                         check=True).stdout
+    return {line.split()[-1] for line in out.splitlines() if line.strip()}
+
+
+def test_header_declares_the_boundary():
+    assert declared_functions() == sorted([
+        "kda_abi_version", "kda_status_string", "kda_last_error",
+        "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step"])
+
+
+def test_library_exports_every_declared_symbol():
+    syms = exported_symbols(kda.library_path())
+    missing = [f for f in declared_functions() if f not in syms]
+    assert not missing, f"not exported: {missing}"
+
+
+def test_abi_version_matches_header():
+    m = re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read())
+    assert kda.abi_version() == int(m.group(1))
+
+
+def test_problem_struct_layout_matches_header():
+    # int64 first, then nine 4-byte fields: 8 + 36 = 44, padded to 48.
+    assert ctypes.sizeof(Problem) == 48
+    assert Problem.total_tokens.offset == 0 and Problem.num_seqs.offset == 8
+    assert Problem.chunk_size.offset == 40
+
+
+def test_status_strings():
+    lib = kda.raw_library()
+    names = {i: lib.kda_status_string(i).decode() for i in range(6)}
+    assert names[0] == "ok" and names[5] == "HIP error"
+    assert lib.kda_status_string(99).decode() == "unknown status"
+
+
+def _prob(**kw):
+    base = dict(total_tokens=128, num_seqs=1, num_heads=2, head_k=128, head_v=128, qkv_dtype=1,
+                out_dtype=0, scale=0.088, qk_l2norm=1, chunk_size=64)
+    base.update(kw)
+    return Problem(**base)
+
+
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every case below fails validation first
+
+
+def _chunk(prob, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fs=None, ws=None,
+             ws_bytes=0)
+    p.update(ptrs)
+    st = lib.kda_chunk_fwd(None if prob is None else ctypes.byref(prob), p["q"], p["k"], p["v"],
+                           p["g"], p["beta"], p["cu"], p["s0"], p["out"], p["fs"], p["ws"],
+                           p["ws_bytes"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def _step(prob, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE)
+    p.update(ptrs)
+    st = lib.kda_recurrent_step(None if prob is None else ctypes.byref(prob), p["q"], p["k"],
+                                p["v"], p["g"], p["beta"], p["state"], p["out"], None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(num_seqs=-1), 2, "num_seqs"),
+    (dict(total_tokens=-5), 2, "total_tokens"),
+    (dict(num_heads=0), 2, "num_heads"),
+    (dict(head_k=96, head_v=96), 3, "head size 96"),
+    (dict(head_k=128, head_v=64), 3, "head_k"),
+    (dict(head_k=0), 2, "head sizes"),
+    (dict(qkv_dtype=7), 3, "qkv_dtype"),
+    (dict(out_dtype=2), 3, "out_dtype"),
+    (dict(qk_l2norm=3), 2, "qk_l2norm"),
+    (dict(chunk_size=32), 3, "chunk_size"),
+])
+def test_chunk_fwd_rejects_bad_problem(kw, status, needle):
+    st, msg = _chunk(_prob(**kw))
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_chunk_fwd_null_pointers():
+    assert _chunk(None)[0] == 1
+    st, msg = _chunk(_prob(), cu=None)
+    assert st == 1 and "cu_seqlens" in msg
+    for name in ("q", "k", "v", "g", "beta", "out"):
+        st, msg = _chunk(_prob(), **{name: None})
+        assert st == 1, name
+
+
+def test_chunk_fwd_empty_batch_is_a_noop():
+    st, msg = _chunk(_prob(num_seqs=0, total_tokens=0), q=None, k=None, v=None, g=None, beta=None,
+                     cu=None, out=None)
+    assert st == 0 and msg == ""
+
+
+def test_workspace_query_is_zero_and_checked():
+    lib = kda.raw_library()
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_prob())) == 0
+    assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(total_tokens=3, num_seqs=2), 2, "one token each"),
+    (dict(total_tokens=2, num_seqs=2, head_k=32, head_v=32), 3, "head size 32"),
+    (dict(total_tokens=2, num_seqs=2, num_heads=-1), 2, "num_heads"),
+])
+def test_recurrent_step_rejects_bad_problem(kw, status, needle):
+    st, msg = _step(_prob(**kw))
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_recurrent_step_null_pointers_and_empty():
+    assert _step(None)[0] == 1
+    for name in ("q", "k", "v", "g", "beta", "state", "out"):
+        st, _ = _step(_prob(total_tokens=2, num_seqs=2), **{name: None})
+        assert st == 1, name
+    st, msg = _step(_prob(total_tokens=0, num_seqs=0), q=None, state=None)
+    assert st == 0
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    x = torch.zeros(4, 2, 64)
+    with pytest.raises(kda.KdaError):
+        kda.chunk_fwd(x, x, x, x, torch.zeros(4, 2))
+    with pytest.raises(kda.KdaError):
+        kda.recurrent_step(x, x, x, x, torch.zeros(4, 2), torch.zeros(4, 2, 64, 64))
+
+
+def test_product_package_does_not_reference_the_oracle():
+    pkg = os.path.dirname(kda.__file__)
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in text.lower(), f"{f} mentions the oracle"
