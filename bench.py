@@ -1,0 +1,239 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA core on one MI355X.
+
+A step is one chunked prefill (kda_chunk_fwd) over the Kimi-Linear-shaped
+workload: one sequence of T=4096 tokens, H=32 heads, dk=dv=128, bf16 q/k/v,
+fp32 g/beta, fp32 initial state, bf16 output.  ``value`` is prefill tokens/s
+with inputs resident in HBM.  Three copies of the inputs rotate from step to
+step so that the 256 MB Infinity Cache cannot serve a step's reads from the
+previous one.
+
+The decode kernel (kda_recurrent_step) is timed on its own workload, 256
+sequences x 64 steps, H=32, d=128, and reported under ``decode``.
+
+Kernel durations come from HIP events recorded around every launch on the
+stream the kernels run on; ``roofline.achieved`` divides the algorithmic bytes
+of one launch by the mean launch duration.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s + decode steps/s (H=32,d=128) and % of MFMA/HBM roofline"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 2   # q,k,v bf16; g fp32; beta; out bf16
+STATE_BYTES = 128 * 128 * 4
+DECODE_BYTES_PER_HEAD_STEP = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+KERNEL_SOURCES = {
+    "prefill": ["gated_delta_rule_53_amd/csrc/kda_prefill.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
+    "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
+}
+
+
+def source_digest(kind: str) -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES[kind]:
+        h.update(open(os.path.join(ROOT, rel), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they match this source."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))[kind]
+    except (OSError, KeyError, ValueError):
+        return None
+    if rec.get("source_digest") != source_digest(kind):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def time_launches(fn, n: int, stream):
+    """Run fn() n times; returns (wall seconds, mean per-launch seconds from events)."""
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(n):
+        evs[i][0].record(stream)
+        fn(i)
+        evs[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = sum(a.elapsed_time(b) for a, b in evs) / n / 1e3
+    return wall, per
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+    import kda_workloads as w
+
+    x = w.prefill_4k()
+    dev = "cuda:0"
+    copies = []
+    for _ in range(3):
+        copies.append(dict(q=x.q.to(dev), k=x.k.to(dev), v=x.v.to(dev), g=x.g.to(dev),
+                           beta=x.beta.to(dev), cu=x.cu_seqlens.to(dev),
+                           s0=x.initial_state.to(dev),
+                           out=torch.empty_like(x.v, device=dev),
+                           fs=torch.empty_like(x.initial_state, device=dev)))
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = copies[i % 3]
+        kda.chunk_fwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["cu"], c["s0"],
+                      scale=x.scale, out=c["out"], final_state=c["fs"])
+
+    for i in range(warmup):
+        step(i)
+    wall, per = time_launches(step, steps, stream)
+    T, H = x.total_tokens, x.num_heads
+    alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + x.num_seqs * H * 2 * STATE_BYTES
+    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T)
+
+
+def bench_decode(loops: int):
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+    import kda_workloads as w
+
+    x = w.decode_256x64()
+    dev = "cuda:0"
+    q, k, v, g, b = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
+    st = x.initial_state.to(dev)
+    out = torch.empty_like(v[0])
+    stream = torch.cuda.current_stream()
+
+    def one(i):
+        t = i % x.steps
+        kda.recurrent_step(q[t], k[t], v[t], g[t], b[t], st, scale=x.scale, out=out)
+
+    for i in range(x.steps):  # warm-up pass over all 64 steps
+        one(i)
+    n = loops * x.steps
+    wall, per = time_launches(one, n, stream)
+    N, H = x.q.shape[1], x.q.shape[2]
+    alg_bytes = N * H * DECODE_BYTES_PER_HEAD_STEP
+    return dict(x=x, wall=wall, per_launch=per, launches=n, alg_bytes=alg_bytes, num_seqs=N)
+
+
+def cpu_baseline(min_seconds: float = 8.0):
+    """The fp64 oracle on the host cores, over whole passes of the same prefill workload."""
+    import kda_workloads as w
+    import oracle
+    x = w.prefill_4k()
+    passes, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, x.initial_state, scale=x.scale)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds or passes >= 50:
+            break
+    return dict(value=passes * x.total_tokens / el, unit="tokens/s", cores=oracle.threads(),
+                kind="oracle",
+                sample=f"{passes} full pass(es) of prefill_T4096_H32_d128 (fp64 recurrence, "
+                       f"{el:.1f} s wall)")
+
+
+def copy_calibration(gib: int = 1, reps: int = 4):
+    """A plain device-to-device copy of known size, for scaling the HBM byte counters."""
+    import torch
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration": {"bytes_read_per_launch": n * 4,
+                                           "bytes_written_per_launch": n * 4, "launches": reps}}))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=30)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-loops", type=int, default=4, help="timed passes over the 64 decode steps")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (reference for HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the KDA core "
+              "shards heads and sequences with no exchange, so more GPUs would only repeat this "
+              "measurement per GPU).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.copy_calibration:
+        copy_calibration()
+        return
+
+    pf = bench_prefill(args.steps, args.warmup)
+    print(f"prefill: {pf['per_launch'] * 1e6:.1f} us per launch (events), "
+          f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
+    dc = bench_decode(args.decode_loops)
+    print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+
+    ms_per_step = pf["wall"] / args.steps * 1e3
+    tokens_per_s = pf["tokens"] * args.steps / pf["wall"]
+    achieved = pf["alg_bytes"] / pf["per_launch"] / 1e9
+    tr = measured_traffic("prefill")
+    d_achieved = dc["alg_bytes"] / dc["per_launch"] / 1e9
+    d_tr = measured_traffic("decode")
+    decode_steps_per_s = dc["launches"] / dc["wall"]
+
+    line = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": pf["x"].name, "num_seqs": 1, "seq_len": pf["tokens"],
+                   "heads": 32, "head_dim": 128, "chunk": 64, "qkv": "bf16", "g_beta": "f32",
+                   "state": "f32", "out": "bf16", "input_copies_rotated": 3},
+        "roofline": {"kernel": "prefill_chunk_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None if tr is None else round(tr / pf["per_launch"] / 1e9, 2),
+                     "alg_bytes_per_launch": pf["alg_bytes"],
+                     "launch_us": round(pf["per_launch"] * 1e6, 2)},
+        "decode": {"workload": dc["x"].name, "steps_per_s": round(decode_steps_per_s, 1),
+                   "tokens_per_s": round(decode_steps_per_s * dc["num_seqs"], 1),
+                   "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
+                                "achieved": round(d_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                "frac": round(d_achieved / HBM_PEAK_GBS, 4),
+                                "traffic": None if d_tr is None else round(d_tr / dc["per_launch"] / 1e9, 2),
+                                "alg_bytes_per_launch": dc["alg_bytes"],
+                                "launch_us": round(dc["per_launch"] * 1e6, 2)}},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
