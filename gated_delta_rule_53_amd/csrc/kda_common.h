@@ -38,6 +38,21 @@ __device__ __forceinline__ float from_f32<float>(float x) { return x; }
 template <>
 __device__ __forceinline__ bf16_t from_f32<bf16_t>(float x) { return f32_to_bf16(x); }
 
+// Vector load of N contiguous elements (N * sizeof(T) a multiple of 8 bytes,
+// source aligned to min(16, N * sizeof(T))).
+template <int N, typename T>
+__device__ __forceinline__ void load_vec(T (&dst)[N], const T* src) {
+    constexpr int BYTES = N * static_cast<int>(sizeof(T));
+    static_assert(BYTES % 8 == 0, "vector load size");
+    if constexpr (BYTES == 8) {
+        *reinterpret_cast<uint2*>(dst) = *reinterpret_cast<const uint2*>(src);
+    } else {
+#pragma unroll
+        for (int i = 0; i < BYTES / 16; ++i)
+            reinterpret_cast<uint4*>(dst)[i] = reinterpret_cast<const uint4*>(src)[i];
+    }
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Sum over the lanes of a wave64 whose lane ids differ only in the bits of `mask_lo..32`.
@@ -51,5 +66,36 @@ __device__ __forceinline__ float wave_sum_from(float x, int first_offset) {
 __device__ __forceinline__ floatx4 mfma_f32_16x16x4(float a, float b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+
+// Phase timing for kernel tuning.  Compiled out unless KDA_PHASE_TIMING is
+// defined; then thread 0 of every workgroup accumulates clock64() deltas
+// between consecutive marks into kda_phase_cycles[mark].
+#ifdef KDA_PHASE_TIMING
+__device__ unsigned long long kda_phase_cycles[32];
+#define KDA_PHASE_BEGIN long long kda_phase_t = clock64(); long long kda_phase_acc[32] = {0};
+#define KDA_PHASE_MARK(i)                                  \
+    do {                                                   \
+        if (threadIdx.x == 0) {                            \
+            const long long kda_now = clock64();           \
+            kda_phase_acc[i] += kda_now - kda_phase_t;     \
+            kda_phase_t = kda_now;                         \
+        }                                                  \
+    } while (0)
+#define KDA_PHASE_END                                                          \
+    do {                                                                       \
+        if (threadIdx.x == 0)                                                  \
+            for (int kda_i = 0; kda_i < 32; ++kda_i)                           \
+                if (kda_phase_acc[kda_i])                                      \
+                    atomicAdd(&kda_phase_cycles[kda_i], (unsigned long long)kda_phase_acc[kda_i]); \
+    } while (0)
+#else
+#define KDA_PHASE_BEGIN
+#define KDA_PHASE_MARK(i) \
+    do {                  \
+    } while (0)
+#define KDA_PHASE_END \
+    do {              \
+    } while (0)
+#endif
 
 }  // namespace kda

@@ -46,5 +46,7 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
+// bf16 q/k/v with dk = dv = 128 (called by launch_prefill).
+hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 
 }  // namespace kda

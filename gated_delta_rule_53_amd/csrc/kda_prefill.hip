@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     __shared__ float sP[kC * kSC];   // P
     __shared__ float sS[D * kDVT];   // state tile at chunk start
     __shared__ float sY[kC * kDVT];  // diag(beta)(V - Gamma K S), then Delta
+    __shared__ float sV[kC * kDVT];  // value tile of the chunk
     __shared__ float srk[kC], srq[kC], sbeta[kC];
     __shared__ float sB[4 * D];      // G at block starts (log2 units)
     __shared__ float sGam[4 * D];    // exp(G[s_R])
@@ -84,6 +85,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     float* sT = sQl;
 
     const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
+    KDA_PHASE_BEGIN
 
     floatx4 Sacc[CBW];
 #pragma unroll
@@ -99,25 +101,71 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     }
     __syncthreads();
 
+    // Register prefetch of one chunk.  Thread (pq, pc) holds rows 4pq..4pq+3 and
+    // channels CPT*pc .. CPT*pc+CPT-1 of k, q and g; threads < 128 hold half a row
+    // of the value tile, threads < 64 one beta.
+    constexpr int CPT = D / 16;
+    const int pq = tid >> 4, pc = tid & 15;
+    alignas(16) TIn pk[4][CPT];
+    alignas(16) TIn pqv[4][CPT];
+    alignas(16) float pg[4][CPT];
+    alignas(16) TIn pv[8];
+    float pb = 0.f;
+    auto fetch = [&](int64_t c0) {
+        const int Ln = static_cast<int>(min<int64_t>(kC, t1 - c0));
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * pq + j;
+            if (r < Ln) {
+                const size_t off = (static_cast<size_t>(c0 + r) * num_heads + h) * D + CPT * pc;
+                load_vec(pk[j], k + off);
+                load_vec(pqv[j], q + off);
+                load_vec(pg[j], g + off);
+            } else {
+#pragma unroll
+                for (int i = 0; i < CPT; ++i) {
+                    pk[j][i] = from_f32<TIn>(0.f);
+                    pqv[j][i] = from_f32<TIn>(0.f);
+                    pg[j][i] = 0.f;
+                }
+            }
+        }
+        if (tid < 2 * kC) {
+            const int r = tid >> 1;
+            if (r < Ln) {
+                load_vec(pv, v + (static_cast<size_t>(c0 + r) * num_heads + h) * D + col0 + 8 * (tid & 1));
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) pv[i] = from_f32<TIn>(0.f);
+            }
+        }
+        if (tid < kC) pb = tid < Ln ? beta[static_cast<size_t>(c0 + tid) * num_heads + h] : 0.f;
+    };
+    if (t0 < t1) fetch(t0);
+
     for (int64_t cs = t0; cs < t1; cs += kC) {
         const int L = static_cast<int>(min<int64_t>(kC, t1 - cs));
 
-        // ---- load the chunk: raw k, q and g (log2 units); beta ----
-        for (int idx = tid; idx < kC * D; idx += 256) {
-            const int r = idx / D, c = idx % D;
-            float kk = 0.f, qq = 0.f, gg = 0.f;
-            if (r < L) {
-                const size_t off = (static_cast<size_t>(cs + r) * num_heads + h) * D + c;
-                kk = to_f32(k[off]);
-                qq = to_f32(q[off]);
-                gg = g[off] * kLog2e;
+        // ---- stage the prefetched chunk in LDS, then prefetch the next one ----
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 4 * pq + j;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) {
+                sKl[r * SD + CPT * pc + i] = to_f32(pk[j][i]);
+                sQl[r * SD + CPT * pc + i] = to_f32(pqv[j][i]);
+                sKi[r * SD + CPT * pc + i] = pg[j][i] * kLog2e;
             }
-            sKl[r * SD + c] = kk;
-            sQl[r * SD + c] = qq;
-            sKi[r * SD + c] = gg;
         }
-        if (tid < kC) sbeta[tid] = tid < L ? beta[static_cast<size_t>(cs + tid) * num_heads + h] : 0.f;
+        if (tid < 2 * kC) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sV[(tid >> 1) * kDVT + 8 * (tid & 1) + i] = to_f32(pv[i]);
+        }
+        if (tid < kC) sbeta[tid] = pb;
         __syncthreads();
+        KDA_PHASE_MARK(1);
+        if (cs + kC < t1) fetch(cs + kC);
+        KDA_PHASE_MARK(2);
 
         // ---- row norms: four lanes per row ----
         {
@@ -151,6 +199,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             sCarry[seg * D + c] = acc;
         }
         __syncthreads();
+        KDA_PHASE_MARK(4);
         {
             float carry = 0.f;
             for (int s = 0; s < seg; ++s) carry += sCarry[s * D + c];
@@ -162,6 +211,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             if (seg == NSEG - 1) sGLlog[c] = Gv[SEGLEN - 1];
         }
         __syncthreads();
+        KDA_PHASE_MARK(5);
 
         // ---- scaled operands and per-channel block factors ----
 #pragma unroll
@@ -191,6 +241,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             sGL[c] = fast_exp2(gl);
         }
         __syncthreads();
+        KDA_PHASE_MARK(6);
 
         // ---- Z = (Gamma K) S and Oq = (Gamma Q) S for row block R = wave ----
         floatx4 Z = {0.f, 0.f, 0.f, 0.f}, Oq = {0.f, 0.f, 0.f, 0.f};
@@ -233,6 +284,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             }
         }
         __syncthreads();
+        KDA_PHASE_MARK(7);
 
         // ---- diagonal blocks of X = (I+A)^{-1}; Y = diag(beta)(V - Z) ----
         {
@@ -253,12 +305,11 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * R + 4 * l4 + j;
-                float vv = 0.f;
-                if (r < L) vv = to_f32(v[(static_cast<size_t>(cs + r) * num_heads + h) * D + col0 + l16]);
-                sY[r * kDVT + l16] = sbeta[r] * (vv - Z[j]);
+                sY[r * kDVT + l16] = sbeta[r] * (sV[r * kDVT + l16] - Z[j]);
             }
         }
         __syncthreads();
+        KDA_PHASE_MARK(8);
 
         // ---- off-diagonal blocks of X, one block distance at a time ----
 #pragma unroll
@@ -278,6 +329,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 for (int j = 0; j < 4; ++j) T[(4 * l4 + j) * 17 + l16] = acc[j];
             }
             __syncthreads();
+        KDA_PHASE_MARK(9);
             if (active) {
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -288,6 +340,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 for (int j = 0; j < 4; ++j) sX[(16 * R + 4 * l4 + j) * kSC + 16 * I + l16] = -acc[j];
             }
             __syncthreads();
+        KDA_PHASE_MARK(10);
         }
 
         // ---- Delta = X Y for row block R = wave ----
@@ -302,9 +355,11 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             }
         }
         __syncthreads();
+        KDA_PHASE_MARK(11);
 #pragma unroll
         for (int j = 0; j < 4; ++j) sY[(16 * wave + 4 * l4 + j) * kDVT + l16] = Dl[j];
         __syncthreads();
+        KDA_PHASE_MARK(12);
 
         // ---- O = Oq + P Delta, written out ----
         {
@@ -340,6 +395,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             for (int j = 0; j < 4; ++j) sS[(16 * cb + 4 * l4 + j) * kDVT + l16] = Sacc[b][j];
         }
         __syncthreads();
+        KDA_PHASE_MARK(13);
     }
 
     if (final_state) {
@@ -351,6 +407,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 final_state[head_state + (16 * cb + 4 * l4 + j) * D + col0 + l16] = Sacc[b][j];
         }
     }
+    KDA_PHASE_END;
 }
 
 template <int D, typename TIn, typename TOut>
@@ -377,6 +434,7 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
+    if (a.qkv_bf16 && a.head_dim == 128) return launch_prefill_bf16(a, stream);
     return a.head_dim == 128 ? launch_prefill_d<128>(a, stream) : launch_prefill_d<64>(a, stream);
 }
 
