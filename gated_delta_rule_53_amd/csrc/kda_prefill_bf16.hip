@@ -42,36 +42,39 @@ constexpr int DVT = 16;     // value columns per workgroup
 constexpr int NT = 512;     // threads per workgroup
 constexpr int SW = D + 8;   // bf16 row stride of 128-wide planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide planes
-constexpr int SF = C + 1;   // fp32 row stride of the inverse
-constexpr int SL = C + 8;   // fp32 row stride of I + A
 
 // LDS map (bytes).  Region A holds Kg/Qg during the contraction phase and
-// Ki^T, P', Delta'^T and inverse scratch afterwards.
-constexpr int PLANE_W = C * SW * 2;                  // 17408
+// P', Delta'^T and the substitution scratch afterwards.
+constexpr int PLANE_W = C * SW * 2;                  // 17408: [64][SW] bf16
+constexpr int PLANE_N = C * SN * 2;                  // 9216:  [64][SN] bf16
 constexpr int OFF_KGH = 0;
 constexpr int OFF_KGL = OFF_KGH + PLANE_W;
 constexpr int OFF_QGH = OFF_KGL + PLANE_W;
 constexpr int OFF_QGL = OFF_QGH + PLANE_W;
 constexpr int REGION_A = 4 * PLANE_W;                // 69632
-constexpr int OFF_KTH = 0;                           // Ki^T [128][SN]
-constexpr int OFF_KTL = OFF_KTH + D * SN * 2;
-constexpr int OFF_PH = OFF_KTL + D * SN * 2;         // P' [64][SN]
-constexpr int OFF_PL = OFF_PH + C * SN * 2;
-constexpr int OFF_DH = OFF_PL + C * SN * 2;          // Delta'^T [16][SN]
+constexpr int OFF_PH = 0;                            // P' [64][SN]
+constexpr int OFF_PL = OFF_PH + PLANE_N;
+constexpr int OFF_DH = OFF_PL + PLANE_N;             // Delta'^T [16][SN]
 constexpr int OFF_DL = OFF_DH + DVT * SN * 2;
-constexpr int OFF_TS = OFF_DL + DVT * SN * 2;        // 4 x 16x17 fp32 scratch
-static_assert(OFF_TS + 4 * 16 * 17 * 4 <= REGION_A, "region A overflow");
+constexpr int TT_STRIDE = 24;                        // bf16 row stride of T^T [16][24]
+constexpr int OFF_TTH = OFF_DL + DVT * SN * 2;
+constexpr int OFF_TTL = OFF_TTH + DVT * TT_STRIDE * 2;
+static_assert(OFF_TTL + DVT * TT_STRIDE * 2 <= REGION_A, "region A overflow");
 constexpr int OFF_KIH = REGION_A;                    // Ki [64][SW]
 constexpr int OFF_KIL = OFF_KIH + PLANE_W;
-constexpr int OFF_L = OFF_KIL + PLANE_W;             // I + A fp32 [64][SL], later X'
-constexpr int OFF_XH = OFF_L;
-constexpr int OFF_XL = OFF_XH + C * SN * 2;
-constexpr int OFF_XF = OFF_L + C * SL * 4;           // X fp32 [64][SF]; early: wave totals
-constexpr int OFF_SPH = OFF_XF + C * SF * 4;         // (e^{G_m} S)^T [16][SW]
+constexpr int OFF_AH = OFF_KIL + PLANE_W;            // A' off-diagonal blocks [64][SN]
+constexpr int OFF_AL = OFF_AH + PLANE_N;
+constexpr int LD_STRIDE = 20;                        // fp32 row stride of the diagonal blocks
+constexpr int OFF_LDT = OFF_AL + PLANE_N;            // L' diagonal blocks, transposed: [4][16][20] fp32
+constexpr int XD_STRIDE = 24;                        // bf16 row stride of the diagonal inverses
+constexpr int OFF_XDH = OFF_LDT + 4 * 16 * LD_STRIDE * 4;   // [4][16][24] bf16
+constexpr int OFF_XDL = OFF_XDH + 4 * 16 * XD_STRIDE * 2;
+constexpr int OFF_SPH = OFF_XDL + 4 * 16 * XD_STRIDE * 2;   // (e^{G_m} S)^T [16][SW]
 constexpr int OFF_SPL = OFF_SPH + DVT * SW * 2;
-constexpr int OFF_YH = OFF_SPL + DVT * SW * 2;       // Y^T [16][SN]
-constexpr int OFF_YL = OFF_YH + DVT * SN * 2;
-constexpr int OFF_RK = OFF_YL + DVT * SN * 2;        // fp32 [64]
+constexpr int YS = DVT + 1;                          // fp32 row stride of Y'
+constexpr int OFF_Y = OFF_SPL + DVT * SW * 2;        // Y' [64][17] fp32
+constexpr int OFF_WT = OFF_Y + C * YS * 4;           // wave totals of g [8][128] fp32
+constexpr int OFF_RK = OFF_WT + 8 * D * 4;           // fp32 [64]
 constexpr int OFF_RQ = OFF_RK + C * 4;
 constexpr int OFF_BETA = OFF_RQ + C * 4;
 constexpr int OFF_EM = OFF_BETA + C * 4;             // fp32 [128] exp(G_m)
@@ -79,7 +82,6 @@ constexpr int OFF_EL = OFF_EM + D * 4;               // exp(G_last - G_m)
 constexpr int OFF_GL = OFF_EL + D * 4;               // exp(G_last)
 constexpr int LDS_BYTES = OFF_GL + D * 4;
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
-static_assert(C * SN * 4 <= C * SL * 4, "X' must fit in the I + A buffer");
 
 __device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
@@ -96,9 +98,26 @@ __device__ __forceinline__ bf16x8 ld8(const unsigned char* smem, int off_bytes) 
     return *reinterpret_cast<const bf16x8*>(smem + off_bytes);
 }
 
+// Operand fragment or zeros (for K ranges that lie past the valid rows).
+__device__ __forceinline__ bf16x8 ld8_if(const unsigned char* smem, int off_bytes, bool valid) {
+    const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    return valid ? ld8(smem, off_bytes) : z;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
-// Split 8 floats into bf16 hi and lo parts.
+__device__ __forceinline__ floatx8 unpack8(const uint4& w) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    floatx8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+    return f;
+}
+
+// Split floats into bf16 hi and lo parts (x = hi + lo to about 2^-17 relative).
 __device__ __forceinline__ void split8(const floatx8& x, bf16x8& hi, bf16x8& lo) {
     hi = __builtin_convertvector(x, bf16x8);
     const floatx8 hf = __builtin_convertvector(hi, floatx8);
@@ -111,9 +130,70 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
     lo = __builtin_convertvector(x - hf, bf16x4);
 }
 
-// Row blocks and (row, column) block pairs of the 64x64 products, per wave.
-// Units: Z_R (even waves) / Oq_R (odd waves) for R = wave / 2, plus up to two
-// (R, I) blocks of A and P.  Balances MFMA work across the four SIMDs.
+// Z_R = Kg_R (e^{G_m} S) (kg = true) or Oq_R = Qg_R (e^{G_m} S): one 16x16
+// tile, K = 128 channels.  R is uniform across the wave.
+__device__ __forceinline__ floatx4 unit_zo(const unsigned char* smem, int R, bool kg, int l16, int l4) {
+    const int AH = kg ? OFF_KGH : OFF_QGH, AL = kg ? OFF_KGL : OFF_QGL;
+    const int ar = (16 * R + l16) * SW;
+    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int ko = 32 * s + 8 * l4;
+        acc = mma3(ld8(smem, AH + (ar + ko) * 2), ld8(smem, AL + (ar + ko) * 2),
+                   ld8(smem, OFF_SPH + (l16 * SW + ko) * 2), ld8(smem, OFF_SPL + (l16 * SW + ko) * 2), acc);
+    }
+    return acc;
+}
+
+// Block (R, I) of A' = diag(beta rk^2) (Kg Ki^T) and of P' = diag(rq) (Qg Ki^T).
+// Off-diagonal A' blocks go to the bf16 hi/lo planes, the diagonal ones
+// (unit diagonal added, upper part zero) to the fp32 transposed store.
+// Returns the P' block (masked to i <= r) in accumulator layout.
+__device__ __forceinline__ floatx4 unit_ap(unsigned char* smem, int R, int I, int l16, int l4) {
+    const float* srk = reinterpret_cast<const float*>(smem + OFF_RK);
+    const float* srq = reinterpret_cast<const float*>(smem + OFF_RQ);
+    const float* sbeta = reinterpret_cast<const float*>(smem + OFF_BETA);
+    const int ar = (16 * R + l16) * SW, br = (16 * I + l16) * SW;
+    floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+        const int ko = 32 * s + 8 * l4;
+        const bf16x8 bh = ld8(smem, OFF_KIH + (br + ko) * 2);
+        const bf16x8 bl = ld8(smem, OFF_KIL + (br + ko) * 2);
+        accA = mma(ld8(smem, OFF_KGH + (ar + ko) * 2), bh, accA);
+        accP = mma3(ld8(smem, OFF_QGH + (ar + ko) * 2), ld8(smem, OFF_QGL + (ar + ko) * 2), bh, bl, accP);
+    }
+    floatx4 a, pv;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * R + 4 * l4 + j;
+        const float rk = srk[r];
+        a[j] = sbeta[r] * rk * rk * accA[j];
+        pv[j] = srq[r] * accP[j];
+    }
+    if (I < R) {
+        bf16x4 hi, lo;
+        split4(a, hi, lo);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * R + 4 * l4 + j;
+            reinterpret_cast<__bf16*>(smem + OFF_AH)[r * SN + 16 * I + l16] = hi[j];
+            reinterpret_cast<__bf16*>(smem + OFF_AL)[r * SN + 16 * I + l16] = lo[j];
+        }
+    } else {
+        // local row 4*l4 + j, local column l16
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int lr = 4 * l4 + j;
+            a[j] = l16 < lr ? a[j] : (l16 == lr ? 1.f : 0.f);
+            pv[j] = l16 <= lr ? pv[j] : 0.f;
+        }
+        *reinterpret_cast<floatx4*>(smem + OFF_LDT + ((R * 16 + l16) * LD_STRIDE + 4 * l4) * 4) = a;
+    }
+    return pv;
+}
+
+// (R, I) blocks whose P' each wave holds after the contraction phase.
 __constant__ int8_t kPairs[8][2][2] = {
     {{0, 0}, {-1, -1}}, {{3, 1}, {-1, -1}}, {{1, 0}, {-1, -1}}, {{1, 1}, {-1, -1}},
     {{2, 0}, {2, 1}},   {{2, 2}, {-1, -1}}, {{3, 0}, {-1, -1}}, {{3, 2}, {3, 3}},
@@ -129,10 +209,8 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
     float* final_state, int64_t total_tokens, int num_seqs, int num_heads, float scale,
     int l2norm) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
-    float* sL = reinterpret_cast<float*>(smem + OFF_L);
-    float* sXf = reinterpret_cast<float*>(smem + OFF_XF);
-    float* sWT = sXf;  // wave totals of the log-decay, [8][128], before the inverse
-    float* sTS = reinterpret_cast<float*>(smem + OFF_TS);
+    float* sY = reinterpret_cast<float*>(smem + OFF_Y);
+    float* sWT = reinterpret_cast<float*>(smem + OFF_WT);
     float* srk = reinterpret_cast<float*>(smem + OFF_RK);
     float* srq = reinterpret_cast<float*>(smem + OFF_RQ);
     float* sbeta = reinterpret_cast<float*>(smem + OFF_BETA);
@@ -152,6 +230,7 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
 
     // State tile: wave w owns rows 16w..16w+15 (accumulator layout).
     const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
+    KDA_PHASE_BEGIN
     floatx4 Sacc;
 #pragma unroll
     for (int j = 0; j < 4; ++j)
@@ -159,15 +238,14 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
 
     // Prefetch mapping: thread (rp, cc) holds rows 2rp, 2rp+1 and channels
     // 8cc..8cc+7 of k, q, g.  Even waves also hold the value entries they
-    // need for Y = beta (V - Z), threads < 64 one beta.
-    const int rp = tid >> 4, cc = tid & 15;
+    // need for Y' (rows 16*(wave/2) + 4*l4 + j, column l16), threads < 64 one beta.
     uint4 pk[2], pq[2];
-    floatx4 pg[2][2];
+    floatx4 pg[4];
     uint16_t pv[4];
     float pb = 0.f;
     const bool zwave = (wave & 1) == 0;
     const int zR = wave >> 1;
-    auto fetch = [&](int64_t c0) {
+    auto fetch = [&](int64_t c0, int rp, int cc, int l16, int l4, int tid) {
         const int Ln = static_cast<int>(min<int64_t>(C, t1 - c0));
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
@@ -176,13 +254,13 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
                 const size_t off = (static_cast<size_t>(c0 + r) * num_heads + h) * D + 8 * cc;
                 pk[j] = *reinterpret_cast<const uint4*>(k + off);
                 pq[j] = *reinterpret_cast<const uint4*>(q + off);
-                pg[j][0] = *reinterpret_cast<const floatx4*>(g + off);
-                pg[j][1] = *reinterpret_cast<const floatx4*>(g + off + 4);
+                pg[2 * j] = *reinterpret_cast<const floatx4*>(g + off);
+                pg[2 * j + 1] = *reinterpret_cast<const floatx4*>(g + off + 4);
             } else {
                 pk[j] = uint4{0, 0, 0, 0};
                 pq[j] = uint4{0, 0, 0, 0};
-                pg[j][0] = floatx4{0.f, 0.f, 0.f, 0.f};
-                pg[j][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                pg[2 * j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                pg[2 * j + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
             }
         }
         if (zwave) {
@@ -195,64 +273,48 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
         }
         if (tid < C) pb = tid < Ln ? beta[static_cast<size_t>(c0 + tid) * num_heads + h] : 0.f;
     };
-    if (t0 < t1) fetch(t0);
+    if (t0 < t1) fetch(t0, tid >> 4, tid & 15, l16, l4, tid);
 
     for (int64_t cs = t0; cs < t1; cs += C) {
         const int L = static_cast<int>(min<int64_t>(C, t1 - cs));
+        // Lane indices are re-materialised opaquely every chunk so that the
+        // compiler cannot hoist lane-dependent constants (masks, addresses,
+        // unit vectors) out of the loop; kept live across it they would be
+        // spilled to scratch.
+        int lane_o;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(lane_o) : "v"(lane));
+        const int l16 = lane_o & 15, l4 = lane_o >> 4;
+        const int tid = wave * 64 + lane_o;
+        const int rp = tid >> 4, cc = tid & 15;
 
         // ================= phase 1: per-element operands =================
-        floatx8 kf[2], qf[2], gf[2];
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const uint32_t kw[4] = {pk[j].x, pk[j].y, pk[j].z, pk[j].w};
-            const uint32_t qw[4] = {pq[j].x, pq[j].y, pq[j].z, pq[j].w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                kf[j][2 * i] = __uint_as_float(kw[i] << 16);
-                kf[j][2 * i + 1] = __uint_as_float(kw[i] & 0xffff0000u);
-                qf[j][2 * i] = __uint_as_float(qw[i] << 16);
-                qf[j][2 * i + 1] = __uint_as_float(qw[i] & 0xffff0000u);
-            }
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                gf[j][i] = pg[j][0][i];
-                gf[j][4 + i] = pg[j][1][i];
-            }
-        }
-        float vv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) vv[j] = bf2f(pv[j]);
-        const float bcur = pb;
-
         // Row norms: the 16 lanes of a row pair share rows 2rp, 2rp+1.
-        float rkr[2], rqr[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
+            const floatx8 kf = unpack8(pk[j]), qf = unpack8(pq[j]);
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                sk += kf[j][i] * kf[j][i];
-                sq += qf[j][i] * qf[j][i];
+                sk += kf[i] * kf[i];
+                sq += qf[i] * qf[i];
             }
 #pragma unroll
             for (int off = 1; off < 16; off <<= 1) {
                 sk += __shfl_xor(sk, off, 64);
                 sq += __shfl_xor(sq, off, 64);
             }
-            rkr[j] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
-            rqr[j] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
+            if (cc == 0) {
+                srk[2 * rp + j] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+                srq[2 * rp + j] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
+            }
         }
-        if (cc == 0) {
-            srk[2 * rp] = rkr[0];
-            srk[2 * rp + 1] = rkr[1];
-            srq[2 * rp] = rqr[0];
-            srq[2 * rp + 1] = rqr[1];
-        }
-        if (tid < C) sbeta[tid] = bcur;
+        if (tid < C) sbeta[tid] = pb;
 
-        // Cumulative log-decay: pair sums, scan over the wave's four pairs,
-        // then wave totals through LDS.
-        floatx8 pair = gf[0] + gf[1];
+        // Cumulative log-decay: pair sums, scan over the wave's four row
+        // pairs, then wave totals through LDS.
+        const floatx8 g0 = {pg[0][0], pg[0][1], pg[0][2], pg[0][3], pg[1][0], pg[1][1], pg[1][2], pg[1][3]};
+        const floatx8 g1 = {pg[2][0], pg[2][1], pg[2][2], pg[2][3], pg[3][0], pg[3][1], pg[3][2], pg[3][3]};
+        const floatx8 pair = g0 + g1;
         floatx8 incl = pair;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -267,49 +329,32 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
         }
         __syncthreads();
 
-        floatx8 carry = {0, 0, 0, 0, 0, 0, 0, 0}, gm = carry, glast = carry;
+        // cm = (sum of the totals of earlier waves) - G_m, per channel.
+        floatx8 cm = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int w2 = 0; w2 < 8; ++w2) {
             const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc);
             const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc + 4);
             const floatx8 t = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-            glast += t;
-            if (w2 < 4) gm += t;
-            if (w2 < wave) carry += t;
+            if (w2 < wave) cm += t;
+            if (w2 < 4) cm -= t;
         }
-        const floatx8 G0 = carry + (incl - pair) + gf[0];
-        const floatx8 G1 = G0 + gf[1];
-        bf16x8 kih[2], kil[2];  // Ki hi/lo kept for the transposed copy
+        // Exponents (log2 units) of E = exp(G - G_m) for rows 2rp and 2rp+1.
+        const floatx8 d0 = (cm + (incl - pair) + g0) * kLog2e;
+        const floatx8 d1 = d0 + g1 * kLog2e;
+        if (tid < 3 * D) {
+            // per-channel factors: thread t computes factor t / 128 of channel t % 128
+            const int c = tid & (D - 1), which = tid >> 7;
+            float gm = 0.f, gl = 0.f;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 2 * rp + j;
-            const floatx8 d = ((j == 0 ? G0 : G1) - gm) * kLog2e;
-            floatx8 e, ei;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                e[i] = fast_exp2(d[i]);
-                ei[i] = fast_exp2(-d[i]);
+            for (int w2 = 0; w2 < 8; ++w2) {
+                const float t = sWT[w2 * D + c];
+                gl += t;
+                if (w2 < 4) gm += t;
             }
-            const int o = (r * SW + 8 * cc) * 2;
-            bf16x8 hi, lo;
-            split8(kf[j] * e, hi, lo);
-            *reinterpret_cast<bf16x8*>(smem + OFF_KGH + o) = hi;
-            *reinterpret_cast<bf16x8*>(smem + OFF_KGL + o) = lo;
-            split8(qf[j] * e, hi, lo);
-            *reinterpret_cast<bf16x8*>(smem + OFF_QGH + o) = hi;
-            *reinterpret_cast<bf16x8*>(smem + OFF_QGL + o) = lo;
-            split8(kf[j] * ei, kih[j], kil[j]);
-            *reinterpret_cast<bf16x8*>(smem + OFF_KIH + o) = kih[j];
-            *reinterpret_cast<bf16x8*>(smem + OFF_KIL + o) = kil[j];
-        }
-        if (rp == 0) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int c = 8 * cc + i;
-                sEm[c] = fast_exp2(gm[i] * kLog2e);
-                sEL[c] = fast_exp2((glast[i] - gm[i]) * kLog2e);
-                sGL[c] = fast_exp2(glast[i] * kLog2e);
-            }
+            const float ex = which == 0 ? gm : (which == 1 ? gl - gm : gl);
+            float* dst = which == 0 ? sEm : (which == 1 ? sEL : sGL);
+            dst[c] = fast_exp2(ex * kLog2e);
         }
         // (e^{G_m} S)^T for this wave's 16 state rows.
         {
@@ -324,75 +369,65 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
             *reinterpret_cast<bf16x4*>(smem + OFF_SPH + (l16 * SW + 16 * wave + 4 * l4) * 2) = hi;
             *reinterpret_cast<bf16x4*>(smem + OFF_SPL + (l16 * SW + 16 * wave + 4 * l4) * 2) = lo;
         }
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int o = ((2 * rp + j) * SW + 8 * cc) * 2;
+            const floatx8 d = j == 0 ? d0 : d1;
+            floatx8 e, ei;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                e[i] = fast_exp2(d[i]);
+                ei[i] = fast_exp2(-d[i]);
+            }
+            const floatx8 kf = unpack8(pk[j]), qf = unpack8(pq[j]);
+            bf16x8 hi, lo;
+            split8(kf * e, hi, lo);
+            *reinterpret_cast<bf16x8*>(smem + OFF_KGH + o) = hi;
+            *reinterpret_cast<bf16x8*>(smem + OFF_KGL + o) = lo;
+            split8(qf * e, hi, lo);
+            *reinterpret_cast<bf16x8*>(smem + OFF_QGH + o) = hi;
+            *reinterpret_cast<bf16x8*>(smem + OFF_QGL + o) = lo;
+            split8(kf * ei, hi, lo);
+            *reinterpret_cast<bf16x8*>(smem + OFF_KIH + o) = hi;
+            *reinterpret_cast<bf16x8*>(smem + OFF_KIL + o) = lo;
+            __builtin_amdgcn_sched_barrier(0);  // keep the two rows' temporaries apart
+        }
+        float vv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) vv[j] = bf2f(pv[j]);
+        // The raw inputs are consumed: the next chunk's loads fly from here on.
+        if (cs + C < t1) fetch(cs + C, rp, cc, l16, l4, tid);
         __syncthreads();
-
-        // The next chunk's loads fly while this one is contracted.
-        if (cs + C < t1) fetch(cs + C);
+        KDA_PHASE_MARK(1);
 
         // ================= phase 2: contractions over channels =================
-        floatx4 Oq = {0.f, 0.f, 0.f, 0.f};
-        floatx4 Pacc[2];
+        floatx4 zo = {0.f, 0.f, 0.f, 0.f}, pa0 = zo, pa1 = zo;
+        zo = unit_zo(smem, zR, zwave, l16, l4);
         {
-            const int R = zR;
-            const int ar = (16 * R + l16) * SW;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int ah = zwave ? OFF_KGH : OFF_QGH, al = zwave ? OFF_KGL : OFF_QGL;
-#pragma unroll 1
-            for (int s = 0; s < 4; ++s) {
-                const int ko = 32 * s + 8 * l4;
-                acc = mma3(ld8(smem, ah + (ar + ko) * 2), ld8(smem, al + (ar + ko) * 2),
-                           ld8(smem, OFF_SPH + (l16 * SW + ko) * 2), ld8(smem, OFF_SPL + (l16 * SW + ko) * 2), acc);
-            }
-            if (zwave) {
-                // Y = beta (V - rk Z), stored transposed as bf16 hi/lo
-                floatx4 y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int r = 16 * R + 4 * l4 + j;
-                    y[j] = sbeta[r] * (vv[j] - srk[r] * acc[j]);
-                }
-                bf16x4 hi, lo;
-                split4(y, hi, lo);
-                *reinterpret_cast<bf16x4*>(smem + OFF_YH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
-                *reinterpret_cast<bf16x4*>(smem + OFF_YL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
-            } else {
-                Oq = acc;
-            }
+            const int R0 = kPairs[wave][0][0], I0 = kPairs[wave][0][1];
+            pa0 = unit_ap(smem, R0, I0, l16, l4);
+            const int R1 = kPairs[wave][1][0], I1 = kPairs[wave][1][1];
+            if (R1 >= 0) pa1 = unit_ap(smem, R1, I1, l16, l4);
         }
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int R = kPairs[wave][u][0], I = kPairs[wave][u][1];
-            Pacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-            if (R < 0) continue;
-            floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
-            const int ar = (16 * R + l16) * SW, br = (16 * I + l16) * SW;
-#pragma unroll 1
-            for (int s = 0; s < 4; ++s) {
-                const int ko = 32 * s + 8 * l4;
-                const bf16x8 bh = ld8(smem, OFF_KIH + (br + ko) * 2);
-                const bf16x8 bl = ld8(smem, OFF_KIL + (br + ko) * 2);
-                accA = mma(ld8(smem, OFF_KGH + (ar + ko) * 2), bh, accA);
-                accP = mma3(ld8(smem, OFF_QGH + (ar + ko) * 2), ld8(smem, OFF_QGL + (ar + ko) * 2), bh, bl, accP);
-            }
-            const int i = 16 * I + l16;
-            const float rki = srk[i];
+        if (zwave) {
+            // Y' = rk beta (V - rk Z), kept in fp32 for the substitution
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * l4 + j;
-                const bool below = I < R || i < r;
-                sL[r * SL + i] = below ? sbeta[r] * srk[r] * rki * accA[j] : (i == r ? 1.f : 0.f);
-                Pacc[u][j] = (I < R || i <= r) ? srq[r] * accP[j] : 0.f;
+                const int r = 16 * zR + 4 * l4 + j;
+                const float rk = srk[r];
+                sY[r * YS + l16] = rk * sbeta[r] * (vv[j] - rk * zo[j]);
             }
         }
         __syncthreads();
+        KDA_PHASE_MARK(2);
 
-        // ================= phase 3: inverse of I + A; P', Ki^T =================
+        // ================= phase 3: P', diagonal inverses =================
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
             const int R = kPairs[wave][u][0], I = kPairs[wave][u][1];
             if (R < 0) continue;
             bf16x4 hi, lo;
-            split4(Pacc[u], hi, lo);
+            split4(u == 0 ? pa0 : pa1, hi, lo);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * R + 4 * l4 + j;
@@ -400,108 +435,98 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
                 reinterpret_cast<__bf16*>(smem + OFF_PL)[r * SN + 16 * I + l16] = lo[j];
             }
         }
-        // Blocks (0,1) and (2,3) lie inside the K range of the 32-wide MFMA
-        // steps of rows 0-15 and 32-47; they must read as zero.
-        if (tid < 128) {
-            const int blk = tid >> 6, row = (tid >> 2) & 15, part = tid & 3;
-            const int r = (blk ? 32 : 0) + row, c0 = (blk ? 48 : 16) + 4 * part;
-            const bf16x4 z = {0, 0, 0, 0};
-            *reinterpret_cast<bf16x4*>(smem + OFF_PH + (r * SN + c0) * 2) = z;
-            *reinterpret_cast<bf16x4*>(smem + OFF_PL + (r * SN + c0) * 2) = z;
-        }
-        // Ki^T [c][r] from this thread's two rows.
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int c = 8 * cc + i;
-            const bf16x2 hi = {kih[0][i], kih[1][i]};
-            const bf16x2 lo = {kil[0][i], kil[1][i]};
-            *reinterpret_cast<bf16x2*>(smem + OFF_KTH + (c * SN + 2 * rp) * 2) = hi;
-            *reinterpret_cast<bf16x2*>(smem + OFF_KTL + (c * SN + 2 * rp) * 2) = lo;
-        }
-        // Diagonal 16x16 blocks by forward substitution: lane (block l4, column l16).
         if (wave == 0) {
-            const int B = l4, jcol = l16;
+            // Lane (block l4, column l16): forward substitution L'_BB x = e_j.
+            // Row p of the transposed store is column p of the block.
+            const float* ldt = reinterpret_cast<const float*>(smem + OFF_LDT) + l4 * 16 * LD_STRIDE;
             float x[16];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) x[m] = (m == jcol) ? 1.f : 0.f;
+            for (int m = 0; m < 16; ++m) x[m] = (m == l16) ? 1.f : 0.f;
+            // Four columns per step: finish x[p0..p0+3] inside their 4x4
+            // block, then eliminate them from all later rows.
 #pragma unroll
-            for (int p = 0; p < 15; ++p) {
+            for (int p0 = 0; p0 < 16; p0 += 4) {
+                floatx4 col[4][4];  // col[t][qd]: column p0 + t of the block, rows 4qd..4qd+3
 #pragma unroll
-                for (int m = p + 1; m < 16; ++m) x[m] -= sL[(16 * B + m) * SL + 16 * B + p] * x[p];
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int qd = p0 / 4; qd < 4; ++qd)
+                        col[t][qd] = *reinterpret_cast<const floatx4*>(ldt + (p0 + t) * LD_STRIDE + 4 * qd);
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+#pragma unroll
+                    for (int m = p0 + t + 1; m < p0 + 4; ++m) x[m] -= col[t][m >> 2][m & 3] * x[p0 + t];
+#pragma unroll
+                for (int m = p0 + 4; m < 16; ++m)
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) x[m] -= col[t][m >> 2][m & 3] * x[p0 + t];
                 __builtin_amdgcn_sched_barrier(0);
             }
 #pragma unroll
-            for (int m = 0; m < 16; ++m) sXf[(16 * B + m) * SF + 16 * B + jcol] = x[m];
+            for (int m = 0; m < 16; ++m) {
+                const __bf16 hi = static_cast<__bf16>(x[m]);
+                const __bf16 lo = static_cast<__bf16>(x[m] - static_cast<float>(hi));
+                reinterpret_cast<__bf16*>(smem + OFF_XDH)[(l4 * 16 + m) * XD_STRIDE + l16] = hi;
+                reinterpret_cast<__bf16*>(smem + OFF_XDL)[(l4 * 16 + m) * XD_STRIDE + l16] = lo;
+            }
         }
         __syncthreads();
-        // Off-diagonal blocks: X_RI = -X_RR sum_{J=I}^{R-1} L_RJ X_JI, by block distance.
-#pragma unroll
-        for (int dist = 1; dist < 4; ++dist) {
-            const bool active = wave < 4 - dist;
-            const int I = wave, R = wave + dist;
-            float* T = sTS + wave * 16 * 17;
-            if (active) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                for (int J = I; J < R; ++J) {
-#pragma unroll
-                    for (int k0 = 0; k0 < 16; k0 += 4)
-                        acc = mfma_f32_16x16x4(sL[(16 * R + l16) * SL + 16 * J + k0 + l4],
-                                               sXf[(16 * J + k0 + l4) * SF + 16 * I + l16], acc);
-                }
-#pragma unroll
-                for (int j = 0; j < 4; ++j) T[(4 * l4 + j) * 17 + l16] = acc[j];
-            }
-            __syncthreads();
-            if (active) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int k0 = 0; k0 < 16; k0 += 4)
-                    acc = mfma_f32_16x16x4(sXf[(16 * R + l16) * SF + 16 * R + k0 + l4], T[(k0 + l4) * 17 + l16], acc);
-#pragma unroll
-                for (int j = 0; j < 4; ++j) sXf[(16 * R + 4 * l4 + j) * SF + 16 * I + l16] = -acc[j];
-            }
-            __syncthreads();
-        }
-        // X' = diag(rk) X, lower triangle, as bf16 hi/lo (over the dead I + A buffer).
-        {
-            const int r = tid >> 3, c0 = 8 * (tid & 7);
-            const float rk = srk[r];
-            floatx8 xv;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) xv[i] = (c0 + i <= r) ? rk * sXf[r * SF + c0 + i] : 0.f;
-            bf16x8 hi, lo;
-            split8(xv, hi, lo);
-            *reinterpret_cast<bf16x8*>(smem + OFF_XH + (r * SN + c0) * 2) = hi;
-            *reinterpret_cast<bf16x8*>(smem + OFF_XL + (r * SN + c0) * 2) = lo;
-        }
-        __syncthreads();
+        KDA_PHASE_MARK(3);
 
-        // ================= phase 4: Delta', O, state =================
-        if (wave < 4) {
-            const int R = wave, ns = R < 2 ? 1 : 2;
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int s = 0; s < ns; ++s) {
-                const int ko = 32 * s + 8 * l4;
-                acc = mma3(ld8(smem, OFF_XH + ((16 * R + l16) * SN + ko) * 2),
-                           ld8(smem, OFF_XL + ((16 * R + l16) * SN + ko) * 2),
-                           ld8(smem, OFF_YH + (l16 * SN + ko) * 2), ld8(smem, OFF_YL + (l16 * SN + ko) * 2), acc);
+        // ================= phase 4: Delta' by block forward substitution =================
+        // Delta'_R = X_RR (Y'_R - sum_{J<R} A'_RJ Delta'_J); one wave, LDS hand-off within it.
+        if (wave == 0) {
+#pragma unroll
+            for (int R = 0; R < 4; ++R) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (32 * s >= 16 * R) continue;
+                    const int ko = 32 * s + 8 * l4;
+                    const bool ok = ko < 16 * R;
+                    acc = mma3(ld8_if(smem, OFF_AH + ((16 * R + l16) * SN + ko) * 2, ok),
+                               ld8_if(smem, OFF_AL + ((16 * R + l16) * SN + ko) * 2, ok),
+                               ld8_if(smem, OFF_DH + (l16 * SN + ko) * 2, ok),
+                               ld8_if(smem, OFF_DL + (l16 * SN + ko) * 2, ok), acc);
+                }
+                floatx4 t;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) t[j] = sY[(16 * R + 4 * l4 + j) * YS + l16] - acc[j];
+                bf16x4 hi, lo;
+                split4(t, hi, lo);
+                *reinterpret_cast<bf16x4*>(smem + OFF_TTH + (l16 * TT_STRIDE + 4 * l4) * 2) = hi;
+                *reinterpret_cast<bf16x4*>(smem + OFF_TTL + (l16 * TT_STRIDE + 4 * l4) * 2) = lo;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+                const bool ok = l4 < 2;
+                const int xo = ((R * 16 + l16) * XD_STRIDE + 8 * l4) * 2;
+                const int to = (l16 * TT_STRIDE + 8 * l4) * 2;
+                floatx4 dl = {0.f, 0.f, 0.f, 0.f};
+                dl = mma3(ld8_if(smem, OFF_XDH + xo, ok), ld8_if(smem, OFF_XDL + xo, ok),
+                          ld8_if(smem, OFF_TTH + to, ok), ld8_if(smem, OFF_TTL + to, ok), dl);
+                split4(dl, hi, lo);
+                *reinterpret_cast<bf16x4*>(smem + OFF_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
+                *reinterpret_cast<bf16x4*>(smem + OFF_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
+                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
-            bf16x4 hi, lo;
-            split4(acc, hi, lo);
-            *reinterpret_cast<bf16x4*>(smem + OFF_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
-            *reinterpret_cast<bf16x4*>(smem + OFF_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
         }
         __syncthreads();
+        KDA_PHASE_MARK(4);
+
+        // ================= phase 5: output and state =================
         if (!zwave) {
-            const int R = zR, ns = R < 2 ? 1 : 2;
+            const int R = zR;
             floatx4 acc;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j] = srq[16 * R + 4 * l4 + j] * Oq[j];
-            for (int s = 0; s < ns; ++s) {
+            for (int j = 0; j < 4; ++j) acc[j] = srq[16 * R + 4 * l4 + j] * zo[j];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                if (32 * s > 16 * R) continue;
                 const int ko = 32 * s + 8 * l4;
-                acc = mma3(ld8(smem, OFF_PH + ((16 * R + l16) * SN + ko) * 2),
-                           ld8(smem, OFF_PL + ((16 * R + l16) * SN + ko) * 2),
-                           ld8(smem, OFF_DH + (l16 * SN + ko) * 2), ld8(smem, OFF_DL + (l16 * SN + ko) * 2), acc);
+                const bool ok = ko < 16 * R + 16;
+                acc = mma3(ld8_if(smem, OFF_PH + ((16 * R + l16) * SN + ko) * 2, ok),
+                           ld8_if(smem, OFF_PL + ((16 * R + l16) * SN + ko) * 2, ok),
+                           ld8_if(smem, OFF_DH + (l16 * SN + ko) * 2, ok),
+                           ld8_if(smem, OFF_DL + (l16 * SN + ko) * 2, ok), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -510,13 +535,23 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
             }
         }
         {
+            // U = Ki^T Delta' for state rows c = 16 wave + (0..15).  The A operand
+            // (8 consecutive tokens of one channel) is gathered from the
+            // row-major Ki planes.
             floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-            const int cr = (16 * wave + l16) * SN;
+            const __bf16* kih = reinterpret_cast<const __bf16*>(smem + OFF_KIH);
+            const __bf16* kil = reinterpret_cast<const __bf16*>(smem + OFF_KIL);
+            const int cidx = 16 * wave + l16;
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 const int ko = 32 * s + 8 * l4;
-                acc = mma3(ld8(smem, OFF_KTH + (cr + ko) * 2), ld8(smem, OFF_KTL + (cr + ko) * 2),
-                           ld8(smem, OFF_DH + (l16 * SN + ko) * 2), ld8(smem, OFF_DL + (l16 * SN + ko) * 2), acc);
+                bf16x8 ah, al;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    ah[i] = kih[(ko + i) * SW + cidx];
+                    al[i] = kil[(ko + i) * SW + cidx];
+                }
+                acc = mma3(ah, al, ld8(smem, OFF_DH + (l16 * SN + ko) * 2), ld8(smem, OFF_DL + (l16 * SN + ko) * 2), acc);
             }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
@@ -525,6 +560,7 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
             }
         }
         __syncthreads();
+        KDA_PHASE_MARK(5);
     }
 
     if (final_state) {
@@ -532,6 +568,7 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
         for (int j = 0; j < 4; ++j)
             final_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + l16] = Sacc[j];
     }
+    KDA_PHASE_END;
 }
 
 template <typename TOut>
