@@ -44,7 +44,7 @@ constexpr int SW = D + 8;   // bf16 row stride of 128-wide planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide planes
 
 // LDS map (bytes).  Region A holds Kg/Qg during the contraction phase and
-// P', Delta'^T and the substitution scratch afterwards.
+// P', Delta'^T, the substitution operators and X Y' afterwards.
 constexpr int PLANE_W = C * SW * 2;                  // 17408: [64][SW] bf16
 constexpr int PLANE_N = C * SN * 2;                  // 9216:  [64][SN] bf16
 constexpr int OFF_KGH = 0;
@@ -56,24 +56,25 @@ constexpr int OFF_PH = 0;                            // P' [64][SN]
 constexpr int OFF_PL = OFF_PH + PLANE_N;
 constexpr int OFF_DH = OFF_PL + PLANE_N;             // Delta'^T [16][SN]
 constexpr int OFF_DL = OFF_DH + DVT * SN * 2;
-constexpr int TT_STRIDE = 24;                        // bf16 row stride of T^T [16][24]
-constexpr int OFF_TTH = OFF_DL + DVT * SN * 2;
-constexpr int OFF_TTL = OFF_TTH + DVT * TT_STRIDE * 2;
-static_assert(OFF_TTL + DVT * TT_STRIDE * 2 <= REGION_A, "region A overflow");
+constexpr int OFF_WH = OFF_DL + DVT * SN * 2;        // -X_RR A'_RJ, [64][SN]
+constexpr int OFF_WL = OFF_WH + PLANE_N;
+constexpr int YS = DVT + 1;                          // fp32 row stride of X_RR Y'_R
+constexpr int OFF_XY = OFF_WL + PLANE_N;             // X_RR Y'_R [64][17] fp32
+static_assert(OFF_XY + C * YS * 4 <= REGION_A, "region A overflow");
 constexpr int OFF_KIH = REGION_A;                    // Ki [64][SW]
 constexpr int OFF_KIL = OFF_KIH + PLANE_W;
-constexpr int OFF_AH = OFF_KIL + PLANE_W;            // A' off-diagonal blocks [64][SN]
-constexpr int OFF_AL = OFF_AH + PLANE_N;
+constexpr int OFF_ATH = OFF_KIL + PLANE_W;           // A' off-diagonal blocks, transposed [64][SN]
+constexpr int OFF_ATL = OFF_ATH + PLANE_N;
 constexpr int LD_STRIDE = 20;                        // fp32 row stride of the diagonal blocks
-constexpr int OFF_LDT = OFF_AL + PLANE_N;            // L' diagonal blocks, transposed: [4][16][20] fp32
+constexpr int OFF_LDT = OFF_ATL + PLANE_N;           // L' diagonal blocks, transposed: [4][16][20] fp32
 constexpr int XD_STRIDE = 24;                        // bf16 row stride of the diagonal inverses
 constexpr int OFF_XDH = OFF_LDT + 4 * 16 * LD_STRIDE * 4;   // [4][16][24] bf16
 constexpr int OFF_XDL = OFF_XDH + 4 * 16 * XD_STRIDE * 2;
 constexpr int OFF_SPH = OFF_XDL + 4 * 16 * XD_STRIDE * 2;   // (e^{G_m} S)^T [16][SW]
 constexpr int OFF_SPL = OFF_SPH + DVT * SW * 2;
-constexpr int YS = DVT + 1;                          // fp32 row stride of Y'
-constexpr int OFF_Y = OFF_SPL + DVT * SW * 2;        // Y' [64][17] fp32
-constexpr int OFF_WT = OFF_Y + C * YS * 4;           // wave totals of g [8][128] fp32
+constexpr int OFF_YH = OFF_SPL + DVT * SW * 2;       // Y'^T [16][SN]
+constexpr int OFF_YL = OFF_YH + DVT * SN * 2;
+constexpr int OFF_WT = OFF_YL + DVT * SN * 2;        // wave totals of g [8][128] fp32
 constexpr int OFF_RK = OFF_WT + 8 * D * 4;           // fp32 [64]
 constexpr int OFF_RQ = OFF_RK + C * 4;
 constexpr int OFF_BETA = OFF_RQ + C * 4;
@@ -104,6 +105,22 @@ __device__ __forceinline__ bf16x8 ld8_if(const unsigned char* smem, int off_byte
     return valid ? ld8(smem, off_bytes) : z;
 }
 
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load (vmcnt(0)), which would expose the full
+// latency of the next chunk's prefetch at the first barrier after it; here
+// only this wave's LDS operations are drained before s_barrier.  The memory
+// clobber keeps the compiler from moving loads or stores across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Sum over the 16 lanes of a DPP row (all lanes receive the total).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror 4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror 8
+    return x;
+}
+
 __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
 
 __device__ __forceinline__ floatx8 unpack8(const uint4& w) {
@@ -117,17 +134,36 @@ __device__ __forceinline__ floatx8 unpack8(const uint4& w) {
     return f;
 }
 
-// Split floats into bf16 hi and lo parts (x = hi + lo to about 2^-17 relative).
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+
+// Split two floats into packed bf16 hi and lo words (x = hi + lo to about
+// 2^-17 relative).  The high halves are recovered from the packed word with
+// integer ops so the rounding conversion runs once per pair.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const floatx2 xv = {x0, x1};
+    const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(xv, bf16x2v));
+    const floatx2 r = {x0 - __uint_as_float(hu << 16), x1 - __uint_as_float(hu & 0xffff0000u)};
+    hi = hu;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+}
+
 __device__ __forceinline__ void split8(const floatx8& x, bf16x8& hi, bf16x8& lo) {
-    hi = __builtin_convertvector(x, bf16x8);
-    const floatx8 hf = __builtin_convertvector(hi, floatx8);
-    lo = __builtin_convertvector(x - hf, bf16x8);
+    uint4 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
 }
 
 __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo) {
-    hi = __builtin_convertvector(x, bf16x4);
-    const floatx4 hf = __builtin_convertvector(hi, floatx4);
-    lo = __builtin_convertvector(x - hf, bf16x4);
+    uint2 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    hi = __builtin_bit_cast(bf16x4, h);
+    lo = __builtin_bit_cast(bf16x4, l);
 }
 
 // Z_R = Kg_R (e^{G_m} S) (kg = true) or Oq_R = Qg_R (e^{G_m} S): one 16x16
@@ -146,7 +182,7 @@ __device__ __forceinline__ floatx4 unit_zo(const unsigned char* smem, int R, boo
 }
 
 // Block (R, I) of A' = diag(beta rk^2) (Kg Ki^T) and of P' = diag(rq) (Qg Ki^T).
-// Off-diagonal A' blocks go to the bf16 hi/lo planes, the diagonal ones
+// Off-diagonal A' blocks go to the transposed bf16 hi/lo planes, the diagonal ones
 // (unit diagonal added, upper part zero) to the fp32 transposed store.
 // Returns the P' block (masked to i <= r) in accumulator layout.
 __device__ __forceinline__ floatx4 unit_ap(unsigned char* smem, int R, int I, int l16, int l4) {
@@ -172,14 +208,12 @@ __device__ __forceinline__ floatx4 unit_ap(unsigned char* smem, int R, int I, in
         pv[j] = srq[r] * accP[j];
     }
     if (I < R) {
+        // transposed: row = column i, four consecutive rows r per lane
         bf16x4 hi, lo;
         split4(a, hi, lo);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int r = 16 * R + 4 * l4 + j;
-            reinterpret_cast<__bf16*>(smem + OFF_AH)[r * SN + 16 * I + l16] = hi[j];
-            reinterpret_cast<__bf16*>(smem + OFF_AL)[r * SN + 16 * I + l16] = lo[j];
-        }
+        const int o = ((16 * I + l16) * SN + 16 * R + 4 * l4) * 2;
+        *reinterpret_cast<bf16x4*>(smem + OFF_ATH + o) = hi;
+        *reinterpret_cast<bf16x4*>(smem + OFF_ATL + o) = lo;
     } else {
         // local row 4*l4 + j, local column l16
 #pragma unroll
@@ -209,8 +243,7 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
     float* final_state, int64_t total_tokens, int num_seqs, int num_heads, float scale,
     int l2norm) {
     __shared__ __align__(16) unsigned char smem[LDS_BYTES];
-    float* sY = reinterpret_cast<float*>(smem + OFF_Y);
-    float* sWT = reinterpret_cast<float*>(smem + OFF_WT);
+        float* sWT = reinterpret_cast<float*>(smem + OFF_WT);
     float* srk = reinterpret_cast<float*>(smem + OFF_RK);
     float* srq = reinterpret_cast<float*>(smem + OFF_RQ);
     float* sbeta = reinterpret_cast<float*>(smem + OFF_BETA);
@@ -222,7 +255,9 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
     if (chain >= num_seqs * num_heads) return;
     const int n = chain / num_heads, h = chain % num_heads;
     const int col0 = blockIdx.y * DVT;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: wave-uniform branches and loop bounds stay scalar
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int l16 = lane & 15, l4 = lane >> 4;
 
     int64_t t0 = cu_seqlens[n], t1 = cu_seqlens[n + 1];
@@ -245,33 +280,56 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
     float pb = 0.f;
     const bool zwave = (wave & 1) == 0;
     const int zR = wave >> 1;
+    const int row_stride = num_heads * D;  // elements between consecutive tokens
     auto fetch = [&](int64_t c0, int rp, int cc, int l16, int l4, int tid) {
         const int Ln = static_cast<int>(min<int64_t>(C, t1 - c0));
+        // chunk base (wave-uniform) plus 32-bit lane offsets
+        const size_t base = (static_cast<size_t>(c0) * num_heads + h) * D;
+        const bf16_t* kb = k + base;
+        const bf16_t* qb = q + base;
+        const float* gb = g + base;
+        const bf16_t* vb = v + base + col0;
+        const float* bb = beta + static_cast<size_t>(c0) * num_heads + h;
+        if (Ln == C) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 2 * rp + j;
-            if (r < Ln) {
-                const size_t off = (static_cast<size_t>(c0 + r) * num_heads + h) * D + 8 * cc;
-                pk[j] = *reinterpret_cast<const uint4*>(k + off);
-                pq[j] = *reinterpret_cast<const uint4*>(q + off);
-                pg[2 * j] = *reinterpret_cast<const floatx4*>(g + off);
-                pg[2 * j + 1] = *reinterpret_cast<const floatx4*>(g + off + 4);
-            } else {
-                pk[j] = uint4{0, 0, 0, 0};
-                pq[j] = uint4{0, 0, 0, 0};
-                pg[2 * j] = floatx4{0.f, 0.f, 0.f, 0.f};
-                pg[2 * j + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int j = 0; j < 2; ++j) {
+                const int off = (2 * rp + j) * row_stride + 8 * cc;
+                pk[j] = *reinterpret_cast<const uint4*>(kb + off);
+                pq[j] = *reinterpret_cast<const uint4*>(qb + off);
+                pg[2 * j] = *reinterpret_cast<const floatx4*>(gb + off);
+                pg[2 * j + 1] = *reinterpret_cast<const floatx4*>(gb + off + 4);
             }
-        }
-        if (zwave) {
+            if (zwave) {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * zR + 4 * l4 + j;
-                pv[j] = r < Ln ? v[(static_cast<size_t>(c0 + r) * num_heads + h) * D + col0 + l16].bits
-                               : uint16_t(0);
+                for (int j = 0; j < 4; ++j) pv[j] = vb[(16 * zR + 4 * l4 + j) * row_stride + l16].bits;
             }
+            if (tid < C) pb = bb[tid * num_heads];
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int r = 2 * rp + j;
+                const int off = r * row_stride + 8 * cc;
+                if (r < Ln) {
+                    pk[j] = *reinterpret_cast<const uint4*>(kb + off);
+                    pq[j] = *reinterpret_cast<const uint4*>(qb + off);
+                    pg[2 * j] = *reinterpret_cast<const floatx4*>(gb + off);
+                    pg[2 * j + 1] = *reinterpret_cast<const floatx4*>(gb + off + 4);
+                } else {
+                    pk[j] = uint4{0, 0, 0, 0};
+                    pq[j] = uint4{0, 0, 0, 0};
+                    pg[2 * j] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    pg[2 * j + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
+                }
+            }
+            if (zwave) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * zR + 4 * l4 + j;
+                    pv[j] = r < Ln ? vb[r * row_stride + l16].bits : uint16_t(0);
+                }
+            }
+            if (tid < C) pb = tid < Ln ? bb[tid * num_heads] : 0.f;
         }
-        if (tid < C) pb = tid < Ln ? beta[static_cast<size_t>(c0 + tid) * num_heads + h] : 0.f;
     };
     if (t0 < t1) fetch(t0, tid >> 4, tid & 15, l16, l4, tid);
 
@@ -298,11 +356,8 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
                 sk += kf[i] * kf[i];
                 sq += qf[i] * qf[i];
             }
-#pragma unroll
-            for (int off = 1; off < 16; off <<= 1) {
-                sk += __shfl_xor(sk, off, 64);
-                sq += __shfl_xor(sq, off, 64);
-            }
+            sk = row16_sum(sk);
+            sq = row16_sum(sq);
             if (cc == 0) {
                 srk[2 * rp + j] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
                 srq[2 * rp + j] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
@@ -327,17 +382,22 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc) = floatx4{incl[0], incl[1], incl[2], incl[3]};
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc + 4) = floatx4{incl[4], incl[5], incl[6], incl[7]};
         }
-        __syncthreads();
+        lds_barrier();
 
-        // cm = (sum of the totals of earlier waves) - G_m, per channel.
+        // cm = (sum of the totals of earlier waves) - G_m, per channel; G_m is the
+        // sum of the first four wave totals, so only waves between this one
+        // and wave 4 contribute.
         floatx8 cm = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-        for (int w2 = 0; w2 < 8; ++w2) {
-            const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc);
-            const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc + 4);
-            const floatx8 t = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-            if (w2 < wave) cm += t;
-            if (w2 < 4) cm -= t;
+        {
+            const int lo_w = wave < 4 ? wave : 4, hi_w = wave < 4 ? 4 : wave;
+            const float sgn = wave < 4 ? -1.f : 1.f;
+            for (int w2 = lo_w; w2 < hi_w; ++w2) {
+                const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc);
+                const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc + 4);
+                const floatx8 t = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                cm += t;
+            }
+            cm *= sgn;
         }
         // Exponents (log2 units) of E = exp(G - G_m) for rows 2rp and 2rp+1.
         const floatx8 d0 = (cm + (incl - pair) + g0) * kLog2e;
@@ -397,7 +457,7 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
         for (int j = 0; j < 4; ++j) vv[j] = bf2f(pv[j]);
         // The raw inputs are consumed: the next chunk's loads fly from here on.
         if (cs + C < t1) fetch(cs + C, rp, cc, l16, l4, tid);
-        __syncthreads();
+        lds_barrier();
         KDA_PHASE_MARK(1);
 
         // ================= phase 2: contractions over channels =================
@@ -410,15 +470,20 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
             if (R1 >= 0) pa1 = unit_ap(smem, R1, I1, l16, l4);
         }
         if (zwave) {
-            // Y' = rk beta (V - rk Z), kept in fp32 for the substitution
+            // Y' = rk beta (V - rk Z), stored transposed as bf16 hi/lo
+            floatx4 y;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int r = 16 * zR + 4 * l4 + j;
                 const float rk = srk[r];
-                sY[r * YS + l16] = rk * sbeta[r] * (vv[j] - rk * zo[j]);
+                y[j] = rk * sbeta[r] * (vv[j] - rk * zo[j]);
             }
+            bf16x4 hi, lo;
+            split4(y, hi, lo);
+            *reinterpret_cast<bf16x4*>(smem + OFF_YH + (l16 * SN + 16 * zR + 4 * l4) * 2) = hi;
+            *reinterpret_cast<bf16x4*>(smem + OFF_YL + (l16 * SN + 16 * zR + 4 * l4) * 2) = lo;
         }
-        __syncthreads();
+        lds_barrier();
         KDA_PHASE_MARK(2);
 
         // ================= phase 3: P', diagonal inverses =================
@@ -470,49 +535,77 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
                 reinterpret_cast<__bf16*>(smem + OFF_XDL)[(l4 * 16 + m) * XD_STRIDE + l16] = lo;
             }
         }
-        __syncthreads();
+        lds_barrier();
         KDA_PHASE_MARK(3);
 
-        // ================= phase 4: Delta' by block forward substitution =================
-        // Delta'_R = X_RR (Y'_R - sum_{J<R} A'_RJ Delta'_J); one wave, LDS hand-off within it.
+        // ================= phase 4: substitution operators =================
+        // W_RJ = -X_RR A'_RJ (six blocks) and X_RR Y'_R (four blocks), K = 16.
+        {
+            const bool ok = l4 < 2;
+            if (wave < 6) {
+                const int R = wave < 1 ? 1 : wave < 3 ? 2 : 3;
+                const int J = wave - (R * (R - 1)) / 2;
+                const int xo = ((R * 16 + l16) * XD_STRIDE + 8 * l4) * 2;
+                const int bo = ((16 * J + l16) * SN + 16 * R + 8 * l4) * 2;
+                floatx4 w = {0.f, 0.f, 0.f, 0.f};
+                w = mma3(ld8_if(smem, OFF_XDH + xo, ok), ld8_if(smem, OFF_XDL + xo, ok),
+                         ld8_if(smem, OFF_ATH + bo, ok), ld8_if(smem, OFF_ATL + bo, ok), w);
+                bf16x4 hi, lo;
+                split4(-w, hi, lo);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = 16 * R + 4 * l4 + j;
+                    reinterpret_cast<__bf16*>(smem + OFF_WH)[r * SN + 16 * J + l16] = hi[j];
+                    reinterpret_cast<__bf16*>(smem + OFF_WL)[r * SN + 16 * J + l16] = lo[j];
+                }
+            } else {
+                float* sXY = reinterpret_cast<float*>(smem + OFF_XY);
+#pragma unroll
+                for (int u = 0; u < 2; ++u) {
+                    const int R = 2 * (wave - 6) + u;
+                    const int xo = ((R * 16 + l16) * XD_STRIDE + 8 * l4) * 2;
+                    const int yo = (l16 * SN + 16 * R + 8 * l4) * 2;
+                    floatx4 xy = {0.f, 0.f, 0.f, 0.f};
+                    xy = mma3(ld8_if(smem, OFF_XDH + xo, ok), ld8_if(smem, OFF_XDL + xo, ok),
+                              ld8_if(smem, OFF_YH + yo, ok), ld8_if(smem, OFF_YL + yo, ok), xy);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sXY[(16 * R + 4 * l4 + j) * YS + l16] = xy[j];
+                }
+            }
+        }
+        lds_barrier();
+        KDA_PHASE_MARK(4);
+
+        // ================= phase 5: Delta' by block forward substitution =================
+        // Delta'_R = X_RR Y'_R + sum_{J<R} W_RJ Delta'_J; one wave, LDS hand-off within it.
         if (wave == 0) {
+            const float* sXY = reinterpret_cast<const float*>(smem + OFF_XY);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                floatx4 acc;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = sXY[(16 * R + 4 * l4 + j) * YS + l16];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (32 * s >= 16 * R) continue;
                     const int ko = 32 * s + 8 * l4;
                     const bool ok = ko < 16 * R;
-                    acc = mma3(ld8_if(smem, OFF_AH + ((16 * R + l16) * SN + ko) * 2, ok),
-                               ld8_if(smem, OFF_AL + ((16 * R + l16) * SN + ko) * 2, ok),
+                    acc = mma3(ld8_if(smem, OFF_WH + ((16 * R + l16) * SN + ko) * 2, ok),
+                               ld8_if(smem, OFF_WL + ((16 * R + l16) * SN + ko) * 2, ok),
                                ld8_if(smem, OFF_DH + (l16 * SN + ko) * 2, ok),
                                ld8_if(smem, OFF_DL + (l16 * SN + ko) * 2, ok), acc);
                 }
-                floatx4 t;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) t[j] = sY[(16 * R + 4 * l4 + j) * YS + l16] - acc[j];
                 bf16x4 hi, lo;
-                split4(t, hi, lo);
-                *reinterpret_cast<bf16x4*>(smem + OFF_TTH + (l16 * TT_STRIDE + 4 * l4) * 2) = hi;
-                *reinterpret_cast<bf16x4*>(smem + OFF_TTL + (l16 * TT_STRIDE + 4 * l4) * 2) = lo;
-                __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
-                const bool ok = l4 < 2;
-                const int xo = ((R * 16 + l16) * XD_STRIDE + 8 * l4) * 2;
-                const int to = (l16 * TT_STRIDE + 8 * l4) * 2;
-                floatx4 dl = {0.f, 0.f, 0.f, 0.f};
-                dl = mma3(ld8_if(smem, OFF_XDH + xo, ok), ld8_if(smem, OFF_XDL + xo, ok),
-                          ld8_if(smem, OFF_TTH + to, ok), ld8_if(smem, OFF_TTL + to, ok), dl);
-                split4(dl, hi, lo);
+                split4(acc, hi, lo);
                 *reinterpret_cast<bf16x4*>(smem + OFF_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
                 *reinterpret_cast<bf16x4*>(smem + OFF_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
                 __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             }
         }
-        __syncthreads();
-        KDA_PHASE_MARK(4);
+        lds_barrier();
+        KDA_PHASE_MARK(5);
 
-        // ================= phase 5: output and state =================
+        // ================= phase 6: output and state =================
         if (!zwave) {
             const int R = zR;
             floatx4 acc;
@@ -559,8 +652,8 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(
                 Sacc[j] = sGL[c] * Sacc[j] + sEL[c] * acc[j];
             }
         }
-        __syncthreads();
-        KDA_PHASE_MARK(5);
+        lds_barrier();
+        KDA_PHASE_MARK(6);
     }
 
     if (final_state) {
