@@ -85,8 +85,12 @@ const char* kda_status_string(kda_status_t s) {
 const char* kda_last_error(void) { return g_last_error; }
 
 size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t* problem) {
-    (void)problem;
-    return 0;  // the chunk kernel keeps every intermediate on chip
+    if (!problem || problem->num_seqs <= 0 || problem->num_heads < 1 || problem->total_tokens < 0) return 0;
+    // bf16 inputs with 128-wide heads take the two-pass path, which stores the
+    // per-chunk operands; every other configuration keeps them on chip.
+    if (problem->qkv_dtype == KDA_BF16 && problem->head_k == 128 && problem->head_v == 128)
+        return kda::split_workspace_bytes(problem->total_tokens, problem->num_seqs, problem->num_heads);
+    return 0;
 }
 
 kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k, const void* v,
@@ -98,10 +102,6 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
     if (st != KDA_OK) return st;
     if (p->chunk_size != 0 && p->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
-    if (workspace_bytes < kda_chunk_fwd_workspace_bytes(p))
-        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes,
-                    kda_chunk_fwd_workspace_bytes(p));
-    (void)workspace;
     if (p->num_seqs == 0) {
         g_last_error[0] = '\0';
         return KDA_OK;
@@ -113,6 +113,12 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
         g_last_error[0] = '\0';
         return KDA_OK;
     }
+    const size_t need = kda_chunk_fwd_workspace_bytes(p);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(KDA_ERR_NULL_POINTER, "%s: workspace is NULL", what);
+    if (need > 0 && ((p->total_tokens + 63) / 64 + p->num_seqs) * int64_t(p->num_heads) > (int64_t(1) << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: too many (chunk, head) pairs", what);
     kda::PrefillArgs a{};
     a.q = q;
     a.k = k;
@@ -132,6 +138,7 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
     a.scale = p->scale;
     a.l2norm = p->qk_l2norm;
     hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::split_prefill_applies(a)) return finish(kda::launch_prefill_split(a, workspace, s), s, what);
     return finish(kda::launch_prefill(a, s), s, what);
 }
 

@@ -1,0 +1,120 @@
+// Private helpers for the bf16 MFMA kernels (gfx950, wave64).
+//
+// Operands are carried as bf16 hi/lo pairs (x = hi + lo to about 2^-17
+// relative); products use hi*hi + hi*lo + lo*hi on the 16x16x32 bf16 MFMA with
+// fp32 accumulation.  Lane layout of v_mfma_f32_16x16x32_bf16: lane l supplies
+// A[l%16][8*(l/16) .. +7] and B[8*(l/16) .. +7][l%16]; the accumulator holds
+// D[4*(l/16)+j][l%16] in element j.
+#pragma once
+
+#include "kda_common.h"
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2v __attribute__((ext_vector_type(2)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ floatx4 mma(bf16x8 a, bf16x8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+// hi*hi + hi*lo + lo*hi
+__device__ __forceinline__ floatx4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 bl, floatx4 c) {
+    c = mma(ah, bh, c);
+    c = mma(ah, bl, c);
+    return mma(al, bh, c);
+}
+
+__device__ __forceinline__ bf16x8 ld8(const unsigned char* smem, int off_bytes) {
+    return *reinterpret_cast<const bf16x8*>(smem + off_bytes);
+}
+
+// Operand fragment or zeros (K ranges past the valid rows).
+__device__ __forceinline__ bf16x8 ld8_if(const unsigned char* smem, int off_bytes, bool valid) {
+    const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+    return valid ? ld8(smem, off_bytes) : z;
+}
+
+// Eight bf16 at base[0], base[stride], ..., base[7*stride] (a column gather).
+__device__ __forceinline__ bf16x8 gather8(const __bf16* base, int stride) {
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = base[i * stride];
+    return r;
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Workgroup barrier that orders LDS only.  __syncthreads() also waits for
+// every outstanding global load, which would expose the latency of a
+// prefetch issued before it; here only this wave's LDS operations are
+// drained.  The memory clobber keeps the compiler from moving loads or
+// stores across it.
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+// Sum over the 16 lanes of a DPP row (all lanes receive the total).
+__device__ __forceinline__ float row16_sum(float x) {
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0xB1, 0xF, 0xF, false));   // quad_perm 1,0,3,2
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x4E, 0xF, 0xF, false));   // quad_perm 2,3,0,1
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x124, 0xF, 0xF, false));  // row_ror 4
+    x += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128, 0xF, 0xF, false));  // row_ror 8
+    return x;
+}
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(static_cast<uint32_t>(b) << 16); }
+
+__device__ __forceinline__ floatx8 unpack8(const uint4& w) {
+    const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+    floatx8 f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f[2 * i] = __uint_as_float(u[i] << 16);
+        f[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
+    }
+    return f;
+}
+
+__device__ __forceinline__ floatx8 bf8_to_f(const bf16x8& b) { return unpack8(__builtin_bit_cast(uint4, b)); }
+
+// Split two floats into packed bf16 hi and lo words.  The high halves are
+// recovered from the packed word with integer ops so the rounding
+// conversion runs once per pair.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t& hi, uint32_t& lo) {
+    const floatx2 xv = {x0, x1};
+    const uint32_t hu = __builtin_bit_cast(uint32_t, __builtin_convertvector(xv, bf16x2v));
+    const floatx2 r = {x0 - __uint_as_float(hu << 16), x1 - __uint_as_float(hu & 0xffff0000u)};
+    hi = hu;
+    lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2v));
+}
+
+__device__ __forceinline__ void split8(const floatx8& x, bf16x8& hi, bf16x8& lo) {
+    uint4 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    split2(x[4], x[5], h.z, l.z);
+    split2(x[6], x[7], h.w, l.w);
+    hi = __builtin_bit_cast(bf16x8, h);
+    lo = __builtin_bit_cast(bf16x8, l);
+}
+
+__device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo) {
+    uint2 h, l;
+    split2(x[0], x[1], h.x, l.x);
+    split2(x[2], x[3], h.y, l.y);
+    hi = __builtin_bit_cast(bf16x4, h);
+    lo = __builtin_bit_cast(bf16x4, l);
+}
+
+// Opaque copy of a lane-dependent value: re-materialised where it is used so
+// the compiler cannot hoist lane-dependent constants out of long loops (kept
+// live across them they would be spilled).
+__device__ __forceinline__ int opaque(int x) {
+    int r;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(r) : "v"(x));
+    return r;
+}
+
+}  // namespace kda

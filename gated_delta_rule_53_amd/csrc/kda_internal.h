@@ -46,7 +46,12 @@ struct PrefillArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// bf16 q/k/v with dk = dv = 128 (called by launch_prefill).
+// bf16 q/k/v with dk = dv = 128, everything on chip (called by launch_prefill).
 hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
+// bf16 q/k/v with dk = dv = 128: chunk-parallel preparation into a workspace of
+// split_workspace_bytes() bytes, then the state scan.
+bool split_prefill_applies(const PrefillArgs& a);
+size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int num_heads);
+hipError_t launch_prefill_split(const PrefillArgs& a, void* workspace, hipStream_t stream);
 
 }  // namespace kda

@@ -28,9 +28,14 @@
  *     kda_last_error() gives a human-readable detail for the calling thread.
  *   - NaN or Inf inputs propagate into the outputs; they are not checked.
  *   - The numeric domain of the chunked kernel: g must be finite and <= 0,
- *     and within every aligned 16-token block the per-channel sum of g must be
- *     >= -80 (the kernel factors exp(G_r - G_i) through the block start, and
- *     exp(80) is near the float32 limit).  Decode has no such limit.
+ *     and the chunk form factors exp(G_r - G_i) (G: cumulative sum of g inside
+ *     a chunk) through a reference token, so partial sums of g around it must
+ *     stay above -80 per channel (exp(80) is near the float32 limit).  With
+ *     bf16 q/k/v and dk = 128 the reference is the chunk's token 31: the sums
+ *     over the chunk's tokens 1..31 and over its tokens 32..63 must be >= -80.
+ *     Otherwise the reference is the start of each aligned 16-token block and
+ *     the sum over every such block must be >= -80.  Chunks are counted from
+ *     the start of each sequence.  Decode has no such limit.
  *   - Setting the environment variable KDA_DEBUG=1 makes every call wait for
  *     its own kernels and report their errors (this synchronises the stream).
  */
@@ -87,6 +92,13 @@ const char *kda_last_error(void);
 /*
  * Bytes of device workspace kda_chunk_fwd needs for this problem (0 if none).
  * Returns 0 as well for an invalid problem; kda_chunk_fwd then reports why.
+ *
+ * bf16 q/k/v with dk = dv = 128 runs in two passes: every (chunk, head) pair
+ * is prepared independently and its state-independent operands are stored in
+ * the workspace, then a short scan carries the state across chunks.  The size
+ * is 4 * (N + 1) bytes of chunk offsets rounded up to a multiple of 256, plus
+ * 132352 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 2 KiB per
+ * token and head).  Other configurations keep everything on chip and need 0.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
 

@@ -122,10 +122,31 @@ def test_chunk_fwd_empty_batch_is_a_noop():
     assert st == 0 and msg == ""
 
 
-def test_workspace_query_is_zero_and_checked():
+# bytes of one (chunk, head) record of the two-pass bf16 path
+REC_BYTES = 132352
+
+
+def test_workspace_query():
     lib = kda.raw_library()
-    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_prob())) == 0
+    q = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_prob(**kw)))
+    # bf16, 128-wide heads: 256-byte aligned chunk offsets, then one record per
+    # (chunk, head) for up to ceil(T/64) + N chunks.
+    assert q() == 256 + (2 + 1) * 2 * REC_BYTES
+    assert q(total_tokens=4096, num_seqs=1, num_heads=32) == 256 + (64 + 1) * 32 * REC_BYTES
+    assert q(total_tokens=100, num_seqs=70, num_heads=1) == 512 + (2 + 70) * REC_BYTES
+    # every other configuration needs none
+    assert q(qkv_dtype=0) == 0
+    assert q(head_k=64, head_v=64) == 0
+    assert q(num_seqs=0, total_tokens=0) == 0
     assert lib.kda_chunk_fwd_workspace_bytes(None) == 0
+
+
+def test_workspace_is_checked():
+    need = 256 + 3 * 2 * REC_BYTES
+    st, msg = _chunk(_prob(), ws=FAKE, ws_bytes=need - 1)
+    assert st == 4 and "workspace" in msg, (st, msg)
+    st, msg = _chunk(_prob(), ws=None, ws_bytes=need)
+    assert st == 1 and "workspace" in msg, (st, msg)
 
 
 @pytest.mark.parametrize("kw,status,needle", [
