@@ -108,6 +108,23 @@ __device__ __forceinline__ void split4(const floatx4& x, bf16x4& hi, bf16x4& lo)
     lo = __builtin_bit_cast(bf16x4, l);
 }
 
+// Raw buffer resource over [base, base + bytes): loads past the end return
+// zero and stores past the end are dropped by the hardware, so ragged tails
+// need no branches and every wave issues the same number of memory operations.
+// Word 3 selects 32-bit data format with no swizzle (gfx9 family).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+// s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
+// vmcnt in bits 3:0, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).  Emitted through the
+// builtin, so the compiler's own wait insertion knows about it.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 16, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+}
+
 // Opaque copy of a lane-dependent value: re-materialised where it is used so
 // the compiler cannot hoist lane-dependent constants out of long loops (kept
 // live across them they would be spilled).

@@ -52,14 +52,17 @@ constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
 // A fragment is one wave-wide MFMA operand: 64 lanes x 16 bytes, lane l
 // holding M[row0 + l%16][k0 + 8*(l/16) .. +7].
 constexpr int FRAG = 1024;
-constexpr int REC_PSI = 0;                    // Psi' : [R 4][s 4][hi/lo] fragments
-constexpr int REC_QG = REC_PSI + 32 * FRAG;   // Qg'  : same
+// Psi' is stored as single bf16: its rounding error enters only through
+// Psi' S, which the rest of the chunk step damps (measured against the fp64
+// recurrence it changes the output error by a few percent of itself).
+constexpr int REC_PSI = 0;                    // Psi' : [R 4][s 4] fragments, bf16
+constexpr int REC_QG = REC_PSI + 16 * FRAG;   // Qg'  : [R 4][s 4][hi/lo]
 constexpr int REC_KIT = REC_QG + 32 * FRAG;   // Ki^T : [c-block 8][s 2][hi/lo]
-constexpr int REC_X = REC_KIT + 32 * FRAG;    // X'   : [R 4][s 2][hi/lo]
+constexpr int REC_X = REC_KIT + 32 * FRAG;    // X' diag(rk beta) : [R 4][s 2][hi/lo]
 constexpr int REC_P = REC_X + 16 * FRAG;      // P'   : [R 4][s 2][hi/lo]
-constexpr int REC_VEC = REC_P + 16 * FRAG;    // fp32 rk*beta[64], e^{G_last}[128], e^{G_last-G_31}[128]
-constexpr int VEC_RKB = 0, VEC_GL = 64, VEC_EL = 192;
-constexpr int REC_BYTES = REC_VEC + 320 * 4;  // 132352
+constexpr int REC_VEC = REC_P + 16 * FRAG;    // fp32 e^{G_last}[128], e^{G_last - G_31}[128]
+constexpr int VEC_GL = 0, VEC_EL = 128;
+constexpr int REC_BYTES = REC_VEC + 256 * 4;  // 115712
 
 // ---- prep_kernel LDS map (bytes) ----
 constexpr int PW = C * SW * 2;                 // 17408: [64][SW] bf16
@@ -97,9 +100,10 @@ static_assert(8 * D * 4 <= 4 * 16 * LDS_STR * 4, "wave totals alias the diagonal
 
 // ---- scan_kernel LDS map (bytes) ----
 constexpr int S_STH = 0, S_STL = DVT * SW * 2;                  // S^T [16][SW]
-constexpr int S_YH = 2 * DVT * SW * 2, S_YL = S_YH + DVT * SN * 2;   // Delta0 RHS^T [16][SN]
-constexpr int S_DH = S_YL + DVT * SN * 2, S_DL = S_DH + DVT * SN * 2;  // D^T [16][SN]
-constexpr int S_LDS = S_DL + DVT * SN * 2;
+constexpr int S_V = 2 * DVT * SW * 2;                            // V^T [16][SN] (bf16, exact)
+constexpr int S_DH = S_V + DVT * SN * 2, S_DL = S_DH + DVT * SN * 2;  // D^T [16][SN]
+constexpr int S_VEC = S_DL + DVT * SN * 2;                       // two slots of e^{G_last}, e^{G_last-G_31}
+constexpr int S_LDS = S_VEC + 2 * 256 * 4;
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -181,6 +185,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(
     float* sEL = reinterpret_cast<float*>(smem + P_EL);
     float* sGL = reinterpret_cast<float*>(smem + P_GL);
 
+    KDA_PHASE_BEGIN
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int n_chunks = offsets[num_seqs];
     const int items = n_chunks * num_heads;
@@ -215,9 +220,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         }
         if (tid < C) pb = tid < L ? beta[static_cast<size_t>(start + tid) * num_heads + h] : 0.f;
     };
-    if (static_cast<int>(blockIdx.x) < items) fetch(blockIdx.x, threadIdx.x);
+    // Items run from the last chunk to the first: the records the state scan
+    // reads first are the ones written last, still in the last-level cache.
+    if (static_cast<int>(blockIdx.x) < items) fetch(items - 1 - static_cast<int>(blockIdx.x), threadIdx.x);
 
-    for (int item = blockIdx.x; item < items; item += gridDim.x) {
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+        const int item = items - 1 - it;
         const int lane = opaque(static_cast<int>(threadIdx.x) & 63);
         const int tid = wave * 64 + lane;
         const int l16 = lane & 15, l4 = lane >> 4;
@@ -308,8 +316,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             __builtin_amdgcn_sched_barrier(0);
         }
         // the next item's loads fly from here on
-        if (item + static_cast<int>(gridDim.x) < items) fetch(item + gridDim.x, tid);
+        if (it + static_cast<int>(gridDim.x) < items) fetch(items - 1 - (it + static_cast<int>(gridDim.x)), tid);
         lds_barrier();
+        KDA_PHASE_MARK(0);
 
         // ======== phase 2: A' and P' blocks (K = 128 channels) ========
         floatx4 pacc[2];
@@ -354,6 +363,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             pacc[u] = pv;
         }
         lds_barrier();
+        KDA_PHASE_MARK(1);
 
         // ======== phase 3: diagonal inverses (wave 0); P', Ki^T, Qg', vectors (waves 1-7) ========
         if (wave == 0) {
@@ -439,11 +449,11 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 *reinterpret_cast<bf16x8*>(rec + REC_QG + ((R * 4 + s) * 2 + 1) * FRAG + ln * 16) = lo;
             }
             float* vec = reinterpret_cast<float*>(rec + REC_VEC);
-            if (t1 < C) vec[VEC_RKB + t1] = srk[t1] * sbeta[t1];
-            else if (t1 < C + D) vec[VEC_GL + t1 - C] = sGL[t1 - C];
-            else if (t1 < C + 2 * D) vec[VEC_EL + t1 - C - D] = sEL[t1 - C - D];
+            if (t1 < D) vec[VEC_GL + t1] = sGL[t1];
+            else if (t1 < 2 * D) vec[VEC_EL + t1 - D] = sEL[t1 - D];
         }
         lds_barrier();
+        KDA_PHASE_MARK(2);
 
         // ======== phase 4: W_RJ = -X_RR A'_RJ (six blocks, K = 16) ========
         if (wave < 6) {
@@ -464,6 +474,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             }
         }
         lds_barrier();
+        KDA_PHASE_MARK(3);
 
         // ======== phase 5: Psi' and X' by block forward substitution ========
         // Column tile t of Psi' (wave t) and of X' (waves 0-3).  Step R:
@@ -503,11 +514,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 for (int R = 0; R < 4; ++R) {
                     floatx4 acc = {0.f, 0.f, 0.f, 0.f};
                     if (R == t) {
+                        // columns scaled by rk beta: the scan multiplies this X' by V directly
+                        const float cs = srk[16 * t + l16] * sbeta[16 * t + l16];
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             const int o = ((R * 16 + 4 * l4 + j) * WSTR + l16) * 2;
-                            acc[j] = static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDH + o)) +
-                                     static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDL + o));
+                            acc[j] = (static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDH + o)) +
+                                      static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDL + o))) * cs;
                         }
                     }
                     for (int J = t; J < R; ++J) {
@@ -526,32 +539,35 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             }
         }
         lds_barrier();
+        KDA_PHASE_MARK(4);
 
         // ======== phase 6: Psi', X', P' fragments out ========
-        for (int f = tid; f < 64 * 64; f += NT) {
+        for (int f = tid; f < 48 * 64; f += NT) {
             const int fr = f >> 6, ln = f & 63;
             const int li = ln & 15, lk = 8 * (ln >> 4);
             bf16x8 v8;
             unsigned char* dst;
-            if (fr < 32) {  // Psi' [R][s][hl]: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
-                const int R = fr >> 3, s = (fr >> 1) & 3, hl = fr & 1;
-                const __bf16* plane = reinterpret_cast<const __bf16*>(smem + (hl ? P_PTL : P_PTH));
+            if (fr < 16) {  // Psi' [R][s], hi only: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
+                const int R = fr >> 2, s = fr & 3;
+                const __bf16* plane = reinterpret_cast<const __bf16*>(smem + P_PTH);
                 v8 = gather8(plane + (32 * s + lk) * SN + 16 * R + li, SN);
                 dst = rec + REC_PSI + fr * FRAG + ln * 16;
-            } else if (fr < 48) {  // X' [R][s][hl]
-                const int f2 = fr - 32, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
+            } else if (fr < 32) {  // X' diag(rk beta) [R][s][hl]
+                const int f2 = fr - 16, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
                 const __bf16* plane = reinterpret_cast<const __bf16*>(smem + (hl ? P_XTL : P_XTH));
                 v8 = gather8(plane + (32 * s + lk) * SN + 16 * R + li, SN);
                 dst = rec + REC_X + f2 * FRAG + ln * 16;
             } else {  // P' [R][s][hl], row-major in LDS
-                const int f2 = fr - 48, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
+                const int f2 = fr - 32, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
                 v8 = ld8(smem, (hl ? P_PL : P_PH) + ((16 * R + li) * SN + 32 * s + lk) * 2);
                 dst = rec + REC_P + f2 * FRAG + ln * 16;
             }
             *reinterpret_cast<bf16x8*>(dst) = v8;
         }
         lds_barrier();
+        KDA_PHASE_MARK(5);
     }
+    KDA_PHASE_END;
 }
 
 // --------------------------------------------------------------------------
@@ -563,13 +579,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     __shared__ __align__(16) unsigned char smem[S_LDS];
     const int chain = blockIdx.x;
     if (chain >= num_seqs * num_heads) return;
+    KDA_PHASE_BEGIN
     const int n = chain / num_heads, h = chain % num_heads;
     const int col0 = blockIdx.y * DVT;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
-    const int R = wave >> 1;
+    const int R = wave >> 1;        // row block of the chunk this wave computes in phase (b)
     const bool even = (wave & 1) == 0;
-    const int ns = R < 2 ? 1 : 2;  // 32-wide K steps that reach the lower triangle of row block R
+    const bool wide = R >= 2;       // row blocks 2, 3 reach past the first 32 columns of X' and P'
     const int c_begin = offsets[n], c_end = offsets[n + 1];
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
     const int row_stride = num_heads * D;
@@ -583,88 +600,133 @@ __global__ __launch_bounds__(NT) void scan_kernel(
             S[j] = initial_state ? initial_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + l16] : 0.f;
     }
 
+    // Operands of one chunk held in registers.
+    //   even waves: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv four values of V
+    //   odd waves:  a[0..7] Qg'_R (hi/lo), b P'_R
+    //   all waves:  kt Ki^T rows 16 wave .. +15; wave 0 also the chunk's vectors (gv)
     struct Frag {
-        uint4 a[8];   // even: Psi'_R, odd: Qg'_R      [s*2 + hi/lo]
-        uint4 b[4];   // even: X'_R,   odd: P'_R       [s*2 + hi/lo]
-        uint4 kt[4];  // Ki^T rows 16 wave .. +15      [s*2 + hi/lo]
-        floatx4 gl, el, rkb;
-        uint16_t vv[4];
+        uint4 a[8];
+        uint4 b[4];   // [s*2 + hi/lo]; s = 1 only for wide row blocks
+        uint4 kt[4];  // [s*2 + hi/lo]
+        uint4 gv;     // wave 0: 16 bytes of the vector block (lane l: floats 4l .. 4l+3)
+        uint32_t vv[4];  // bf16 bits, zero-extended (packed only at use)
     };
-    auto load = [&](Frag& F, int cg, int lane) {
+    // The loads come in three parts, issued at three points of the previous
+    // chunk's step, so the memory pipeline never holds a whole chunk's requests
+    // in front of the step's own instructions.
+    auto load = [&](Frag& F, int cg, int lane, int part) {
         const unsigned char* rec = records + (static_cast<size_t>(cg) * num_heads + h) * REC_BYTES;
         const int l16 = lane & 15, l4 = lane >> 4;
-        const int abase = even ? REC_PSI : REC_QG, bbase = even ? REC_X : REC_P;
+        if (part == 0) {
+            {
+                // V rows of this wave's row block (odd waves load them too, so
+                // every wave runs the same loads); rows past the chunk's end
+                // read as zero
+                const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
+                const int L = static_cast<int>(min64(C, t_last - tok0));
+                const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0,
+                                            L * row_stride * 2);
 #pragma unroll
-        for (int s = 0; s < 4; ++s)
+                for (int j = 0; j < 4; ++j)
+                    F.vv[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, ((16 * R + 4 * l4 + j) * row_stride + l16) * 2,
+                                                                   0, 0);
+            }
+            if (even) {
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    F.a[s] = *reinterpret_cast<const uint4*>(rec + REC_PSI + (R * 4 + s) * FRAG + lane * 16);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
+            }
+        } else if (part == 1) {
+            if (!even) {
+#pragma unroll
+                for (int s = 2; s < 4; ++s)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+                        F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
+            }
+            const int bbase = even ? REC_X : REC_P;
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl)
-                F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, abase, R, 4, s, hl, lane));
+                F.b[hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, 0, hl, lane));
+            if (wide) {
 #pragma unroll
-        for (int s = 0; s < 2; ++s)
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl) {
-                F.b[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, s, hl, lane));
-                F.kt[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_KIT, wave, 2, s, hl, lane));
+                for (int hl = 0; hl < 2; ++hl)
+                    F.b[2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, 1, hl, lane));
             }
-        const float* vec = reinterpret_cast<const float*>(rec + REC_VEC);
-        F.gl = *reinterpret_cast<const floatx4*>(vec + VEC_GL + 16 * wave + 4 * l4);
-        F.el = *reinterpret_cast<const floatx4*>(vec + VEC_EL + 16 * wave + 4 * l4);
-        if (even) {
-            F.rkb = *reinterpret_cast<const floatx4*>(vec + VEC_RKB + 16 * R + 4 * l4);
-            const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
-            const int L = static_cast<int>(min64(C, t_last - tok0));
-            const bf16_t* vb = v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0 + l16;
+        } else {
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * l4 + j;
-                F.vv[j] = r < L ? vb[static_cast<size_t>(r) * row_stride].bits : uint16_t(0);
-            }
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+                    F.kt[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_KIT, wave, 2, s, hl, lane));
+            if (wave == 0) F.gv = *reinterpret_cast<const uint4*>(rec + REC_VEC + lane * 16);
         }
     };
-    auto step = [&](const Frag& F, int cg, int lane) {
+    // One chunk.  An inactive step (the pad after an odd chunk count) leaves
+    // S unchanged and stores nothing.  Fn / cg_next: the buffer and chunk
+    // whose loads are issued during this step.
+    auto step = [&](const Frag& F, int cg, int lane, bool active, Frag& Fn, int cg_next) {
         const int l16 = lane & 15, l4 = lane >> 4;
         const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
-        const int L = static_cast<int>(min64(C, t_last - tok0));
-        // (a) S^T and the Delta0 right-hand side diag(rk beta) V, transposed, bf16 hi/lo
+        const int L = active ? static_cast<int>(min64(C, t_last - tok0)) : 0;
+        const int slot = S_VEC + (cg & 1) * 1024;
+        load(Fn, cg_next, lane, 0);
+        // (a) S^T (bf16 hi/lo), V^T, the chunk's vectors
         {
             bf16x4 hi, lo;
             split4(S, hi, lo);
             *reinterpret_cast<bf16x4*>(smem + S_STH + (l16 * SW + 16 * wave + 4 * l4) * 2) = hi;
             *reinterpret_cast<bf16x4*>(smem + S_STL + (l16 * SW + 16 * wave + 4 * l4) * 2) = lo;
             if (even) {
-                floatx4 y;
-#pragma unroll
-                for (int j = 0; j < 4; ++j) y[j] = F.rkb[j] * bf2f(F.vv[j]);
-                split4(y, hi, lo);
-                *reinterpret_cast<bf16x4*>(smem + S_YH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
-                *reinterpret_cast<bf16x4*>(smem + S_YL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
+                const uint2 vp = {F.vv[0] | (F.vv[1] << 16),
+                                  F.vv[2] | (F.vv[3] << 16)};
+                *reinterpret_cast<uint2*>(smem + S_V + (l16 * SN + 16 * R + 4 * l4) * 2) = vp;
             }
+            if (wave == 0) *reinterpret_cast<uint4*>(smem + slot + lane * 16) = F.gv;
         }
         lds_barrier();
-        // (b) even: D_R = Delta0_R - Psi'_R S; odd: Qg'_R S
+        KDA_PHASE_MARK(8);
+        load(Fn, cg_next, lane, 1);
+        // (b) even: D_R = X'_R diag(rk beta) V - Psi'_R S; odd: Qg'_R S
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
-            acc = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, S_STH + ko), ld8(smem, S_STL + ko),
-                       acc);
-        }
         if (even) {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
+                const bf16x8 a = as_bf16x8(F.a[s]);
+                acc = mma(a, ld8(smem, S_STH + ko), acc);
+                acc = mma(a, ld8(smem, S_STL + ko), acc);
+            }
             floatx4 d0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                if (s >= ns) break;
-                const int ko = (l16 * SN + 32 * s + 8 * l4) * 2;
-                d0 = mma3(as_bf16x8(F.b[2 * s]), as_bf16x8(F.b[2 * s + 1]), ld8(smem, S_YH + ko), ld8(smem, S_YL + ko),
-                          d0);
+                if (s == 1 && !wide) break;
+                const bf16x8 vb = ld8(smem, S_V + (l16 * SN + 32 * s + 8 * l4) * 2);
+                d0 = mma(as_bf16x8(F.b[2 * s]), vb, d0);
+                d0 = mma(as_bf16x8(F.b[2 * s + 1]), vb, d0);
             }
             bf16x4 hi, lo;
             split4(d0 - acc, hi, lo);
             *reinterpret_cast<bf16x4*>(smem + S_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
             *reinterpret_cast<bf16x4*>(smem + S_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
+                acc = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, S_STH + ko),
+                           ld8(smem, S_STL + ko), acc);
+            }
         }
         lds_barrier();
-        // (c) U = Ki^T D, state update; odd: O_R = Qg'_R S + P'_R D
+        KDA_PHASE_MARK(9);
+        load(Fn, cg_next, lane, 2);
+        // (c) U = Ki^T D and the state update; odd: O_R = Qg'_R S + P'_R D
         {
             floatx4 u = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -672,34 +734,57 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                 const int ko = (l16 * SN + 32 * s + 8 * l4) * 2;
                 u = mma3(as_bf16x8(F.kt[2 * s]), as_bf16x8(F.kt[2 * s + 1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko), u);
             }
-            S = F.gl * S + F.el * u;
+            const floatx4 gl = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_GL + 16 * wave + 4 * l4) * 4);
+            const floatx4 el = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_EL + 16 * wave + 4 * l4) * 4);
+            const floatx4 s_new = gl * S + el * u;
+            S = active ? s_new : S;
         }
         if (!even) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                if (s >= ns) break;
+                if (s == 1 && !wide) break;
                 const int ko = (l16 * SN + 32 * s + 8 * l4) * 2;
                 acc = mma3(as_bf16x8(F.b[2 * s]), as_bf16x8(F.b[2 * s + 1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko),
                            acc);
             }
-            TOut* ob = out + (static_cast<size_t>(tok0) * num_heads + h) * D + col0 + l16;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * l4 + j;
-                if (r < L) ob[static_cast<size_t>(r) * row_stride] = from_f32<TOut>(acc[j]);
-            }
         }
+        // Exactly four stores per lane on every wave, so the wait counts in the
+        // chunk loop are fixed: even waves (no output) and rows past the
+        // chunk's end go through an empty or shorter range and are dropped.
+        const int out_bytes = even ? 0 : L * row_stride * static_cast<int>(sizeof(TOut));
+        const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok0) * num_heads + h) * D + col0, out_bytes);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int off = ((16 * R + 4 * l4 + j) * row_stride + l16) * static_cast<int>(sizeof(TOut));
+            if constexpr (sizeof(TOut) == 4)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j]), orr, off, 0, 0);
+            else
+                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[j]).bits, orr, off, 0, 0);
+        }
+        KDA_PHASE_MARK(10);
     };
 
-    Frag F0, F1;
-    if (c_begin < c_end) load(F0, c_begin, lane0);
-    for (int cg = c_begin; cg < c_end; cg += 2) {
-        const int lane = opaque(lane0);
-        if (cg + 1 < c_end) load(F1, cg + 1, lane);
-        step(F0, cg, lane);
-        if (cg + 1 >= c_end) break;
-        if (cg + 2 < c_end) load(F0, cg + 2, lane);
-        step(F1, cg + 1, lane);
+    // Two register buffers: the loads for chunk c+1 are issued during chunk
+    // c.  Loads past the last chunk re-read it, and the pad step is inactive,
+    // so no memory operation depends on data, and the wait after each step
+    // names exactly what may still be in flight: that step's four stores.
+    // (Left to itself the compiler loses count across the loop's back edge and
+    // drains every load, prefetch included, before each chunk.)
+    if (c_begin < c_end) {
+        Frag F0, F1;
+        load(F0, c_begin, lane0, 0);
+        load(F0, c_begin, lane0, 1);
+        load(F0, c_begin, lane0, 2);
+        wait_vmcnt<0>();
+        for (int cg = c_begin; cg < c_end; cg += 2) {
+            const int lane = opaque(lane0);
+            step(F0, cg, lane, true, F1, min(cg + 1, c_end - 1));
+            wait_vmcnt<4>();
+            KDA_PHASE_MARK(11);
+            step(F1, cg + 1, lane, cg + 1 < c_end, F0, min(cg + 2, c_end - 1));
+            wait_vmcnt<4>();
+            KDA_PHASE_MARK(11);
+        }
     }
 
     if (final_state) {
@@ -708,6 +793,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         for (int j = 0; j < 4; ++j)
             final_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + l16] = S[j];
     }
+    KDA_PHASE_END;
 }
 
 // --------------------------------------------------------------------------
