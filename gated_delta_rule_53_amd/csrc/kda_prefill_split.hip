@@ -584,8 +584,10 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     const int col0 = blockIdx.y * DVT;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
-    const int R = wave >> 1;        // row block of the chunk this wave computes in phase (b)
-    const bool even = (wave & 1) == 0;
+    // Waves 0-3 form D (row block R = wave & 3), waves 4-7 the outputs of the
+    // same row blocks; each SIMD (waves w and w+4) holds one of each.
+    const int R = wave & 3;
+    const bool forms_d = wave < 4;
     const bool wide = R >= 2;       // row blocks 2, 3 reach past the first 32 columns of X' and P'
     const int c_begin = offsets[n], c_end = offsets[n + 1];
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
@@ -601,8 +603,8 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     }
 
     // Operands of one chunk held in registers.
-    //   even waves: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv four values of V
-    //   odd waves:  a[0..7] Qg'_R (hi/lo), b P'_R
+    //   waves 0-3: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv four values of V
+    //   waves 4-7: a[0..7] Qg'_R (hi/lo), b P'_R
     //   all waves:  kt Ki^T rows 16 wave .. +15; wave 0 also the chunk's vectors (gv)
     struct Frag {
         uint4 a[8];
@@ -619,7 +621,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         const int l16 = lane & 15, l4 = lane >> 4;
         if (part == 0) {
             {
-                // V rows of this wave's row block (odd waves load them too, so
+                // V rows of this wave's row block (waves 4-7 load them too, so
                 // every wave runs the same loads); rows past the chunk's end
                 // read as zero
                 const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                     F.vv[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, ((16 * R + 4 * l4 + j) * row_stride + l16) * 2,
                                                                    0, 0);
             }
-            if (even) {
+            if (forms_d) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     F.a[s] = *reinterpret_cast<const uint4*>(rec + REC_PSI + (R * 4 + s) * FRAG + lane * 16);
@@ -643,14 +645,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                         F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
             }
         } else if (part == 1) {
-            if (!even) {
+            if (!forms_d) {
 #pragma unroll
                 for (int s = 2; s < 4; ++s)
 #pragma unroll
                     for (int hl = 0; hl < 2; ++hl)
                         F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
             }
-            const int bbase = even ? REC_X : REC_P;
+            const int bbase = forms_d ? REC_X : REC_P;
 #pragma unroll
             for (int hl = 0; hl < 2; ++hl)
                 F.b[hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, 0, hl, lane));
@@ -683,7 +685,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(
             split4(S, hi, lo);
             *reinterpret_cast<bf16x4*>(smem + S_STH + (l16 * SW + 16 * wave + 4 * l4) * 2) = hi;
             *reinterpret_cast<bf16x4*>(smem + S_STL + (l16 * SW + 16 * wave + 4 * l4) * 2) = lo;
-            if (even) {
+            if (forms_d) {
                 const uint2 vp = {F.vv[0] | (F.vv[1] << 16),
                                   F.vv[2] | (F.vv[3] << 16)};
                 *reinterpret_cast<uint2*>(smem + S_V + (l16 * SN + 16 * R + 4 * l4) * 2) = vp;
@@ -693,9 +695,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         lds_barrier();
         KDA_PHASE_MARK(8);
         load(Fn, cg_next, lane, 1);
-        // (b) even: D_R = X'_R diag(rk beta) V - Psi'_R S; odd: Qg'_R S
+        // (b) waves 0-3: D_R = X'_R diag(rk beta) V - Psi'_R S; waves 4-7: Qg'_R S
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-        if (even) {
+        if (forms_d) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
                 const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
@@ -716,30 +718,37 @@ __global__ __launch_bounds__(NT) void scan_kernel(
             *reinterpret_cast<bf16x4*>(smem + S_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
             *reinterpret_cast<bf16x4*>(smem + S_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
         } else {
+            // two accumulation chains, summed at the end
+            floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int s = 0; s < 4; s += 2) {
                 const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
                 acc = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, S_STH + ko),
                            ld8(smem, S_STL + ko), acc);
+                acc1 = mma3(as_bf16x8(F.a[2 * s + 2]), as_bf16x8(F.a[2 * s + 3]), ld8(smem, S_STH + ko + 64),
+                            ld8(smem, S_STL + ko + 64), acc1);
             }
+            acc += acc1;
         }
         lds_barrier();
         KDA_PHASE_MARK(9);
         load(Fn, cg_next, lane, 2);
-        // (c) U = Ki^T D and the state update; odd: O_R = Qg'_R S + P'_R D
+        // (c) U = Ki^T D and the state update; waves 4-7: O_R = Qg'_R S + P'_R D
         {
-            floatx4 u = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int ko = (l16 * SN + 32 * s + 8 * l4) * 2;
-                u = mma3(as_bf16x8(F.kt[2 * s]), as_bf16x8(F.kt[2 * s + 1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko), u);
+            floatx4 u = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+            {
+                const int ko = (l16 * SN + 8 * l4) * 2;
+                u = mma3(as_bf16x8(F.kt[0]), as_bf16x8(F.kt[1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko), u);
+                u1 = mma3(as_bf16x8(F.kt[2]), as_bf16x8(F.kt[3]), ld8(smem, S_DH + ko + 64), ld8(smem, S_DL + ko + 64),
+                          u1);
             }
+            u += u1;
             const floatx4 gl = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_GL + 16 * wave + 4 * l4) * 4);
             const floatx4 el = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_EL + 16 * wave + 4 * l4) * 4);
             const floatx4 s_new = gl * S + el * u;
             S = active ? s_new : S;
         }
-        if (!even) {
+        if (!forms_d) {
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
                 if (s == 1 && !wide) break;
@@ -749,9 +758,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(
             }
         }
         // Exactly four stores per lane on every wave, so the wait counts in the
-        // chunk loop are fixed: even waves (no output) and rows past the
+        // chunk loop are fixed: waves 0-3 (no output) and rows past the
         // chunk's end go through an empty or shorter range and are dropped.
-        const int out_bytes = even ? 0 : L * row_stride * static_cast<int>(sizeof(TOut));
+        const int out_bytes = forms_d ? 0 : L * row_stride * static_cast<int>(sizeof(TOut));
         const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok0) * num_heads + h) * D + col0, out_bytes);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
