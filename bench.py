@@ -36,9 +36,12 @@ STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_HEAD_STEP = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
-    "prefill": ["gated_delta_rule_53_amd/csrc/kda_prefill.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
+    "prefill": ["gated_delta_rule_53_amd/csrc/kda_prefill_split.hip", "gated_delta_rule_53_amd/csrc/kda_bf16_mfma.h",
+                "gated_delta_rule_53_amd/csrc/kda_common.h"],
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
+# kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
+PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
 
 def source_digest(kind: str) -> str:
@@ -90,19 +93,24 @@ def bench_prefill(steps: int, warmup: int):
                            s0=x.initial_state.to(dev),
                            out=torch.empty_like(x.v, device=dev),
                            fs=torch.empty_like(x.initial_state, device=dev)))
+    prob = kda.Problem(total_tokens=x.total_tokens, num_seqs=x.num_seqs, num_heads=x.num_heads,
+                       head_k=x.head_k, head_v=x.head_v, qkv_dtype=1, out_dtype=1,
+                       scale=x.scale, qk_l2norm=1, chunk_size=64)
+    workspace = torch.empty(max(kda.chunk_fwd_workspace_bytes(prob), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
     def step(i):
         c = copies[i % 3]
         kda.chunk_fwd(c["q"], c["k"], c["v"], c["g"], c["beta"], c["cu"], c["s0"],
-                      scale=x.scale, out=c["out"], final_state=c["fs"])
+                      scale=x.scale, out=c["out"], final_state=c["fs"], workspace=workspace)
 
     for i in range(warmup):
         step(i)
     wall, per = time_launches(step, steps, stream)
     T, H = x.total_tokens, x.num_heads
     alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + x.num_seqs * H * 2 * STATE_BYTES
-    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T)
+    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T,
+                workspace_bytes=workspace.numel())
 
 
 def bench_decode(loops: int):
@@ -211,16 +219,20 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",
+        "dtype_note": "bf16 MFMA operands (hi/lo bf16 pairs where fp32 accuracy is needed), fp32 "
+                      "accumulation and fp32 state",
         "data": "synthetic",
         "config": {"workload": pf["x"].name, "num_seqs": 1, "seq_len": pf["tokens"],
                    "heads": 32, "head_dim": 128, "chunk": 64, "qkv": "bf16", "g_beta": "f32",
                    "state": "f32", "out": "bf16", "input_copies_rotated": 3},
-        "roofline": {"kernel": "prefill_chunk_kernel", "bound": "hbm", "achieved": round(achieved, 2),
+        "roofline": {"kernel": "kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), "bound": "hbm",
+                     "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": None if tr is None else round(tr / pf["per_launch"] / 1e9, 2),
                      "alg_bytes_per_launch": pf["alg_bytes"],
-                     "launch_us": round(pf["per_launch"] * 1e6, 2)},
+                     "launch_us": round(pf["per_launch"] * 1e6, 2),
+                     "workspace_bytes": pf["workspace_bytes"]},
         "decode": {"workload": dc["x"].name, "steps_per_s": round(decode_steps_per_s, 1),
                    "tokens_per_s": round(decode_steps_per_s * dc["num_seqs"], 1),
                    "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",

@@ -45,9 +45,9 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+// fp32 q/k/v, or dk = dv = 64: one workgroup per (sequence, head, 16-column
+// tile) carries the state through the chunks with everything on chip.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);
-// bf16 q/k/v with dk = dv = 128, everything on chip (called by launch_prefill).
-hipError_t launch_prefill_bf16(const PrefillArgs& a, hipStream_t stream);
 // bf16 q/k/v with dk = dv = 128: chunk-parallel preparation into a workspace of
 // split_workspace_bytes() bytes, then the state scan.
 bool split_prefill_applies(const PrefillArgs& a);

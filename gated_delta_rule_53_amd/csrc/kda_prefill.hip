@@ -434,7 +434,6 @@ static hipError_t launch_prefill_d(const PrefillArgs& a, hipStream_t stream) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream) {
-    if (a.qkv_bf16 && a.head_dim == 128) return launch_prefill_bf16(a, stream);
     return a.head_dim == 128 ? launch_prefill_d<128>(a, stream) : launch_prefill_d<64>(a, stream);
 }
 
