@@ -48,6 +48,29 @@ __device__ __forceinline__ bf16x8 gather8(const __bf16* base, int stride) {
 
 __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_bit_cast(bf16x8, u); }
 
+// Column read through the transposing LDS load ds_read_b64_tr_b16.  Within
+// each group of 16 lanes, lane L reads 8 bytes at its own address and lane i
+// receives element i%4 of the reads of lanes i/4, i/4+4, i/4+8, i/4+12.  So
+// if lane L reads row r0 + L/4, columns c0 + 4(L%4) .. +3 of a row-major
+// 16-bit array, lane i gets column c0 + i of rows r0 .. r0+3.  col8_tr does
+// that twice: lane i of the group gets rows r0 .. r0+7 of column c0 + i (the
+// same result as gather8, in two LDS instructions instead of eight).
+// base: byte offset of the array in LDS, stride: row stride in elements,
+// r0, c0: per 16-lane group; l16: the lane's index in its group.
+typedef short shortx4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 col8_tr(const unsigned char* smem, int base, int stride, int r0, int c0, int l16) {
+    const int off = base + ((r0 + (l16 >> 2)) * stride + c0 + 4 * (l16 & 3)) * 2;
+    typedef __attribute__((address_space(3))) shortx4* lds_v4;
+    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + off));
+    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + off + 4 * stride * 2));
+    const shortx4 lo4 = a, hi4 = b;
+    const short t[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    bf16x8 r;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, t[i]);
+    return r;
+}
+
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for
 // every outstanding global load, which would expose the latency of a
 // prefetch issued before it; here only this wave's LDS operations are
@@ -117,12 +140,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, 
 }
 
 // s_waitcnt vmcnt(N) with the other counters left alone (gfx9 encoding:
-// vmcnt in bits 3:0, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).  Emitted through the
-// builtin, so the compiler's own wait insertion knows about it.
+// vmcnt bits 3:0 and 15:14, expcnt 6:4 = 7, lgkmcnt 11:8 = 15).  Emitted
+// through the builtin, so the compiler's own wait insertion knows about it.
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 16, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt(0x0F70 | N);
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
 }
 
 // Opaque copy of a lane-dependent value: re-materialised where it is used so

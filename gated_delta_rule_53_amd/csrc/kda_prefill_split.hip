@@ -43,7 +43,7 @@ namespace {
 
 constexpr int C = 64;       // chunk length
 constexpr int D = 128;      // head size
-constexpr int DVT = 16;     // value columns per scan workgroup
+constexpr int DVT = 16;     // value columns of one MFMA tile in the scan
 constexpr int NT = 512;     // threads per workgroup (both kernels)
 constexpr int SW = D + 8;   // bf16 row stride of 128-wide LDS planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
@@ -98,12 +98,16 @@ constexpr int P_LDS = P_GL + D * 4;
 static_assert(P_LDS <= 160 * 1024, "prep LDS budget");
 static_assert(8 * D * 4 <= 4 * 16 * LDS_STR * 4, "wave totals alias the diagonal blocks");
 
-// ---- scan_kernel LDS map (bytes) ----
-constexpr int S_STH = 0, S_STL = DVT * SW * 2;                  // S^T [16][SW]
-constexpr int S_V = 2 * DVT * SW * 2;                            // V^T [16][SN] (bf16, exact)
-constexpr int S_DH = S_V + DVT * SN * 2, S_DL = S_DH + DVT * SN * 2;  // D^T [16][SN]
-constexpr int S_VEC = S_DL + DVT * SN * 2;                       // two slots of e^{G_last}, e^{G_last-G_31}
-constexpr int S_LDS = S_VEC + 2 * 256 * 4;
+// ---- scan_kernel LDS map (bytes), for NTL column tiles of 16 per workgroup ----
+template <int NTL>
+struct ScanLds {
+    static constexpr int COLS = DVT * NTL;
+    static constexpr int STH = 0, STL = COLS * SW * 2;                     // S^T [COLS][SW] hi, lo
+    static constexpr int V = 2 * COLS * SW * 2;                            // V^T [COLS][SN] (bf16, exact)
+    static constexpr int DH = V + COLS * SN * 2, DL = DH + COLS * SN * 2;  // D^T [COLS][SN] hi, lo
+    static constexpr int VEC = DL + COLS * SN * 2;                         // two slots of the vector block
+    static constexpr int BYTES = VEC + 2 * 256 * 4;
+};
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -430,8 +434,7 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             for (int f = t1; f < 32 * 64; f += 448) {
                 const int fr = f >> 6, ln = f & 63;
                 const int w = fr >> 2, s = (fr >> 1) & 1, hl = fr & 1;
-                const __bf16* plane = reinterpret_cast<const __bf16*>(smem + (hl ? P_KIL : P_KIH));
-                const bf16x8 v8 = gather8(plane + (32 * s + 8 * (ln >> 4)) * SW + 16 * w + (ln & 15), SW);
+                const bf16x8 v8 = col8_tr(smem, hl ? P_KIL : P_KIH, SW, 32 * s + 8 * (ln >> 4), 16 * w, ln & 15);
                 *reinterpret_cast<bf16x8*>(rec + REC_KIT + fr * FRAG + ln * 16) = v8;
             }
             // Qg' fragments (hi and lo together): rq_r Qg[r][c] e^{G_31}[c]
@@ -483,17 +486,17 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             const bool ok = l4 < 2;
             const int t = wave, c0 = 16 * t;
             const float em = sEm[c0 + l16];
-            const __bf16* kgh = reinterpret_cast<const __bf16*>(smem + P_KGH);
-            const __bf16* kgl = reinterpret_cast<const __bf16*>(smem + P_KGL);
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
                 // rhs: (X_RR diag(rk^2 beta)) Kg_R[:, tile] e^{G_31}[col]
                 const int xo = ((R * 16 + l16) * WSTR + 8 * l4) * 2;
-                const int go = (16 * R + 8 * l4) * SW + c0 + l16;
+                // rows past 16R + 15 (lanes with l4 >= 2) read other LDS data and are zeroed
                 const bf16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+                const bf16x8 kgh8 = col8_tr(smem, P_KGH, SW, 16 * R + 8 * l4, c0, l16);
+                const bf16x8 kgl8 = col8_tr(smem, P_KGL, SW, 16 * R + 8 * l4, c0, l16);
                 floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma3(ld8_if(smem, P_XFH + xo, ok), ld8_if(smem, P_XFL + xo, ok),
-                           ok ? gather8(kgh + go, SW) : z8, ok ? gather8(kgl + go, SW) : z8, acc);
+                acc = mma3(ld8_if(smem, P_XFH + xo, ok), ld8_if(smem, P_XFL + xo, ok), ok ? kgh8 : z8, ok ? kgl8 : z8,
+                           acc);
                 acc *= em;
 #pragma unroll
                 for (int J = 0; J < R; ++J) {
@@ -549,13 +552,11 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             unsigned char* dst;
             if (fr < 16) {  // Psi' [R][s], hi only: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
                 const int R = fr >> 2, s = fr & 3;
-                const __bf16* plane = reinterpret_cast<const __bf16*>(smem + P_PTH);
-                v8 = gather8(plane + (32 * s + lk) * SN + 16 * R + li, SN);
+                v8 = col8_tr(smem, P_PTH, SN, 32 * s + lk, 16 * R, li);
                 dst = rec + REC_PSI + fr * FRAG + ln * 16;
             } else if (fr < 32) {  // X' diag(rk beta) [R][s][hl]
                 const int f2 = fr - 16, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
-                const __bf16* plane = reinterpret_cast<const __bf16*>(smem + (hl ? P_XTL : P_XTH));
-                v8 = gather8(plane + (32 * s + lk) * SN + 16 * R + li, SN);
+                v8 = col8_tr(smem, hl ? P_XTL : P_XTH, SN, 32 * s + lk, 16 * R, li);
                 dst = rec + REC_X + f2 * FRAG + ln * 16;
             } else {  // P' [R][s][hl], row-major in LDS
                 const int f2 = fr - 32, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
@@ -571,17 +572,18 @@ __global__ __launch_bounds__(NT) void prep_kernel(
 }
 
 // --------------------------------------------------------------------------
-template <typename TOut>
+template <typename TOut, int NTL>
 __global__ __launch_bounds__(NT) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int num_seqs, int num_heads) {
-    __shared__ __align__(16) unsigned char smem[S_LDS];
+    using L_ = ScanLds<NTL>;
+    __shared__ __align__(16) unsigned char smem[L_::BYTES];
     const int chain = blockIdx.x;
     if (chain >= num_seqs * num_heads) return;
     KDA_PHASE_BEGIN
     const int n = chain / num_heads, h = chain % num_heads;
-    const int col0 = blockIdx.y * DVT;
+    const int col0 = blockIdx.y * L_::COLS;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
     // Waves 0-3 form D (row block R = wave & 3), waves 4-7 the outputs of the
@@ -593,17 +595,22 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
     const int row_stride = num_heads * D;
 
+    // This wave's rows 16 wave .. +15 of the state, NTL tiles of 16 columns.
     const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
-    floatx4 S;
+    floatx4 S[NTL];
     {
         const int l16 = lane0 & 15, l4 = lane0 >> 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            S[j] = initial_state ? initial_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + l16] : 0.f;
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S[t][j] = initial_state
+                              ? initial_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + DVT * t + l16]
+                              : 0.f;
     }
 
     // Operands of one chunk held in registers.
-    //   waves 0-3: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv four values of V
+    //   waves 0-3: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv values of V
     //   waves 4-7: a[0..7] Qg'_R (hi/lo), b P'_R
     //   all waves:  kt Ki^T rows 16 wave .. +15; wave 0 also the chunk's vectors (gv)
     struct Frag {
@@ -611,7 +618,7 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         uint4 b[4];   // [s*2 + hi/lo]; s = 1 only for wide row blocks
         uint4 kt[4];  // [s*2 + hi/lo]
         uint4 gv;     // wave 0: 16 bytes of the vector block (lane l: floats 4l .. 4l+3)
-        uint32_t vv[4];  // bf16 bits, zero-extended (packed only at use)
+        uint32_t vv[NTL][4];  // bf16 bits, zero-extended (packed only at use)
     };
     // The loads come in three parts, issued at three points of the previous
     // chunk's step, so the memory pipeline never holds a whole chunk's requests
@@ -629,9 +636,11 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                 const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0,
                                             L * row_stride * 2);
 #pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    F.vv[j] = __builtin_amdgcn_raw_buffer_load_b16(vr, ((16 * R + 4 * l4 + j) * row_stride + l16) * 2,
-                                                                   0, 0);
+                for (int t = 0; t < NTL; ++t)
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        F.vv[t][j] = __builtin_amdgcn_raw_buffer_load_b16(
+                            vr, ((16 * R + 4 * l4 + j) * row_stride + DVT * t + l16) * 2, 0, 0);
             }
             if (forms_d) {
 #pragma unroll
@@ -677,106 +686,120 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         const int l16 = lane & 15, l4 = lane >> 4;
         const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
         const int L = active ? static_cast<int>(min64(C, t_last - tok0)) : 0;
-        const int slot = S_VEC + (cg & 1) * 1024;
+        const int slot = L_::VEC + (cg & 1) * 1024;
         load(Fn, cg_next, lane, 0);
         // (a) S^T (bf16 hi/lo), V^T, the chunk's vectors
-        {
+#pragma unroll
+        for (int t = 0; t < NTL; ++t) {
             bf16x4 hi, lo;
-            split4(S, hi, lo);
-            *reinterpret_cast<bf16x4*>(smem + S_STH + (l16 * SW + 16 * wave + 4 * l4) * 2) = hi;
-            *reinterpret_cast<bf16x4*>(smem + S_STL + (l16 * SW + 16 * wave + 4 * l4) * 2) = lo;
+            split4(S[t], hi, lo);
+            const int o = ((DVT * t + l16) * SW + 16 * wave + 4 * l4) * 2;
+            *reinterpret_cast<bf16x4*>(smem + L_::STH + o) = hi;
+            *reinterpret_cast<bf16x4*>(smem + L_::STL + o) = lo;
             if (forms_d) {
-                const uint2 vp = {F.vv[0] | (F.vv[1] << 16),
-                                  F.vv[2] | (F.vv[3] << 16)};
-                *reinterpret_cast<uint2*>(smem + S_V + (l16 * SN + 16 * R + 4 * l4) * 2) = vp;
+                const uint2 vp = {F.vv[t][0] | (F.vv[t][1] << 16), F.vv[t][2] | (F.vv[t][3] << 16)};
+                *reinterpret_cast<uint2*>(smem + L_::V + ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2) = vp;
             }
-            if (wave == 0) *reinterpret_cast<uint4*>(smem + slot + lane * 16) = F.gv;
         }
+        if (wave == 0) *reinterpret_cast<uint4*>(smem + slot + lane * 16) = F.gv;
         lds_barrier();
         KDA_PHASE_MARK(8);
         load(Fn, cg_next, lane, 1);
         // (b) waves 0-3: D_R = X'_R diag(rk beta) V - Psi'_R S; waves 4-7: Qg'_R S
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        floatx4 acc[NTL];
         if (forms_d) {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
-                const bf16x8 a = as_bf16x8(F.a[s]);
-                acc = mma(a, ld8(smem, S_STH + ko), acc);
-                acc = mma(a, ld8(smem, S_STL + ko), acc);
-            }
-            floatx4 d0 = {0.f, 0.f, 0.f, 0.f};
+            for (int t = 0; t < NTL; ++t) {
+                acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+                floatx4 d0 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && !wide) break;
-                const bf16x8 vb = ld8(smem, S_V + (l16 * SN + 32 * s + 8 * l4) * 2);
-                d0 = mma(as_bf16x8(F.b[2 * s]), vb, d0);
-                d0 = mma(as_bf16x8(F.b[2 * s + 1]), vb, d0);
+                for (int s = 0; s < 4; ++s) {
+                    const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
+                    const bf16x8 a = as_bf16x8(F.a[s]);
+                    acc[t] = mma(a, ld8(smem, L_::STH + ko), acc[t]);
+                    acc[t] = mma(a, ld8(smem, L_::STL + ko), acc[t]);
+                }
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s == 1 && !wide) break;
+                    const bf16x8 vb = ld8(smem, L_::V + ((DVT * t + l16) * SN + 32 * s + 8 * l4) * 2);
+                    d0 = mma(as_bf16x8(F.b[2 * s]), vb, d0);
+                    d0 = mma(as_bf16x8(F.b[2 * s + 1]), vb, d0);
+                }
+                bf16x4 hi, lo;
+                split4(d0 - acc[t], hi, lo);
+                const int o = ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2;
+                *reinterpret_cast<bf16x4*>(smem + L_::DH + o) = hi;
+                *reinterpret_cast<bf16x4*>(smem + L_::DL + o) = lo;
             }
-            bf16x4 hi, lo;
-            split4(d0 - acc, hi, lo);
-            *reinterpret_cast<bf16x4*>(smem + S_DH + (l16 * SN + 16 * R + 4 * l4) * 2) = hi;
-            *reinterpret_cast<bf16x4*>(smem + S_DL + (l16 * SN + 16 * R + 4 * l4) * 2) = lo;
         } else {
-            // two accumulation chains, summed at the end
-            floatx4 acc1 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int s = 0; s < 4; s += 2) {
-                const int ko = (l16 * SW + 32 * s + 8 * l4) * 2;
-                acc = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, S_STH + ko),
-                           ld8(smem, S_STL + ko), acc);
-                acc1 = mma3(as_bf16x8(F.a[2 * s + 2]), as_bf16x8(F.a[2 * s + 3]), ld8(smem, S_STH + ko + 64),
-                            ld8(smem, S_STL + ko + 64), acc1);
+            for (int t = 0; t < NTL; ++t) {
+                // two accumulation chains, summed at the end
+                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; s += 2) {
+                    const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
+                    a0 = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, L_::STH + ko),
+                              ld8(smem, L_::STL + ko), a0);
+                    a1 = mma3(as_bf16x8(F.a[2 * s + 2]), as_bf16x8(F.a[2 * s + 3]), ld8(smem, L_::STH + ko + 64),
+                              ld8(smem, L_::STL + ko + 64), a1);
+                }
+                acc[t] = a0 + a1;
             }
-            acc += acc1;
         }
         lds_barrier();
         KDA_PHASE_MARK(9);
         load(Fn, cg_next, lane, 2);
         // (c) U = Ki^T D and the state update; waves 4-7: O_R = Qg'_R S + P'_R D
         {
-            floatx4 u = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
-            {
-                const int ko = (l16 * SN + 8 * l4) * 2;
-                u = mma3(as_bf16x8(F.kt[0]), as_bf16x8(F.kt[1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko), u);
-                u1 = mma3(as_bf16x8(F.kt[2]), as_bf16x8(F.kt[3]), ld8(smem, S_DH + ko + 64), ld8(smem, S_DL + ko + 64),
-                          u1);
-            }
-            u += u1;
             const floatx4 gl = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_GL + 16 * wave + 4 * l4) * 4);
             const floatx4 el = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_EL + 16 * wave + 4 * l4) * 4);
-            const floatx4 s_new = gl * S + el * u;
-            S = active ? s_new : S;
+#pragma unroll
+            for (int t = 0; t < NTL; ++t) {
+                floatx4 u = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
+                const int ko = ((DVT * t + l16) * SN + 8 * l4) * 2;
+                u = mma3(as_bf16x8(F.kt[0]), as_bf16x8(F.kt[1]), ld8(smem, L_::DH + ko), ld8(smem, L_::DL + ko), u);
+                u1 = mma3(as_bf16x8(F.kt[2]), as_bf16x8(F.kt[3]), ld8(smem, L_::DH + ko + 64),
+                          ld8(smem, L_::DL + ko + 64), u1);
+                const floatx4 s_new = gl * S[t] + el * (u + u1);
+                S[t] = active ? s_new : S[t];
+            }
         }
         if (!forms_d) {
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && !wide) break;
-                const int ko = (l16 * SN + 32 * s + 8 * l4) * 2;
-                acc = mma3(as_bf16x8(F.b[2 * s]), as_bf16x8(F.b[2 * s + 1]), ld8(smem, S_DH + ko), ld8(smem, S_DL + ko),
-                           acc);
+            for (int t = 0; t < NTL; ++t) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    if (s == 1 && !wide) break;
+                    const int ko = ((DVT * t + l16) * SN + 32 * s + 8 * l4) * 2;
+                    acc[t] = mma3(as_bf16x8(F.b[2 * s]), as_bf16x8(F.b[2 * s + 1]), ld8(smem, L_::DH + ko),
+                                  ld8(smem, L_::DL + ko), acc[t]);
+                }
             }
         }
-        // Exactly four stores per lane on every wave, so the wait counts in the
-        // chunk loop are fixed: waves 0-3 (no output) and rows past the
+        // Exactly 4 NTL stores per lane on every wave, so the wait counts in
+        // the chunk loop are fixed: waves 0-3 (no output) and rows past the
         // chunk's end go through an empty or shorter range and are dropped.
         const int out_bytes = forms_d ? 0 : L * row_stride * static_cast<int>(sizeof(TOut));
         const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok0) * num_heads + h) * D + col0, out_bytes);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int off = ((16 * R + 4 * l4 + j) * row_stride + l16) * static_cast<int>(sizeof(TOut));
-            if constexpr (sizeof(TOut) == 4)
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j]), orr, off, 0, 0);
-            else
-                __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[j]).bits, orr, off, 0, 0);
-        }
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int off = ((16 * R + 4 * l4 + j) * row_stride + DVT * t + l16) * static_cast<int>(sizeof(TOut));
+                if constexpr (sizeof(TOut) == 4)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[t][j]), orr, off, 0, 0);
+                else
+                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[t][j]).bits, orr, off, 0, 0);
+            }
         KDA_PHASE_MARK(10);
     };
 
     // Two register buffers: the loads for chunk c+1 are issued during chunk
     // c.  Loads past the last chunk re-read it, and the pad step is inactive,
     // so no memory operation depends on data, and the wait after each step
-    // names exactly what may still be in flight: that step's four stores.
+    // names exactly what may still be in flight: that step's stores.
     // (Left to itself the compiler loses count across the loop's back edge and
     // drains every load, prefetch included, before each chunk.)
     if (c_begin < c_end) {
@@ -788,10 +811,10 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         for (int cg = c_begin; cg < c_end; cg += 2) {
             const int lane = opaque(lane0);
             step(F0, cg, lane, true, F1, min(cg + 1, c_end - 1));
-            wait_vmcnt<4>();
+            wait_vmcnt<4 * NTL>();
             KDA_PHASE_MARK(11);
             step(F1, cg + 1, lane, cg + 1 < c_end, F0, min(cg + 2, c_end - 1));
-            wait_vmcnt<4>();
+            wait_vmcnt<4 * NTL>();
             KDA_PHASE_MARK(11);
         }
     }
@@ -799,13 +822,19 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     if (final_state) {
         const int l16 = lane0 & 15, l4 = lane0 >> 4;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            final_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + l16] = S[j];
+        for (int t = 0; t < NTL; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                final_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + DVT * t + l16] = S[t][j];
     }
     KDA_PHASE_END;
 }
 
 // --------------------------------------------------------------------------
+#ifndef SCAN_NTL
+#define SCAN_NTL 1  // 16-column tiles per scan workgroup
+#endif
+
 bool split_prefill_applies(const PrefillArgs& a) { return a.qkv_bf16 && a.head_dim == D; }
 
 size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int num_heads) {
@@ -848,10 +877,10 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
     // tiles of one chain (linear ids chain + k * grid.x) share an XCD when grid.x % 8 == 0
-    const dim3 grid((chains + 7u) & ~7u, D / DVT);
-    scan_kernel<TOut><<<grid, NT, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, records,
-                                              a.initial_state, static_cast<TOut*>(a.out), a.final_state,
-                                              a.num_seqs, a.num_heads);
+    const dim3 grid((chains + 7u) & ~7u, D / (DVT * SCAN_NTL));
+    scan_kernel<TOut, SCAN_NTL><<<grid, NT, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets,
+                                                         records, a.initial_state, static_cast<TOut*>(a.out),
+                                                         a.final_state, a.num_seqs, a.num_heads);
     return hipGetLastError();
 }
 
