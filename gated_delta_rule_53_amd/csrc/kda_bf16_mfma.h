@@ -28,6 +28,28 @@ __device__ __forceinline__ floatx4 mma3(bf16x8 ah, bf16x8 al, bf16x8 bh, bf16x8 
     return mma(al, bh, c);
 }
 
+// fp16 operands (v_mfma_f32_16x16x32_f16 has the same lane layout as the
+// bf16 instruction).
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ floatx4 mmah(halfx8 a, halfx8 b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ halfx8 ldh8(const unsigned char* smem, int off_bytes) {
+    return *reinterpret_cast<const halfx8*>(smem + off_bytes);
+}
+
+__device__ __forceinline__ halfx8 as_halfx8(const uint4& u) { return __builtin_bit_cast(halfx8, u); }
+
+// fp16 hi/lo pair of four floats (x = hi + lo to about 2^-22 relative while
+// |x| stays in the fp16 normal range).
+__device__ __forceinline__ void split4h(const floatx4& x, halfx4& hi, halfx4& lo) {
+    hi = __builtin_convertvector(x, halfx4);
+    lo = __builtin_convertvector(x - __builtin_convertvector(hi, floatx4), halfx4);
+}
+
 __device__ __forceinline__ bf16x8 ld8(const unsigned char* smem, int off_bytes) {
     return *reinterpret_cast<const bf16x8*>(smem + off_bytes);
 }

@@ -52,17 +52,20 @@ constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
 // A fragment is one wave-wide MFMA operand: 64 lanes x 16 bytes, lane l
 // holding M[row0 + l%16][k0 + 8*(l/16) .. +7].
 constexpr int FRAG = 1024;
-// Psi' is stored as single bf16: its rounding error enters only through
-// Psi' S, which the rest of the chunk step damps (measured against the fp64
-// recurrence it changes the output error by a few percent of itself).
-constexpr int REC_PSI = 0;                    // Psi' : [R 4][s 4] fragments, bf16
-constexpr int REC_QG = REC_PSI + 16 * FRAG;   // Qg'  : [R 4][s 4][hi/lo]
-constexpr int REC_KIT = REC_QG + 32 * FRAG;   // Ki^T : [c-block 8][s 2][hi/lo]
-constexpr int REC_X = REC_KIT + 32 * FRAG;    // X' diag(rk beta) : [R 4][s 2][hi/lo]
-constexpr int REC_P = REC_X + 16 * FRAG;      // P'   : [R 4][s 2][hi/lo]
-constexpr int REC_VEC = REC_P + 16 * FRAG;    // fp32 e^{G_last}[128], e^{G_last - G_31}[128]
-constexpr int VEC_GL = 0, VEC_EL = 128;
-constexpr int REC_BYTES = REC_VEC + 256 * 4;  // 115712
+// The operands the state meets (Psi', Qg', Ke^T, P') are single fp16; the
+// state side (S, D) is an fp16 hi/lo pair.  fp16 keeps 11 significant bits,
+// and every one of these operands is bounded: Qg' by |q_hat|, P' by
+// |q_hat||k_hat|, Ke = k e^{G_last - G} by |k|, Psi' by the scaled inverse.
+// X' diag(rk beta), which multiplies the bf16 values V, stays a bf16 hi/lo
+// pair.
+constexpr int REC_PSI = 0;                    // Psi' : [R 4][s 4] fragments, fp16
+constexpr int REC_QG = REC_PSI + 16 * FRAG;   // Qg'  : [R 4][s 4], fp16
+constexpr int REC_KE = REC_QG + 16 * FRAG;    // Ke^T : [c-block 8][s 2], fp16
+constexpr int REC_X = REC_KE + 16 * FRAG;     // X' diag(rk beta) : [R 4][s 2][hi/lo], bf16
+constexpr int REC_P = REC_X + 16 * FRAG;      // P'   : [R 4][s 2], fp16
+constexpr int REC_VEC = REC_P + 8 * FRAG;     // fp32 e^{G_last}[128], unused[128]
+constexpr int VEC_GL = 0;
+constexpr int REC_BYTES = REC_VEC + 256 * 4;  // 74752
 
 // ---- prep_kernel LDS map (bytes) ----
 constexpr int PW = C * SW * 2;                 // 17408: [64][SW] bf16
@@ -102,9 +105,9 @@ static_assert(8 * D * 4 <= 4 * 16 * LDS_STR * 4, "wave totals alias the diagonal
 template <int NTL>
 struct ScanLds {
     static constexpr int COLS = DVT * NTL;
-    static constexpr int STH = 0, STL = COLS * SW * 2;                     // S^T [COLS][SW] hi, lo
+    static constexpr int STH = 0, STL = COLS * SW * 2;                     // S^T [COLS][SW] fp16 hi, lo
     static constexpr int V = 2 * COLS * SW * 2;                            // V^T [COLS][SN] (bf16, exact)
-    static constexpr int DH = V + COLS * SN * 2, DL = DH + COLS * SN * 2;  // D^T [COLS][SN] hi, lo
+    static constexpr int DH = V + COLS * SN * 2, DL = DH + COLS * SN * 2;  // D^T [COLS][SN] fp16 hi, lo
     static constexpr int VEC = DL + COLS * SN * 2;                         // two slots of the vector block
     static constexpr int BYTES = VEC + 2 * 256 * 4;
 };
@@ -430,14 +433,18 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         }
         if (wave >= 1) {
             const int t1 = tid - 64;  // 0..447
-            // Ki^T fragments: lane holds Ki[32s + 8(l/16) + i][16w + l%16]
-            for (int f = t1; f < 32 * 64; f += 448) {
+            // Ke^T fragments: lane holds Ki[32s + 8(l/16) + i][16w + l%16] e^{G_last - G_31}[16w + l%16]
+            //   = k e^{G_last - G} for 8 tokens of one channel (the decay to the chunk's end)
+            for (int f = t1; f < 16 * 64; f += 448) {
                 const int fr = f >> 6, ln = f & 63;
-                const int w = fr >> 2, s = (fr >> 1) & 1, hl = fr & 1;
-                const bf16x8 v8 = col8_tr(smem, hl ? P_KIL : P_KIH, SW, 32 * s + 8 * (ln >> 4), 16 * w, ln & 15);
-                *reinterpret_cast<bf16x8*>(rec + REC_KIT + fr * FRAG + ln * 16) = v8;
+                const int w = fr >> 1, s = fr & 1;
+                const int r0 = 32 * s + 8 * (ln >> 4), c = 16 * w + (ln & 15);
+                floatx8 x = bf8_to_f(col8_tr(smem, P_KIH, SW, r0, 16 * w, ln & 15)) +
+                            bf8_to_f(col8_tr(smem, P_KIL, SW, r0, 16 * w, ln & 15));
+                x *= sEL[c];
+                *reinterpret_cast<halfx8*>(rec + REC_KE + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
             }
-            // Qg' fragments (hi and lo together): rq_r Qg[r][c] e^{G_31}[c]
+            // Qg' fragments: rq_r Qg[r][c] e^{G_31}[c]
             for (int f = t1; f < 16 * 64; f += 448) {
                 const int fr = f >> 6, ln = f & 63;
                 const int R = fr >> 2, s = fr & 3;
@@ -446,14 +453,10 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 const float rq = srq[r];
 #pragma unroll
                 for (int i = 0; i < 8; ++i) x[i] *= rq * sEm[c0 + i];
-                bf16x8 hi, lo;
-                split8(x, hi, lo);
-                *reinterpret_cast<bf16x8*>(rec + REC_QG + ((R * 4 + s) * 2 + 0) * FRAG + ln * 16) = hi;
-                *reinterpret_cast<bf16x8*>(rec + REC_QG + ((R * 4 + s) * 2 + 1) * FRAG + ln * 16) = lo;
+                *reinterpret_cast<halfx8*>(rec + REC_QG + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
             }
             float* vec = reinterpret_cast<float*>(rec + REC_VEC);
             if (t1 < D) vec[VEC_GL + t1] = sGL[t1];
-            else if (t1 < 2 * D) vec[VEC_EL + t1 - D] = sEL[t1 - D];
         }
         lds_barrier();
         KDA_PHASE_MARK(2);
@@ -545,25 +548,24 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         KDA_PHASE_MARK(4);
 
         // ======== phase 6: Psi', X', P' fragments out ========
-        for (int f = tid; f < 48 * 64; f += NT) {
+        for (int f = tid; f < 40 * 64; f += NT) {
             const int fr = f >> 6, ln = f & 63;
             const int li = ln & 15, lk = 8 * (ln >> 4);
-            bf16x8 v8;
-            unsigned char* dst;
-            if (fr < 16) {  // Psi' [R][s], hi only: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
+            if (fr < 16) {  // Psi' [R][s], fp16: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
                 const int R = fr >> 2, s = fr & 3;
-                v8 = col8_tr(smem, P_PTH, SN, 32 * s + lk, 16 * R, li);
-                dst = rec + REC_PSI + fr * FRAG + ln * 16;
-            } else if (fr < 32) {  // X' diag(rk beta) [R][s][hl]
+                const floatx8 x = bf8_to_f(col8_tr(smem, P_PTH, SN, 32 * s + lk, 16 * R, li)) +
+                                  bf8_to_f(col8_tr(smem, P_PTL, SN, 32 * s + lk, 16 * R, li));
+                *reinterpret_cast<halfx8*>(rec + REC_PSI + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+            } else if (fr < 32) {  // X' diag(rk beta) [R][s][hl], bf16
                 const int f2 = fr - 16, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
-                v8 = col8_tr(smem, hl ? P_XTL : P_XTH, SN, 32 * s + lk, 16 * R, li);
-                dst = rec + REC_X + f2 * FRAG + ln * 16;
-            } else {  // P' [R][s][hl], row-major in LDS
-                const int f2 = fr - 32, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
-                v8 = ld8(smem, (hl ? P_PL : P_PH) + ((16 * R + li) * SN + 32 * s + lk) * 2);
-                dst = rec + REC_P + f2 * FRAG + ln * 16;
+                *reinterpret_cast<bf16x8*>(rec + REC_X + f2 * FRAG + ln * 16) =
+                    col8_tr(smem, hl ? P_XTL : P_XTH, SN, 32 * s + lk, 16 * R, li);
+            } else {  // P' [R][s], fp16, from the row-major hi/lo planes
+                const int f2 = fr - 32, R = f2 >> 1, s = f2 & 1;
+                const int o = ((16 * R + li) * SN + 32 * s + lk) * 2;
+                const floatx8 x = bf8_to_f(ld8(smem, P_PH + o)) + bf8_to_f(ld8(smem, P_PL + o));
+                *reinterpret_cast<halfx8*>(rec + REC_P + f2 * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
             }
-            *reinterpret_cast<bf16x8*>(dst) = v8;
         }
         lds_barrier();
         KDA_PHASE_MARK(5);
@@ -610,13 +612,13 @@ __global__ __launch_bounds__(NT) void scan_kernel(
     }
 
     // Operands of one chunk held in registers.
-    //   waves 0-3: a[0..3] Psi'_R (bf16), b X'_R diag(rk beta), vv values of V
-    //   waves 4-7: a[0..7] Qg'_R (hi/lo), b P'_R
-    //   all waves:  kt Ki^T rows 16 wave .. +15; wave 0 also the chunk's vectors (gv)
+    //   waves 0-3: a Psi'_R (fp16), b X'_R diag(rk beta) (bf16 hi/lo), vv values of V
+    //   waves 4-7: a Qg'_R (fp16), b P'_R (fp16)
+    //   all waves:  kt Ke^T rows 16 wave .. +15 (fp16); wave 0 also the chunk's vectors (gv)
     struct Frag {
-        uint4 a[8];
-        uint4 b[4];   // [s*2 + hi/lo]; s = 1 only for wide row blocks
-        uint4 kt[4];  // [s*2 + hi/lo]
+        uint4 a[4];   // [s]
+        uint4 b[4];   // [s*2 + hi/lo] (waves 4-7: hi slot only); s = 1 only for wide row blocks
+        uint4 kt[2];  // [s]
         uint4 gv;     // wave 0: 16 bytes of the vector block (lane l: floats 4l .. 4l+3)
         uint32_t vv[NTL][4];  // bf16 bits, zero-extended (packed only at use)
     };
@@ -642,40 +644,24 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                         F.vv[t][j] = __builtin_amdgcn_raw_buffer_load_b16(
                             vr, ((16 * R + 4 * l4 + j) * row_stride + DVT * t + l16) * 2, 0, 0);
             }
-            if (forms_d) {
+            const int abase = forms_d ? REC_PSI : REC_QG;
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    F.a[s] = *reinterpret_cast<const uint4*>(rec + REC_PSI + (R * 4 + s) * FRAG + lane * 16);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 2; ++s)
-#pragma unroll
-                    for (int hl = 0; hl < 2; ++hl)
-                        F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
-            }
+            for (int s = 0; s < 4; ++s)
+                F.a[s] = *reinterpret_cast<const uint4*>(rec + abase + (R * 4 + s) * FRAG + lane * 16);
         } else if (part == 1) {
-            if (!forms_d) {
+            // waves 0-3: X' (bf16 hi/lo) in b[2s + hl]; waves 4-7: P' (fp16) in b[2s]
+            const unsigned char* xb = rec + REC_X + (R * 2 * 2) * FRAG + lane * 16;
+            const unsigned char* pb = rec + REC_P + (R * 2) * FRAG + lane * 16;
 #pragma unroll
-                for (int s = 2; s < 4; ++s)
-#pragma unroll
-                    for (int hl = 0; hl < 2; ++hl)
-                        F.a[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_QG, R, 4, s, hl, lane));
-            }
-            const int bbase = forms_d ? REC_X : REC_P;
-#pragma unroll
-            for (int hl = 0; hl < 2; ++hl)
-                F.b[hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, 0, hl, lane));
-            if (wide) {
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    F.b[2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, bbase, R, 2, 1, hl, lane));
+            for (int s = 0; s < 2; ++s) {
+                if (s == 1 && !wide) break;
+                F.b[2 * s] = *reinterpret_cast<const uint4*>(forms_d ? xb + (2 * s) * FRAG : pb + s * FRAG);
+                if (forms_d) F.b[2 * s + 1] = *reinterpret_cast<const uint4*>(xb + (2 * s + 1) * FRAG);
             }
         } else {
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-                    F.kt[s * 2 + hl] = *reinterpret_cast<const uint4*>(frag_ptr(rec, REC_KIT, wave, 2, s, hl, lane));
+                F.kt[s] = *reinterpret_cast<const uint4*>(rec + REC_KE + (wave * 2 + s) * FRAG + lane * 16);
             if (wave == 0) F.gv = *reinterpret_cast<const uint4*>(rec + REC_VEC + lane * 16);
         }
     };
@@ -688,14 +674,14 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         const int L = active ? static_cast<int>(min64(C, t_last - tok0)) : 0;
         const int slot = L_::VEC + (cg & 1) * 1024;
         load(Fn, cg_next, lane, 0);
-        // (a) S^T (bf16 hi/lo), V^T, the chunk's vectors
+        // (a) S^T (fp16 hi/lo), V^T (bf16), the chunk's vectors
 #pragma unroll
         for (int t = 0; t < NTL; ++t) {
-            bf16x4 hi, lo;
-            split4(S[t], hi, lo);
+            halfx4 hi, lo;
+            split4h(S[t], hi, lo);
             const int o = ((DVT * t + l16) * SW + 16 * wave + 4 * l4) * 2;
-            *reinterpret_cast<bf16x4*>(smem + L_::STH + o) = hi;
-            *reinterpret_cast<bf16x4*>(smem + L_::STL + o) = lo;
+            *reinterpret_cast<halfx4*>(smem + L_::STH + o) = hi;
+            *reinterpret_cast<halfx4*>(smem + L_::STL + o) = lo;
             if (forms_d) {
                 const uint2 vp = {F.vv[t][0] | (F.vv[t][1] << 16), F.vv[t][2] | (F.vv[t][3] << 16)};
                 *reinterpret_cast<uint2*>(smem + L_::V + ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2) = vp;
@@ -707,18 +693,22 @@ __global__ __launch_bounds__(NT) void scan_kernel(
         load(Fn, cg_next, lane, 1);
         // (b) waves 0-3: D_R = X'_R diag(rk beta) V - Psi'_R S; waves 4-7: Qg'_R S
         floatx4 acc[NTL];
-        if (forms_d) {
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) {
-                acc[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NTL; ++t) {
+            // two accumulation chains, summed at the end
+            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; s += 2) {
+                const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
+                const halfx8 x0 = as_halfx8(F.a[s]), x1 = as_halfx8(F.a[s + 1]);
+                a0 = mmah(x0, ldh8(smem, L_::STH + ko), a0);
+                a0 = mmah(x0, ldh8(smem, L_::STL + ko), a0);
+                a1 = mmah(x1, ldh8(smem, L_::STH + ko + 64), a1);
+                a1 = mmah(x1, ldh8(smem, L_::STL + ko + 64), a1);
+            }
+            acc[t] = a0 + a1;
+            if (forms_d) {
                 floatx4 d0 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
-                    const bf16x8 a = as_bf16x8(F.a[s]);
-                    acc[t] = mma(a, ld8(smem, L_::STH + ko), acc[t]);
-                    acc[t] = mma(a, ld8(smem, L_::STL + ko), acc[t]);
-                }
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     if (s == 1 && !wide) break;
@@ -726,43 +716,29 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                     d0 = mma(as_bf16x8(F.b[2 * s]), vb, d0);
                     d0 = mma(as_bf16x8(F.b[2 * s + 1]), vb, d0);
                 }
-                bf16x4 hi, lo;
-                split4(d0 - acc[t], hi, lo);
+                halfx4 hi, lo;
+                split4h(d0 - acc[t], hi, lo);
                 const int o = ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2;
-                *reinterpret_cast<bf16x4*>(smem + L_::DH + o) = hi;
-                *reinterpret_cast<bf16x4*>(smem + L_::DL + o) = lo;
-            }
-        } else {
-#pragma unroll
-            for (int t = 0; t < NTL; ++t) {
-                // two accumulation chains, summed at the end
-                floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int s = 0; s < 4; s += 2) {
-                    const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
-                    a0 = mma3(as_bf16x8(F.a[2 * s]), as_bf16x8(F.a[2 * s + 1]), ld8(smem, L_::STH + ko),
-                              ld8(smem, L_::STL + ko), a0);
-                    a1 = mma3(as_bf16x8(F.a[2 * s + 2]), as_bf16x8(F.a[2 * s + 3]), ld8(smem, L_::STH + ko + 64),
-                              ld8(smem, L_::STL + ko + 64), a1);
-                }
-                acc[t] = a0 + a1;
+                *reinterpret_cast<halfx4*>(smem + L_::DH + o) = hi;
+                *reinterpret_cast<halfx4*>(smem + L_::DL + o) = lo;
             }
         }
         lds_barrier();
         KDA_PHASE_MARK(9);
         load(Fn, cg_next, lane, 2);
-        // (c) U = Ki^T D and the state update; waves 4-7: O_R = Qg'_R S + P'_R D
+        // (c) U = Ke^T D and the state update; waves 4-7: O_R = Qg'_R S + P'_R D
         {
             const floatx4 gl = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_GL + 16 * wave + 4 * l4) * 4);
-            const floatx4 el = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_EL + 16 * wave + 4 * l4) * 4);
+            const halfx8 k0 = as_halfx8(F.kt[0]), k1 = as_halfx8(F.kt[1]);
 #pragma unroll
             for (int t = 0; t < NTL; ++t) {
                 floatx4 u = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
                 const int ko = ((DVT * t + l16) * SN + 8 * l4) * 2;
-                u = mma3(as_bf16x8(F.kt[0]), as_bf16x8(F.kt[1]), ld8(smem, L_::DH + ko), ld8(smem, L_::DL + ko), u);
-                u1 = mma3(as_bf16x8(F.kt[2]), as_bf16x8(F.kt[3]), ld8(smem, L_::DH + ko + 64),
-                          ld8(smem, L_::DL + ko + 64), u1);
-                const floatx4 s_new = gl * S[t] + el * (u + u1);
+                u = mmah(k0, ldh8(smem, L_::DH + ko), u);
+                u1 = mmah(k1, ldh8(smem, L_::DH + ko + 64), u1);
+                u = mmah(k0, ldh8(smem, L_::DL + ko), u);
+                u1 = mmah(k1, ldh8(smem, L_::DL + ko + 64), u1);
+                const floatx4 s_new = gl * S[t] + (u + u1);
                 S[t] = active ? s_new : S[t];
             }
         }
@@ -773,8 +749,9 @@ __global__ __launch_bounds__(NT) void scan_kernel(
                 for (int s = 0; s < 2; ++s) {
                     if (s == 1 && !wide) break;
                     const int ko = ((DVT * t + l16) * SN + 32 * s + 8 * l4) * 2;
-                    acc[t] = mma3(as_bf16x8(F.b[2 * s]), as_bf16x8(F.b[2 * s + 1]), ld8(smem, L_::DH + ko),
-                                  ld8(smem, L_::DL + ko), acc[t]);
+                    const halfx8 pb = as_halfx8(F.b[2 * s]);
+                    acc[t] = mmah(pb, ldh8(smem, L_::DH + ko), acc[t]);
+                    acc[t] = mmah(pb, ldh8(smem, L_::DL + ko), acc[t]);
                 }
             }
         }

@@ -36,6 +36,11 @@
  *     Otherwise the reference is the start of each aligned 16-token block and
  *     the sum over every such block must be >= -80.  Chunks are counted from
  *     the start of each sequence.  Decode has no such limit.
+ *   - With bf16 q/k/v and dk = 128 the chunk pass carries the state and the
+ *     per-chunk operands through fp16 (11 significant bits, largest finite
+ *     value 65504): |k|, |v| and the entries of the state must stay well
+ *     below 1e4 (with qk_l2norm = 0 also |q|).  Values beyond it overflow to
+ *     Inf in the result.
  *   - Setting the environment variable KDA_DEBUG=1 makes every call wait for
  *     its own kernels and report their errors (this synchronises the stream).
  */
@@ -97,7 +102,7 @@ const char *kda_last_error(void);
  * is prepared independently and its state-independent operands are stored in
  * the workspace, then a short scan carries the state across chunks.  The size
  * is 4 * (N + 1) bytes of chunk offsets rounded up to a multiple of 256, plus
- * 115712 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 2 KiB per
+ * 74752 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 2 KiB per
  * token and head).  Other configurations keep everything on chip and need 0.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
