@@ -50,6 +50,28 @@ __device__ __forceinline__ void split4h(const floatx4& x, halfx4& hi, halfx4& lo
     lo = __builtin_convertvector(x - __builtin_convertvector(hi, floatx4), halfx4);
 }
 
+// fp16 hi/lo pair of eight floats (a then b) in MFMA operand order.  hi is
+// the rounded conversion; lo = round(x - hi) comes from one mixed-precision
+// FMA per value (x - hi is exact in fp32, so the single rounding gives the
+// same lo as converting hi back and subtracting).
+__device__ __forceinline__ void split8h(const floatx4& a, const floatx4& b, halfx8& hi, halfx8& lo) {
+    const halfx4 ha = __builtin_convertvector(a, halfx4), hb = __builtin_convertvector(b, halfx4);
+    hi = halfx8{ha[0], ha[1], ha[2], ha[3], hb[0], hb[1], hb[2], hb[3]};
+    const uint4 h = __builtin_bit_cast(uint4, hi);
+    uint4 l = {0u, 0u, 0u, 0u};
+    const float x[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    const uint32_t hw[4] = {h.x, h.y, h.z, h.w};
+    uint32_t lw[4] = {l.x, l.y, l.z, l.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        asm("v_fma_mixlo_f16 %0, %1, 1.0, -%2 op_sel_hi:[0,0,1]" : "+v"(lw[k]) : "v"(x[2 * k]), "v"(hw[k]));
+        asm("v_fma_mixhi_f16 %0, %1, 1.0, -%2 op_sel:[0,0,1] op_sel_hi:[0,0,1]"
+            : "+v"(lw[k])
+            : "v"(x[2 * k + 1]), "v"(hw[k]));
+    }
+    lo = __builtin_bit_cast(halfx8, uint4{lw[0], lw[1], lw[2], lw[3]});
+}
+
 __device__ __forceinline__ bf16x8 ld8(const unsigned char* smem, int off_bytes) {
     return *reinterpret_cast<const bf16x8*>(smem + off_bytes);
 }
@@ -79,18 +101,67 @@ __device__ __forceinline__ bf16x8 as_bf16x8(const uint4& u) { return __builtin_b
 // same result as gather8, in two LDS instructions instead of eight).
 // base: byte offset of the array in LDS, stride: row stride in elements,
 // r0, c0: per 16-lane group; l16: the lane's index in its group.
+// col8_tr2 takes the two groups of four rows from independent starts r0, r1.
 typedef short shortx4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ bf16x8 col8_tr(const unsigned char* smem, int base, int stride, int r0, int c0, int l16) {
-    const int off = base + ((r0 + (l16 >> 2)) * stride + c0 + 4 * (l16 & 3)) * 2;
+__device__ __forceinline__ bf16x8 col8_tr2(const unsigned char* smem, int base, int stride, int r0, int r1, int c0,
+                                           int l16) {
+    const int col = c0 + 4 * (l16 & 3);
     typedef __attribute__((address_space(3))) shortx4* lds_v4;
-    const shortx4 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + off));
-    const shortx4 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + off + 4 * stride * 2));
-    const shortx4 lo4 = a, hi4 = b;
-    const short t[8] = {lo4[0], lo4[1], lo4[2], lo4[3], hi4[0], hi4[1], hi4[2], hi4[3]};
+    const shortx4 a =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + base + ((r0 + (l16 >> 2)) * stride + col) * 2));
+    const shortx4 b =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4)(smem + base + ((r1 + (l16 >> 2)) * stride + col) * 2));
+    const short t[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     bf16x8 r;
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, t[i]);
     return r;
+}
+
+__device__ __forceinline__ bf16x8 col8_tr(const unsigned char* smem, int base, int stride, int r0, int c0, int l16) {
+    return col8_tr2(smem, base, stride, r0, r0 + 4, c0, l16);
+}
+
+// Two floats to packed bf16 (round to nearest even in hardware): element 0 in
+// the low half.  (Converting a four-wide vector and taking its elements
+// apart is avoided: the compiler at hand keeps only element 0 there.)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    const floatx2 xv = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(xv, bf16x2v));
+}
+
+// Four bf16 at smem[off_bytes] (8-byte aligned).
+__device__ __forceinline__ bf16x4 ld4(const unsigned char* smem, int off_bytes) {
+    return *reinterpret_cast<const bf16x4*>(smem + off_bytes);
+}
+
+// Direct copy global -> LDS: each lane's 16 bytes at src + off land at
+// lds + off + 16 * lane (lds is wave-uniform; it goes to M0; the constant
+// off is the instruction offset, which applies to both addresses).  Counted
+// by vmcnt like any other load; the data is in LDS once the count says so.
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+template <int OFF>
+__device__ __forceinline__ void copy16_to_lds(const void* src, lds_u8* lds) {
+    typedef __attribute__((address_space(1))) void gvoid;
+    typedef __attribute__((address_space(3))) void lvoid;
+    __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)lds, 16, OFF, 0);
+}
+
+// Buffer form: lane l's 16 bytes at byte voff of the resource land at
+// lds + 16 l; bytes past the resource's end read as zero.
+__device__ __forceinline__ void copy16_to_lds_buf(__amdgpu_buffer_rsrc_t r, int voff, lds_u8* lds) {
+    typedef __attribute__((address_space(3))) void lvoid;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lvoid*)lds, 16, voff, 0, 0, 0);
+}
+
+// The same with off = 1024 q, q = 0 .. 3 chosen at run time (a constant after unrolling).
+__device__ __forceinline__ void copy16_to_lds_q(const void* src, lds_u8* lds, int q) {
+    switch (q) {
+        case 0: copy16_to_lds<0>(src, lds); break;
+        case 1: copy16_to_lds<1024>(src, lds); break;
+        case 2: copy16_to_lds<2048>(src, lds); break;
+        default: copy16_to_lds<3072>(src, lds); break;
+    }
 }
 
 // Workgroup barrier that orders LDS only.  __syncthreads() also waits for

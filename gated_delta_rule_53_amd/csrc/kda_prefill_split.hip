@@ -25,15 +25,18 @@
 //   prep_kernel       persistent, fully parallel over (chunk, head): builds
 //                     Kg/Qg/Ki, A and P on MFMA, the four 16x16 diagonal
 //                     inverses, W_RJ = -X_RR A'_RJ, and solves for Psi' and X'
-//                     by block forward substitution.  Writes Psi', Qg', Ki^T,
-//                     X', P' and three vectors to a per-(chunk, head) record,
-//                     in the lane order the scan's MFMA operands use.
-//   scan_kernel       per (sequence, head, 16-column value tile): the chunk
-//                     chain above; per chunk two barriers and 36 bf16 MFMAs
-//                     on the dependent path.  The next chunk's record is
-//                     prefetched into registers during the current one.
-// All operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except k.k in
-// A (inverted afterwards); the 16x16 diagonal inverses are fp32.
+//                     by block forward substitution.  Writes -Psi', Qg', Ke^T,
+//                     X', P' and e^{G_last} to a per-(chunk, head) record, in
+//                     the lane order the scan's MFMA operands use.
+//   scan_kernel       one wave per (sequence, head, 16-column value tile)
+//                     runs the chunk chain above alone: the state tile stays
+//                     in MFMA accumulators and is fed back as the B operand
+//                     without moving (see "accumulator order"), so a chunk
+//                     costs no barrier and no LDS exchange.  The record is
+//                     copied into LDS one chunk ahead by direct loads, shared
+//                     by the waves of one workgroup (tiles of one head).
+// Inside prep, operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except
+// k.k in A (inverted afterwards); the 16x16 diagonal inverses are fp32.
 #include "kda_bf16_mfma.h"
 #include "kda_internal.h"
 
@@ -44,13 +47,18 @@ namespace {
 constexpr int C = 64;       // chunk length
 constexpr int D = 128;      // head size
 constexpr int DVT = 16;     // value columns of one MFMA tile in the scan
-constexpr int NT = 512;     // threads per workgroup (both kernels)
+constexpr int PNT = 1024;   // threads per prep workgroup (16 waves)
 constexpr int SW = D + 8;   // bf16 row stride of 128-wide LDS planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
 
 // ---- per-(chunk, head) record written by prep_kernel ----
-// A fragment is one wave-wide MFMA operand: 64 lanes x 16 bytes, lane l
-// holding M[row0 + l%16][k0 + 8*(l/16) .. +7].
+// A fragment is one wave-wide MFMA A operand: 64 lanes x 16 bytes, lane l
+// holding row row0 + l%16 at the eight K indices of lane group g = l/16.
+// Accumulator order: within each 32-wide K block, group g holds K indices
+// 4g .. 4g+3 and 16+4g .. 16+4g+3.  Those are exactly the rows a pair of
+// 16x16 accumulator tiles (K rows 0-15 and 16-31 of the block) leaves in the
+// lanes of group g, so an accumulator pair converts into a B operand in
+// place.  Every fragment below is in accumulator order.
 constexpr int FRAG = 1024;
 // The operands the state meets (Psi', Qg', Ke^T, P') are single fp16; the
 // state side (S, D) is an fp16 hi/lo pair.  fp16 keeps 11 significant bits,
@@ -58,14 +66,15 @@ constexpr int FRAG = 1024;
 // |q_hat||k_hat|, Ke = k e^{G_last - G} by |k|, Psi' by the scaled inverse.
 // X' diag(rk beta), which multiplies the bf16 values V, stays a bf16 hi/lo
 // pair.
-constexpr int REC_PSI = 0;                    // Psi' : [R 4][s 4] fragments, fp16
-constexpr int REC_QG = REC_PSI + 16 * FRAG;   // Qg'  : [R 4][s 4], fp16
-constexpr int REC_KE = REC_QG + 16 * FRAG;    // Ke^T : [c-block 8][s 2], fp16
-constexpr int REC_X = REC_KE + 16 * FRAG;     // X' diag(rk beta) : [R 4][s 2][hi/lo], bf16
-constexpr int REC_P = REC_X + 16 * FRAG;      // P'   : [R 4][s 2], fp16
-constexpr int REC_VEC = REC_P + 8 * FRAG;     // fp32 e^{G_last}[128], unused[128]
-constexpr int VEC_GL = 0;
-constexpr int REC_BYTES = REC_VEC + 256 * 4;  // 74752
+// X' and P' are lower triangular: only the six (R, s) blocks with
+// 32 s <= 16 R + 15 are stored (tri_block).
+constexpr int REC_NPSI = 0;                   // -Psi' : [R 4][s 4] fragments, fp16
+constexpr int REC_QG = 16 * FRAG;             // Qg'   : [R 4][s 4], fp16
+constexpr int REC_KE = 32 * FRAG;             // Ke^T  : [channel block 8][s 2], fp16
+constexpr int REC_X = 48 * FRAG;              // X' diag(rk beta) : [tri 6][hi/lo], bf16
+constexpr int REC_P = 60 * FRAG;              // P'    : [tri 6], fp16
+constexpr int REC_VEC = 66 * FRAG;            // fp32 e^{G_last}[128]
+constexpr int REC_BYTES = REC_VEC + D * 4;    // 68096
 
 // ---- prep_kernel LDS map (bytes) ----
 constexpr int PW = C * SW * 2;                 // 17408: [64][SW] bf16
@@ -99,27 +108,22 @@ constexpr int P_EL = P_EM + D * 4;                              // e^{G_last - G
 constexpr int P_GL = P_EL + D * 4;                              // e^{G_last}
 constexpr int P_LDS = P_GL + D * 4;
 static_assert(P_LDS <= 160 * 1024, "prep LDS budget");
-static_assert(8 * D * 4 <= 4 * 16 * LDS_STR * 4, "wave totals alias the diagonal blocks");
-
-// ---- scan_kernel LDS map (bytes), for NTL column tiles of 16 per workgroup ----
-template <int NTL>
-struct ScanLds {
-    static constexpr int COLS = DVT * NTL;
-    static constexpr int STH = 0, STL = COLS * SW * 2;                     // S^T [COLS][SW] fp16 hi, lo
-    static constexpr int V = 2 * COLS * SW * 2;                            // V^T [COLS][SN] (bf16, exact)
-    static constexpr int DH = V + COLS * SN * 2, DL = DH + COLS * SN * 2;  // D^T [COLS][SN] fp16 hi, lo
-    static constexpr int VEC = DL + COLS * SN * 2;                         // two slots of the vector block
-    static constexpr int BYTES = VEC + 2 * 256 * 4;
-};
+constexpr int P_WT = P_XDH;                                     // 16 wave totals [16][128] fp32 (phase 1 only)
+static_assert(16 * D * 4 <= 4 * 4 * BLK, "wave totals alias X_RR and X_RR diag(rk^2 beta)");
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
-// (R, I) blocks of A and P computed by each wave of prep_kernel.
-__constant__ int8_t kPrepPairs[8][2][2] = {
-    {{0, 0}, {3, 3}}, {{1, 0}, {3, 2}}, {{1, 1}, {3, 1}}, {{2, 0}, {3, 0}},
-    {{2, 1}, {-1, -1}}, {{2, 2}, {-1, -1}}, {{-1, -1}, {-1, -1}}, {{-1, -1}, {-1, -1}},
+// Stored (R, s) blocks of the triangular operands: R = 0, 1 have s = 0 only.
+__host__ __device__ constexpr int tri_block(int R, int s) { return R < 2 ? R : 2 * R - 2 + s; }
+__host__ __device__ constexpr int tri_R(int b) { return b < 2 ? b : 2 + ((b - 2) >> 1); }
+__host__ __device__ constexpr int tri_s(int b) { return b < 2 ? 0 : (b - 2) & 1; }
+
+// (R, I) block of A and P computed by waves 1-10 of prep_kernel (one each).
+__constant__ int8_t kPrepUnit[16][2] = {
+    {-1, -1}, {1, 0}, {3, 3}, {2, 0}, {2, 2}, {2, 1}, {1, 1}, {3, 0},
+    {0, 0}, {3, 1}, {3, 2}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1},
 };
 
 __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* rec, int base, int unit, int ns,
@@ -178,13 +182,13 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 }
 
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(NT) void prep_kernel(
+__global__ __launch_bounds__(PNT) void prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
     const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
     float scale, int l2norm) {
     __shared__ __align__(16) unsigned char smem[P_LDS];
-    float* sWT = reinterpret_cast<float*>(smem + P_LDT);
+    float* sWT = reinterpret_cast<float*>(smem + P_WT);
     float* srk = reinterpret_cast<float*>(smem + P_RK);
     float* srq = reinterpret_cast<float*>(smem + P_RQ);
     float* sbeta = reinterpret_cast<float*>(smem + P_BETA);
@@ -198,9 +202,9 @@ __global__ __launch_bounds__(NT) void prep_kernel(
     const int items = n_chunks * num_heads;
     const int row_stride = num_heads * D;
 
-    // Prefetch registers: rows 2rp, 2rp+1, channels 8cc..8cc+7 of k, q, g; beta.
-    uint4 pk[2], pq[2];
-    floatx4 pg[4];
+    // Prefetch registers: row tid/16, channels 8(tid%16) .. +7 of k, q, g; beta.
+    uint4 pk, pq;
+    floatx4 pg0, pg1;
     float pb = 0.f;
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
@@ -208,22 +212,18 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         const int64_t start = cu_seqlens[n] + static_cast<int64_t>(C) * (cg - offsets[n]);
         const int L = static_cast<int>(min64(C, cu_seqlens[n + 1] - start));
         const size_t base = (static_cast<size_t>(start) * num_heads + h) * D;
-        const int rp = tid >> 4, cc = tid & 15;
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int r = 2 * rp + j;
-            const int off = r * row_stride + 8 * cc;
-            if (r < L) {
-                pk[j] = *reinterpret_cast<const uint4*>(k + base + off);
-                pq[j] = *reinterpret_cast<const uint4*>(q + base + off);
-                pg[2 * j] = *reinterpret_cast<const floatx4*>(g + base + off);
-                pg[2 * j + 1] = *reinterpret_cast<const floatx4*>(g + base + off + 4);
-            } else {
-                pk[j] = uint4{0, 0, 0, 0};
-                pq[j] = uint4{0, 0, 0, 0};
-                pg[2 * j] = floatx4{0.f, 0.f, 0.f, 0.f};
-                pg[2 * j + 1] = floatx4{0.f, 0.f, 0.f, 0.f};
-            }
+        const int r = tid >> 4, cc = tid & 15;
+        const int off = r * row_stride + 8 * cc;
+        if (r < L) {
+            pk = *reinterpret_cast<const uint4*>(k + base + off);
+            pq = *reinterpret_cast<const uint4*>(q + base + off);
+            pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
+            pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
+        } else {
+            pk = uint4{0, 0, 0, 0};
+            pq = uint4{0, 0, 0, 0};
+            pg0 = floatx4{0.f, 0.f, 0.f, 0.f};
+            pg1 = floatx4{0.f, 0.f, 0.f, 0.f};
         }
         if (tid < C) pb = tid < L ? beta[static_cast<size_t>(start + tid) * num_heads + h] : 0.f;
     };
@@ -236,14 +236,13 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         const int lane = opaque(static_cast<int>(threadIdx.x) & 63);
         const int tid = wave * 64 + lane;
         const int l16 = lane & 15, l4 = lane >> 4;
-        const int rp = tid >> 4, cc = tid & 15;
+        const int rp = tid >> 4, cc = tid & 15;  // phase 1: row rp, channels 8cc .. 8cc+7
         const int cg = item / num_heads, h = item - cg * num_heads;
         unsigned char* rec = records + (static_cast<size_t>(cg) * num_heads + h) * REC_BYTES;
 
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const floatx8 kf = unpack8(pk[j]), qf = unpack8(pq[j]);
+        const floatx8 kf = unpack8(pk), qf = unpack8(pq);
+        {
             float sk = 0.f, sq = 0.f;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
@@ -253,15 +252,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             sk = row16_sum(sk);
             sq = row16_sum(sq);
             if (cc == 0) {
-                srk[2 * rp + j] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
-                srq[2 * rp + j] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
+                srk[rp] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+                srq[rp] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
             }
         }
         if (tid < C) sbeta[tid] = pb;
-        const floatx8 g0 = {pg[0][0], pg[0][1], pg[0][2], pg[0][3], pg[1][0], pg[1][1], pg[1][2], pg[1][3]};
-        const floatx8 g1 = {pg[2][0], pg[2][1], pg[2][2], pg[2][3], pg[3][0], pg[3][1], pg[3][2], pg[3][3]};
-        const floatx8 pair = g0 + g1;
-        floatx8 incl = pair;
+        // inclusive prefix of g over the wave's four rows (16-lane groups), then
+        // the totals of the 16 waves through LDS
+        const floatx8 gr = {pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
+        floatx8 incl = gr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float t = __shfl_up(incl[i], 16, 64);
@@ -274,42 +273,39 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc + 4) = floatx4{incl[4], incl[5], incl[6], incl[7]};
         }
         lds_barrier();
-        floatx8 cm = {0, 0, 0, 0, 0, 0, 0, 0};  // (totals of earlier waves) - G_31
+        // G_r - G_31 for this row (token 31 is the last row of wave 7)
+        floatx8 cm = {0, 0, 0, 0, 0, 0, 0, 0};
         {
-            const int lo_w = wave < 4 ? wave : 4, hi_w = wave < 4 ? 4 : wave;
+            const int lo_w = wave < 8 ? wave : 8, hi_w = wave < 8 ? 8 : wave;
             for (int w2 = lo_w; w2 < hi_w; ++w2) {
                 const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc);
                 const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc + 4);
                 cm += floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
             }
-            if (wave < 4) cm = -cm;
+            if (wave < 8) cm = -cm;
         }
-        const floatx8 d0 = (cm + (incl - pair) + g0) * kLog2e;
-        const floatx8 d1 = d0 + g1 * kLog2e;
+        const floatx8 d = (cm + incl) * kLog2e;
         if (tid < 3 * D) {
             const int c = tid & (D - 1), which = tid >> 7;
             float gm = 0.f, gl = 0.f;
 #pragma unroll
-            for (int w2 = 0; w2 < 8; ++w2) {
+            for (int w2 = 0; w2 < 16; ++w2) {
                 const float t = sWT[w2 * D + c];
                 gl += t;
-                if (w2 < 4) gm += t;
+                if (w2 < 8) gm += t;
             }
             const float ex = which == 0 ? gm : (which == 1 ? gl - gm : gl);
             float* dst = which == 0 ? sEm : (which == 1 ? sEL : sGL);
             dst[c] = fast_exp2(ex * kLog2e);
         }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int o = ((2 * rp + j) * SW + 8 * cc) * 2;
-            const floatx8 d = j == 0 ? d0 : d1;
+        {
+            const int o = (rp * SW + 8 * cc) * 2;
             floatx8 e, ei;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 e[i] = fast_exp2(d[i]);
                 ei[i] = fast_exp2(-d[i]);
             }
-            const floatx8 kf = unpack8(pk[j]), qf = unpack8(pq[j]);
             bf16x8 hi, lo;
             split8(kf * e, hi, lo);
             *reinterpret_cast<bf16x8*>(smem + P_KGH + o) = hi;
@@ -320,21 +316,17 @@ __global__ __launch_bounds__(NT) void prep_kernel(
             split8(kf * ei, hi, lo);
             *reinterpret_cast<bf16x8*>(smem + P_KIH + o) = hi;
             *reinterpret_cast<bf16x8*>(smem + P_KIL + o) = lo;
-            __builtin_amdgcn_sched_barrier(0);
         }
         // the next item's loads fly from here on
         if (it + static_cast<int>(gridDim.x) < items) fetch(items - 1 - (it + static_cast<int>(gridDim.x)), tid);
         lds_barrier();
         KDA_PHASE_MARK(0);
 
-        // ======== phase 2: A' and P' blocks (K = 128 channels) ========
-        floatx4 pacc[2];
-#pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            pacc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
-            const int R = kPrepPairs[wave][u][0], I = kPrepPairs[wave][u][1];
-            if (R < 0) continue;
-            const int ar = (16 * R + l16) * SW, br = (16 * I + l16) * SW;
+        // ======== phase 2: A' and P' blocks (K = 128 channels), one per wave 1-10 ========
+        const int uR = kPrepUnit[wave][0], uI = kPrepUnit[wave][1];
+        floatx4 pacc = {0.f, 0.f, 0.f, 0.f};
+        if (uR >= 0) {
+            const int ar = (16 * uR + l16) * SW, br = (16 * uI + l16) * SW;
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
@@ -344,18 +336,18 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 accA = mma(ld8(smem, P_KGH + (ar + ko) * 2), bh, accA);
                 accP = mma3(ld8(smem, P_QGH + (ar + ko) * 2), ld8(smem, P_QGL + (ar + ko) * 2), bh, bl, accP);
             }
-            floatx4 a, pv;
+            floatx4 a;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const int r = 16 * R + 4 * l4 + j;
+                const int r = 16 * uR + 4 * l4 + j;
                 const float rk = srk[r];
                 a[j] = sbeta[r] * rk * rk * accA[j];
-                pv[j] = srq[r] * accP[j];
+                pacc[j] = srq[r] * accP[j];
             }
-            if (I < R) {
+            if (uI < uR) {
                 bf16x4 hi, lo;
                 split4(a, hi, lo);
-                const int o = ((pair_index(R, I) * 16 + l16) * WSTR + 4 * l4) * 2;
+                const int o = ((pair_index(uR, uI) * 16 + l16) * WSTR + 4 * l4) * 2;
                 *reinterpret_cast<bf16x4*>(smem + P_ATH + o) = hi;
                 *reinterpret_cast<bf16x4*>(smem + P_ATL + o) = lo;
             } else {
@@ -363,16 +355,15 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 for (int j = 0; j < 4; ++j) {
                     const int lr = 4 * l4 + j;
                     a[j] = l16 < lr ? a[j] : (l16 == lr ? 1.f : 0.f);
-                    pv[j] = l16 <= lr ? pv[j] : 0.f;
+                    pacc[j] = l16 <= lr ? pacc[j] : 0.f;
                 }
-                *reinterpret_cast<floatx4*>(smem + P_LDT + ((R * 16 + l16) * LDS_STR + 4 * l4) * 4) = a;
+                *reinterpret_cast<floatx4*>(smem + P_LDT + ((uR * 16 + l16) * LDS_STR + 4 * l4) * 4) = a;
             }
-            pacc[u] = pv;
         }
         lds_barrier();
         KDA_PHASE_MARK(1);
 
-        // ======== phase 3: diagonal inverses (wave 0); P', Ki^T, Qg', vectors (waves 1-7) ========
+        // ======== phase 3: diagonal inverses (wave 0); P' (waves 1-10), Ke^T, Qg', vectors ========
         if (wave == 0) {
             const float* ldt = reinterpret_cast<const float*>(smem + P_LDT) + l4 * 16 * LDS_STR;
             float x[16];
@@ -408,55 +399,59 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 *reinterpret_cast<__bf16*>(smem + P_XFH + o) = fh;
                 *reinterpret_cast<__bf16*>(smem + P_XFL + o) = static_cast<__bf16>(xf - static_cast<float>(fh));
             }
-        }
-        // P' from the accumulators of phase 2 (any wave)
+        } else {
+            if (uR >= 0) {
+                // P' from this wave's accumulator of phase 2
+                bf16x4 hi, lo;
+                split4(pacc, hi, lo);
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            const int R = kPrepPairs[wave][u][0], I = kPrepPairs[wave][u][1];
-            if (R < 0) continue;
-            bf16x4 hi, lo;
-            split4(pacc[u], hi, lo);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int o = ((16 * R + 4 * l4 + j) * SN + 16 * I + l16) * 2;
-                *reinterpret_cast<__bf16*>(smem + P_PH + o) = hi[j];
-                *reinterpret_cast<__bf16*>(smem + P_PL + o) = lo[j];
+                for (int j = 0; j < 4; ++j) {
+                    const int o = ((16 * uR + 4 * l4 + j) * SN + 16 * uI + l16) * 2;
+                    *reinterpret_cast<__bf16*>(smem + P_PH + o) = hi[j];
+                    *reinterpret_cast<__bf16*>(smem + P_PL + o) = lo[j];
+                }
+            } else if (wave == 15) {
+                // blocks (0,1) and (2,3) lie in the K range of 32-wide steps and read as zero
+                const int blk = lane >> 5, row = (lane >> 1) & 15, part = lane & 1;
+                const int r = (blk ? 32 : 0) + row, c0 = (blk ? 48 : 16) + 8 * part;
+                const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
+                *reinterpret_cast<bf16x8*>(smem + P_PH + (r * SN + c0) * 2) = z;
+                *reinterpret_cast<bf16x8*>(smem + P_PL + (r * SN + c0) * 2) = z;
             }
-        }
-        if (wave == 7) {
-            // blocks (0,1) and (2,3) lie in the K range of 32-wide steps and read as zero
-            const int blk = lane >> 5, row = (lane >> 1) & 15, part = lane & 1;
-            const int r = (blk ? 32 : 0) + row, c0 = (blk ? 48 : 16) + 8 * part;
-            const bf16x8 z = {0, 0, 0, 0, 0, 0, 0, 0};
-            *reinterpret_cast<bf16x8*>(smem + P_PH + (r * SN + c0) * 2) = z;
-            *reinterpret_cast<bf16x8*>(smem + P_PL + (r * SN + c0) * 2) = z;
-        }
-        if (wave >= 1) {
-            const int t1 = tid - 64;  // 0..447
-            // Ke^T fragments: lane holds Ki[32s + 8(l/16) + i][16w + l%16] e^{G_last - G_31}[16w + l%16]
-            //   = k e^{G_last - G} for 8 tokens of one channel (the decay to the chunk's end)
-            for (int f = t1; f < 16 * 64; f += 448) {
+            const int t1 = tid - 64;  // 0..959: 32 fragments over waves 1-15
+            for (int f = t1; f < 32 * 64; f += PNT - 64) {
                 const int fr = f >> 6, ln = f & 63;
-                const int w = fr >> 1, s = fr & 1;
-                const int r0 = 32 * s + 8 * (ln >> 4), c = 16 * w + (ln & 15);
-                floatx8 x = bf8_to_f(col8_tr(smem, P_KIH, SW, r0, 16 * w, ln & 15)) +
-                            bf8_to_f(col8_tr(smem, P_KIL, SW, r0, 16 * w, ln & 15));
-                x *= sEL[c];
-                *reinterpret_cast<halfx8*>(rec + REC_KE + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
-            }
-            // Qg' fragments: rq_r Qg[r][c] e^{G_31}[c]
-            for (int f = t1; f < 16 * 64; f += 448) {
-                const int fr = f >> 6, ln = f & 63;
-                const int R = fr >> 2, s = fr & 3;
-                const int r = 16 * R + (ln & 15), c0 = 32 * s + 8 * (ln >> 4);
-                floatx8 x = bf8_to_f(ld8(smem, P_QGH + (r * SW + c0) * 2)) + bf8_to_f(ld8(smem, P_QGL + (r * SW + c0) * 2));
-                const float rq = srq[r];
+                const int li = ln & 15, ka = 4 * (ln >> 4);  // K indices ka .. ka+3, ka+16 .. ka+19
+                if (fr < 16) {
+                    // Ke^T [w][s]: Ki[32s + k][16w + li] e^{G_last - G_31}[16w + li]
+                    //   = k e^{G_last - G} (the decay to the chunk's end) at tokens 32s + k
+                    const int w = fr >> 1, s = fr & 1;
+                    const int r0 = 32 * s + ka;
+                    floatx8 x = bf8_to_f(col8_tr2(smem, P_KIH, SW, r0, r0 + 16, 16 * w, li)) +
+                                bf8_to_f(col8_tr2(smem, P_KIL, SW, r0, r0 + 16, 16 * w, li));
+                    x *= sEL[16 * w + li];
+                    *reinterpret_cast<halfx8*>(rec + REC_KE + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+                } else {
+                    // Qg' [R][s]: rq_r Qg[r][c] e^{G_31}[c] at channels c = 32s + k
+                    const int f2 = fr - 16, R = f2 >> 2, s = f2 & 3;
+                    const int r = 16 * R + li, c0 = 32 * s + ka;
+                    const int o = (r * SW + c0) * 2;
+                    const bf16x4 h0 = ld4(smem, P_QGH + o), h1 = ld4(smem, P_QGH + o + 32);
+                    const bf16x4 q0 = ld4(smem, P_QGL + o), q1 = ld4(smem, P_QGL + o + 32);
+                    const floatx4 e0 = *reinterpret_cast<const floatx4*>(sEm + c0);
+                    const floatx4 e1 = *reinterpret_cast<const floatx4*>(sEm + c0 + 16);
+                    const float rq = srq[r];
+                    floatx8 x;
 #pragma unroll
-                for (int i = 0; i < 8; ++i) x[i] *= rq * sEm[c0 + i];
-                *reinterpret_cast<halfx8*>(rec + REC_QG + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+                    for (int i = 0; i < 4; ++i) {
+                        x[i] = (static_cast<float>(h0[i]) + static_cast<float>(q0[i])) * (rq * e0[i]);
+                        x[4 + i] = (static_cast<float>(h1[i]) + static_cast<float>(q1[i])) * (rq * e1[i]);
+                    }
+                    *reinterpret_cast<halfx8*>(rec + REC_QG + f2 * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+                }
             }
             float* vec = reinterpret_cast<float*>(rec + REC_VEC);
-            if (t1 < D) vec[VEC_GL + t1] = sGL[t1];
+            if (t1 < D) vec[t1] = sGL[t1];
         }
         lds_barrier();
         KDA_PHASE_MARK(2);
@@ -483,11 +478,12 @@ __global__ __launch_bounds__(NT) void prep_kernel(
         KDA_PHASE_MARK(3);
 
         // ======== phase 5: Psi' and X' by block forward substitution ========
-        // Column tile t of Psi' (wave t) and of X' (waves 0-3).  Step R:
-        // out_R = rhs_R + sum_{J<R} W_RJ out_J, with out kept transposed in LDS.
-        {
+        // Waves 0-7: column tile t = wave of Psi'; waves 8-11: column tile
+        // t = wave - 8 of X'.  Step R: out_R = rhs_R + sum_{J<R} W_RJ out_J,
+        // with out kept transposed in LDS (each wave reads only its own rows).
+        if (wave < 8) {
             const bool ok = l4 < 2;
-            const int t = wave, c0 = 16 * t;
+            const int c0 = 16 * wave;
             const float em = sEm[c0 + l16];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
@@ -515,56 +511,65 @@ __global__ __launch_bounds__(NT) void prep_kernel(
                 *reinterpret_cast<bf16x4*>(smem + P_PTL + oo) = lo;
                 asm volatile("" ::: "memory");
             }
-            if (wave < 4) {
+        } else if (wave < 12) {
+            const bool ok = l4 < 2;
+            const int t = wave - 8;
+            // columns scaled by rk beta: the scan multiplies this X' by V directly
+            const float cs = srk[16 * t + l16] * sbeta[16 * t + l16];
 #pragma unroll
-                for (int R = 0; R < 4; ++R) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                    if (R == t) {
-                        // columns scaled by rk beta: the scan multiplies this X' by V directly
-                        const float cs = srk[16 * t + l16] * sbeta[16 * t + l16];
+            for (int R = 0; R < 4; ++R) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (R == t) {
 #pragma unroll
-                        for (int j = 0; j < 4; ++j) {
-                            const int o = ((R * 16 + 4 * l4 + j) * WSTR + l16) * 2;
-                            acc[j] = (static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDH + o)) +
-                                      static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDL + o))) * cs;
-                        }
+                    for (int j = 0; j < 4; ++j) {
+                        const int o = ((R * 16 + 4 * l4 + j) * WSTR + l16) * 2;
+                        acc[j] = (static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDH + o)) +
+                                  static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDL + o))) * cs;
                     }
-                    for (int J = t; J < R; ++J) {
-                        const int wo = ((pair_index(R, J) * 16 + l16) * WSTR + 8 * l4) * 2;
-                        const int xo2 = ((16 * t + l16) * SN + 16 * J + 8 * l4) * 2;
-                        acc = mma3(ld8_if(smem, P_WH + wo, ok), ld8_if(smem, P_WL + wo, ok),
-                                   ld8_if(smem, P_XTH + xo2, ok), ld8_if(smem, P_XTL + xo2, ok), acc);
-                    }
-                    bf16x4 hi, lo;
-                    split4(acc, hi, lo);
-                    const int oo = ((16 * t + l16) * SN + 16 * R + 4 * l4) * 2;
-                    *reinterpret_cast<bf16x4*>(smem + P_XTH + oo) = hi;
-                    *reinterpret_cast<bf16x4*>(smem + P_XTL + oo) = lo;
-                    asm volatile("" ::: "memory");
                 }
+                for (int J = t; J < R; ++J) {
+                    const int wo = ((pair_index(R, J) * 16 + l16) * WSTR + 8 * l4) * 2;
+                    const int xo2 = ((16 * t + l16) * SN + 16 * J + 8 * l4) * 2;
+                    acc = mma3(ld8_if(smem, P_WH + wo, ok), ld8_if(smem, P_WL + wo, ok),
+                               ld8_if(smem, P_XTH + xo2, ok), ld8_if(smem, P_XTL + xo2, ok), acc);
+                }
+                bf16x4 hi, lo;
+                split4(acc, hi, lo);
+                const int oo = ((16 * t + l16) * SN + 16 * R + 4 * l4) * 2;
+                *reinterpret_cast<bf16x4*>(smem + P_XTH + oo) = hi;
+                *reinterpret_cast<bf16x4*>(smem + P_XTL + oo) = lo;
+                asm volatile("" ::: "memory");
             }
         }
         lds_barrier();
         KDA_PHASE_MARK(4);
 
-        // ======== phase 6: Psi', X', P' fragments out ========
-        for (int f = tid; f < 40 * 64; f += NT) {
+        // ======== phase 6: -Psi', X', P' fragments out (K indices in accumulator order) ========
+        for (int f = tid; f < 34 * 64; f += PNT) {
             const int fr = f >> 6, ln = f & 63;
-            const int li = ln & 15, lk = 8 * (ln >> 4);
-            if (fr < 16) {  // Psi' [R][s], fp16: lane holds Psi'[16R + li][32s + lk + i] = Psi'^T[..][..]
-                const int R = fr >> 2, s = fr & 3;
-                const floatx8 x = bf8_to_f(col8_tr(smem, P_PTH, SN, 32 * s + lk, 16 * R, li)) +
-                                  bf8_to_f(col8_tr(smem, P_PTL, SN, 32 * s + lk, 16 * R, li));
-                *reinterpret_cast<halfx8*>(rec + REC_PSI + fr * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
-            } else if (fr < 32) {  // X' diag(rk beta) [R][s][hl], bf16
-                const int f2 = fr - 16, R = f2 >> 2, s = (f2 >> 1) & 1, hl = f2 & 1;
+            const int li = ln & 15, ka = 4 * (ln >> 4);
+            if (fr < 16) {  // -Psi' [R][s], fp16: -Psi'[16R + li][32s + k] = -Psi'^T[32s + k][16R + li]
+                const int R = fr >> 2, s = fr & 3, r0 = 32 * s + ka;
+                const floatx8 x = bf8_to_f(col8_tr2(smem, P_PTH, SN, r0, r0 + 16, 16 * R, li)) +
+                                  bf8_to_f(col8_tr2(smem, P_PTL, SN, r0, r0 + 16, 16 * R, li));
+                *reinterpret_cast<halfx8*>(rec + REC_NPSI + fr * FRAG + ln * 16) = __builtin_convertvector(-x, halfx8);
+            } else if (fr < 28) {  // X' diag(rk beta) [tri][hl], bf16: X'^T[32s + k][16R + li]
+                const int f2 = fr - 16, b = f2 >> 1, hl = f2 & 1;
+                const int R = tri_R(b), r0 = 32 * tri_s(b) + ka;
                 *reinterpret_cast<bf16x8*>(rec + REC_X + f2 * FRAG + ln * 16) =
-                    col8_tr(smem, hl ? P_XTL : P_XTH, SN, 32 * s + lk, 16 * R, li);
-            } else {  // P' [R][s], fp16, from the row-major hi/lo planes
-                const int f2 = fr - 32, R = f2 >> 1, s = f2 & 1;
-                const int o = ((16 * R + li) * SN + 32 * s + lk) * 2;
-                const floatx8 x = bf8_to_f(ld8(smem, P_PH + o)) + bf8_to_f(ld8(smem, P_PL + o));
-                *reinterpret_cast<halfx8*>(rec + REC_P + f2 * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+                    col8_tr2(smem, hl ? P_XTL : P_XTH, SN, r0, r0 + 16, 16 * R, li);
+            } else {  // P' [tri], fp16, from the row-major hi/lo planes
+                const int b = fr - 28, R = tri_R(b);
+                const int o = ((16 * R + li) * SN + 32 * tri_s(b) + ka) * 2;
+                const bf16x4 h0 = ld4(smem, P_PH + o), h1 = ld4(smem, P_PH + o + 32);
+                const bf16x4 q0 = ld4(smem, P_PL + o), q1 = ld4(smem, P_PL + o + 32);
+                floatx8 x;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = static_cast<float>(h0[i]) + static_cast<float>(q0[i]);
+                    x[4 + i] = static_cast<float>(h1[i]) + static_cast<float>(q1[i]);
+                }
+                *reinterpret_cast<halfx8*>(rec + REC_P + b * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
             }
         }
         lds_barrier();
@@ -574,243 +579,298 @@ __global__ __launch_bounds__(NT) void prep_kernel(
 }
 
 // --------------------------------------------------------------------------
-template <typename TOut, int NTL>
-__global__ __launch_bounds__(NT) void scan_kernel(
+// ---- scan_kernel: two waves per (sequence, head, 16-column value tile) ----
+// Wave 0 (the state wave) carries the chunk recurrence alone: D from S, then
+// S'.  Its operands (X', -Psi', Ke^T, e^{G_last} and the chunk's V rows) are
+// copied into LDS two chunks ahead by wave 1 (the output wave), which also
+// forms O = Qg' S + P' D one chunk behind, from S and D handed over through
+// LDS already in B-operand form.  One barrier per chunk.
+constexpr int SB_X = 0;                        // X' diag(rk beta) [tri 6][hl 2]
+constexpr int SB_NP = 12 * FRAG;               // -Psi' [m 4][s 4]
+constexpr int SB_KE = 28 * FRAG;               // Ke^T [w 8][s 2]
+constexpr int SB_V = 44 * FRAG;                // V rows [64][16] bf16
+constexpr int SB_GL = 46 * FRAG;               // e^{G_last}[128] (then 512 bytes of zeros)
+constexpr int SB_BYTES = 47 * FRAG;
+constexpr int XCH = 2 * SB_BYTES;              // exchange, two slots (step parity)
+constexpr int XCH_S = 0;                       // S as B operand: [hl 2][s 4] fragments, fp16
+constexpr int XCH_D = 8 * FRAG;                // D as B operand: [hl 2][s 2]
+constexpr int XCH_SLOT = 12 * FRAG;
+constexpr int SCAN_LDS = XCH + 2 * XCH_SLOT;   // 120832
+static_assert(SCAN_LDS <= 160 * 1024, "scan LDS budget");
+
+constexpr int SCAN_THREADS = 128;
+
+template <typename TOut>
+__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int num_seqs, int num_heads) {
-    using L_ = ScanLds<NTL>;
-    __shared__ __align__(16) unsigned char smem[L_::BYTES];
+    __shared__ __align__(16) unsigned char smem[SCAN_LDS];
     const int chain = blockIdx.x;
     if (chain >= num_seqs * num_heads) return;
     KDA_PHASE_BEGIN
     const int n = chain / num_heads, h = chain % num_heads;
-    const int col0 = blockIdx.y * L_::COLS;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
-    // Waves 0-3 form D (row block R = wave & 3), waves 4-7 the outputs of the
-    // same row blocks; each SIMD (waves w and w+4) holds one of each.
-    const int R = wave & 3;
-    const bool forms_d = wave < 4;
-    const bool wide = R >= 2;       // row blocks 2, 3 reach past the first 32 columns of X' and P'
+    const int col0 = static_cast<int>(blockIdx.y) * DVT;
     const int c_begin = offsets[n], c_end = offsets[n + 1];
+    const int nc = c_end - c_begin;
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
     const int row_stride = num_heads * D;
-
-    // This wave's rows 16 wave .. +15 of the state, NTL tiles of 16 columns.
     const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
-    floatx4 S[NTL];
-    {
-        const int l16 = lane0 & 15, l4 = lane0 >> 4;
-#pragma unroll
-        for (int t = 0; t < NTL; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                S[t][j] = initial_state
-                              ? initial_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + DVT * t + l16]
-                              : 0.f;
-    }
+    auto rec_of = [&](int j) { return records + (static_cast<size_t>(c_begin + j) * num_heads + h) * REC_BYTES; };
+    auto tok_of = [&](int j) { return t_first + static_cast<int64_t>(C) * j; };
+    auto len_of = [&](int j) { return static_cast<int>(min64(C, t_last - tok_of(j))); };
 
-    // Operands of one chunk held in registers.
-    //   waves 0-3: a Psi'_R (fp16), b X'_R diag(rk beta) (bf16 hi/lo), vv values of V
-    //   waves 4-7: a Qg'_R (fp16), b P'_R (fp16)
-    //   all waves:  kt Ke^T rows 16 wave .. +15 (fp16); wave 0 also the chunk's vectors (gv)
-    struct Frag {
-        uint4 a[4];   // [s]
-        uint4 b[4];   // [s*2 + hi/lo] (waves 4-7: hi slot only); s = 1 only for wide row blocks
-        uint4 kt[2];  // [s]
-        uint4 gv;     // wave 0: 16 bytes of the vector block (lane l: floats 4l .. 4l+3)
-        uint32_t vv[NTL][4];  // bf16 bits, zero-extended (packed only at use)
-    };
-    // The loads come in three parts, issued at three points of the previous
-    // chunk's step, so the memory pipeline never holds a whole chunk's requests
-    // in front of the step's own instructions.
-    auto load = [&](Frag& F, int cg, int lane, int part) {
-        const unsigned char* rec = records + (static_cast<size_t>(cg) * num_heads + h) * REC_BYTES;
-        const int l16 = lane & 15, l4 = lane >> 4;
-        if (part == 0) {
-            {
-                // V rows of this wave's row block (waves 4-7 load them too, so
-                // every wave runs the same loads); rows past the chunk's end
-                // read as zero
-                const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
-                const int L = static_cast<int>(min64(C, t_last - tok0));
-                const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0,
-                                            L * row_stride * 2);
+    if (wave == 0) {
+        // ================= state wave =================
+        // S[w][j] = S[16w + 4(l/16) + j][col0 + l%16]: the accumulator layout of U = Ke^T D.
+        floatx4 S[8];
 #pragma unroll
-                for (int t = 0; t < NTL; ++t)
+        for (int w = 0; w < 8; ++w) S[w] = floatx4{0.f, 0.f, 0.f, 0.f};
+        if (initial_state) {
+            const int l16 = lane0 & 15, g = lane0 >> 4;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j)
-                        F.vv[t][j] = __builtin_amdgcn_raw_buffer_load_b16(
-                            vr, ((16 * R + 4 * l4 + j) * row_stride + DVT * t + l16) * 2, 0, 0);
+            for (int w = 0; w < 8; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    S[w][j] = initial_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
+        }
+        // Step j of the chain from state buffer and exchange slot b; an
+        // inactive step (the pad after an odd chunk count) leaves S unchanged.
+        // Each stage's operands are read from LDS into registers a stage
+        // ahead, and independent accumulator chains are issued round-robin.
+        auto step = [&](int b, int lane, bool active) {
+            const unsigned char* sb = smem + b * SB_BYTES;
+            unsigned char* xch = smem + XCH + b * XCH_SLOT;
+            const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
+            // The wave issues in order and its LDS queue is short, so LDS
+            // traffic is spread over small fenced groups, each paired with
+            // compute that does not depend on it.
+            // stage 1 (four groups): S as the B operand, handed over; operands of D
+            halfx8 fx[12], fp[16];
+            bf16x8 vb[2];
+            halfx8 sh[4], sl[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+#pragma unroll
+                for (int i = 3 * s; i < 3 * s + 3; ++i) fx[i] = ldh8(sb, SB_X + i * FRAG + lo16);
+#pragma unroll
+                for (int i = 4 * s; i < 4 * s + 4; ++i) fp[i] = ldh8(sb, SB_NP + i * FRAG + lo16);
+                if (s < 2) {
+                    const int r0 = 32 * s + 4 * g;
+                    vb[s] = col8_tr2(sb, SB_V, DVT, r0, r0 + 16, 0, l16);
+                }
+                split8h(S[2 * s], S[2 * s + 1], sh[s], sl[s]);
+                *reinterpret_cast<halfx8*>(xch + XCH_S + s * FRAG + lo16) = sh[s];
+                *reinterpret_cast<halfx8*>(xch + XCH_S + (4 + s) * FRAG + lo16) = sl[s];
+                __builtin_amdgcn_sched_barrier(0);
             }
-            const int abase = forms_d ? REC_PSI : REC_QG;
+            // stage 2: D = X' diag(rk beta) V - Psi' S (row blocks m round-robin);
+            // operands of U read three per group of MFMAs
+            halfx8 fk[16];
+            floatx4 fg[8];
+            floatx4 Dm[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
-                F.a[s] = *reinterpret_cast<const uint4*>(rec + abase + (R * 4 + s) * FRAG + lane * 16);
-        } else if (part == 1) {
-            // waves 0-3: X' (bf16 hi/lo) in b[2s + hl]; waves 4-7: P' (fp16) in b[2s]
-            const unsigned char* xb = rec + REC_X + (R * 2 * 2) * FRAG + lane * 16;
-            const unsigned char* pb = rec + REC_P + (R * 2) * FRAG + lane * 16;
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                if (s == 1 && !wide) break;
-                F.b[2 * s] = *reinterpret_cast<const uint4*>(forms_d ? xb + (2 * s) * FRAG : pb + s * FRAG);
-                if (forms_d) F.b[2 * s + 1] = *reinterpret_cast<const uint4*>(xb + (2 * s + 1) * FRAG);
-            }
-        } else {
+            for (int m = 0; m < 4; ++m) Dm[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 2; ++s)
-                F.kt[s] = *reinterpret_cast<const uint4*>(rec + REC_KE + (wave * 2 + s) * FRAG + lane * 16);
-            if (wave == 0) F.gv = *reinterpret_cast<const uint4*>(rec + REC_VEC + lane * 16);
-        }
-    };
-    // One chunk.  An inactive step (the pad after an odd chunk count) leaves
-    // S unchanged and stores nothing.  Fn / cg_next: the buffer and chunk
-    // whose loads are issued during this step.
-    auto step = [&](const Frag& F, int cg, int lane, bool active, Frag& Fn, int cg_next) {
-        const int l16 = lane & 15, l4 = lane >> 4;
-        const int64_t tok0 = t_first + static_cast<int64_t>(C) * (cg - c_begin);
-        const int L = active ? static_cast<int>(min64(C, t_last - tok0)) : 0;
-        const int slot = L_::VEC + (cg & 1) * 1024;
-        load(Fn, cg_next, lane, 0);
-        // (a) S^T (fp16 hi/lo), V^T (bf16), the chunk's vectors
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-            halfx4 hi, lo;
-            split4h(S[t], hi, lo);
-            const int o = ((DVT * t + l16) * SW + 16 * wave + 4 * l4) * 2;
-            *reinterpret_cast<halfx4*>(smem + L_::STH + o) = hi;
-            *reinterpret_cast<halfx4*>(smem + L_::STL + o) = lo;
-            if (forms_d) {
-                const uint2 vp = {F.vv[t][0] | (F.vv[t][1] << 16), F.vv[t][2] | (F.vv[t][3] << 16)};
-                *reinterpret_cast<uint2*>(smem + L_::V + ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2) = vp;
-            }
-        }
-        if (wave == 0) *reinterpret_cast<uint4*>(smem + slot + lane * 16) = F.gv;
-        lds_barrier();
-        KDA_PHASE_MARK(8);
-        load(Fn, cg_next, lane, 1);
-        // (b) waves 0-3: D_R = X'_R diag(rk beta) V - Psi'_R S; waves 4-7: Qg'_R S
-        floatx4 acc[NTL];
+                for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-        for (int t = 0; t < NTL; ++t) {
-            // two accumulation chains, summed at the end
-            floatx4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = {0.f, 0.f, 0.f, 0.f};
+                    for (int m = 0; m < 4; ++m)
+                        if (s < (m < 2 ? 1 : 2))
+                            Dm[m] = mma(__builtin_bit_cast(bf16x8, fx[2 * tri_block(m, s) + hl]), vb[s], Dm[m]);
 #pragma unroll
-            for (int s = 0; s < 4; s += 2) {
-                const int ko = ((DVT * t + l16) * SW + 32 * s + 8 * l4) * 2;
-                const halfx8 x0 = as_halfx8(F.a[s]), x1 = as_halfx8(F.a[s + 1]);
-                a0 = mmah(x0, ldh8(smem, L_::STH + ko), a0);
-                a0 = mmah(x0, ldh8(smem, L_::STL + ko), a0);
-                a1 = mmah(x1, ldh8(smem, L_::STH + ko + 64), a1);
-                a1 = mmah(x1, ldh8(smem, L_::STL + ko + 64), a1);
-            }
-            acc[t] = a0 + a1;
-            if (forms_d) {
-                floatx4 d0 = {0.f, 0.f, 0.f, 0.f};
+            for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (s == 1 && !wide) break;
-                    const bf16x8 vb = ld8(smem, L_::V + ((DVT * t + l16) * SN + 32 * s + 8 * l4) * 2);
-                    d0 = mma(as_bf16x8(F.b[2 * s]), vb, d0);
-                    d0 = mma(as_bf16x8(F.b[2 * s + 1]), vb, d0);
+                for (int hl = 0; hl < 2; ++hl) {
+                    const int grp = 2 * s + hl;  // 8 groups of 4 MFMAs, 3 reads each
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) Dm[m] = mmah(fp[4 * m + s], hl ? sl[s] : sh[s], Dm[m]);
+#pragma unroll
+                    for (int q = 3 * grp; q < 3 * grp + 3; ++q) {
+                        if (q < 16)
+                            fk[q] = ldh8(sb, SB_KE + q * FRAG + lo16);
+                        else
+                            fg[q - 16] = *reinterpret_cast<const floatx4*>(sb + SB_GL + (16 * (q - 16) + 4 * g) * 4);
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
-                halfx4 hi, lo;
-                split4h(d0 - acc[t], hi, lo);
-                const int o = ((DVT * t + l16) * SN + 16 * R + 4 * l4) * 2;
-                *reinterpret_cast<halfx4*>(smem + L_::DH + o) = hi;
-                *reinterpret_cast<halfx4*>(smem + L_::DL + o) = lo;
+            KDA_PHASE_MARK(8);
+            // stage 3: D as the B operand (handed over); decay of S
+            halfx8 dh[2], dl[2];
+            floatx4 U[8];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                split8h(Dm[2 * s], Dm[2 * s + 1], dh[s], dl[s]);
+                *reinterpret_cast<halfx8*>(xch + XCH_D + s * FRAG + lo16) = dh[s];
+                *reinterpret_cast<halfx8*>(xch + XCH_D + (2 + s) * FRAG + lo16) = dl[s];
             }
-        }
-        lds_barrier();
-        KDA_PHASE_MARK(9);
-        load(Fn, cg_next, lane, 2);
-        // (c) U = Ke^T D and the state update; waves 4-7: O_R = Qg'_R S + P'_R D
-        {
-            const floatx4 gl = *reinterpret_cast<const floatx4*>(smem + slot + (VEC_GL + 16 * wave + 4 * l4) * 4);
-            const halfx8 k0 = as_halfx8(F.kt[0]), k1 = as_halfx8(F.kt[1]);
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) {
-                floatx4 u = {0.f, 0.f, 0.f, 0.f}, u1 = {0.f, 0.f, 0.f, 0.f};
-                const int ko = ((DVT * t + l16) * SN + 8 * l4) * 2;
-                u = mmah(k0, ldh8(smem, L_::DH + ko), u);
-                u1 = mmah(k1, ldh8(smem, L_::DH + ko + 64), u1);
-                u = mmah(k0, ldh8(smem, L_::DL + ko), u);
-                u1 = mmah(k1, ldh8(smem, L_::DL + ko + 64), u1);
-                const floatx4 s_new = gl * S[t] + (u + u1);
-                S[t] = active ? s_new : S[t];
-            }
-        }
-        if (!forms_d) {
+            for (int w = 0; w < 8; ++w) U[w] = fg[w] * S[w];
+            __builtin_amdgcn_sched_barrier(0);
+            // stage 4: S' = diag(e^{G_last}) S + Ke^T D (channel blocks w round-robin)
 #pragma unroll
-            for (int t = 0; t < NTL; ++t) {
+            for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int s = 0; s < 2; ++s) {
-                    if (s == 1 && !wide) break;
-                    const int ko = ((DVT * t + l16) * SN + 32 * s + 8 * l4) * 2;
-                    const halfx8 pb = as_halfx8(F.b[2 * s]);
-                    acc[t] = mmah(pb, ldh8(smem, L_::DH + ko), acc[t]);
-                    acc[t] = mmah(pb, ldh8(smem, L_::DL + ko), acc[t]);
-                }
-            }
-        }
-        // Exactly 4 NTL stores per lane on every wave, so the wait counts in
-        // the chunk loop are fixed: waves 0-3 (no output) and rows past the
-        // chunk's end go through an empty or shorter range and are dropped.
-        const int out_bytes = forms_d ? 0 : L * row_stride * static_cast<int>(sizeof(TOut));
-        const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok0) * num_heads + h) * D + col0, out_bytes);
+                for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-        for (int t = 0; t < NTL; ++t)
+                    for (int w = 0; w < 8; ++w) U[w] = mmah(fk[2 * w + s], hl ? dl[s] : dh[s], U[w]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const int off = ((16 * R + 4 * l4 + j) * row_stride + DVT * t + l16) * static_cast<int>(sizeof(TOut));
-                if constexpr (sizeof(TOut) == 4)
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[t][j]), orr, off, 0, 0);
-                else
-                    __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(acc[t][j]).bits, orr, off, 0, 0);
-            }
-        KDA_PHASE_MARK(10);
-    };
+            for (int w = 0; w < 8; ++w) S[w] = active ? U[w] : S[w];
+            KDA_PHASE_MARK(9);
+            lds_barrier();
+            KDA_PHASE_MARK(10);
+        };
 
-    // Two register buffers: the loads for chunk c+1 are issued during chunk
-    // c.  Loads past the last chunk re-read it, and the pad step is inactive,
-    // so no memory operation depends on data, and the wait after each step
-    // names exactly what may still be in flight: that step's stores.
-    // (Left to itself the compiler loses count across the loop's back edge and
-    // drains every load, prefetch included, before each chunk.)
-    if (c_begin < c_end) {
-        Frag F0, F1;
-        load(F0, c_begin, lane0, 0);
-        load(F0, c_begin, lane0, 1);
-        load(F0, c_begin, lane0, 2);
-        wait_vmcnt<0>();
-        for (int cg = c_begin; cg < c_end; cg += 2) {
+        lds_barrier();  // the first two chunks' operands are in place
+        for (int j = 0; j < nc; j += 2) {
             const int lane = opaque(lane0);
-            step(F0, cg, lane, true, F1, min(cg + 1, c_end - 1));
-            wait_vmcnt<4 * NTL>();
-            KDA_PHASE_MARK(11);
-            step(F1, cg + 1, lane, cg + 1 < c_end, F0, min(cg + 2, c_end - 1));
-            wait_vmcnt<4 * NTL>();
-            KDA_PHASE_MARK(11);
+            step(0, lane, true);
+            step(1, lane, j + 1 < nc);
         }
-    }
+        if (final_state) {
+            const int l16 = lane0 & 15, g = lane0 >> 4;
+#pragma unroll
+            for (int w = 0; w < 8; ++w)
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    final_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
+        }
+    } else {
+        // ================= output wave =================
+        // Copy of chunk j's state-wave operands into state buffer b.
+        auto fetch = [&](int b, int j, int lane) {
+            lds_u8* dst = (lds_u8*)smem + b * SB_BYTES;
+            const unsigned char* rec = rec_of(j) + lane * 16;
+#pragma unroll
+            for (int f = 0; f < 12; f += 4) {  // X'
+                copy16_to_lds<0>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
+                copy16_to_lds<1024>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
+                copy16_to_lds<2048>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
+                copy16_to_lds<3072>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
+            }
+#pragma unroll
+            for (int f = 0; f < 16; f += 4) {  // -Psi' and Ke^T
+                copy16_to_lds<0>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
+                copy16_to_lds<1024>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
+                copy16_to_lds<2048>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
+                copy16_to_lds<3072>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
+                copy16_to_lds<0>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
+                copy16_to_lds<1024>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
+                copy16_to_lds<2048>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
+                copy16_to_lds<3072>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
+            }
+            // e^{G_last}: 512 bytes; lanes 32-63 read past the record's end as zero
+            copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16, dst + SB_GL);
+            // V rows (lane/2) + 32k, columns 8(lane%2) .. +7; rows past the chunk's end read as zero
+            const int64_t tok0 = tok_of(j);
+            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0,
+                                        len_of(j) * row_stride * 2);
+#pragma unroll
+            for (int k = 0; k < 2; ++k)
+                copy16_to_lds_buf(vr, (((lane >> 1) + 32 * k) * row_stride + 8 * (lane & 1)) * 2,
+                                  dst + SB_V + k * FRAG);
+        };
+        struct Ops {
+            uint4 q[16];  // Qg' [m][s]
+            uint4 p[6];   // P' [tri]
+        };
+        auto load = [&](Ops& o, int j, int lane) {
+            const unsigned char* rec = rec_of(j) + lane * 16;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) o.q[i] = *reinterpret_cast<const uint4*>(rec + REC_QG + i * FRAG);
+#pragma unroll
+            for (int i = 0; i < 6; ++i) o.p[i] = *reinterpret_cast<const uint4*>(rec + REC_P + i * FRAG);
+        };
+        // Output rows of chunk j (O in the accumulator layout of row blocks
+        // m); rows past the chunk's end, and everything when L = 0, fall
+        // outside the range and are dropped.
+        auto store_o = [&](const floatx4 (&O)[4], int j, int L, int lane) {
+            const int l16 = lane & 15, g = lane >> 4;
+            const int out_bytes = L * row_stride * static_cast<int>(sizeof(TOut));
+            const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0, out_bytes);
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const uint32_t p01 = pack_bf16x2(O[m][0], O[m][1]), p23 = pack_bf16x2(O[m][2], O[m][3]);
+                const uint32_t ob[4] = {p01 & 0xffffu, p01 >> 16, p23 & 0xffffu, p23 >> 16};
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) {
+                    const int off = ((16 * m + 4 * g + jj) * row_stride + l16) * static_cast<int>(sizeof(TOut));
+                    if constexpr (sizeof(TOut) == 4)
+                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m][jj]), orr, off, 0, 0);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ob[jj]), orr, off, 0, 0);
+                }
+            }
+        };
+        // Step j (between the state wave's barriers j and j+1): store chunk
+        // j-1's outputs, copy chunk j+2's state operands into the buffer the
+        // state wave has just finished with, request chunk j+1's own operands,
+        // and form chunk j's outputs.  Everything has landed before the barrier.
+        auto step = [&](Ops& cur, Ops& nxt, int b, int lane, int j, floatx4 (&O)[4], int& o_len) {
+            const unsigned char* xch = smem + XCH + b * XCH_SLOT;
+            const int lo16 = lane * 16;
+            store_o(O, j - 1, o_len, lane);
+            o_len = j < nc ? len_of(j) : 0;
+            if (j + 2 < nc) fetch(b, j + 2, lane);
+            load(nxt, min(j + 1, nc - 1), lane);
+            halfx8 sh[4], sl[4], dh[2], dl[2];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                sh[s] = ldh8(xch, XCH_S + s * FRAG + lo16);
+                sl[s] = ldh8(xch, XCH_S + (4 + s) * FRAG + lo16);
+            }
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                dh[s] = ldh8(xch, XCH_D + s * FRAG + lo16);
+                dl[s] = ldh8(xch, XCH_D + (2 + s) * FRAG + lo16);
+            }
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) O[m] = mmah(as_halfx8(cur.q[4 * m + s]), hl ? sl[s] : sh[s], O[m]);
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (s < (m < 2 ? 1 : 2))
+                            O[m] = mmah(as_halfx8(cur.p[tri_block(m, s)]), hl ? dl[s] : dh[s], O[m]);
+            wait_vmcnt<0>();
+        };
 
-    if (final_state) {
-        const int l16 = lane0 & 15, l4 = lane0 >> 4;
+        Ops B0, B1;
+        floatx4 O[4];
 #pragma unroll
-        for (int t = 0; t < NTL; ++t)
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                final_state[head_state + (16 * wave + 4 * l4 + j) * D + col0 + DVT * t + l16] = S[t][j];
+        for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        int o_len = 0;
+        if (nc > 0) {
+            fetch(0, 0, lane0);
+            fetch(1, min(1, nc - 1), lane0);
+            load(B0, 0, lane0);
+            wait_vmcnt<0>();
+        }
+        lds_barrier();
+        for (int j = 0; j < nc; j += 2) {
+            const int lane = opaque(lane0);
+            lds_barrier();
+            step(B0, B1, 0, lane, j, O, o_len);
+            lds_barrier();
+            step(B1, B0, 1, lane, j + 1, O, o_len);
+        }
+        store_o(O, (nc + 1) / 2 * 2 - 1, o_len, lane0);
     }
     KDA_PHASE_END;
 }
 
 // --------------------------------------------------------------------------
-#ifndef SCAN_NTL
-#define SCAN_NTL 1  // 16-column tiles per scan workgroup
-#endif
 
 bool split_prefill_applies(const PrefillArgs& a) { return a.qkv_bf16 && a.head_dim == D; }
 
@@ -846,7 +906,7 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     const size_t max_items = max_chunks * static_cast<size_t>(a.num_heads);
     const unsigned prep_grid = static_cast<unsigned>(max_items < static_cast<size_t>(device_cu_count()) ? max_items : static_cast<size_t>(device_cu_count()));
     if (prep_grid > 0) {
-        prep_kernel<<<prep_grid, NT, 0, stream>>>(static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
+        prep_kernel<<<prep_grid, PNT, 0, stream>>>(static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
                                                   a.g, a.beta, a.cu_seqlens, offsets, records, a.num_seqs,
                                                   a.num_heads, a.scale, a.l2norm);
         e = hipGetLastError();
@@ -854,8 +914,8 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
     // tiles of one chain (linear ids chain + k * grid.x) share an XCD when grid.x % 8 == 0
-    const dim3 grid((chains + 7u) & ~7u, D / (DVT * SCAN_NTL));
-    scan_kernel<TOut, SCAN_NTL><<<grid, NT, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets,
+    const dim3 grid((chains + 7u) & ~7u, D / DVT);
+    scan_kernel<TOut><<<grid, SCAN_THREADS, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets,
                                                          records, a.initial_state, static_cast<TOut*>(a.out),
                                                          a.final_state, a.num_seqs, a.num_heads);
     return hipGetLastError();

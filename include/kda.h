@@ -102,7 +102,7 @@ const char *kda_last_error(void);
  * is prepared independently and its state-independent operands are stored in
  * the workspace, then a short scan carries the state across chunks.  The size
  * is 4 * (N + 1) bytes of chunk offsets rounded up to a multiple of 256, plus
- * 74752 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 2 KiB per
+ * 68096 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 1 KiB per
  * token and head).  Other configurations keep everything on chip and need 0.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
