@@ -9,7 +9,9 @@ step so that the 256 MB Infinity Cache cannot serve a step's reads from the
 previous one.
 
 The decode kernel (kda_recurrent_step) is timed on its own workload, 256
-sequences x 64 steps, H=32, d=128, and reported under ``decode``.
+sequences x 64 steps, H=32, d=128, and reported under ``decode``.  The same
+prefill workload through the fused-gate entry point (kda_chunk_fwd_gated: raw
+bf16 gate and beta activated in the kernel) is reported under ``gated_prefill``.
 
 Kernel durations come from HIP events recorded around every launch on the
 stream the kernels run on; ``roofline.achieved`` divides the algorithmic bytes
@@ -34,6 +36,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 2   # q,k,v bf16; g fp32; beta; out bf16
 STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_HEAD_STEP = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD
+# fused gate: raw gate [dk] and raw beta in bf16 replace fp32 g and beta
+GATED_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 2 + 2 + 128 * 2
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["gated_delta_rule_53_amd/csrc/kda_prefill_split.hip", "gated_delta_rule_53_amd/csrc/kda_bf16_mfma.h",
@@ -111,6 +115,40 @@ def bench_prefill(steps: int, warmup: int):
     alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + x.num_seqs * H * 2 * STATE_BYTES
     return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T,
                 workspace_bytes=workspace.numel())
+
+
+def bench_prefill_gated(steps: int, warmup: int):
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+    import kda_workloads as w
+
+    x = w.prefill_4k()
+    T, H = x.total_tokens, x.num_heads
+    gi = w.make_gate(T, H, x.head_k, torch.bfloat16, seed=1)
+    dev = "cuda:0"
+    copies = []
+    for _ in range(3):
+        copies.append(dict(q=x.q.to(dev), k=x.k.to(dev), v=x.v.to(dev), rg=gi.raw_g.to(dev),
+                           rb=gi.raw_beta.to(dev), cu=x.cu_seqlens.to(dev), s0=x.initial_state.to(dev),
+                           out=torch.empty_like(x.v, device=dev),
+                           fs=torch.empty_like(x.initial_state, device=dev)))
+    a_log, dt_bias = gi.a_log.to(dev), gi.dt_bias.to(dev)
+    prob = kda.Problem(total_tokens=T, num_seqs=x.num_seqs, num_heads=H, head_k=x.head_k, head_v=x.head_v,
+                       qkv_dtype=1, out_dtype=1, scale=x.scale, qk_l2norm=1, chunk_size=64)
+    workspace = torch.empty(max(kda.chunk_fwd_workspace_bytes(prob), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        c = copies[i % 3]
+        kda.chunk_fwd_gated(c["q"], c["k"], c["v"], c["rg"], c["rb"], a_log, dt_bias, c["cu"], c["s0"],
+                            scale=x.scale, out=c["out"], final_state=c["fs"], workspace=workspace)
+
+    for i in range(warmup):
+        step(i)
+    wall, per = time_launches(step, steps, stream)
+    alg_bytes = T * H * GATED_BYTES_PER_TOKEN_HEAD + x.num_seqs * H * 2 * STATE_BYTES
+    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T)
 
 
 def bench_decode(loops: int):
@@ -199,6 +237,9 @@ def main():
           f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
     dc = bench_decode(args.decode_loops)
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    gp = bench_prefill_gated(args.steps, args.warmup)
+    print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    g_achieved = gp["alg_bytes"] / gp["per_launch"] / 1e9
 
     ms_per_step = pf["wall"] / args.steps * 1e3
     tokens_per_s = pf["tokens"] * args.steps / pf["wall"]
@@ -220,8 +261,8 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
-        "dtype_note": "bf16 MFMA operands (hi/lo bf16 pairs where fp32 accuracy is needed), fp32 "
-                      "accumulation and fp32 state",
+        "dtype_note": "MFMA on fp16/bf16 operands (fp16 hi/lo pairs for the state side, bf16 hi/lo "
+                      "where fp32 accuracy is needed in the chunk pass), fp32 accumulation and fp32 state",
         "data": "synthetic",
         "config": {"workload": pf["x"].name, "num_seqs": 1, "seq_len": pf["tokens"],
                    "heads": 32, "head_dim": 128, "chunk": 64, "qkv": "bf16", "g_beta": "f32",
@@ -241,6 +282,13 @@ def main():
                                 "traffic": None if d_tr is None else round(d_tr / dc["per_launch"] / 1e9, 2),
                                 "alg_bytes_per_launch": dc["alg_bytes"],
                                 "launch_us": round(dc["per_launch"] * 1e6, 2)}},
+        "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
+                          "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
+                          "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),
+                                       "bound": "hbm", "achieved": round(g_achieved, 2), "peak": HBM_PEAK_GBS,
+                                       "unit": "GB/s", "frac": round(g_achieved / HBM_PEAK_GBS, 4),
+                                       "traffic": None, "alg_bytes_per_launch": gp["alg_bytes"],
+                                       "launch_us": round(gp["per_launch"] * 1e6, 2)}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

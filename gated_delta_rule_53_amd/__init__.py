@@ -13,19 +13,25 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     KDA_BF16,
     KDA_F32,
+    Gate,
     KdaError,
     Problem,
     abi_version,
     chunk_fwd,
+    chunk_fwd_gated,
     chunk_fwd_workspace_bytes,
     library_path,
     raw_library,
     recurrent_step,
+    recurrent_step_gated,
 )
 
 __all__ = [
     "chunk_fwd",
+    "chunk_fwd_gated",
     "recurrent_step",
+    "recurrent_step_gated",
+    "Gate",
     "chunk_fwd_workspace_bytes",
     "abi_version",
     "library_path",

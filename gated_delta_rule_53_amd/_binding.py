@@ -47,6 +47,17 @@ class Problem(ctypes.Structure):
     ]
 
 
+class Gate(ctypes.Structure):
+    """Mirror of ``kda_gate_t``."""
+
+    _fields_ = [
+        ("a_log", ctypes.c_void_p),
+        ("dt_bias", ctypes.c_void_p),
+        ("has_lower_bound", ctypes.c_int32),
+        ("lower_bound", ctypes.c_float),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -66,6 +77,11 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
+    G = ctypes.POINTER(Gate)
+    lib.kda_chunk_fwd_gated.argtypes = [P, G, vp, vp, vp, vp, vp, vp, fp, vp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_recurrent_step_gated.argtypes = [P, G, vp, vp, vp, vp, vp, fp, vp, vp]
+    lib.kda_recurrent_step_gated.restype = ctypes.c_int
     return lib
 
 
@@ -211,4 +227,99 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
     _check(_lib.kda_recurrent_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state), _ptr(out), _stream(dev)))
+    return out
+
+
+def _gate(a_log: torch.Tensor, dt_bias: torch.Tensor, H: int, dk: int, lower_bound: Optional[float],
+          dev) -> Gate:
+    _need(a_log, "a_log", (H,), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H, dk), torch.float32, dev)
+    return Gate(a_log=a_log.data_ptr(), dt_bias=dt_bias.data_ptr(),
+                has_lower_bound=int(lower_bound is not None),
+                lower_bound=float(0.0 if lower_bound is None else lower_bound))
+
+
+def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: torch.Tensor,
+                    raw_beta: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
+                    cu_seqlens: Optional[torch.Tensor] = None,
+                    initial_state: Optional[torch.Tensor] = None, *, lower_bound: Optional[float] = None,
+                    scale: Optional[float] = None, qk_l2norm: bool = True,
+                    out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
+                    out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                    workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """``chunk_fwd`` with the gate activation fused in (``kda_chunk_fwd_gated``).
+
+    raw_g [T, H, dk] and raw_beta [T, H] in q's dtype; a_log [H] and dt_bias
+    [H, dk] float32; lower_bound None (softplus gate) or a float <= 0 (bounded
+    sigmoid gate).  Other arguments and the result are as for ``chunk_fwd``.
+    """
+    if q.dim() != 3:
+        raise KdaArgumentError(2, f"q must be [T, H, dk], got {tuple(q.shape)}")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = cu_seqlens.numel() - 1
+    _need(q, "q", (T, H, dk), None, dev)
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(v, "v", (T, H, dv), q.dtype, dev)
+    _need(raw_g, "raw_g", (T, H, dk), q.dtype, dev)
+    _need(raw_beta, "raw_beta", (T, H), q.dtype, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, dv), out_dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    ws_bytes = chunk_fwd_workspace_bytes(prob)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kda_chunk_fwd_gated(ctypes.byref(prob), ctypes.byref(gate), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(raw_g), _ptr(raw_beta), _ptr(cu_seqlens), _ptr(initial_state),
+                                    _ptr(out), _ptr(final_state), _ptr(workspace), ws_len, _stream(dev)))
+    return out, final_state
+
+
+def recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: torch.Tensor,
+                         raw_beta: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
+                         state: torch.Tensor, *, lower_bound: Optional[float] = None,
+                         scale: Optional[float] = None, qk_l2norm: bool = True,
+                         out_dtype: Optional[torch.dtype] = None,
+                         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """``recurrent_step`` with the gate activation fused in (``kda_recurrent_step_gated``).
+
+    raw_g [N, H, dk] and raw_beta [N, H] in q's dtype; a_log [H], dt_bias
+    [H, dk] float32; ``state`` is updated in place.
+    """
+    if q.dim() != 3:
+        raise KdaArgumentError(2, f"q must be [N, H, dk], got {tuple(q.shape)}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    _need(k, "k", (N, H, dk), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    _need(raw_g, "raw_g", (N, H, dk), q.dtype, dev)
+    _need(raw_beta, "raw_beta", (N, H), q.dtype, dev)
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", (N, H, dv), out_dtype, dev)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    _check(_lib.kda_recurrent_step_gated(ctypes.byref(prob), ctypes.byref(gate), _ptr(q), _ptr(k), _ptr(v),
+                                         _ptr(raw_g), _ptr(raw_beta), _ptr(state), _ptr(out), _stream(dev)))
     return out

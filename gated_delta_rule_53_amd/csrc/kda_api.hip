@@ -64,6 +64,100 @@ kda_status_t check_problem(const kda_problem_t* p, const char* what) {
     return KDA_OK;
 }
 
+// Gate parameters of the *_gated entry points.
+kda_status_t check_gate(const kda_gate_t* gate, const char* what, kda::GateParams& gp) {
+    if (!gate) return fail(KDA_ERR_NULL_POINTER, "%s: gate is NULL", what);
+    if (!gate->a_log || !gate->dt_bias) return fail(KDA_ERR_NULL_POINTER, "%s: gate a_log and dt_bias are required", what);
+    if (gate->has_lower_bound != 0 && gate->has_lower_bound != 1)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: gate has_lower_bound must be 0 or 1", what);
+    if (gate->has_lower_bound && !(gate->lower_bound <= 0.f && gate->lower_bound > -1e30f))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: gate lower_bound must be finite and <= 0", what);
+    gp.a_log = gate->a_log;
+    gp.dt_bias = gate->dt_bias;
+    gp.has_lower_bound = gate->has_lower_bound;
+    gp.lower_bound = gate->has_lower_bound ? gate->lower_bound : 0.f;
+    return KDA_OK;
+}
+
+kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda::GateParams& gp,
+                            const void* q, const void* k, const void* v, const void* g, const void* beta,
+                            const int32_t* cu_seqlens, const float* initial_state, void* out,
+                            float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    if (p->chunk_size != 0 && p->chunk_size != 64)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
+    if (p->num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "%s: cu_seqlens is NULL", what);
+    if (p->total_tokens > 0 && (!q || !k || !v || !g || !beta || !out))
+        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta and out are required", what);
+    if (p->total_tokens == 0 && !final_state) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    const size_t need = kda_chunk_fwd_workspace_bytes(p);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
+    if (need > 0 && !workspace) return fail(KDA_ERR_NULL_POINTER, "%s: workspace is NULL", what);
+    if (need > 0 && ((p->total_tokens + 63) / 64 + p->num_seqs) * int64_t(p->num_heads) > (int64_t(1) << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: too many (chunk, head) pairs", what);
+    kda::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.gate = gp;
+    a.cu_seqlens = cu_seqlens;
+    a.initial_state = initial_state;
+    a.out = out;
+    a.final_state = final_state;
+    a.total_tokens = p->total_tokens;
+    a.num_seqs = p->num_seqs;
+    a.num_heads = p->num_heads;
+    a.head_dim = p->head_k;
+    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
+    a.out_bf16 = p->out_dtype == KDA_BF16;
+    a.scale = p->scale;
+    a.l2norm = p->qk_l2norm;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (kda::split_prefill_applies(a)) return finish(kda::launch_prefill_split(a, workspace, s), s, what);
+    return finish(kda::launch_prefill(a, s), s, what);
+}
+
+kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const kda::GateParams& gp,
+                                 const void* q, const void* k, const void* v, const void* g,
+                                 const void* beta, float* state, void* out, void* stream) {
+    if (p->total_tokens != p->num_seqs)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld must equal num_seqs = %d (one token each)",
+                    what, (long long)p->total_tokens, p->num_seqs);
+    if (p->num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !g || !beta || !state || !out)
+        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state and out are required", what);
+    kda::DecodeArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.gate = gp;
+    a.state = state;
+    a.out = out;
+    a.num_seqs = p->num_seqs;
+    a.num_heads = p->num_heads;
+    a.head_dim = p->head_k;
+    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
+    a.out_bf16 = p->out_dtype == KDA_BF16;
+    a.scale = p->scale;
+    a.l2norm = p->qk_l2norm;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_decode(a, s), s, what);
+}
+
 }  // namespace
 
 extern "C" {
@@ -98,82 +192,45 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
                            const float* initial_state, void* out, float* final_state,
                            void* workspace, size_t workspace_bytes, void* stream) {
     const char* what = "kda_chunk_fwd";
+    const kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    return chunk_fwd_impl(what, p, kda::GateParams{}, q, k, v, g, beta, cu_seqlens, initial_state, out,
+                          final_state, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_gated(const kda_problem_t* p, const kda_gate_t* gate, const void* q, const void* k,
+                                 const void* v, const void* raw_g, const void* raw_beta,
+                                 const int32_t* cu_seqlens, const float* initial_state, void* out,
+                                 float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+    const char* what = "kda_chunk_fwd_gated";
     kda_status_t st = check_problem(p, what);
     if (st != KDA_OK) return st;
-    if (p->chunk_size != 0 && p->chunk_size != 64)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
-    if (p->num_seqs == 0) {
-        g_last_error[0] = '\0';
-        return KDA_OK;
-    }
-    if (!cu_seqlens) return fail(KDA_ERR_NULL_POINTER, "%s: cu_seqlens is NULL", what);
-    if (p->total_tokens > 0 && (!q || !k || !v || !g || !beta || !out))
-        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta and out are required", what);
-    if (p->total_tokens == 0 && !final_state) {
-        g_last_error[0] = '\0';
-        return KDA_OK;
-    }
-    const size_t need = kda_chunk_fwd_workspace_bytes(p);
-    if (workspace_bytes < need)
-        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
-    if (need > 0 && !workspace) return fail(KDA_ERR_NULL_POINTER, "%s: workspace is NULL", what);
-    if (need > 0 && ((p->total_tokens + 63) / 64 + p->num_seqs) * int64_t(p->num_heads) > (int64_t(1) << 31) - 1)
-        return fail(KDA_ERR_UNSUPPORTED, "%s: too many (chunk, head) pairs", what);
-    kda::PrefillArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.cu_seqlens = cu_seqlens;
-    a.initial_state = initial_state;
-    a.out = out;
-    a.final_state = final_state;
-    a.total_tokens = p->total_tokens;
-    a.num_seqs = p->num_seqs;
-    a.num_heads = p->num_heads;
-    a.head_dim = p->head_k;
-    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
-    a.out_bf16 = p->out_dtype == KDA_BF16;
-    a.scale = p->scale;
-    a.l2norm = p->qk_l2norm;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    if (kda::split_prefill_applies(a)) return finish(kda::launch_prefill_split(a, workspace, s), s, what);
-    return finish(kda::launch_prefill(a, s), s, what);
+    kda::GateParams gp{};
+    st = check_gate(gate, what, gp);
+    if (st != KDA_OK) return st;
+    return chunk_fwd_impl(what, p, gp, q, k, v, raw_g, raw_beta, cu_seqlens, initial_state, out, final_state,
+                          workspace, workspace_bytes, stream);
 }
 
 kda_status_t kda_recurrent_step(const kda_problem_t* p, const void* q, const void* k, const void* v,
                                 const float* g, const float* beta, float* state, void* out,
                                 void* stream) {
     const char* what = "kda_recurrent_step";
+    const kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    return recurrent_step_impl(what, p, kda::GateParams{}, q, k, v, g, beta, state, out, stream);
+}
+
+kda_status_t kda_recurrent_step_gated(const kda_problem_t* p, const kda_gate_t* gate, const void* q,
+                                      const void* k, const void* v, const void* raw_g, const void* raw_beta,
+                                      float* state, void* out, void* stream) {
+    const char* what = "kda_recurrent_step_gated";
     kda_status_t st = check_problem(p, what);
     if (st != KDA_OK) return st;
-    if (p->total_tokens != p->num_seqs)
-        return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld must equal num_seqs = %d (one token each)",
-                    what, (long long)p->total_tokens, p->num_seqs);
-    if (p->num_seqs == 0) {
-        g_last_error[0] = '\0';
-        return KDA_OK;
-    }
-    if (!q || !k || !v || !g || !beta || !state || !out)
-        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state and out are required", what);
-    kda::DecodeArgs a{};
-    a.q = q;
-    a.k = k;
-    a.v = v;
-    a.g = g;
-    a.beta = beta;
-    a.state = state;
-    a.out = out;
-    a.num_seqs = p->num_seqs;
-    a.num_heads = p->num_heads;
-    a.head_dim = p->head_k;
-    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
-    a.out_bf16 = p->out_dtype == KDA_BF16;
-    a.scale = p->scale;
-    a.l2norm = p->qk_l2norm;
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    return finish(kda::launch_decode(a, s), s, what);
+    kda::GateParams gp{};
+    st = check_gate(gate, what, gp);
+    if (st != KDA_OK) return st;
+    return recurrent_step_impl(what, p, gp, q, k, v, raw_g, raw_beta, state, out, stream);
 }
 
 }  // extern "C"

@@ -55,6 +55,42 @@ __device__ __forceinline__ void load_vec(T (&dst)[N], const T* src) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Gate activation on raw inputs (the Ascend model file's gated prefill and
+// decode paths, `_prefill_torch_kda` and the decode branch of the attention
+// forward, with its `_softplus`): u = x + dt_bias[h][c], then
+//   g = -e^{a_log[h]} softplus(u)             or, with a lower bound,
+//   g = lower_bound * sigmoid(e^{a_log[h]} u),
+// and beta = sigmoid(raw beta).
+struct GateParams {
+    const float* a_log;    // [H]; nullptr: g and beta arrive activated, in float32
+    const float* dt_bias;  // [H, dk]
+    float lower_bound;
+    int has_lower_bound;
+};
+
+// e^x and 1/x through the hardware exp2 and reciprocal (about 1 ulp each).
+__device__ __forceinline__ float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float gate_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + gate_exp(-x)); }
+
+// log(1 + y) for y >= 0 to a few ulp: with w = 1 + y rounded, log(w) * y / (w - 1)
+// cancels the rounding of w (Goldberg's correction; w == 1 means log1p(y) = y to
+// float precision).
+__device__ __forceinline__ float gate_log1p(float y) {
+    const float w = 1.f + y;
+    const float d = w - 1.f;
+    const float lw = __builtin_amdgcn_logf(w) * 0.69314718055994531f;  // log2 -> ln
+    return d == 0.f ? y : lw * (y * __builtin_amdgcn_rcpf(d));
+}
+
+// softplus(u) = max(u, 0) + log(1 + e^{-|u|}): no overflow for any u.
+__device__ __forceinline__ float gate_softplus(float u) { return fmaxf(u, 0.f) + gate_log1p(gate_exp(-fabsf(u))); }
+
+// g for raw value x with bias b; a = e^{a_log[h]}.
+__device__ __forceinline__ float gate_g(float x, float b, float a, float lower_bound, int has_lower_bound) {
+    const float u = x + b;
+    return has_lower_bound ? lower_bound * gate_sigmoid(a * u) : -a * gate_softplus(u);
+}
+
 // Sum over the lanes of a wave64 whose lane ids differ only in the bits of `mask_lo..32`.
 __device__ __forceinline__ float wave_sum_from(float x, int first_offset) {
     for (int off = first_offset; off < 64; off <<= 1) x += __shfl_xor(x, off, 64);

@@ -14,6 +14,9 @@
 // so HBM sees exactly one read and one write of the state, 2*dk*dv*4 bytes
 // per (sequence, head), which bounds the kernel.
 //
+// With GATED, g and beta are the raw gate and raw beta (q/k/v dtype),
+// activated here as they are loaded.
+//
 // Launch: one 256-thread workgroup per (sequence, head).  Thread (cg, rg)
 // owns value columns 4cg..4cg+3 of rows rg, rg+NRG, ...: every load and store
 // of the state is a float4, and a wave touches whole 512-byte rows.
@@ -22,11 +25,11 @@
 
 namespace kda {
 
-template <int D, typename TIn, typename TOut>
+template <int D, typename TIn, typename TOut, bool GATED>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta, float* __restrict__ state,
-    TOut* __restrict__ out, float scale, int l2norm) {
+    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, float* __restrict__ state,
+    TOut* __restrict__ out, int num_heads, float scale, int l2norm) {
     constexpr int NCG = D / 4;      // column groups of four
     constexpr int NRG = 256 / NCG;  // row groups
     constexpr int RPT = D / NRG;    // rows per thread
@@ -51,7 +54,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const size_t off = static_cast<size_t>(pair) * D + tid;
         sq[tid] = to_f32(q[off]);
         sk[tid] = to_f32(k[off]);
-        se[tid] = fast_exp2(g[off] * kLog2e);
+        float gv;
+        if constexpr (GATED) {
+            const int h = pair % num_heads;
+            gv = gate_g(to_f32(static_cast<const TIn*>(g)[off]), gp.dt_bias[h * D + tid], gate_exp(gp.a_log[h]),
+                        gp.lower_bound, gp.has_lower_bound);
+        } else {
+            gv = static_cast<const float*>(g)[off];
+        }
+        se[tid] = fast_exp2(gv * kLog2e);
     }
     __syncthreads();
 
@@ -101,7 +112,11 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 
     const size_t voff = static_cast<size_t>(pair) * D + 4 * cg;
-    const float b = beta[pair];
+    float b;
+    if constexpr (GATED)
+        b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[pair]));
+    else
+        b = static_cast<const float*>(beta)[pair];
     floatx4 delta;
 #pragma unroll
     for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
@@ -125,9 +140,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <int D, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads));
-    decode_step_kernel<D, TIn, TOut><<<grid, 256, 0, stream>>>(
-        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
-        a.g, a.beta, a.state, static_cast<TOut*>(a.out), a.scale, a.l2norm);
+    const TIn* q = static_cast<const TIn*>(a.q);
+    const TIn* k = static_cast<const TIn*>(a.k);
+    const TIn* v = static_cast<const TIn*>(a.v);
+    if (a.gate.a_log)
+        decode_step_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.state, static_cast<TOut*>(a.out), a.num_heads, a.scale, a.l2norm);
+    else
+        decode_step_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.state, static_cast<TOut*>(a.out), a.num_heads, a.scale, a.l2norm);
     return hipGetLastError();
 }
 

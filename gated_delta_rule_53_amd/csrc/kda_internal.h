@@ -5,14 +5,20 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "kda_common.h"
+
 namespace kda {
 
+// g and beta are float32 when gate.a_log is null; otherwise they are the raw
+// gate [rows, H, dk] and raw beta [rows, H] in the q/k/v dtype, activated in
+// the kernels.
 struct DecodeArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* g;
-    const float* beta;
+    const void* g;
+    const void* beta;
+    GateParams gate;
     float* state;
     void* out;
     int num_seqs;
@@ -28,8 +34,9 @@ struct PrefillArgs {
     const void* q;
     const void* k;
     const void* v;
-    const float* g;
-    const float* beta;
+    const void* g;
+    const void* beta;
+    GateParams gate;
     const int32_t* cu_seqlens;
     const float* initial_state;
     void* out;

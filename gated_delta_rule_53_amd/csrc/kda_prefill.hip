@@ -29,6 +29,8 @@
 //     a copy in LDS feeds the (Gamma*K) S and (Gamma*Q) S products.
 //   * A tail chunk is masked, not padded: rows past the sequence end read as
 //     k = q = v = g = beta = 0, which makes them no-ops.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -44,13 +46,18 @@ __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2
 
 }  // namespace
 
-template <int D, typename TIn, typename TOut>
+// With GATED, g and beta are the raw gate and raw beta (q/k/v dtype),
+// activated as each chunk is staged; rows past a sequence's end get g = beta = 0.
+template <int D, typename TIn, typename TOut, bool GATED>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const float* __restrict__ g, const float* __restrict__ beta,
+    const void* __restrict__ g_in, const void* __restrict__ beta_in, GateParams gp,
     const int32_t* __restrict__ cu_seqlens, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int64_t total_tokens, int num_seqs, int num_heads, float scale,
     int l2norm) {
+    using GT = typename std::conditional<GATED, TIn, float>::type;  // element type of g and beta
+    const GT* __restrict__ g = static_cast<const GT*>(g_in);
+    const GT* __restrict__ beta = static_cast<const GT*>(beta_in);
     constexpr int SD = D + 2;           // LDS row stride of [64][D] buffers (floats)
     constexpr int NSEG = 256 / D;       // token segments per channel in the cumsum
     constexpr int SEGLEN = kC / NSEG;
@@ -108,7 +115,15 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const int pq = tid >> 4, pc = tid & 15;
     alignas(16) TIn pk[4][CPT];
     alignas(16) TIn pqv[4][CPT];
-    alignas(16) float pg[4][CPT];
+    alignas(16) GT pg[4][CPT];
+    // gate parameters of this thread's channels (one head per workgroup)
+    float gbias[CPT], ga = 0.f;
+    if constexpr (GATED) {
+        ga = gate_exp(gp.a_log[h]);
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) gbias[i] = gp.dt_bias[h * D + CPT * pc + i];
+    }
+    int valid_rows = 0;  // rows of the prefetched chunk inside the sequence
     alignas(16) TIn pv[8];
     float pb = 0.f;
     auto fetch = [&](int64_t c0) {
@@ -126,7 +141,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 for (int i = 0; i < CPT; ++i) {
                     pk[j][i] = from_f32<TIn>(0.f);
                     pqv[j][i] = from_f32<TIn>(0.f);
-                    pg[j][i] = 0.f;
+                    pg[j][i] = from_f32<GT>(0.f);
                 }
             }
         }
@@ -139,7 +154,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 for (int i = 0; i < 8; ++i) pv[i] = from_f32<TIn>(0.f);
             }
         }
-        if (tid < kC) pb = tid < Ln ? beta[static_cast<size_t>(c0 + tid) * num_heads + h] : 0.f;
+        if (tid < kC) {
+            if constexpr (GATED)
+                pb = tid < Ln ? gate_sigmoid(to_f32(beta[static_cast<size_t>(c0 + tid) * num_heads + h])) : 0.f;
+            else
+                pb = tid < Ln ? beta[static_cast<size_t>(c0 + tid) * num_heads + h] : 0.f;
+        }
+        valid_rows = Ln;
     };
     if (t0 < t1) fetch(t0);
 
@@ -154,7 +175,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             for (int i = 0; i < CPT; ++i) {
                 sKl[r * SD + CPT * pc + i] = to_f32(pk[j][i]);
                 sQl[r * SD + CPT * pc + i] = to_f32(pqv[j][i]);
-                sKi[r * SD + CPT * pc + i] = pg[j][i] * kLog2e;
+                float gv = to_f32(pg[j][i]);
+                if constexpr (GATED)
+                    gv = r < valid_rows ? gate_g(gv, gbias[i], ga, gp.lower_bound, gp.has_lower_bound) : 0.f;
+                sKi[r * SD + CPT * pc + i] = gv * kLog2e;
             }
         }
         if (tid < 2 * kC) {
@@ -416,10 +440,17 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     // Round the chain count up to a multiple of 8 so that the value tiles of one
     // chain (linear ids chain + k * grid.x) land on the same XCD.
     const dim3 grid((chains + 7u) & ~7u, D / kDVT);
-    prefill_chunk_kernel<D, TIn, TOut><<<grid, 256, 0, stream>>>(
-        static_cast<const TIn*>(a.q), static_cast<const TIn*>(a.k), static_cast<const TIn*>(a.v),
-        a.g, a.beta, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out), a.final_state,
-        a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+    const TIn* q = static_cast<const TIn*>(a.q);
+    const TIn* k = static_cast<const TIn*>(a.k);
+    const TIn* v = static_cast<const TIn*>(a.v);
+    if (a.gate.a_log)
+        prefill_chunk_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
+            a.final_state, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+    else
+        prefill_chunk_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
+            a.final_state, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
     return hipGetLastError();
 }
 

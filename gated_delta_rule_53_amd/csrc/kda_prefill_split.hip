@@ -182,11 +182,18 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 }
 
 // --------------------------------------------------------------------------
+// With GATED, g and beta are the raw gate and raw beta (bf16), activated as
+// each item is consumed; rows past a sequence's end get g = beta = 0.
+template <bool GATED>
 __global__ __launch_bounds__(PNT) void prep_kernel(
-    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const float* __restrict__ g,
-    const float* __restrict__ beta, const int32_t* __restrict__ cu_seqlens,
+    const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const void* __restrict__ g_in,
+    const void* __restrict__ beta_in, GateParams gp, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
     float scale, int l2norm) {
+    const float* __restrict__ g = static_cast<const float*>(g_in);
+    const float* __restrict__ beta = static_cast<const float*>(beta_in);
+    const bf16_t* __restrict__ graw = static_cast<const bf16_t*>(g_in);
+    const bf16_t* __restrict__ braw = static_cast<const bf16_t*>(beta_in);
     __shared__ __align__(16) unsigned char smem[P_LDS];
     float* sWT = reinterpret_cast<float*>(smem + P_WT);
     float* srk = reinterpret_cast<float*>(smem + P_RK);
@@ -203,9 +210,11 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     const int row_stride = num_heads * D;
 
     // Prefetch registers: row tid/16, channels 8(tid%16) .. +7 of k, q, g; beta.
-    uint4 pk, pq;
-    floatx4 pg0, pg1;
+    // Gated: the raw gate row in pgr and the item's valid length in pL.
+    uint4 pk, pq, pgr = {0u, 0u, 0u, 0u};
+    floatx4 pg0 = {0.f, 0.f, 0.f, 0.f}, pg1 = {0.f, 0.f, 0.f, 0.f};
     float pb = 0.f;
+    int pL = 0;
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
         const int n = find_seq(offsets, num_seqs, cg);
@@ -217,15 +226,30 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         if (r < L) {
             pk = *reinterpret_cast<const uint4*>(k + base + off);
             pq = *reinterpret_cast<const uint4*>(q + base + off);
-            pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
-            pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
+            if constexpr (GATED) {
+                pgr = *reinterpret_cast<const uint4*>(graw + base + off);
+            } else {
+                pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
+                pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
+            }
         } else {
             pk = uint4{0, 0, 0, 0};
             pq = uint4{0, 0, 0, 0};
-            pg0 = floatx4{0.f, 0.f, 0.f, 0.f};
-            pg1 = floatx4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (GATED) {
+                pgr = uint4{0, 0, 0, 0};
+            } else {
+                pg0 = floatx4{0.f, 0.f, 0.f, 0.f};
+                pg1 = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
         }
-        if (tid < C) pb = tid < L ? beta[static_cast<size_t>(start + tid) * num_heads + h] : 0.f;
+        if (tid < C) {
+            const size_t bi = static_cast<size_t>(start + tid) * num_heads + h;
+            if constexpr (GATED)
+                pb = tid < L ? gate_sigmoid(to_f32(braw[bi])) : 0.f;
+            else
+                pb = tid < L ? beta[bi] : 0.f;
+        }
+        pL = L;
     };
     // Items run from the last chunk to the first: the records the state scan
     // reads first are the ones written last, still in the last-level cache.
@@ -259,7 +283,19 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         if (tid < C) sbeta[tid] = pb;
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
-        const floatx8 gr = {pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
+        floatx8 gr;
+        if constexpr (GATED) {
+            const floatx4 b0 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc);
+            const floatx4 b1 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc + 4);
+            const float a = gate_exp(gp.a_log[h]);
+            const floatx8 x = unpack8(pgr);
+            const float bias[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                gr[i] = rp < pL ? gate_g(x[i], bias[i], a, gp.lower_bound, gp.has_lower_bound) : 0.f;
+        } else {
+            gr = floatx8{pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
+        }
         floatx8 incl = gr;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
@@ -906,9 +942,14 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     const size_t max_items = max_chunks * static_cast<size_t>(a.num_heads);
     const unsigned prep_grid = static_cast<unsigned>(max_items < static_cast<size_t>(device_cu_count()) ? max_items : static_cast<size_t>(device_cu_count()));
     if (prep_grid > 0) {
-        prep_kernel<<<prep_grid, PNT, 0, stream>>>(static_cast<const bf16_t*>(a.q), static_cast<const bf16_t*>(a.k),
-                                                  a.g, a.beta, a.cu_seqlens, offsets, records, a.num_seqs,
-                                                  a.num_heads, a.scale, a.l2norm);
+        const bf16_t* q = static_cast<const bf16_t*>(a.q);
+        const bf16_t* k = static_cast<const bf16_t*>(a.k);
+        if (a.gate.a_log)
+            prep_kernel<true><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets,
+                                                             records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+        else
+            prep_kernel<false><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets,
+                                                              records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }

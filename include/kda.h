@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -84,6 +84,29 @@ typedef struct kda_problem {
     int32_t qk_l2norm;    /* 1: L2-normalise q and k inside the kernel; 0: use as given   */
     int32_t chunk_size;   /* prefill chunk length; 64 only (0 selects 64)                 */
 } kda_problem_t;
+
+/*
+ * Gate parameters of the *_gated entry points, which take the raw gate and
+ * raw beta projections and activate them inside the kernels.  The activation
+ * is that of the Ascend model file's gated paths (`_prefill_torch_kda`, the
+ * decode branch of the attention forward, and its `_softplus`): for token t,
+ * head h, key channel c, with raw gate x and raw beta y,
+ *
+ *     u    = x[t][h][c] + dt_bias[h][c]
+ *     g    = -exp(a_log[h]) * softplus(u)                (has_lower_bound == 0)
+ *     g    = lower_bound * sigmoid(exp(a_log[h]) * u)    (has_lower_bound == 1)
+ *     beta = sigmoid(y[t][h])
+ *
+ * with softplus(u) = max(u, 0) + log(1 + exp(-|u|)) and sigmoid(z) =
+ * 1 / (1 + exp(-z)), evaluated in float32.  The activated g must meet the
+ * numeric domain stated above.
+ */
+typedef struct kda_gate {
+    const float *a_log;      /* [H] float32 (device): the gate scale is exp(a_log[h])   */
+    const float *dt_bias;    /* [H, dk] float32 (device)                                */
+    int32_t has_lower_bound; /* 0: softplus gate; 1: bounded sigmoid gate               */
+    float lower_bound;       /* used when has_lower_bound == 1: finite and <= 0        */
+} kda_gate_t;
 
 /* ABI revision of the loaded library; compare with KDA_ABI_VERSION. */
 int kda_abi_version(void);
@@ -144,6 +167,19 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
                            void *stream);
 
 /*
+ * kda_chunk_fwd with the gate activation fused in: raw_g [T, H, dk] and
+ * raw_beta [T, H] are in qkv_dtype (what the gate projections produce) and
+ * are turned into g and beta as described at kda_gate_t; gate, a_log and
+ * dt_bias must be non-NULL.  Everything else, the workspace included, is as
+ * for kda_chunk_fwd.
+ */
+kda_status_t kda_chunk_fwd_gated(const kda_problem_t *problem, const kda_gate_t *gate, const void *q,
+                                 const void *k, const void *v, const void *raw_g, const void *raw_beta,
+                                 const int32_t *cu_seqlens, const float *initial_state, void *out,
+                                 float *final_state, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * One decode step: every sequence advances by exactly one token, and its state
  * is updated IN PLACE.  This is the token-by-token form (the nnterp page's
  * decode kernel; the Ascend model file's decode paths update the recurrent
@@ -160,6 +196,14 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
 kda_status_t kda_recurrent_step(const kda_problem_t *problem, const void *q, const void *k,
                                 const void *v, const float *g, const float *beta, float *state,
                                 void *out, void *stream);
+
+/*
+ * kda_recurrent_step with the gate activation fused in: raw_g [N, H, dk] and
+ * raw_beta [N, H] in qkv_dtype, activated as described at kda_gate_t.
+ */
+kda_status_t kda_recurrent_step_gated(const kda_problem_t *problem, const kda_gate_t *gate,
+                                      const void *q, const void *k, const void *v, const void *raw_g,
+                                      const void *raw_beta, float *state, void *out, void *stream);
 
 #ifdef __cplusplus
 }

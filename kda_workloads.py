@@ -20,6 +20,11 @@ Recipe (one CPU ``torch.Generator`` per workload, seed 0 unless given):
 * g = logsigmoid(x_g), x_g ~ N(mu_g, 1), fp32 (so g <= 0);
 * beta = sigmoid(x_beta), x_beta ~ N(0, 1), fp32;
 * initial state ~ N(0, 0.01**2) (standard deviation 0.01), fp32, or absent.
+
+Raw gate inputs for the fused-gate entry points (``make_gate``, its own
+generator): raw gate ~ N(mu, 0.5**2) and raw beta ~ N(0, 1), both rounded to
+the q/k/v dtype; a_log = log(U(1, 16)) per head (the Ascend model file's
+``A_log`` initialisation); dt_bias ~ N(0, 0.5**2) per head and channel, fp32.
 """
 from __future__ import annotations
 
@@ -199,3 +204,27 @@ def decode_256x64() -> DecodeInputs:
     """256 sequences x 64 decode steps, H=32, d=128, bf16 q/k/v, g=logsigmoid(N(2,1))."""
     return make_decode(256, 64, 32, 128, torch.bfloat16, g_mu=2.0, state_std=0.01,
                        name="decode_N256_steps64_H32_d128")
+
+
+@dataclasses.dataclass
+class GateInputs:
+    """Raw gate inputs: raw_g [rows, H, dk] and raw_beta [rows, H] in the
+    q/k/v dtype, a_log [H] fp32, dt_bias [H, dk] fp32, lower_bound (None for
+    the softplus gate)."""
+
+    raw_g: torch.Tensor
+    raw_beta: torch.Tensor
+    a_log: torch.Tensor
+    dt_bias: torch.Tensor
+    lower_bound: Optional[float]
+
+
+def make_gate(rows: int, num_heads: int, head_k: int, dtype: torch.dtype, *, mu: float = -5.0,
+              lower_bound: Optional[float] = None, seed: int = 0, lead: tuple = ()) -> GateInputs:
+    """Draw raw gate inputs of ``lead + (rows, num_heads, head_k)``."""
+    gen = torch.Generator().manual_seed(seed)
+    raw_g = (torch.randn(*lead, rows, num_heads, head_k, generator=gen) * 0.5 + mu).to(dtype)
+    raw_beta = torch.randn(*lead, rows, num_heads, generator=gen).to(dtype)
+    a_log = torch.log(torch.empty(num_heads).uniform_(1.0, 16.0, generator=gen))
+    dt_bias = torch.randn(num_heads, head_k, generator=gen) * 0.5
+    return GateInputs(raw_g, raw_beta, a_log, dt_bias, lower_bound)

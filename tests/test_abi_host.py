@@ -32,7 +32,8 @@ def exported_symbols(path):
 def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_last_error",
-        "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step"])
+        "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
+        "kda_chunk_fwd_gated", "kda_recurrent_step_gated"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -44,6 +45,11 @@ def test_library_exports_every_declared_symbol():
 def test_abi_version_matches_header():
     m = re.search(r"#define KDA_ABI_VERSION (\d+)", open(HEADER).read())
     assert kda.abi_version() == int(m.group(1))
+
+
+def test_gate_struct_layout():
+    assert ctypes.sizeof(kda.Gate) == 24
+    assert kda.Gate.has_lower_bound.offset == 16 and kda.Gate.lower_bound.offset == 20
 
 
 def test_problem_struct_layout_matches_header():
@@ -166,6 +172,64 @@ def test_recurrent_step_null_pointers_and_empty():
         assert st == 1, name
     st, msg = _step(_prob(total_tokens=0, num_seqs=0), q=None, state=None)
     assert st == 0
+
+
+def _gate(**kw):
+    base = dict(a_log=0x2000, dt_bias=0x3000, has_lower_bound=0, lower_bound=0.0)
+    base.update(kw)
+    return kda.Gate(**base)
+
+
+def _chunk_gated(prob, gate, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fs=None, ws=None,
+             ws_bytes=0)
+    p.update(ptrs)
+    st = lib.kda_chunk_fwd_gated(ctypes.byref(prob), None if gate is None else ctypes.byref(gate), p["q"],
+                                 p["k"], p["v"], p["g"], p["beta"], p["cu"], p["s0"], p["out"], p["fs"],
+                                 p["ws"], p["ws_bytes"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def _step_gated(prob, gate, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, state=FAKE, out=FAKE)
+    p.update(ptrs)
+    st = lib.kda_recurrent_step_gated(ctypes.byref(prob), None if gate is None else ctypes.byref(gate),
+                                      p["q"], p["k"], p["v"], p["g"], p["beta"], p["state"], p["out"], None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("gate,status,needle", [
+    (None, 1, "gate is NULL"),
+    (dict(a_log=None), 1, "a_log"),
+    (dict(dt_bias=None), 1, "dt_bias"),
+    (dict(has_lower_bound=2), 2, "has_lower_bound"),
+    (dict(has_lower_bound=1, lower_bound=0.5), 2, "lower_bound"),
+    (dict(has_lower_bound=1, lower_bound=float("nan")), 2, "lower_bound"),
+    (dict(has_lower_bound=1, lower_bound=float("-inf")), 2, "lower_bound"),
+])
+def test_gated_entry_points_check_the_gate(gate, status, needle):
+    g = None if gate is None else _gate(**gate)
+    st, msg = _chunk_gated(_prob(), g)
+    assert st == status and needle in msg, (st, msg)
+    st, msg = _step_gated(_prob(total_tokens=2, num_seqs=2), g)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_gated_entry_points_check_problem_and_pointers():
+    st, msg = _chunk_gated(_prob(head_k=96, head_v=96), _gate())
+    assert st == 3 and "head size 96" in msg
+    for name in ("q", "k", "v", "g", "beta", "out"):
+        st, _ = _chunk_gated(_prob(), _gate(), **{name: None})
+        assert st == 1, name
+    st, msg = _chunk_gated(_prob(), _gate(), ws=FAKE, ws_bytes=16)
+    assert st == 4 and "workspace" in msg
+    for name in ("q", "k", "v", "g", "beta", "state", "out"):
+        st, _ = _step_gated(_prob(total_tokens=2, num_seqs=2), _gate(), **{name: None})
+        assert st == 1, name
+    st, msg = _step_gated(_prob(total_tokens=3, num_seqs=2), _gate())
+    assert st == 2 and "one token each" in msg
 
 
 def test_python_binding_rejects_cpu_tensors():
