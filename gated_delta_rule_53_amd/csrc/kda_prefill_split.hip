@@ -615,33 +615,40 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
 }
 
 // --------------------------------------------------------------------------
-// ---- scan_kernel: two waves per (sequence, head, 16-column value tile) ----
+// ---- scan_kernel: four waves per (sequence, head, 16-column value tile) ----
 // Wave 0 (the state wave) carries the chunk recurrence alone: D from S, then
-// S'.  Its operands (X', -Psi', Ke^T, e^{G_last} and the chunk's V rows) are
-// copied into LDS two chunks ahead by wave 1 (the output wave), which also
-// forms O = Qg' S + P' D one chunk behind, from S and D handed over through
-// LDS already in B-operand form.  One barrier per chunk.
-constexpr int SB_X = 0;                        // X' diag(rk beta) [tri 6][hl 2]
-constexpr int SB_NP = 12 * FRAG;               // -Psi' [m 4][s 4]
-constexpr int SB_KE = 28 * FRAG;               // Ke^T [w 8][s 2]
-constexpr int SB_V = 44 * FRAG;                // V rows [64][16] bf16
-constexpr int SB_GL = 46 * FRAG;               // e^{G_last}[128] (then 512 bytes of zeros)
-constexpr int SB_BYTES = 47 * FRAG;
-constexpr int XCH = 2 * SB_BYTES;              // exchange, two slots (step parity)
-constexpr int XCH_S = 0;                       // S as B operand: [hl 2][s 4] fragments, fp16
+// S'.  Wave 3 copies its operands (-Psi', Ke^T) into LDS three chunks ahead;
+// wave 2 forms Delta0 = X' diag(rk beta) V two chunks ahead; wave 1 (the
+// output wave) forms O = Qg' S + P' D one chunk behind, from S and D handed
+// over through LDS already in B-operand form.  One barrier per chunk.  The
+// copies of wave 3 are never read by wave 3 itself, so nothing makes it wait
+// for them before the barrier two chunks later.
+constexpr int SB_NP = 0;                       // -Psi' [m 4][s 4]
+constexpr int SB_KE = 16 * FRAG;               // Ke^T [w 8][s 2]
+// LDS regions, each its own array: the compiler then sees that the direct
+// loads into one region do not write the others, and waits only where needed.
+constexpr int SB_BYTES = 32 * FRAG;            // one of three state buffers (chunk mod 3)
+constexpr int XV_X = 0, XV_V = 12 * FRAG;      // the loader's X' [tri 6][hl 2] and V rows [64][16] bf16
+constexpr int XV_BYTES = 14 * FRAG;
+constexpr int DG_D = 0, DG_GL = 4 * FRAG;      // Delta0 (accumulator layout) and e^{G_last}, two slots
+constexpr int DG_SLOT = 5 * FRAG;
+constexpr int XCH_S = 0;                       // exchange, two slots: S as B operand, [hl 2][s 4], fp16
 constexpr int XCH_D = 8 * FRAG;                // D as B operand: [hl 2][s 2]
 constexpr int XCH_SLOT = 12 * FRAG;
-constexpr int SCAN_LDS = XCH + 2 * XCH_SLOT;   // 120832
+constexpr int SCAN_LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT;  // 147456
 static_assert(SCAN_LDS <= 160 * 1024, "scan LDS budget");
 
-constexpr int SCAN_THREADS = 128;
+constexpr int SCAN_THREADS = 256;
 
 template <typename TOut>
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int num_seqs, int num_heads) {
-    __shared__ __align__(16) unsigned char smem[SCAN_LDS];
+    __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
+    __shared__ __align__(16) unsigned char lds_xv[XV_BYTES];
+    __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
+    __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
     const int chain = blockIdx.x;
     if (chain >= num_seqs * num_heads) return;
     KDA_PHASE_BEGIN
@@ -672,51 +679,31 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 for (int j = 0; j < 4; ++j)
                     S[w][j] = initial_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
         }
-        // Step j of the chain from state buffer and exchange slot b; an
+        // Step j from state buffer sb (chunk j mod 3) and slots of parity p; an
         // inactive step (the pad after an odd chunk count) leaves S unchanged.
-        // Each stage's operands are read from LDS into registers a stage
-        // ahead, and independent accumulator chains are issued round-robin.
-        auto step = [&](int b, int lane, bool active) {
-            const unsigned char* sb = smem + b * SB_BYTES;
-            unsigned char* xch = smem + XCH + b * XCH_SLOT;
-            const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
-            // The wave issues in order and its LDS queue is short, so LDS
-            // traffic is spread over small fenced groups, each paired with
-            // compute that does not depend on it.
+        auto step = [&](int sbuf, int p, int lane, bool active) {
+            const unsigned char* sb = lds_sb + sbuf * SB_BYTES;
+            const unsigned char* dg = lds_dg + p * DG_SLOT;
+            unsigned char* xch = lds_xch + p * XCH_SLOT;
+            const int g = lane >> 4, lo16 = lane * 16;
             // stage 1 (four groups): S as the B operand, handed over; operands of D
-            halfx8 fx[12], fp[16];
-            bf16x8 vb[2];
+            halfx8 fp[16];
             halfx8 sh[4], sl[4];
+            floatx4 Dm[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Dm[m] = *reinterpret_cast<const floatx4*>(dg + DG_D + m * FRAG + lo16);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
-                for (int i = 3 * s; i < 3 * s + 3; ++i) fx[i] = ldh8(sb, SB_X + i * FRAG + lo16);
-#pragma unroll
                 for (int i = 4 * s; i < 4 * s + 4; ++i) fp[i] = ldh8(sb, SB_NP + i * FRAG + lo16);
-                if (s < 2) {
-                    const int r0 = 32 * s + 4 * g;
-                    vb[s] = col8_tr2(sb, SB_V, DVT, r0, r0 + 16, 0, l16);
-                }
                 split8h(S[2 * s], S[2 * s + 1], sh[s], sl[s]);
                 *reinterpret_cast<halfx8*>(xch + XCH_S + s * FRAG + lo16) = sh[s];
                 *reinterpret_cast<halfx8*>(xch + XCH_S + (4 + s) * FRAG + lo16) = sl[s];
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // stage 2: D = X' diag(rk beta) V - Psi' S (row blocks m round-robin);
-            // operands of U read three per group of MFMAs
+            // stage 2: D = Delta0 - Psi' S (row blocks m round-robin); operands of U
             halfx8 fk[16];
             floatx4 fg[8];
-            floatx4 Dm[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) Dm[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        if (s < (m < 2 ? 1 : 2))
-                            Dm[m] = mma(__builtin_bit_cast(bf16x8, fx[2 * tri_block(m, s) + hl]), vb[s], Dm[m]);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -729,7 +716,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                         if (q < 16)
                             fk[q] = ldh8(sb, SB_KE + q * FRAG + lo16);
                         else
-                            fg[q - 16] = *reinterpret_cast<const floatx4*>(sb + SB_GL + (16 * (q - 16) + 4 * g) * 4);
+                            fg[q - 16] = *reinterpret_cast<const floatx4*>(dg + DG_GL + (16 * (q - 16) + 4 * g) * 4);
                     }
                     __builtin_amdgcn_sched_barrier(0);
                 }
@@ -760,11 +747,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             KDA_PHASE_MARK(10);
         };
 
-        lds_barrier();  // the first two chunks' operands are in place
+        lds_barrier();  // the first chunks' operands are in place
+        int sbuf = 0;
         for (int j = 0; j < nc; j += 2) {
             const int lane = opaque(lane0);
-            step(0, lane, true);
-            step(1, lane, j + 1 < nc);
+            step(sbuf, 0, lane, true);
+            sbuf = sbuf == 2 ? 0 : sbuf + 1;
+            step(sbuf, 1, lane, j + 1 < nc);
+            sbuf = sbuf == 2 ? 0 : sbuf + 1;
         }
         if (final_state) {
             const int l16 = lane0 & 15, g = lane0 >> 4;
@@ -774,21 +764,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 for (int j = 0; j < 4; ++j)
                     final_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
         }
-    } else {
-        // ================= output wave =================
-        // Copy of chunk j's state-wave operands into state buffer b.
-        auto fetch = [&](int b, int j, int lane) {
-            lds_u8* dst = (lds_u8*)smem + b * SB_BYTES;
+    } else if (wave == 3) {
+        // ================= state-copy wave =================
+        // -Psi' and Ke^T of chunk j into state buffer sbuf (32 copies).
+        auto fetch_state = [&](int sbuf, int j, int lane) {
+            lds_u8* dst = (lds_u8*)lds_sb + sbuf * SB_BYTES;
             const unsigned char* rec = rec_of(j) + lane * 16;
 #pragma unroll
-            for (int f = 0; f < 12; f += 4) {  // X'
-                copy16_to_lds<0>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
-                copy16_to_lds<1024>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
-                copy16_to_lds<2048>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
-                copy16_to_lds<3072>(rec + REC_X + f * FRAG, dst + SB_X + f * FRAG);
-            }
-#pragma unroll
-            for (int f = 0; f < 16; f += 4) {  // -Psi' and Ke^T
+            for (int f = 0; f < 16; f += 4) {
                 copy16_to_lds<0>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
                 copy16_to_lds<1024>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
                 copy16_to_lds<2048>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
@@ -798,17 +781,112 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 copy16_to_lds<2048>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
                 copy16_to_lds<3072>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
             }
-            // e^{G_last}: 512 bytes; lanes 32-63 read past the record's end as zero
-            copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16, dst + SB_GL);
+        };
+#pragma unroll
+        for (int j = 0; j < 3; ++j)
+            if (j < nc) fetch_state(j, j, lane0);
+        wait_vmcnt<0>();
+        lds_barrier();
+        // Step j (while the state wave runs chunk j+1): chunk j+3 into buffer
+        // j mod 3, last read by the state wave in step j.  Before each barrier
+        // only the copies of the step just ended may still be in flight, so a
+        // chunk's copies land by the barrier two steps after they are issued.
+        auto step = [&](int sbuf, int lane, int j) {
+            if (j + 3 < nc) {
+                fetch_state(sbuf, j + 3, lane);
+                wait_vmcnt<32>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        };
+        int sbuf = 0;
+        for (int j = 0; j < nc; j += 2) {
+            const int lane = opaque(lane0);
+            lds_barrier();
+            step(sbuf, lane, j);
+            sbuf = sbuf == 2 ? 0 : sbuf + 1;
+            lds_barrier();
+            step(sbuf, lane, j + 1);
+            sbuf = sbuf == 2 ? 0 : sbuf + 1;
+        }
+        wait_vmcnt<0>();
+    } else if (wave == 2) {
+        // ================= Delta0 wave =================
+        // X' and V rows of chunk j into its buffer, e^{G_last} of chunk j into slot p (15 copies).
+        auto fetch_xv = [&](int p, int j, int lane) {
+            lds_u8* xv = (lds_u8*)lds_xv;
+            const unsigned char* rec = rec_of(j) + lane * 16;
+#pragma unroll
+            for (int f = 0; f < 12; f += 4) {
+                copy16_to_lds<0>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
+                copy16_to_lds<1024>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
+                copy16_to_lds<2048>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
+                copy16_to_lds<3072>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
+            }
             // V rows (lane/2) + 32k, columns 8(lane%2) .. +7; rows past the chunk's end read as zero
-            const int64_t tok0 = tok_of(j);
-            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok0) * num_heads + h) * D + col0,
+            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0,
                                         len_of(j) * row_stride * 2);
 #pragma unroll
             for (int k = 0; k < 2; ++k)
                 copy16_to_lds_buf(vr, (((lane >> 1) + 32 * k) * row_stride + 8 * (lane & 1)) * 2,
-                                  dst + SB_V + k * FRAG);
+                                  xv + XV_V + k * FRAG);
+            // 512 bytes; lanes 32-63 read past the record's end as zero
+            copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16,
+                              (lds_u8*)lds_dg + p * DG_SLOT + DG_GL);
         };
+        // Delta0 = X' diag(rk beta) V from the buffer into slot p.
+        auto delta0 = [&](int p, int lane) {
+            const unsigned char* xv = lds_xv;
+            const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
+            bf16x8 vb[2];
+#pragma unroll
+            for (int s = 0; s < 2; ++s) {
+                const int r0 = 32 * s + 4 * g;
+                vb[s] = col8_tr2(xv, XV_V, DVT, r0, r0 + 16, 0, l16);
+            }
+            floatx4 Dm[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Dm[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+#pragma unroll
+                for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (s < (m < 2 ? 1 : 2))
+                            Dm[m] = mma(ld8(xv, XV_X + (2 * tri_block(m, s) + hl) * FRAG + lo16), vb[s], Dm[m]);
+            unsigned char* dg = lds_dg + p * DG_SLOT;
+#pragma unroll
+            for (int m = 0; m < 4; ++m) *reinterpret_cast<floatx4*>(dg + DG_D + m * FRAG + lo16) = Dm[m];
+        };
+        // Chunks 0 and 1 before the first barrier; then in step j (while the
+        // state wave runs chunk j+1) chunk j+2 into slot j mod 2, last read by
+        // the state wave in step j.
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            if (j < nc) {
+                fetch_xv(j, j, lane0);
+                wait_vmcnt<0>();
+                delta0(j, lane0);
+            }
+        }
+        lds_barrier();
+        auto step = [&](int p, int lane, int j) {
+            if (j + 2 < nc) {
+                fetch_xv(p, j + 2, lane);
+                wait_vmcnt<0>();
+                delta0(p, lane);
+            }
+        };
+        for (int j = 0; j < nc; j += 2) {
+            const int lane = opaque(lane0);
+            lds_barrier();
+            step(0, lane, j);
+            lds_barrier();
+            step(1, lane, j + 1);
+        }
+    } else {
+        // ================= output wave =================
         struct Ops {
             uint4 q[16];  // Qg' [m][s]
             uint4 p[6];   // P' [tri]
@@ -842,15 +920,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             }
         };
         // Step j (between the state wave's barriers j and j+1): store chunk
-        // j-1's outputs, copy chunk j+2's state operands into the buffer the
-        // state wave has just finished with, request chunk j+1's own operands,
-        // and form chunk j's outputs.  Everything has landed before the barrier.
+        // j-1's outputs, request chunk j+1's operands and form chunk j's
+        // outputs.  Everything has landed before the barrier.
         auto step = [&](Ops& cur, Ops& nxt, int b, int lane, int j, floatx4 (&O)[4], int& o_len) {
-            const unsigned char* xch = smem + XCH + b * XCH_SLOT;
+            const unsigned char* xch = lds_xch + b * XCH_SLOT;
             const int lo16 = lane * 16;
             store_o(O, j - 1, o_len, lane);
             o_len = j < nc ? len_of(j) : 0;
-            if (j + 2 < nc) fetch(b, j + 2, lane);
             load(nxt, min(j + 1, nc - 1), lane);
             halfx8 sh[4], sl[4], dh[2], dl[2];
 #pragma unroll
@@ -888,8 +964,6 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
         int o_len = 0;
         if (nc > 0) {
-            fetch(0, 0, lane0);
-            fetch(1, min(1, nc - 1), lane0);
             load(B0, 0, lane0);
             wait_vmcnt<0>();
         }
