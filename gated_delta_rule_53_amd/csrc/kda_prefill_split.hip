@@ -898,24 +898,28 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
 #pragma unroll
             for (int i = 0; i < 6; ++i) o.p[i] = *reinterpret_cast<const uint4*>(rec + REC_P + i * FRAG);
         };
-        // Output rows of chunk j (O in the accumulator layout of row blocks
-        // m); rows past the chunk's end, and everything when L = 0, fall
-        // outside the range and are dropped.
+        // Output rows of chunk j.  O is formed transposed (O^T = S^T Qg'^T +
+        // D^T P'^T: the S and D fragments in B-operand form are the A operands
+        // of S^T and D^T, and the Qg', P' fragments the B operands of their
+        // transposes), so lane l holds columns 4(l/16) .. +3 of row 16m + l%16
+        // in O[m]: one 8-byte (bf16) or 16-byte (fp32) store per row block.
+        // Rows past the chunk's end, and everything when L = 0, fall outside
+        // the range and are dropped.
         auto store_o = [&](const floatx4 (&O)[4], int j, int L, int lane) {
             const int l16 = lane & 15, g = lane >> 4;
             const int out_bytes = L * row_stride * static_cast<int>(sizeof(TOut));
             const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0, out_bytes);
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const uint32_t p01 = pack_bf16x2(O[m][0], O[m][1]), p23 = pack_bf16x2(O[m][2], O[m][3]);
-                const uint32_t ob[4] = {p01 & 0xffffu, p01 >> 16, p23 & 0xffffu, p23 >> 16};
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const int off = ((16 * m + 4 * g + jj) * row_stride + l16) * static_cast<int>(sizeof(TOut));
-                    if constexpr (sizeof(TOut) == 4)
-                        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(O[m][jj]), orr, off, 0, 0);
-                    else
-                        __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(ob[jj]), orr, off, 0, 0);
+                const int off = ((16 * m + l16) * row_stride + 4 * g) * static_cast<int>(sizeof(TOut));
+                if constexpr (sizeof(TOut) == 4) {
+                    typedef int intx4 __attribute__((ext_vector_type(4)));
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, O[m]), orr, off, 0, 0);
+                } else {
+                    typedef int intx2 __attribute__((ext_vector_type(2)));
+                    const intx2 pk = {static_cast<int>(pack_bf16x2(O[m][0], O[m][1])),
+                                      static_cast<int>(pack_bf16x2(O[m][2], O[m][3]))};
+                    __builtin_amdgcn_raw_buffer_store_b64(pk, orr, off, 0, 0);
                 }
             }
         };
@@ -946,7 +950,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                    for (int m = 0; m < 4; ++m) O[m] = mmah(as_halfx8(cur.q[4 * m + s]), hl ? sl[s] : sh[s], O[m]);
+                    for (int m = 0; m < 4; ++m) O[m] = mmah(hl ? sl[s] : sh[s], as_halfx8(cur.q[4 * m + s]), O[m]);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
@@ -954,7 +958,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
 #pragma unroll
                     for (int m = 0; m < 4; ++m)
                         if (s < (m < 2 ? 1 : 2))
-                            O[m] = mmah(as_halfx8(cur.p[tri_block(m, s)]), hl ? dl[s] : dh[s], O[m]);
+                            O[m] = mmah(hl ? dl[s] : dh[s], as_halfx8(cur.p[tri_block(m, s)]), O[m]);
             wait_vmcnt<0>();
         };
 
