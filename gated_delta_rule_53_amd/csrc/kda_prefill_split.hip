@@ -21,20 +21,20 @@
 //
 // Kernels.
 //   chunk_map_kernel  one workgroup: per-sequence chunk offsets from
-//                     cu_seqlens (device side, no host synchronisation).
+//                     cu_seqlens (device side, no host synchronisation) and
+//                     the order in which the scan takes the sequences.
 //   prep_kernel       persistent, fully parallel over (chunk, head): builds
 //                     Kg/Qg/Ki, A and P on MFMA, the four 16x16 diagonal
 //                     inverses, W_RJ = -X_RR A'_RJ, and solves for Psi' and X'
 //                     by block forward substitution.  Writes -Psi', Qg', Ke^T,
 //                     X', P' and e^{G_last} to a per-(chunk, head) record, in
 //                     the lane order the scan's MFMA operands use.
-//   scan_kernel       one wave per (sequence, head, 16-column value tile)
-//                     runs the chunk chain above alone: the state tile stays
-//                     in MFMA accumulators and is fed back as the B operand
-//                     without moving (see "accumulator order"), so a chunk
-//                     costs no barrier and no LDS exchange.  The record is
-//                     copied into LDS one chunk ahead by direct loads, shared
-//                     by the waves of one workgroup (tiles of one head).
+//   scan_kernel       one workgroup per (sequence, head, 16-column value
+//                     tile) carries the chunk chain above.  One wave holds the
+//                     state tile in MFMA accumulators and feeds it back as the
+//                     B operand without moving it (see "accumulator order");
+//                     three more waves copy the record into LDS ahead of it,
+//                     form Delta0 ahead of it and form the output behind it.
 // Inside prep, operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except
 // k.k in A (inverted afterwards); the 16x16 diagonal inverses are fp32.
 #include "kda_bf16_mfma.h"
@@ -47,6 +47,7 @@ namespace {
 constexpr int C = 64;       // chunk length
 constexpr int D = 128;      // head size
 constexpr int DVT = 16;     // value columns of one MFMA tile in the scan
+static_assert(D / DVT == 8, "the scan's workgroup mapping assumes eight tiles per head");
 constexpr int PNT = 1024;   // threads per prep workgroup (16 waves)
 constexpr int SW = D + 8;   // bf16 row stride of 128-wide LDS planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
@@ -148,19 +149,43 @@ __device__ __forceinline__ int find_seq(const int32_t* offsets, int num_seqs, in
 // A sequence whose bounds are not 0 <= cu[n] <= cu[n+1] <= total_tokens gets
 // no chunks, and offsets are clamped to max_chunks, the record capacity of the
 // workspace, so later kernels never index past it.
+// order[r] is the sequence with the r-th most chunks (ties by index), so the
+// scan dispatches the longest chains first and the short ones fill the tail
+// (longest-processing-time-first list scheduling).  Beyond SORT_MAX sequences
+// order is the identity.
+constexpr int SORT_MAX = 1024;
+
+__device__ inline int seq_chunks(const int32_t* __restrict__ cu, int i, int64_t total_tokens) {
+    const int64_t a = cu[i], b = cu[i + 1];
+    return (a >= 0 && b <= total_tokens && b >= a) ? static_cast<int>((b - a + C - 1) / C) : 0;
+}
+
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs,
                                                          int64_t total_tokens, int max_chunks,
-                                                         int32_t* __restrict__ offsets) {
+                                                         int32_t* __restrict__ offsets, int32_t* __restrict__ order) {
     __shared__ int wsum[16];
+    __shared__ __align__(16) int slen[SORT_MAX];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    if (num_seqs <= SORT_MAX) {
+        const int i = tid;
+        const int mine = i < num_seqs ? seq_chunks(cu, i, total_tokens) : 0;
+        if (i < num_seqs) slen[i] = mine;
+        __syncthreads();
+        if (i < num_seqs) {
+            int rank = 0;
+            for (int m = 0; m < num_seqs; ++m) {
+                const int other = slen[m];
+                rank += (other > mine) | ((other == mine) & (m < i));
+            }
+            order[rank] = i;
+        }
+    } else {
+        for (int i = tid; i < num_seqs; i += 1024) order[i] = i;
+    }
     int carry = 0;
     for (int base = 0; base < num_seqs; base += 1024) {
         const int i = base + tid;
-        int nch = 0;
-        if (i < num_seqs) {
-            const int64_t a = cu[i], b = cu[i + 1];
-            if (a >= 0 && b <= total_tokens && b >= a) nch = static_cast<int>((b - a + C - 1) / C);
-        }
+        const int nch = i < num_seqs ? seq_chunks(cu, i, total_tokens) : 0;
         int x = nch;
         for (int off = 1; off < 64; off <<= 1) {
             const int y = __shfl_up(x, off, 64);
@@ -632,10 +657,12 @@ constexpr int XV_X = 0, XV_V = 12 * FRAG;      // the loader's X' [tri 6][hl 2] 
 constexpr int XV_BYTES = 14 * FRAG;
 constexpr int DG_D = 0, DG_GL = 4 * FRAG;      // Delta0 (accumulator layout) and e^{G_last}, two slots
 constexpr int DG_SLOT = 5 * FRAG;
-constexpr int XCH_S = 0;                       // exchange, two slots: S as B operand, [hl 2][s 4], fp16
-constexpr int XCH_D = 8 * FRAG;                // D as B operand: [hl 2][s 2]
-constexpr int XCH_SLOT = 12 * FRAG;
-constexpr int SCAN_LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT;  // 147456
+// The output is not fed back, so it takes S and D as single fp16 (their high
+// parts); the state side keeps the hi/lo pairs.
+constexpr int XCH_S = 0;                       // exchange, two slots: S as B operand [s 4], fp16
+constexpr int XCH_D = 4 * FRAG;                // D as B operand [s 2]
+constexpr int XCH_SLOT = 6 * FRAG;
+constexpr int SCAN_LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT;  // 135168
 static_assert(SCAN_LDS <= 160 * 1024, "scan LDS budget");
 
 constexpr int SCAN_THREADS = 256;
@@ -643,19 +670,24 @@ constexpr int SCAN_THREADS = 256;
 template <typename TOut>
 __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
-    const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
+    const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int num_seqs, int num_heads) {
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
     __shared__ __align__(16) unsigned char lds_xv[XV_BYTES];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
-    const int chain = blockIdx.x;
-    if (chain >= num_seqs * num_heads) return;
+    // Workgroup id -> (chain rank, tile): each run of 64 ids holds the 8 tiles
+    // of 8 consecutive chains, and id mod 8 (the XCD the workgroup lands on)
+    // is the chain's, so the tiles of a chain run together on one XCD and
+    // read its records through one L2.
+    const int id = static_cast<int>(blockIdx.x);
+    const int crank = (id >> 6) * 8 + (id & 7);
+    if (crank >= num_seqs * num_heads) return;
     KDA_PHASE_BEGIN
-    const int n = chain / num_heads, h = chain % num_heads;
+    const int n = order[crank / num_heads], h = crank % num_heads;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
-    const int col0 = static_cast<int>(blockIdx.y) * DVT;
+    const int col0 = ((id >> 3) & 7) * DVT;
     const int c_begin = offsets[n], c_end = offsets[n + 1];
     const int nc = c_end - c_begin;
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
@@ -698,7 +730,6 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 for (int i = 4 * s; i < 4 * s + 4; ++i) fp[i] = ldh8(sb, SB_NP + i * FRAG + lo16);
                 split8h(S[2 * s], S[2 * s + 1], sh[s], sl[s]);
                 *reinterpret_cast<halfx8*>(xch + XCH_S + s * FRAG + lo16) = sh[s];
-                *reinterpret_cast<halfx8*>(xch + XCH_S + (4 + s) * FRAG + lo16) = sl[s];
                 __builtin_amdgcn_sched_barrier(0);
             }
             // stage 2: D = Delta0 - Psi' S (row blocks m round-robin); operands of U
@@ -728,7 +759,6 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             for (int s = 0; s < 2; ++s) {
                 split8h(Dm[2 * s], Dm[2 * s + 1], dh[s], dl[s]);
                 *reinterpret_cast<halfx8*>(xch + XCH_D + s * FRAG + lo16) = dh[s];
-                *reinterpret_cast<halfx8*>(xch + XCH_D + (2 + s) * FRAG + lo16) = dl[s];
             }
 #pragma unroll
             for (int w = 0; w < 8; ++w) U[w] = fg[w] * S[w];
@@ -932,33 +962,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             store_o(O, j - 1, o_len, lane);
             o_len = j < nc ? len_of(j) : 0;
             load(nxt, min(j + 1, nc - 1), lane);
-            halfx8 sh[4], sl[4], dh[2], dl[2];
+            halfx8 sh[4], dh[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                sh[s] = ldh8(xch, XCH_S + s * FRAG + lo16);
-                sl[s] = ldh8(xch, XCH_S + (4 + s) * FRAG + lo16);
-            }
+            for (int s = 0; s < 4; ++s) sh[s] = ldh8(xch, XCH_S + s * FRAG + lo16);
 #pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                dh[s] = ldh8(xch, XCH_D + s * FRAG + lo16);
-                dl[s] = ldh8(xch, XCH_D + (2 + s) * FRAG + lo16);
-            }
+            for (int s = 0; s < 2; ++s) dh[s] = ldh8(xch, XCH_D + s * FRAG + lo16);
 #pragma unroll
             for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) O[m] = mmah(hl ? sl[s] : sh[s], as_halfx8(cur.q[4 * m + s]), O[m]);
+                for (int m = 0; m < 4; ++m) O[m] = mmah(sh[s], as_halfx8(cur.q[4 * m + s]), O[m]);
 #pragma unroll
             for (int s = 0; s < 2; ++s)
 #pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        if (s < (m < 2 ? 1 : 2))
-                            O[m] = mmah(hl ? dl[s] : dh[s], as_halfx8(cur.p[tri_block(m, s)]), O[m]);
+                for (int m = 0; m < 4; ++m)
+                    if (s < (m < 2 ? 1 : 2)) O[m] = mmah(dh[s], as_halfx8(cur.p[tri_block(m, s)]), O[m]);
             wait_vmcnt<0>();
         };
 
@@ -988,8 +1007,12 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
 
 bool split_prefill_applies(const PrefillArgs& a) { return a.qkv_bf16 && a.head_dim == D; }
 
+// Workspace: chunk offsets [N + 1] and the dispatch order [N] (int32), padded
+// to 256 bytes, then the records.
+static size_t map_bytes(int num_seqs) { return (static_cast<size_t>(2 * num_seqs + 1) * 4 + 255) & ~size_t(255); }
+
 size_t split_workspace_bytes(int64_t total_tokens, int num_seqs, int num_heads) {
-    const size_t off_bytes = (static_cast<size_t>(num_seqs + 1) * 4 + 255) & ~size_t(255);
+    const size_t off_bytes = map_bytes(num_seqs);
     const size_t max_chunks = static_cast<size_t>((total_tokens + C - 1) / C) + static_cast<size_t>(num_seqs);
     return off_bytes + max_chunks * static_cast<size_t>(num_heads) * REC_BYTES;
 }
@@ -1011,10 +1034,11 @@ template <typename TOut>
 static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStream_t stream) {
     unsigned char* ws = static_cast<unsigned char*>(workspace);
     int32_t* offsets = reinterpret_cast<int32_t*>(ws);
-    unsigned char* records = ws + ((static_cast<size_t>(a.num_seqs + 1) * 4 + 255) & ~size_t(255));
+    int32_t* order = offsets + a.num_seqs + 1;
+    unsigned char* records = ws + map_bytes(a.num_seqs);
     const size_t max_chunks = static_cast<size_t>((a.total_tokens + C - 1) / C) + static_cast<size_t>(a.num_seqs);
     chunk_map_kernel<<<1, 1024, 0, stream>>>(a.cu_seqlens, a.num_seqs, a.total_tokens, static_cast<int>(max_chunks),
-                                             offsets);
+                                             offsets, order);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const size_t max_items = max_chunks * static_cast<size_t>(a.num_heads);
@@ -1032,9 +1056,8 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
         if (e != hipSuccess) return e;
     }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
-    // tiles of one chain (linear ids chain + k * grid.x) share an XCD when grid.x % 8 == 0
-    const dim3 grid((chains + 7u) & ~7u, D / DVT);
-    scan_kernel<TOut><<<grid, SCAN_THREADS, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets,
+    const unsigned grid = ((chains + 7u) & ~7u) * (D / DVT);
+    scan_kernel<TOut><<<grid, SCAN_THREADS, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order,
                                                          records, a.initial_state, static_cast<TOut*>(a.out),
                                                          a.final_state, a.num_seqs, a.num_heads);
     return hipGetLastError();

@@ -124,7 +124,8 @@ const char *kda_last_error(void);
  * bf16 q/k/v with dk = dv = 128 runs in two passes: every (chunk, head) pair
  * is prepared independently and its state-independent operands are stored in
  * the workspace, then a short scan carries the state across chunks.  The size
- * is 4 * (N + 1) bytes of chunk offsets rounded up to a multiple of 256, plus
+ * is 4 * (2N + 1) bytes (chunk offsets and the order the scan takes the
+ * sequences in) rounded up to a multiple of 256, plus
  * 68096 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 1 KiB per
  * token and head).  Other configurations keep everything on chip and need 0.
  */

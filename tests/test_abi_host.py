@@ -135,11 +135,12 @@ REC_BYTES = 68096
 def test_workspace_query():
     lib = kda.raw_library()
     q = lambda **kw: lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(_prob(**kw)))
-    # bf16, 128-wide heads: 256-byte aligned chunk offsets, then one record per
-    # (chunk, head) for up to ceil(T/64) + N chunks.
+    # bf16, 128-wide heads: chunk offsets [N+1] and scan order [N] (int32) padded
+    # to 256 bytes, then one record per (chunk, head) for up to ceil(T/64) + N chunks.
     assert q() == 256 + (2 + 1) * 2 * REC_BYTES
     assert q(total_tokens=4096, num_seqs=1, num_heads=32) == 256 + (64 + 1) * 32 * REC_BYTES
-    assert q(total_tokens=100, num_seqs=70, num_heads=1) == 512 + (2 + 70) * REC_BYTES
+    assert q(total_tokens=100, num_seqs=70, num_heads=1) == 768 + (2 + 70) * REC_BYTES
+    assert q(total_tokens=100, num_seqs=63, num_heads=1) == 512 + (2 + 63) * REC_BYTES
     # every other configuration needs none
     assert q(qkv_dtype=0) == 0
     assert q(head_k=64, head_v=64) == 0
