@@ -25,6 +25,10 @@ HIPCC_FLAGS = [
     # Packed fp32 instructions stay off: the compiler would otherwise pair fp32
     # math into v_pk_* forms, which this code base does not rely on.
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in ordinary VGPRs: the scan's state and D tiles are
+    # read back by VALU code every chunk, and accumulators in AGPRs would cost
+    # a v_accvgpr move per element each time.
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wall",
     "-Wno-unused-function",
 ]

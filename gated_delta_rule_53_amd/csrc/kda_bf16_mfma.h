@@ -154,6 +154,14 @@ __device__ __forceinline__ void copy16_to_lds_buf(__amdgpu_buffer_rsrc_t r, int 
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lvoid*)lds, 16, voff, 0, 0, 0);
 }
 
+// Four bytes per lane at byte voff of the resource into lds + 4 l.  Used to
+// pull lines into L2 ahead of their readers (the LDS copy is the load's only
+// visible effect, so the compiler keeps it).
+__device__ __forceinline__ void copy4_to_lds_buf(__amdgpu_buffer_rsrc_t r, int voff, lds_u8* lds) {
+    typedef __attribute__((address_space(3))) void lvoid;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lvoid*)lds, 4, voff, 0, 0, 0);
+}
+
 // The same with off = 1024 q, q = 0 .. 3 chosen at run time (a constant after unrolling).
 __device__ __forceinline__ void copy16_to_lds_q(const void* src, lds_u8* lds, int q) {
     switch (q) {

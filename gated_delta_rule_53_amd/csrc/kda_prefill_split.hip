@@ -676,6 +676,7 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     __shared__ __align__(16) unsigned char lds_xv[XV_BYTES];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
+    __shared__ __align__(16) unsigned char lds_touch[256];  // sink of the L2 touches, never read
     // Workgroup id -> (chain rank, tile): each run of 64 ids holds the 8 tiles
     // of 8 consecutive chains, and id mod 8 (the XCD the workgroup lands on)
     // is the chain's, so the tiles of a chain run together on one XCD and
@@ -821,10 +822,27 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         // j mod 3, last read by the state wave in step j.  Before each barrier
         // only the copies of the step just ended may still be in flight, so a
         // chunk's copies land by the barrier two steps after they are issued.
+        // The first tile of a chain also touches every 128-byte line of the
+        // record four chunks ahead (one 4-byte load per line, into a scratch
+        // LDS row), so the record is in L2 when the waves of all eight tiles
+        // read it and none of them waits on HBM latency.  Lanes past the
+        // record's end fall outside the buffer range and access nothing.
+        constexpr int TOUCHES = (REC_BYTES + 64 * 128 - 1) / (64 * 128);
+        const bool toucher = col0 == 0;
+        auto touch = [&](int j, int lane) {
+            const auto r = buffer_rsrc(rec_of(j), REC_BYTES);
+#pragma unroll
+            for (int i = 0; i < TOUCHES; ++i) copy4_to_lds_buf(r, (64 * i + lane) * 128, (lds_u8*)lds_touch);
+        };
         auto step = [&](int sbuf, int lane, int j) {
             if (j + 3 < nc) {
                 fetch_state(sbuf, j + 3, lane);
-                wait_vmcnt<32>();
+                if (toucher && j + 4 < nc) {
+                    touch(j + 4, lane);
+                    wait_vmcnt<32 + TOUCHES>();
+                } else {
+                    wait_vmcnt<32>();
+                }
             } else {
                 wait_vmcnt<0>();
             }
