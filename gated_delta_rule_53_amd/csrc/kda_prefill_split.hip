@@ -798,19 +798,23 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     } else if (wave == 3) {
         // ================= state-copy wave =================
         // -Psi' and Ke^T of chunk j into state buffer sbuf (32 copies).
+        // The eight 4 KiB groups (four of -Psi', then four of Ke^T) are taken
+        // in an order rotated by the tile, so the tiles of a chain do not ask
+        // for the same lines at the same moment.
+        const int rot = (col0 / DVT) & 7;
         auto fetch_state = [&](int sbuf, int j, int lane) {
             lds_u8* dst = (lds_u8*)lds_sb + sbuf * SB_BYTES;
             const unsigned char* rec = rec_of(j) + lane * 16;
+            static_assert(SB_NP == 0 && SB_KE == 16 * FRAG && REC_NPSI == 0, "group g at 4g fragments of the buffer");
 #pragma unroll
-            for (int f = 0; f < 16; f += 4) {
-                copy16_to_lds<0>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
-                copy16_to_lds<1024>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
-                copy16_to_lds<2048>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
-                copy16_to_lds<3072>(rec + REC_NPSI + f * FRAG, dst + SB_NP + f * FRAG);
-                copy16_to_lds<0>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
-                copy16_to_lds<1024>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
-                copy16_to_lds<2048>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
-                copy16_to_lds<3072>(rec + REC_KE + f * FRAG, dst + SB_KE + f * FRAG);
+            for (int i = 0; i < 8; ++i) {
+                const int g = (i + rot) & 7;
+                const unsigned char* src = rec + (g < 4 ? REC_NPSI + 4 * g * FRAG : REC_KE + 4 * (g - 4) * FRAG);
+                lds_u8* d = dst + 4 * g * FRAG;
+                copy16_to_lds<0>(src, d);
+                copy16_to_lds<1024>(src, d);
+                copy16_to_lds<2048>(src, d);
+                copy16_to_lds<3072>(src, d);
             }
         };
 #pragma unroll
@@ -861,11 +865,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     } else if (wave == 2) {
         // ================= Delta0 wave =================
         // X' and V rows of chunk j into its buffer, e^{G_last} of chunk j into slot p (15 copies).
+        const int xrot = (col0 / DVT) % 3;
         auto fetch_xv = [&](int p, int j, int lane) {
             lds_u8* xv = (lds_u8*)lds_xv;
             const unsigned char* rec = rec_of(j) + lane * 16;
+            // three 4 KiB groups, in an order rotated by the tile
 #pragma unroll
-            for (int f = 0; f < 12; f += 4) {
+            for (int i = 0; i < 3; ++i) {
+                const int f = 4 * ((i + xrot) % 3);
                 copy16_to_lds<0>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
                 copy16_to_lds<1024>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
                 copy16_to_lds<2048>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
