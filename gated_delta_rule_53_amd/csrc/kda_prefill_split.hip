@@ -291,21 +291,6 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
 
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
         const floatx8 kf = unpack8(pk), qf = unpack8(pq);
-        {
-            float sk = 0.f, sq = 0.f;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                sk += kf[i] * kf[i];
-                sq += qf[i] * qf[i];
-            }
-            sk = row16_sum(sk);
-            sq = row16_sum(sq);
-            if (cc == 0) {
-                srk[rp] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
-                srq[rp] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
-            }
-        }
-        if (tid < C) sbeta[tid] = pb;
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
         floatx8 gr;
@@ -334,31 +319,49 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc + 4) = floatx4{incl[4], incl[5], incl[6], incl[7]};
         }
         lds_barrier();
-        // G_r - G_31 for this row (token 31 is the last row of wave 7)
-        floatx8 cm = {0, 0, 0, 0, 0, 0, 0, 0};
+        // Channel threads turn the wave totals of channel c into offsets in
+        // place: with P_w the sum of the totals of waves 0 .. w-1, entry (w, c)
+        // becomes P_w - P_8, the cumulative g before wave w's first row minus
+        // G_31 (token 31 is the last row of wave 7); and e^{G_31}, e^{G_last -
+        // G_31}, e^{G_last}.  Meanwhile every thread forms its row norms.
+        if (tid < D) {
+            float t[16];
+#pragma unroll
+            for (int w2 = 0; w2 < 16; ++w2) t[w2] = sWT[w2 * D + tid];
+            float pre[17];
+            pre[0] = 0.f;
+#pragma unroll
+            for (int w2 = 0; w2 < 16; ++w2) pre[w2 + 1] = pre[w2] + t[w2];
+#pragma unroll
+            for (int w2 = 0; w2 < 16; ++w2) sWT[w2 * D + tid] = pre[w2] - pre[8];
+            sEm[tid] = fast_exp2(pre[8] * kLog2e);
+            sEL[tid] = fast_exp2((pre[16] - pre[8]) * kLog2e);
+            sGL[tid] = fast_exp2(pre[16] * kLog2e);
+        }
         {
-            const int lo_w = wave < 8 ? wave : 8, hi_w = wave < 8 ? 8 : wave;
-            for (int w2 = lo_w; w2 < hi_w; ++w2) {
-                const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc);
-                const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + w2 * D + 8 * cc + 4);
-                cm += floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+            float sk = 0.f, sq = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                sk += kf[i] * kf[i];
+                sq += qf[i] * qf[i];
             }
-            if (wave < 8) cm = -cm;
+            sk = row16_sum(sk);
+            sq = row16_sum(sq);
+            if (cc == 0) {
+                srk[rp] = l2norm ? rsqrtf(sk + kNormEps) : 1.f;
+                srq[rp] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
+            }
+        }
+        if (tid < C) sbeta[tid] = pb;
+        lds_barrier();
+        // G_r - G_31 for this row
+        floatx8 cm;
+        {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + wave * D + 8 * cc);
+            const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + wave * D + 8 * cc + 4);
+            cm = floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
         const floatx8 d = (cm + incl) * kLog2e;
-        if (tid < 3 * D) {
-            const int c = tid & (D - 1), which = tid >> 7;
-            float gm = 0.f, gl = 0.f;
-#pragma unroll
-            for (int w2 = 0; w2 < 16; ++w2) {
-                const float t = sWT[w2 * D + c];
-                gl += t;
-                if (w2 < 8) gm += t;
-            }
-            const float ex = which == 0 ? gm : (which == 1 ? gl - gm : gl);
-            float* dst = which == 0 ? sEm : (which == 1 ? sEL : sGL);
-            dst[c] = fast_exp2(ex * kLog2e);
-        }
         {
             const int o = (rp * SW + 8 * cc) * 2;
             floatx8 e, ei;
