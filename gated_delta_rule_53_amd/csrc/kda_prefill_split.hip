@@ -29,12 +29,13 @@
 //                     by block forward substitution.  Writes -Psi', Qg', Ke^T,
 //                     X', P' and e^{G_last} to a per-(chunk, head) record, in
 //                     the lane order the scan's MFMA operands use.
-//   scan_kernel       one workgroup per (sequence, head, 16-column value
-//                     tile) carries the chunk chain above.  One wave holds the
-//                     state tile in MFMA accumulators and feeds it back as the
-//                     B operand without moving it (see "accumulator order");
-//                     three more waves copy the record into LDS ahead of it,
-//                     form Delta0 ahead of it and form the output behind it.
+//   scan_kernel       one workgroup per (sequence, head, one or two 16-column
+//                     value tiles) carries the chunk chain above.  One wave
+//                     per tile holds the state tile in MFMA accumulators and
+//                     feeds it back as the B operand without moving it (see
+//                     "accumulator order"); three more waves copy the record
+//                     into LDS ahead of them, form Delta0 ahead of them and
+//                     form the output behind them, for all its tiles.
 // Inside prep, operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except
 // k.k in A (inverted afterwards); the 16x16 diagonal inverses are fp32.
 #include "kda_bf16_mfma.h"
@@ -47,7 +48,6 @@ namespace {
 constexpr int C = 64;       // chunk length
 constexpr int D = 128;      // head size
 constexpr int DVT = 16;     // value columns of one MFMA tile in the scan
-static_assert(D / DVT == 8, "the scan's workgroup mapping assumes eight tiles per head");
 constexpr int PNT = 1024;   // threads per prep workgroup (16 waves)
 constexpr int SW = D + 8;   // bf16 row stride of 128-wide LDS planes
 constexpr int SN = C + 8;   // bf16 row stride of 64-wide LDS planes
@@ -643,55 +643,70 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
 }
 
 // --------------------------------------------------------------------------
-// ---- scan_kernel: four waves per (sequence, head, 16-column value tile) ----
-// Wave 0 (the state wave) carries the chunk recurrence alone: D from S, then
-// S'.  Wave 3 copies its operands (-Psi', Ke^T) into LDS three chunks ahead;
-// wave 2 forms Delta0 = X' diag(rk beta) V two chunks ahead; wave 1 (the
-// output wave) forms O = Qg' S + P' D one chunk behind, from S and D handed
-// over through LDS already in B-operand form.  One barrier per chunk.  The
-// copies of wave 3 are never read by wave 3 itself, so nothing makes it wait
-// for them before the barrier two chunks later.
+// ---- scan_kernel: NT + 3 waves per (sequence, head, NT 16-column value tiles) ----
+// Waves 0 .. NT-1 (the state waves) each carry the chunk recurrence of one
+// tile alone: D from S, then S'.  Wave NT+2 copies their operands (-Psi',
+// Ke^T), which do not depend on the value columns and so serve every tile,
+// into LDS three chunks ahead; wave NT forms Delta0 = X' diag(rk beta) V of
+// the tiles two chunks ahead; wave NT+1 (the output wave) forms O = Qg' S +
+// P' D of the tiles one chunk behind, from S and D handed over through LDS
+// already in B-operand form.  One barrier per chunk.  The copy wave never
+// reads its own copies, so nothing makes it wait for them before the barrier
+// two chunks later.  With NT = 2 a workgroup reads each record once for two
+// tiles: half the L2 traffic per tile, for when there are more tiles than
+// compute units; with NT = 1 a chain's chunk takes the least time.
 constexpr int SB_NP = 0;                       // -Psi' [m 4][s 4]
 constexpr int SB_KE = 16 * FRAG;               // Ke^T [w 8][s 2]
 // LDS regions, each its own array: the compiler then sees that the direct
 // loads into one region do not write the others, and waits only where needed.
 constexpr int SB_BYTES = 32 * FRAG;            // one of three state buffers (chunk mod 3)
-constexpr int XV_X = 0, XV_V = 12 * FRAG;      // the loader's X' [tri 6][hl 2] and V rows [64][16] bf16
-constexpr int XV_BYTES = 14 * FRAG;
-constexpr int DG_D = 0, DG_GL = 4 * FRAG;      // Delta0 (accumulator layout) and e^{G_last}, two slots
-constexpr int DG_SLOT = 5 * FRAG;
+constexpr int XV_X = 0, XV_V = 12 * FRAG;      // the loader's X' [tri 6][hl 2] and V rows [64][16 NT] bf16
+constexpr int DG_D = 0;                        // two slots: Delta0 of tile t (accumulator layout) at 4t fragments,
+                                               // then e^{G_last} [128] fp32 (the copy fills 1 KiB)
 // The output is not fed back, so it takes S and D as single fp16 (their high
 // parts); the state side keeps the hi/lo pairs.
-constexpr int XCH_S = 0;                       // exchange, two slots: S as B operand [s 4], fp16
+constexpr int XCH_S = 0;                       // exchange, two slots, per tile: S as B operand [s 4], fp16
 constexpr int XCH_D = 4 * FRAG;                // D as B operand [s 2]
-constexpr int XCH_SLOT = 6 * FRAG;
-constexpr int SCAN_LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT;  // 135168
-static_assert(SCAN_LDS <= 160 * 1024, "scan LDS budget");
+constexpr int XCH_TILE = 6 * FRAG;
 
-constexpr int SCAN_THREADS = 256;
+template <int NT>
+struct ScanShape {
+    static constexpr int XV_BYTES = XV_V + C * NT * DVT * 2;
+    static constexpr int DG_GL = NT * 4 * FRAG;
+    static constexpr int DG_SLOT = DG_GL + FRAG;
+    static constexpr int XCH_SLOT = NT * XCH_TILE;
+    static constexpr int LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT + 256;
+    static constexpr int THREADS = 64 * (NT + 3);
+    static constexpr int UNITS = D / (NT * DVT);  // workgroups per chain
+    static_assert(LDS <= 160 * 1024, "scan LDS budget");
+    static_assert(UNITS * NT * DVT == D && (UNITS == 8 || UNITS == 4), "eight or four workgroups per chain");
+};
 
-template <typename TOut>
-__global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
+template <typename TOut, int NT>
+__global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
     float* final_state, int num_seqs, int num_heads) {
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
-    __shared__ __align__(16) unsigned char lds_xv[XV_BYTES];
+    using SS = ScanShape<NT>;
+    constexpr int DG_GL = SS::DG_GL, DG_SLOT = SS::DG_SLOT, XCH_SLOT = SS::XCH_SLOT;
+    __shared__ __align__(16) unsigned char lds_xv[SS::XV_BYTES];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
     __shared__ __align__(16) unsigned char lds_touch[256];  // sink of the L2 touches, never read
-    // Workgroup id -> (chain rank, tile): each run of 64 ids holds the 8 tiles
-    // of 8 consecutive chains, and id mod 8 (the XCD the workgroup lands on)
-    // is the chain's, so the tiles of a chain run together on one XCD and
-    // read its records through one L2.
+    // Workgroup id -> (chain rank, unit of NT tiles): each run of 8 UNITS ids
+    // holds the units of 8 consecutive chains, and id mod 8 (the XCD the
+    // workgroup lands on) is the chain's, so the units of a chain run
+    // together on one XCD and read its records through one L2.
     const int id = static_cast<int>(blockIdx.x);
-    const int crank = (id >> 6) * 8 + (id & 7);
+    const int crank = (id / (8 * SS::UNITS)) * 8 + (id & 7);
+    const int unit = (id >> 3) % SS::UNITS;
     if (crank >= num_seqs * num_heads) return;
     KDA_PHASE_BEGIN
     const int n = order[crank / num_heads], h = crank % num_heads;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
-    const int col0 = ((id >> 3) & 7) * DVT;
+    const int colp = unit * NT * DVT;  // first value column of the unit
     const int c_begin = offsets[n], c_end = offsets[n + 1];
     const int nc = c_end - c_begin;
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
@@ -701,9 +716,11 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
     auto tok_of = [&](int j) { return t_first + static_cast<int64_t>(C) * j; };
     auto len_of = [&](int j) { return static_cast<int>(min64(C, t_last - tok_of(j))); };
 
-    if (wave == 0) {
-        // ================= state wave =================
+    if (wave < NT) {
+        // ================= state waves (tile t = wave) =================
         // S[w][j] = S[16w + 4(l/16) + j][col0 + l%16]: the accumulator layout of U = Ke^T D.
+        const int col0 = colp + DVT * wave;
+        const int dg_t = DG_D + 4 * FRAG * wave, xch_t = XCH_TILE * wave;
         floatx4 S[8];
 #pragma unroll
         for (int w = 0; w < 8; ++w) S[w] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -720,14 +737,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         auto step = [&](int sbuf, int p, int lane, bool active) {
             const unsigned char* sb = lds_sb + sbuf * SB_BYTES;
             const unsigned char* dg = lds_dg + p * DG_SLOT;
-            unsigned char* xch = lds_xch + p * XCH_SLOT;
+            unsigned char* xch = lds_xch + p * XCH_SLOT + xch_t;
             const int g = lane >> 4, lo16 = lane * 16;
             // stage 1 (four groups): S as the B operand, handed over; operands of D
             halfx8 fp[16];
             halfx8 sh[4], sl[4];
             floatx4 Dm[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Dm[m] = *reinterpret_cast<const floatx4*>(dg + DG_D + m * FRAG + lo16);
+            for (int m = 0; m < 4; ++m) Dm[m] = *reinterpret_cast<const floatx4*>(dg + dg_t + m * FRAG + lo16);
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
 #pragma unroll
@@ -798,13 +815,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 for (int j = 0; j < 4; ++j)
                     final_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
         }
-    } else if (wave == 3) {
+    } else if (wave == NT + 2) {
         // ================= state-copy wave =================
         // -Psi' and Ke^T of chunk j into state buffer sbuf (32 copies).
         // The eight 4 KiB groups (four of -Psi', then four of Ke^T) are taken
-        // in an order rotated by the tile, so the tiles of a chain do not ask
+        // in an order rotated by the unit, so the units of a chain do not ask
         // for the same lines at the same moment.
-        const int rot = (col0 / DVT) & 7;
+        const int rot = (NT * unit) & 7;
         auto fetch_state = [&](int sbuf, int j, int lane) {
             lds_u8* dst = (lds_u8*)lds_sb + sbuf * SB_BYTES;
             const unsigned char* rec = rec_of(j) + lane * 16;
@@ -829,13 +846,13 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         // j mod 3, last read by the state wave in step j.  Before each barrier
         // only the copies of the step just ended may still be in flight, so a
         // chunk's copies land by the barrier two steps after they are issued.
-        // The first tile of a chain also touches every 128-byte line of the
+        // The first unit of a chain also touches every 128-byte line of the
         // record four chunks ahead (one 4-byte load per line, into a scratch
-        // LDS row), so the record is in L2 when the waves of all eight tiles
+        // LDS row), so the record is in L2 when the waves of all its units
         // read it and none of them waits on HBM latency.  Lanes past the
         // record's end fall outside the buffer range and access nothing.
         constexpr int TOUCHES = (REC_BYTES + 64 * 128 - 1) / (64 * 128);
-        const bool toucher = col0 == 0;
+        const bool toucher = unit == 0;
         auto touch = [&](int j, int lane) {
             const auto r = buffer_rsrc(rec_of(j), REC_BYTES);
 #pragma unroll
@@ -865,14 +882,14 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
             sbuf = sbuf == 2 ? 0 : sbuf + 1;
         }
         wait_vmcnt<0>();
-    } else if (wave == 2) {
+    } else if (wave == NT) {
         // ================= Delta0 wave =================
         // X' and V rows of chunk j into its buffer, e^{G_last} of chunk j into slot p (15 copies).
-        const int xrot = (col0 / DVT) % 3;
+        const int xrot = unit % 3;
         auto fetch_xv = [&](int p, int j, int lane) {
             lds_u8* xv = (lds_u8*)lds_xv;
             const unsigned char* rec = rec_of(j) + lane * 16;
-            // three 4 KiB groups, in an order rotated by the tile
+            // three 4 KiB groups, in an order rotated by the unit
 #pragma unroll
             for (int i = 0; i < 3; ++i) {
                 const int f = 4 * ((i + xrot) % 3);
@@ -881,41 +898,47 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
                 copy16_to_lds<2048>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
                 copy16_to_lds<3072>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
             }
-            // V rows (lane/2) + 32k, columns 8(lane%2) .. +7; rows past the chunk's end read as zero
-            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0,
+            // V rows of the unit's 16 NT columns, 2 NT lanes per row (8 columns
+            // each), 32 / NT rows per copy; rows past the chunk's end read as zero
+            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + colp,
                                         len_of(j) * row_stride * 2);
+            constexpr int LPR = 2 * NT;
 #pragma unroll
-            for (int k = 0; k < 2; ++k)
-                copy16_to_lds_buf(vr, (((lane >> 1) + 32 * k) * row_stride + 8 * (lane & 1)) * 2,
+            for (int k = 0; k < 2 * NT; ++k)
+                copy16_to_lds_buf(vr, ((lane / LPR + (64 / LPR) * k) * row_stride + 8 * (lane % LPR)) * 2,
                                   xv + XV_V + k * FRAG);
             // 512 bytes; lanes 32-63 read past the record's end as zero
             copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16,
                               (lds_u8*)lds_dg + p * DG_SLOT + DG_GL);
         };
-        // Delta0 = X' diag(rk beta) V from the buffer into slot p.
+        // Delta0 = X' diag(rk beta) V of both tiles from the buffer into slot p.
         auto delta0 = [&](int p, int lane) {
             const unsigned char* xv = lds_xv;
             const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
-            bf16x8 vb[2];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                const int r0 = 32 * s + 4 * g;
-                vb[s] = col8_tr2(xv, XV_V, DVT, r0, r0 + 16, 0, l16);
-            }
-            floatx4 Dm[4];
-#pragma unroll
-            for (int m = 0; m < 4; ++m) Dm[m] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                    for (int m = 0; m < 4; ++m)
-                        if (s < (m < 2 ? 1 : 2))
-                            Dm[m] = mma(ld8(xv, XV_X + (2 * tri_block(m, s) + hl) * FRAG + lo16), vb[s], Dm[m]);
             unsigned char* dg = lds_dg + p * DG_SLOT;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) *reinterpret_cast<floatx4*>(dg + DG_D + m * FRAG + lo16) = Dm[m];
+            for (int t = 0; t < NT; ++t) {
+                bf16x8 vb[2];
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const int r0 = 32 * s + 4 * g;
+                    vb[s] = col8_tr2(xv, XV_V, NT * DVT, r0, r0 + 16, DVT * t, l16);
+                }
+                floatx4 Dm[4];
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Dm[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m)
+                            if (s < (m < 2 ? 1 : 2))
+                                Dm[m] = mma(ld8(xv, XV_X + (2 * tri_block(m, s) + hl) * FRAG + lo16), vb[s], Dm[m]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+                    *reinterpret_cast<floatx4*>(dg + DG_D + (4 * t + m) * FRAG + lo16) = Dm[m];
+            }
         };
         // Chunks 0 and 1 before the first barrier; then in step j (while the
         // state wave runs chunk j+1) chunk j+2 into slot j mod 2, last read by
@@ -963,20 +986,22 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         // in O[m]: one 8-byte (bf16) or 16-byte (fp32) store per row block.
         // Rows past the chunk's end, and everything when L = 0, fall outside
         // the range and are dropped.
-        auto store_o = [&](const floatx4 (&O)[4], int j, int L, int lane) {
+        auto store_o = [&](const floatx4 (&O)[NT][4], int j, int L, int lane) {
             const int l16 = lane & 15, g = lane >> 4;
             const int out_bytes = L * row_stride * static_cast<int>(sizeof(TOut));
-            const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0, out_bytes);
+            const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + colp, out_bytes);
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
             for (int m = 0; m < 4; ++m) {
-                const int off = ((16 * m + l16) * row_stride + 4 * g) * static_cast<int>(sizeof(TOut));
+                const int off = ((16 * m + l16) * row_stride + DVT * t + 4 * g) * static_cast<int>(sizeof(TOut));
                 if constexpr (sizeof(TOut) == 4) {
                     typedef int intx4 __attribute__((ext_vector_type(4)));
-                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, O[m]), orr, off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, O[t][m]), orr, off, 0, 0);
                 } else {
                     typedef int intx2 __attribute__((ext_vector_type(2)));
-                    const intx2 pk = {static_cast<int>(pack_bf16x2(O[m][0], O[m][1])),
-                                      static_cast<int>(pack_bf16x2(O[m][2], O[m][3]))};
+                    const intx2 pk = {static_cast<int>(pack_bf16x2(O[t][m][0], O[t][m][1])),
+                                      static_cast<int>(pack_bf16x2(O[t][m][2], O[t][m][3]))};
                     __builtin_amdgcn_raw_buffer_store_b64(pk, orr, off, 0, 0);
                 }
             }
@@ -984,35 +1009,40 @@ __global__ __launch_bounds__(SCAN_THREADS) void scan_kernel(
         // Step j (between the state wave's barriers j and j+1): store chunk
         // j-1's outputs, request chunk j+1's operands and form chunk j's
         // outputs.  Everything has landed before the barrier.
-        auto step = [&](Ops& cur, Ops& nxt, int b, int lane, int j, floatx4 (&O)[4], int& o_len) {
-            const unsigned char* xch = lds_xch + b * XCH_SLOT;
+        auto step = [&](Ops& cur, Ops& nxt, int b, int lane, int j, floatx4 (&O)[NT][4], int& o_len) {
             const int lo16 = lane * 16;
             store_o(O, j - 1, o_len, lane);
             o_len = j < nc ? len_of(j) : 0;
             load(nxt, min(j + 1, nc - 1), lane);
-            halfx8 sh[4], dh[2];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) sh[s] = ldh8(xch, XCH_S + s * FRAG + lo16);
+            for (int t = 0; t < NT; ++t) {
+                const unsigned char* xch = lds_xch + b * XCH_SLOT + XCH_TILE * t;
+                halfx8 sh[4], dh[2];
 #pragma unroll
-            for (int s = 0; s < 2; ++s) dh[s] = ldh8(xch, XCH_D + s * FRAG + lo16);
+                for (int s = 0; s < 4; ++s) sh[s] = ldh8(xch, XCH_S + s * FRAG + lo16);
 #pragma unroll
-            for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+                for (int s = 0; s < 2; ++s) dh[s] = ldh8(xch, XCH_D + s * FRAG + lo16);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                for (int m = 0; m < 4; ++m) O[t][m] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int m = 0; m < 4; ++m) O[m] = mmah(sh[s], as_halfx8(cur.q[4 * m + s]), O[m]);
+                for (int s = 0; s < 4; ++s)
 #pragma unroll
-            for (int s = 0; s < 2; ++s)
+                    for (int m = 0; m < 4; ++m) O[t][m] = mmah(sh[s], as_halfx8(cur.q[4 * m + s]), O[t][m]);
 #pragma unroll
-                for (int m = 0; m < 4; ++m)
-                    if (s < (m < 2 ? 1 : 2)) O[m] = mmah(dh[s], as_halfx8(cur.p[tri_block(m, s)]), O[m]);
+                for (int s = 0; s < 2; ++s)
+#pragma unroll
+                    for (int m = 0; m < 4; ++m)
+                        if (s < (m < 2 ? 1 : 2)) O[t][m] = mmah(dh[s], as_halfx8(cur.p[tri_block(m, s)]), O[t][m]);
+            }
             wait_vmcnt<0>();
         };
 
         Ops B0, B1;
-        floatx4 O[4];
+        floatx4 O[NT][4];
 #pragma unroll
-        for (int m = 0; m < 4; ++m) O[m] = floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int t = 0; t < NT; ++t)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O[t][m] = floatx4{0.f, 0.f, 0.f, 0.f};
         int o_len = 0;
         if (nc > 0) {
             load(B0, 0, lane0);
@@ -1084,10 +1114,18 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
         if (e != hipSuccess) return e;
     }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
-    const unsigned grid = ((chains + 7u) & ~7u) * (D / DVT);
-    scan_kernel<TOut><<<grid, SCAN_THREADS, 0, stream>>>(static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order,
-                                                         records, a.initial_state, static_cast<TOut*>(a.out),
-                                                         a.final_state, a.num_seqs, a.num_heads);
+    // One tile per workgroup while every tile has a compute unit of its own
+    // (the chunk chain is then the limit); two when tiles outnumber them.
+    const bool pairs = static_cast<size_t>(chains) * (D / DVT) > static_cast<size_t>(device_cu_count());
+    const unsigned groups = (chains + 7u) & ~7u;
+    if (pairs)
+        scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(
+            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+            static_cast<TOut*>(a.out), a.final_state, a.num_seqs, a.num_heads);
+    else
+        scan_kernel<TOut, 1><<<groups * ScanShape<1>::UNITS, ScanShape<1>::THREADS, 0, stream>>>(
+            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+            static_cast<TOut*>(a.out), a.final_state, a.num_seqs, a.num_heads);
     return hipGetLastError();
 }
 
