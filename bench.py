@@ -44,6 +44,7 @@ KERNEL_SOURCES = {
                 "gated_delta_rule_53_amd/csrc/kda_common.h"],
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
+KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
@@ -240,6 +241,7 @@ def main():
     gp = bench_prefill_gated(args.steps, args.warmup)
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     g_achieved = gp["alg_bytes"] / gp["per_launch"] / 1e9
+    g_tr = measured_traffic("gated_prefill")
 
     ms_per_step = pf["wall"] / args.steps * 1e3
     tokens_per_s = pf["tokens"] * args.steps / pf["wall"]
@@ -287,7 +289,8 @@ def main():
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),
                                        "bound": "hbm", "achieved": round(g_achieved, 2), "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": round(g_achieved / HBM_PEAK_GBS, 4),
-                                       "traffic": None, "alg_bytes_per_launch": gp["alg_bytes"],
+                                       "traffic": None if g_tr is None else round(g_tr / gp["per_launch"] / 1e9, 2),
+                                       "alg_bytes_per_launch": gp["alg_bytes"],
                                        "launch_us": round(gp["per_launch"] * 1e6, 2)}},
     }
     if not args.no_cpu_baseline:
