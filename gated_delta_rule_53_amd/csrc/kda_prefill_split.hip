@@ -860,6 +860,11 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         };
         auto step = [&](int sbuf, int lane, int j) {
             if (j + 3 < nc) {
+                // Its copies are needed two chunks later: let the Delta0 and
+                // output waves, whose loads are needed sooner, reach the CU's
+                // memory queue first (a wave blocked on a full queue stalls
+                // its MFMAs too).  512 cycles measured best of 0 / 512 / 1024.
+                __builtin_amdgcn_s_sleep(8);
                 fetch_state(sbuf, j + 3, lane);
                 if (toucher && j + 4 < nc) {
                     touch(j + 4, lane);
