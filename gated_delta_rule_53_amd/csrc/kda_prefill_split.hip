@@ -660,9 +660,10 @@ constexpr int SB_KE = 16 * FRAG;               // Ke^T [w 8][s 2]
 // LDS regions, each its own array: the compiler then sees that the direct
 // loads into one region do not write the others, and waits only where needed.
 constexpr int SB_BYTES = 32 * FRAG;            // one of three state buffers (chunk mod 3)
-constexpr int XV_X = 0, XV_V = 12 * FRAG;      // the loader's X' [tri 6][hl 2] and V rows [64][16 NT] bf16
-constexpr int DG_D = 0;                        // two slots: Delta0 of tile t (accumulator layout) at 4t fragments,
+constexpr int XV_X = 0, XV_V = 12 * FRAG;      // X' buffers: X' [tri 6][hl 2], V rows [64][16 NT] bf16,
                                                // then e^{G_last} [128] fp32 (the copy fills 1 KiB)
+constexpr int DG_D = 0;                        // two slots: Delta0 of tile t (accumulator layout) at 4t fragments,
+                                               // then e^{G_last} [128] fp32
 // The output is not fed back, so it takes S and D as single fp16 (their high
 // parts); the state side keeps the hi/lo pairs.
 constexpr int XCH_S = 0;                       // exchange, two slots, per tile: S as B operand [s 4], fp16
@@ -671,11 +672,15 @@ constexpr int XCH_TILE = 6 * FRAG;
 
 template <int NT>
 struct ScanShape {
-    static constexpr int XV_BYTES = XV_V + C * NT * DVT * 2;
+    // With one tile the X' buffer is doubled, so the Delta0 wave forms Delta0
+    // from a copy made a whole chunk earlier; with two there is no room.
+    static constexpr int XVB = NT == 1 ? 2 : 1;
+    static constexpr int XV_GL = XV_V + C * NT * DVT * 2;
+    static constexpr int XV_BYTES = XV_GL + FRAG;
     static constexpr int DG_GL = NT * 4 * FRAG;
-    static constexpr int DG_SLOT = DG_GL + FRAG;
+    static constexpr int DG_SLOT = DG_GL + D * 4;
     static constexpr int XCH_SLOT = NT * XCH_TILE;
-    static constexpr int LDS = 3 * SB_BYTES + XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT + 256;
+    static constexpr int LDS = 3 * SB_BYTES + XVB * XV_BYTES + 2 * DG_SLOT + 2 * XCH_SLOT + 256;
     static constexpr int THREADS = 64 * (NT + 3);
     static constexpr int UNITS = D / (NT * DVT);  // workgroups per chain
     static_assert(LDS <= 160 * 1024, "scan LDS budget");
@@ -690,7 +695,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
     using SS = ScanShape<NT>;
     constexpr int DG_GL = SS::DG_GL, DG_SLOT = SS::DG_SLOT, XCH_SLOT = SS::XCH_SLOT;
-    __shared__ __align__(16) unsigned char lds_xv[SS::XV_BYTES];
+    __shared__ __align__(16) unsigned char lds_xv[SS::XVB * SS::XV_BYTES];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
     __shared__ __align__(16) unsigned char lds_touch[256];  // sink of the L2 touches, never read
@@ -889,10 +894,10 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         wait_vmcnt<0>();
     } else if (wave == NT) {
         // ================= Delta0 wave =================
-        // X' and V rows of chunk j into its buffer, e^{G_last} of chunk j into slot p (15 copies).
+        // X', V rows and e^{G_last} of chunk j into X' buffer xb (15 copies).
         const int xrot = unit % 3;
-        auto fetch_xv = [&](int p, int j, int lane) {
-            lds_u8* xv = (lds_u8*)lds_xv;
+        auto fetch_xv = [&](int xb, int j, int lane) {
+            lds_u8* xv = (lds_u8*)lds_xv + xb * SS::XV_BYTES;
             const unsigned char* rec = rec_of(j) + lane * 16;
             // three 4 KiB groups, in an order rotated by the unit
 #pragma unroll
@@ -913,14 +918,16 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
                 copy16_to_lds_buf(vr, ((lane / LPR + (64 / LPR) * k) * row_stride + 8 * (lane % LPR)) * 2,
                                   xv + XV_V + k * FRAG);
             // 512 bytes; lanes 32-63 read past the record's end as zero
-            copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16,
-                              (lds_u8*)lds_dg + p * DG_SLOT + DG_GL);
+            copy16_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), REC_VEC + lane * 16, xv + SS::XV_GL);
         };
-        // Delta0 = X' diag(rk beta) V of both tiles from the buffer into slot p.
-        auto delta0 = [&](int p, int lane) {
-            const unsigned char* xv = lds_xv;
+        // Delta0 = X' diag(rk beta) V of every tile from X' buffer xb into slot
+        // p, and e^{G_last} along with it.
+        auto delta0 = [&](int xb, int p, int lane) {
+            const unsigned char* xv = lds_xv + xb * SS::XV_BYTES;
             const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
             unsigned char* dg = lds_dg + p * DG_SLOT;
+            *reinterpret_cast<floatx2*>(dg + DG_GL + lane * 8) =
+                *reinterpret_cast<const floatx2*>(xv + SS::XV_GL + lane * 8);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
                 bf16x8 vb[2];
@@ -947,21 +954,42 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         };
         // Chunks 0 and 1 before the first barrier; then in step j (while the
         // state wave runs chunk j+1) chunk j+2 into slot j mod 2, last read by
-        // the state wave in step j.
+        // the state wave in step j.  With two X' buffers chunk j+2 was copied
+        // in step j-1 (into buffer j mod 2), and chunk j+3 is requested once
+        // its Delta0 is formed, into the buffer chunk j+1 has left.
+        if constexpr (SS::XVB == 2) {
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            if (j < nc) {
-                fetch_xv(j, j, lane0);
-                wait_vmcnt<0>();
-                delta0(j, lane0);
+            for (int j = 0; j < 2; ++j)
+                if (j < nc) fetch_xv(j, j, lane0);
+            wait_vmcnt<0>();
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+                if (j < nc) delta0(j, j, lane0);
+            // the reads of buffer 0 are done before the copy into it is issued
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            if (2 < nc) fetch_xv(0, 2, lane0);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                if (j < nc) {
+                    fetch_xv(0, j, lane0);
+                    wait_vmcnt<0>();
+                    delta0(0, j, lane0);
+                }
             }
         }
         lds_barrier();
         auto step = [&](int p, int lane, int j) {
             if (j + 2 < nc) {
-                fetch_xv(p, j + 2, lane);
-                wait_vmcnt<0>();
-                delta0(p, lane);
+                if constexpr (SS::XVB == 2) {
+                    wait_vmcnt<0>();
+                    delta0(p, p, lane);
+                    if (j + 3 < nc) fetch_xv(1 - p, j + 3, lane);
+                } else {
+                    fetch_xv(0, j + 2, lane);
+                    wait_vmcnt<0>();
+                    delta0(0, p, lane);
+                }
             }
         };
         for (int j = 0; j < nc; j += 2) {
