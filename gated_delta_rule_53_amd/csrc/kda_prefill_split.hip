@@ -695,7 +695,10 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
     using SS = ScanShape<NT>;
     constexpr int DG_GL = SS::DG_GL, DG_SLOT = SS::DG_SLOT, XCH_SLOT = SS::XCH_SLOT;
-    __shared__ __align__(16) unsigned char lds_xv[SS::XVB * SS::XV_BYTES];
+    // the X' buffers are separate arrays, so the compiler sees that a copy
+    // into one does not write what is being read from the other
+    __shared__ __align__(16) unsigned char lds_xv0[SS::XV_BYTES];
+    __shared__ __align__(16) unsigned char lds_xv1[SS::XVB == 2 ? SS::XV_BYTES : 16];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
     __shared__ __align__(16) unsigned char lds_touch[256];  // sink of the L2 touches, never read
@@ -737,67 +740,74 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
                 for (int j = 0; j < 4; ++j)
                     S[w][j] = initial_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
         }
-        // Step j from state buffer sb (chunk j mod 3) and slots of parity p; an
-        // inactive step (the pad after an odd chunk count) leaves S unchanged.
-        auto step = [&](int sbuf, int p, int lane, bool active) {
+        // Step j from state buffer sb (chunk j mod 3) and slots of parity p.
+        // D = Delta0 - Psi' S runs K block by K block (32 rows of S each): the
+        // -Psi' fragments of the next block are read, the next block of S is
+        // split and handed over, Ke^T is read and the block of S just used is
+        // decayed by e^{G_last} while the current block's eight MFMAs run.  U
+        // then accumulates in S itself (S' = diag(e^{G_last}) S + Ke^T D),
+        // rows 0-31 of D first, so the second half of D is split while the
+        // first sixteen products run.
+        auto step = [&](int sbuf, int p, int lane) {
             const unsigned char* sb = lds_sb + sbuf * SB_BYTES;
             const unsigned char* dg = lds_dg + p * DG_SLOT;
             unsigned char* xch = lds_xch + p * XCH_SLOT + xch_t;
             const int g = lane >> 4, lo16 = lane * 16;
-            // stage 1 (four groups): S as the B operand, handed over; operands of D
-            halfx8 fp[16];
-            halfx8 sh[4], sl[4];
             floatx4 Dm[4];
+            halfx8 fa[4], fb[4], fk[16];
+            halfx8 sh, sl, shn, sln;
 #pragma unroll
             for (int m = 0; m < 4; ++m) Dm[m] = *reinterpret_cast<const floatx4*>(dg + dg_t + m * FRAG + lo16);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
+            for (int m = 0; m < 4; ++m) fa[m] = ldh8(sb, SB_NP + 4 * m * FRAG + lo16);
+            split8h(S[0], S[1], sh, sl);
+            *reinterpret_cast<halfx8*>(xch + XCH_S + lo16) = sh;
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-                for (int i = 4 * s; i < 4 * s + 4; ++i) fp[i] = ldh8(sb, SB_NP + i * FRAG + lo16);
-                split8h(S[2 * s], S[2 * s + 1], sh[s], sl[s]);
-                *reinterpret_cast<halfx8*>(xch + XCH_S + s * FRAG + lo16) = sh[s];
+            for (int s = 0; s < 4; ++s) {
+                if (s < 3) {
+#pragma unroll
+                    for (int m = 0; m < 4; ++m) fb[m] = ldh8(sb, SB_NP + (4 * m + s + 1) * FRAG + lo16);
+                    split8h(S[2 * s + 2], S[2 * s + 3], shn, sln);
+                    *reinterpret_cast<halfx8*>(xch + XCH_S + (s + 1) * FRAG + lo16) = shn;
+                }
+#pragma unroll
+                for (int q = 4 * s; q < 4 * s + 4; ++q) fk[q] = ldh8(sb, SB_KE + q * FRAG + lo16);
+#pragma unroll
+                for (int w = 2 * s; w < 2 * s + 2; ++w)
+                    S[w] *= *reinterpret_cast<const floatx4*>(dg + DG_GL + (16 * w + 4 * g) * 4);
+                if (s < 3) {
+#pragma unroll
+                    for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                        for (int m = 0; m < 4; ++m) Dm[m] = mmah(fa[m], hl ? sl : sh, Dm[m]);
+                } else {
+                    // rows 0-31 of D complete first
+#pragma unroll
+                    for (int half = 0; half < 2; ++half)
+#pragma unroll
+                        for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+                            for (int m = 2 * half; m < 2 * half + 2; ++m) Dm[m] = mmah(fa[m], hl ? sl : sh, Dm[m]);
+                }
+#pragma unroll
+                for (int m = 0; m < 4; ++m) fa[m] = fb[m];
+                sh = shn;
+                sl = sln;
                 __builtin_amdgcn_sched_barrier(0);
             }
-            // stage 2: D = Delta0 - Psi' S (row blocks m round-robin); operands of U
-            halfx8 fk[16];
-            floatx4 fg[8];
-#pragma unroll
-            for (int s = 0; s < 4; ++s)
-#pragma unroll
-                for (int hl = 0; hl < 2; ++hl) {
-                    const int grp = 2 * s + hl;  // 8 groups of 4 MFMAs, 3 reads each
-#pragma unroll
-                    for (int m = 0; m < 4; ++m) Dm[m] = mmah(fp[4 * m + s], hl ? sl[s] : sh[s], Dm[m]);
-#pragma unroll
-                    for (int q = 3 * grp; q < 3 * grp + 3; ++q) {
-                        if (q < 16)
-                            fk[q] = ldh8(sb, SB_KE + q * FRAG + lo16);
-                        else
-                            fg[q - 16] = *reinterpret_cast<const floatx4*>(dg + DG_GL + (16 * (q - 16) + 4 * g) * 4);
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
             KDA_PHASE_MARK(8);
-            // stage 3: D as the B operand (handed over); decay of S
-            halfx8 dh[2], dl[2];
-            floatx4 U[8];
+            // U: D as the B operand, in two halves, each handed over
 #pragma unroll
             for (int s = 0; s < 2; ++s) {
-                split8h(Dm[2 * s], Dm[2 * s + 1], dh[s], dl[s]);
-                *reinterpret_cast<halfx8*>(xch + XCH_D + s * FRAG + lo16) = dh[s];
-            }
-#pragma unroll
-            for (int w = 0; w < 8; ++w) U[w] = fg[w] * S[w];
-            __builtin_amdgcn_sched_barrier(0);
-            // stage 4: S' = diag(e^{G_last}) S + Ke^T D (channel blocks w round-robin)
-#pragma unroll
-            for (int s = 0; s < 2; ++s)
+                halfx8 dh, dl;
+                split8h(Dm[2 * s], Dm[2 * s + 1], dh, dl);
+                *reinterpret_cast<halfx8*>(xch + XCH_D + s * FRAG + lo16) = dh;
 #pragma unroll
                 for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-                    for (int w = 0; w < 8; ++w) U[w] = mmah(fk[2 * w + s], hl ? dl[s] : dh[s], U[w]);
-#pragma unroll
-            for (int w = 0; w < 8; ++w) S[w] = active ? U[w] : S[w];
+                    for (int w = 0; w < 8; ++w) S[w] = mmah(fk[2 * w + s], hl ? dl : dh, S[w]);
+            }
             KDA_PHASE_MARK(9);
             lds_barrier();
             KDA_PHASE_MARK(10);
@@ -807,9 +817,13 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         int sbuf = 0;
         for (int j = 0; j < nc; j += 2) {
             const int lane = opaque(lane0);
-            step(sbuf, 0, lane, true);
+            step(sbuf, 0, lane);
             sbuf = sbuf == 2 ? 0 : sbuf + 1;
-            step(sbuf, 1, lane, j + 1 < nc);
+            // the pad step after an odd chunk count only keeps the barrier count
+            if (j + 1 < nc)
+                step(sbuf, 1, lane);
+            else
+                lds_barrier();
             sbuf = sbuf == 2 ? 0 : sbuf + 1;
         }
         if (final_state) {
@@ -894,10 +908,10 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         wait_vmcnt<0>();
     } else if (wave == NT) {
         // ================= Delta0 wave =================
-        // X', V rows and e^{G_last} of chunk j into X' buffer xb (15 copies).
+        // X', V rows and e^{G_last} of chunk j into X' buffer xb.
         const int xrot = unit % 3;
         auto fetch_xv = [&](int xb, int j, int lane) {
-            lds_u8* xv = (lds_u8*)lds_xv + xb * SS::XV_BYTES;
+            lds_u8* xv = (lds_u8*)(xb ? lds_xv1 : lds_xv0);
             const unsigned char* rec = rec_of(j) + lane * 16;
             // three 4 KiB groups, in an order rotated by the unit
 #pragma unroll
@@ -923,7 +937,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         // Delta0 = X' diag(rk beta) V of every tile from X' buffer xb into slot
         // p, and e^{G_last} along with it.
         auto delta0 = [&](int xb, int p, int lane) {
-            const unsigned char* xv = lds_xv + xb * SS::XV_BYTES;
+            const unsigned char* xv = xb ? lds_xv1 : lds_xv0;
             const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
             unsigned char* dg = lds_dg + p * DG_SLOT;
             *reinterpret_cast<floatx2*>(dg + DG_GL + lane * 8) =
@@ -982,9 +996,14 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         auto step = [&](int p, int lane, int j) {
             if (j + 2 < nc) {
                 if constexpr (SS::XVB == 2) {
+                    // Form chunk j+2's Delta0, then request chunk j+3 (past the end,
+                    // the last chunk again: the buffer it lands in is not read any
+                    // more; no branch, so no join merges the copies' wait state).
+                    // Requesting first was measured slower: the copies then meet
+                    // the output wave's loads in the memory queue.
                     wait_vmcnt<0>();
                     delta0(p, p, lane);
-                    if (j + 3 < nc) fetch_xv(1 - p, j + 3, lane);
+                    fetch_xv(1 - p, min(j + 3, nc - 1), lane);
                 } else {
                     fetch_xv(0, j + 2, lane);
                     wait_vmcnt<0>();
