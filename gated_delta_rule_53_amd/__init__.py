@@ -19,11 +19,13 @@ from ._binding import (  # noqa: F401
     abi_version,
     chunk_fwd,
     chunk_fwd_gated,
+    chunk_fwd_pooled,
     chunk_fwd_workspace_bytes,
     library_path,
     raw_library,
     recurrent_step,
     recurrent_step_gated,
+    recurrent_verify,
 )
 
 __all__ = [
@@ -31,6 +33,8 @@ __all__ = [
     "chunk_fwd_gated",
     "recurrent_step",
     "recurrent_step_gated",
+    "chunk_fwd_pooled",
+    "recurrent_verify",
     "Gate",
     "chunk_fwd_workspace_bytes",
     "abi_version",

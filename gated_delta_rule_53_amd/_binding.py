@@ -82,6 +82,11 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
     lib.kda_recurrent_step_gated.argtypes = [P, G, vp, vp, vp, vp, vp, fp, vp, vp]
     lib.kda_recurrent_step_gated.restype = ctypes.c_int
+    i32 = ctypes.c_int32
+    lib.kda_chunk_fwd_pooled.argtypes = [P, G, vp, vp, vp, vp, vp, vp, fp, i32, vp, vp, vp, sz, vp]
+    lib.kda_chunk_fwd_pooled.restype = ctypes.c_int
+    lib.kda_recurrent_verify.argtypes = [P, i32, G, vp, vp, vp, vp, vp, fp, i32, vp, vp, vp, vp]
+    lib.kda_recurrent_verify.restype = ctypes.c_int
     return lib
 
 
@@ -322,4 +327,114 @@ def recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_
     prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
     _check(_lib.kda_recurrent_step_gated(ctypes.byref(prob), ctypes.byref(gate), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(raw_g), _ptr(raw_beta), _ptr(state), _ptr(out), _stream(dev)))
+    return out
+
+
+def _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev):
+    if a_log is None:
+        if dt_bias is not None or lower_bound is not None:
+            raise KdaArgumentError(1, "dt_bias and lower_bound need a_log")
+        return None
+    if dt_bias is None:
+        raise KdaArgumentError(1, "a_log needs dt_bias")
+    return _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+
+
+def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, state_pool: torch.Tensor, state_slots: torch.Tensor,
+                     cu_seqlens: Optional[torch.Tensor] = None, *, a_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
+                     scale: Optional[float] = None, qk_l2norm: bool = True,
+                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                     workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Chunked prefill with the states in a slot pool (``kda_chunk_fwd_pooled``).
+
+    state_pool [P, H, dk, dv] float32 is read and written: sequence n starts
+    from slot state_slots[n] (int32 [N], device) and its final state goes back
+    there; a slot outside [0, P) starts from zero and is not written.  Without
+    a_log, g [T, H, dk] and beta [T, H] are float32; with a_log (and dt_bias,
+    lower_bound as for ``chunk_fwd_gated``) they are the raw projections in
+    q's dtype.  Returns out.
+    """
+    if q.dim() != 3:
+        raise KdaArgumentError(2, f"q must be [T, H, dk], got {tuple(q.shape)}")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = cu_seqlens.numel() - 1
+    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev)
+    gdt = torch.float32 if gate is None else q.dtype
+    _need(q, "q", (T, H, dk), None, dev)
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(v, "v", (T, H, dv), q.dtype, dev)
+    _need(g, "g", (T, H, dk), gdt, dev)
+    _need(beta, "beta", (T, H), gdt, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if state_pool.dim() != 4:
+        raise KdaArgumentError(2, f"state_pool must be [P, H, dk, dv], got {tuple(state_pool.shape)}")
+    P = state_pool.shape[0]
+    _need(state_pool, "state_pool", (P, H, dk, dv), torch.float32, dev)
+    _need(state_slots, "state_slots", (N,), torch.int32, dev)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, dv), out_dtype, dev)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    ws_bytes = chunk_fwd_workspace_bytes(prob)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_lib.kda_chunk_fwd_pooled(ctypes.byref(prob), None if gate is None else ctypes.byref(gate), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(cu_seqlens), _ptr(state_pool),
+                                     P, _ptr(state_slots), _ptr(out), _ptr(workspace), ws_len, _stream(dev)))
+    return out
+
+
+def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                     beta: torch.Tensor, state_pool: torch.Tensor, state_indices: torch.Tensor,
+                     num_accepted: Optional[torch.Tensor] = None, *, a_log: Optional[torch.Tensor] = None,
+                     dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
+                     scale: Optional[float] = None, qk_l2norm: bool = True,
+                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Multi-token verify decode over a slot pool (``kda_recurrent_verify``).
+
+    q, k [N, W, H, dk]; v [N, W, H, dv]; g, beta [N, W, H, dk], [N, W, H]
+    (float32, or raw in q's dtype with a_log); state_pool [P, H, dk, dv]
+    float32; state_indices [N, W] int32: sequence n starts from slot
+    state_indices[n, a-1] (a = num_accepted[n] clamped to [1, W], 1 without
+    num_accepted) and writes its state after token t to slot
+    state_indices[n, t].  Returns out [N, W, H, dv].
+    """
+    if q.dim() != 4:
+        raise KdaArgumentError(2, f"q must be [N, W, H, dk], got {tuple(q.shape)}")
+    N, W, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev)
+    gdt = torch.float32 if gate is None else q.dtype
+    _need(k, "k", (N, W, H, dk), q.dtype, dev)
+    _need(v, "v", (N, W, H, dv), q.dtype, dev)
+    _need(g, "g", (N, W, H, dk), gdt, dev)
+    _need(beta, "beta", (N, W, H), gdt, dev)
+    if state_pool.dim() != 4:
+        raise KdaArgumentError(2, f"state_pool must be [P, H, dk, dv], got {tuple(state_pool.shape)}")
+    P = state_pool.shape[0]
+    _need(state_pool, "state_pool", (P, H, dk, dv), torch.float32, dev)
+    _need(state_indices, "state_indices", (N, W), torch.int32, dev)
+    if num_accepted is not None:
+        _need(num_accepted, "num_accepted", (N,), torch.int32, dev)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((N, W, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", (N, W, H, dv), out_dtype, dev)
+    prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, None if gate is None else ctypes.byref(gate), _ptr(q),
+                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
+                                     _ptr(state_indices), _ptr(num_accepted), _ptr(out), _stream(dev)))
     return out

@@ -82,7 +82,8 @@ kda_status_t check_gate(const kda_gate_t* gate, const char* what, kda::GateParam
 kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda::GateParams& gp,
                             const void* q, const void* k, const void* v, const void* g, const void* beta,
                             const int32_t* cu_seqlens, const float* initial_state, void* out,
-                            float* final_state, void* workspace, size_t workspace_bytes, void* stream) {
+                            float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                            const int32_t* slots = nullptr, int num_slots = 0) {
     if (p->chunk_size != 0 && p->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
     if (p->num_seqs == 0) {
@@ -113,6 +114,8 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
     a.initial_state = initial_state;
     a.out = out;
     a.final_state = final_state;
+    a.slots = slots;
+    a.num_slots = num_slots;
     a.total_tokens = p->total_tokens;
     a.num_seqs = p->num_seqs;
     a.num_heads = p->num_heads;
@@ -156,6 +159,12 @@ kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const
     a.l2norm = p->qk_l2norm;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(kda::launch_decode(a, s), s, what);
+}
+
+kda::GateParams optional_gate(const kda_gate_t* gate, const char* what, kda_status_t& st) {
+    kda::GateParams gp{};
+    st = gate ? check_gate(gate, what, gp) : KDA_OK;
+    return gp;
 }
 
 }  // namespace
@@ -231,6 +240,71 @@ kda_status_t kda_recurrent_step_gated(const kda_problem_t* p, const kda_gate_t* 
     st = check_gate(gate, what, gp);
     if (st != KDA_OK) return st;
     return recurrent_step_impl(what, p, gp, q, k, v, raw_g, raw_beta, state, out, stream);
+}
+
+kda_status_t kda_chunk_fwd_pooled(const kda_problem_t* p, const kda_gate_t* gate, const void* q, const void* k,
+                                  const void* v, const void* g, const void* beta, const int32_t* cu_seqlens,
+                                  float* state_pool, int32_t num_slots, const int32_t* state_slots, void* out,
+                                  void* workspace, size_t workspace_bytes, void* stream) {
+    const char* what = "kda_chunk_fwd_pooled";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    const kda::GateParams gp = optional_gate(gate, what, st);
+    if (st != KDA_OK) return st;
+    if (num_slots < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: num_slots = %d < 0", what, num_slots);
+    if (p->num_seqs > 0 && (!state_pool || !state_slots))
+        return fail(KDA_ERR_NULL_POINTER, "%s: state_pool and state_slots are required", what);
+    if (int64_t(num_slots) * p->num_heads > (int64_t(1) << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: state pool too large", what);
+    return chunk_fwd_impl(what, p, gp, q, k, v, g, beta, cu_seqlens, state_pool, out, state_pool, workspace,
+                          workspace_bytes, stream, state_slots, num_slots);
+}
+
+kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const kda_gate_t* gate, const void* q,
+                                  const void* k, const void* v, const void* g, const void* beta,
+                                  float* state_pool, int32_t num_slots, const int32_t* state_indices,
+                                  const int32_t* num_accepted, void* out, void* stream) {
+    const char* what = "kda_recurrent_verify";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    const kda::GateParams gp = optional_gate(gate, what, st);
+    if (st != KDA_OK) return st;
+    if (width < 1) return fail(KDA_ERR_BAD_SHAPE, "%s: width = %d < 1", what, width);
+    if (num_slots < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: num_slots = %d < 0", what, num_slots);
+    if (p->total_tokens != int64_t(p->num_seqs) * width)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld must equal num_seqs * width = %lld", what,
+                    (long long)p->total_tokens, (long long)(int64_t(p->num_seqs) * width));
+    if (int64_t(num_slots) * p->num_heads > (int64_t(1) << 31) - 1)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: state pool too large", what);
+    if (p->num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out)
+        return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state_pool, state_indices and out are required",
+                    what);
+    kda::VerifyArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.g = g;
+    a.beta = beta;
+    a.gate = gp;
+    a.pool = state_pool;
+    a.num_slots = num_slots;
+    a.indices = state_indices;
+    a.accepted = num_accepted;
+    a.out = out;
+    a.num_seqs = p->num_seqs;
+    a.width = width;
+    a.num_heads = p->num_heads;
+    a.head_dim = p->head_k;
+    a.qkv_bf16 = p->qkv_dtype == KDA_BF16;
+    a.out_bf16 = p->out_dtype == KDA_BF16;
+    a.scale = p->scale;
+    a.l2norm = p->qk_l2norm;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_verify(a, s), s, what);
 }
 
 }  // extern "C"

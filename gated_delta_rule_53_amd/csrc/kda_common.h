@@ -103,6 +103,20 @@ __device__ __forceinline__ floatx4 mfma_f32_16x16x4(float a, float b, floatx4 c)
     return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Offset of the (sequence n, head h) state block: sequence-major, or slot
+// slots[n] of a state pool [num_slots, H, D, D].  False for a pool slot
+// outside [0, num_slots): that sequence starts from zero and keeps no state.
+__device__ inline bool state_block(const int32_t* slots, int num_slots, int n, int h, int num_heads, int d,
+                                   size_t& off) {
+    int row = n;
+    if (slots) {
+        row = slots[n];
+        if (row < 0 || row >= num_slots) return false;
+    }
+    off = (static_cast<size_t>(row) * num_heads + h) * d * d;
+    return true;
+}
+
 // Phase timing for kernel tuning.  Compiled out unless KDA_PHASE_TIMING is
 // defined; then thread 0 of every workgroup accumulates clock64() deltas
 // between consecutive marks into kda_phase_cycles[mark].

@@ -137,6 +137,160 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// Multi-token verify decode with state-slot indirection.  Sequence n has
+// `width` tokens (rows n*width .. n*width+width-1) and one state slot per
+// token, idx = indices[n*width ..]: it starts from the state in slot
+// idx[a-1], a = accepted[n] clamped to [1, width] (a = 1 without accepted),
+// and the state after its token t is written to slot idx[t].  A slot outside
+// [0, num_slots) reads as the zero state and is not written.  The whole
+// starting state is read before anything is written, so idx[a-1] may also
+// appear among the destinations.  Each token is the decode step above.
+template <int D, typename TIn, typename TOut, bool GATED>
+__global__ __launch_bounds__(256) void verify_kernel(
+    const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, float* __restrict__ pool,
+    int num_slots, const int32_t* __restrict__ indices, const int32_t* __restrict__ accepted,
+    TOut* __restrict__ out, int num_heads, int width, float scale, int l2norm) {
+    constexpr int NCG = D / 4;
+    constexpr int NRG = 256 / NCG;
+    constexpr int RPT = D / NRG;
+    static_assert(NRG * NCG == 256 && RPT * NRG == D, "tiling");
+
+    const int pair = blockIdx.x;  // n * H + h
+    const int n = pair / num_heads, h = pair - n * num_heads;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int cg = tid % NCG, rg = tid / NCG;
+    const int32_t* idx = indices + static_cast<size_t>(n) * width;
+    const size_t slot_stride = static_cast<size_t>(num_heads) * D * D;
+    auto slot_ptr = [&](int slot) -> float* {
+        return (slot >= 0 && slot < num_slots) ? pool + slot * slot_stride + static_cast<size_t>(h) * D * D
+                                               : nullptr;
+    };
+
+    int a = accepted ? accepted[n] : 1;
+    a = a < 1 ? 1 : (a > width ? width : a);
+    floatx4 s[RPT];
+    {
+        const float* S = slot_ptr(idx[a - 1]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+            s[i] = S ? *reinterpret_cast<const floatx4*>(S + (rg + NRG * i) * D + 4 * cg)
+                     : floatx4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    __shared__ float sq[D], sk[D], se[D];
+    __shared__ float red[4][NCG][8];
+    for (int t = 0; t < width; ++t) {
+        const size_t row = static_cast<size_t>(n) * width + t;  // token row
+        const size_t tok = row * num_heads + h;                  // (token, head)
+        if (tid < D) {
+            const size_t off = tok * D + tid;
+            sq[tid] = to_f32(q[off]);
+            sk[tid] = to_f32(k[off]);
+            float gv;
+            if constexpr (GATED)
+                gv = gate_g(to_f32(static_cast<const TIn*>(g)[off]), gp.dt_bias[h * D + tid], gate_exp(gp.a_log[h]),
+                            gp.lower_bound, gp.has_lower_bound);
+            else
+                gv = static_cast<const float*>(g)[off];
+            se[tid] = fast_exp2(gv * kLog2e);
+        }
+        __syncthreads();
+        float aq = 0.f, ak = 0.f, aqk = 0.f;
+#pragma unroll
+        for (int c = lane; c < D; c += 64) {
+            const float qq = sq[c], kk = sk[c];
+            aq += qq * qq;
+            ak += kk * kk;
+            aqk += qq * kk;
+        }
+        aq = wave_sum_from(aq, 1);
+        ak = wave_sum_from(ak, 1);
+        aqk = wave_sum_from(aqk, 1);
+        const float rq = (l2norm ? rsqrtf(aq + kNormEps) : 1.f) * scale;
+        const float rk = l2norm ? rsqrtf(ak + kNormEps) : 1.f;
+        floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + NRG * i;
+            s[i] *= se[r];
+            pu += sk[r] * s[i];
+            pp += sq[r] * s[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pu[j] = wave_sum_from(pu[j], NCG);
+            pp[j] = wave_sum_from(pp[j], NCG);
+        }
+        if (lane < NCG) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                red[wave][lane][j] = pu[j];
+                red[wave][lane][4 + j] = pp[j];
+            }
+        }
+        __syncthreads();
+        floatx4 u, p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
+            p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
+        }
+        float b;
+        if constexpr (GATED)
+            b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
+        else
+            b = static_cast<const float*>(beta)[tok];
+        const size_t voff = tok * D + 4 * cg;
+        floatx4 delta;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
+        float* S = slot_ptr(idx[t]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + NRG * i;
+            s[i] += (rk * sk[r]) * delta;
+            if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
+        }
+        if (rg == 0) {
+            const float kq = rk * rq * aqk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+        }
+        // sq, sk, se and red are rewritten by the next token
+        __syncthreads();
+    }
+}
+
+template <int D, typename TIn, typename TOut>
+static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
+    const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads));
+    const TIn* q = static_cast<const TIn*>(a.q);
+    const TIn* k = static_cast<const TIn*>(a.k);
+    const TIn* v = static_cast<const TIn*>(a.v);
+    if (a.gate.a_log)
+        verify_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
+            a.num_heads, a.width, a.scale, a.l2norm);
+    else
+        verify_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
+            q, k, v, a.g, a.beta, a.gate, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
+            a.num_heads, a.width, a.scale, a.l2norm);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_verify_d(const VerifyArgs& a, hipStream_t stream) {
+    if (a.qkv_bf16)
+        return a.out_bf16 ? launch_verify_t<D, bf16_t, bf16_t>(a, stream) : launch_verify_t<D, bf16_t, float>(a, stream);
+    return a.out_bf16 ? launch_verify_t<D, float, bf16_t>(a, stream) : launch_verify_t<D, float, float>(a, stream);
+}
+
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream) {
+    return a.head_dim == 128 ? launch_verify_d<128>(a, stream) : launch_verify_d<64>(a, stream);
+}
+
 template <int D, typename TIn, typename TOut>
 static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const dim3 grid(static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads));

@@ -30,6 +30,29 @@ struct DecodeArgs {
     int l2norm;
 };
 
+// Multi-token verify decode over a slot pool [num_slots, H, dk, dv].
+struct VerifyArgs {
+    const void* q;
+    const void* k;
+    const void* v;
+    const void* g;
+    const void* beta;
+    GateParams gate;
+    float* pool;
+    int num_slots;
+    const int32_t* indices;   // [num_seqs, width]
+    const int32_t* accepted;  // [num_seqs] or null
+    void* out;
+    int num_seqs;
+    int width;
+    int num_heads;
+    int head_dim;
+    bool qkv_bf16;
+    bool out_bf16;
+    float scale;
+    int l2norm;
+};
+
 struct PrefillArgs {
     const void* q;
     const void* k;
@@ -41,6 +64,11 @@ struct PrefillArgs {
     const float* initial_state;
     void* out;
     float* final_state;
+    // With slots (a state pool): sequence n's initial and final state are
+    // slot slots[n] of initial_state / final_state (both the pool); a slot
+    // outside [0, num_slots) starts from zero and is not written.
+    const int32_t* slots;
+    int num_slots;
     int64_t total_tokens;
     int num_seqs;
     int num_heads;
@@ -52,6 +80,7 @@ struct PrefillArgs {
 };
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // fp32 q/k/v, or dk = dv = 64: one workgroup per (sequence, head, 16-column
 // tile) carries the state through the chunks with everything on chip.
 hipError_t launch_prefill(const PrefillArgs& a, hipStream_t stream);

@@ -53,8 +53,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const void* __restrict__ g_in, const void* __restrict__ beta_in, GateParams gp,
     const int32_t* __restrict__ cu_seqlens, const float* initial_state, TOut* __restrict__ out,
-    float* final_state, int64_t total_tokens, int num_seqs, int num_heads, float scale,
-    int l2norm) {
+    float* final_state, const int32_t* __restrict__ slots, int num_slots, int64_t total_tokens, int num_seqs,
+    int num_heads, float scale, int l2norm) {
     using GT = typename std::conditional<GATED, TIn, float>::type;  // element type of g and beta
     const GT* __restrict__ g = static_cast<const GT*>(g_in);
     const GT* __restrict__ beta = static_cast<const GT*>(beta_in);
@@ -91,7 +91,10 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     float* sX = sKl;
     float* sT = sQl;
 
-    const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
+    size_t head_state = 0;
+    const bool has_state = state_block(slots, num_slots, n, h, num_heads, D, head_state);
+    const float* init = has_state ? initial_state : nullptr;
+    float* fin = has_state ? final_state : nullptr;
     KDA_PHASE_BEGIN
 
     floatx4 Sacc[CBW];
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 16 * cb + 4 * l4 + j;
-            const float s = initial_state ? initial_state[head_state + c * D + col0 + l16] : 0.f;
+            const float s = init ? init[head_state + c * D + col0 + l16] : 0.f;
             Sacc[b][j] = s;
             sS[c * kDVT + l16] = s;
         }
@@ -422,13 +425,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         KDA_PHASE_MARK(13);
     }
 
-    if (final_state) {
+    if (fin) {
 #pragma unroll
         for (int b = 0; b < CBW; ++b) {
             const int cb = wave * CBW + b;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                final_state[head_state + (16 * cb + 4 * l4 + j) * D + col0 + l16] = Sacc[b][j];
+                fin[head_state + (16 * cb + 4 * l4 + j) * D + col0 + l16] = Sacc[b][j];
         }
     }
     KDA_PHASE_END;
@@ -446,11 +449,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     if (a.gate.a_log)
         prefill_chunk_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
             q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
-            a.final_state, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
     else
         prefill_chunk_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
             q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
-            a.final_state, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
     return hipGetLastError();
 }
 

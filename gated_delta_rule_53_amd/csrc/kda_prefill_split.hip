@@ -691,7 +691,7 @@ template <typename TOut, int NT>
 __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
-    float* final_state, int num_seqs, int num_heads) {
+    float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs, int num_heads) {
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
     using SS = ScanShape<NT>;
     constexpr int DG_GL = SS::DG_GL, DG_SLOT = SS::DG_SLOT, XCH_SLOT = SS::XCH_SLOT;
@@ -719,7 +719,10 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     const int nc = c_end - c_begin;
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
     const int row_stride = num_heads * D;
-    const size_t head_state = (static_cast<size_t>(n) * num_heads + h) * D * D;
+    size_t head_state = 0;
+    const bool has_state = state_block(slots, num_slots, n, h, num_heads, D, head_state);
+    const float* init = has_state ? initial_state : nullptr;
+    float* fin = has_state ? final_state : nullptr;
     auto rec_of = [&](int j) { return records + (static_cast<size_t>(c_begin + j) * num_heads + h) * REC_BYTES; };
     auto tok_of = [&](int j) { return t_first + static_cast<int64_t>(C) * j; };
     auto len_of = [&](int j) { return static_cast<int>(min64(C, t_last - tok_of(j))); };
@@ -732,13 +735,13 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         floatx4 S[8];
 #pragma unroll
         for (int w = 0; w < 8; ++w) S[w] = floatx4{0.f, 0.f, 0.f, 0.f};
-        if (initial_state) {
+        if (init) {
             const int l16 = lane0 & 15, g = lane0 >> 4;
 #pragma unroll
             for (int w = 0; w < 8; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    S[w][j] = initial_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
+                    S[w][j] = init[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
         }
         // Step j from state buffer sb (chunk j mod 3) and slots of parity p.
         // D = Delta0 - Psi' S runs K block by K block (32 rows of S each): the
@@ -826,13 +829,13 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
                 lds_barrier();
             sbuf = sbuf == 2 ? 0 : sbuf + 1;
         }
-        if (final_state) {
+        if (fin) {
             const int l16 = lane0 & 15, g = lane0 >> 4;
 #pragma unroll
             for (int w = 0; w < 8; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    final_state[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
+                    fin[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
         }
     } else if (wave == NT + 2) {
         // ================= state-copy wave =================
@@ -1173,11 +1176,11 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     if (pairs)
         scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
-            static_cast<TOut*>(a.out), a.final_state, a.num_seqs, a.num_heads);
+            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads);
     else
         scan_kernel<TOut, 1><<<groups * ScanShape<1>::UNITS, ScanShape<1>::THREADS, 0, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
-            static_cast<TOut*>(a.out), a.final_state, a.num_seqs, a.num_heads);
+            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads);
     return hipGetLastError();
 }
 

@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -205,6 +205,64 @@ kda_status_t kda_recurrent_step(const kda_problem_t *problem, const void *q, con
 kda_status_t kda_recurrent_step_gated(const kda_problem_t *problem, const kda_gate_t *gate,
                                       const void *q, const void *k, const void *v, const void *raw_g,
                                       const void *raw_beta, float *state, void *out, void *stream);
+
+/*
+ * State pool.  The two calls below keep recurrent states in a pool of slots,
+ * the way the Ascend model file keeps its recurrent cache: the prefill branch
+ * scatters each request's final state into its cache block
+ * (`update_mamba_cache`), and the decode branches hand the kernels one state
+ * index per token (`ssm_state_indices`, checked against the fixed "Verify"
+ * width) and the number of accepted tokens (`num_accepted_tokens`).
+ *
+ *   state_pool   [num_slots, H, dk, dv] float32 (device), read and written.
+ *   A slot index outside [0, num_slots) names no slot: such a state reads as
+ *   zero and is not written.  Slots named by different sequences of one call
+ *   must be distinct (otherwise the result is undefined).
+ */
+
+/*
+ * kda_chunk_fwd with the states in a pool: sequence n starts from slot
+ * state_slots[n] and its final state is written back to that slot.
+ * gate NULL: g [T, H, dk] and beta [T, H] are float32 as for kda_chunk_fwd;
+ * otherwise they are the raw projections and are activated as for
+ * kda_chunk_fwd_gated.  state_slots [N] int32 (device).  Everything else is
+ * as for kda_chunk_fwd, workspace included.
+ */
+kda_status_t kda_chunk_fwd_pooled(const kda_problem_t *problem, const kda_gate_t *gate, const void *q,
+                                  const void *k, const void *v, const void *g, const void *beta,
+                                  const int32_t *cu_seqlens, float *state_pool, int32_t num_slots,
+                                  const int32_t *state_slots, void *out, void *workspace,
+                                  size_t workspace_bytes, void *stream);
+
+/*
+ * Multi-token verify decode over a state pool.  Every sequence advances by
+ * exactly `width` tokens, token by token as kda_recurrent_step does.  The
+ * pages fix only the interface (one state slot per token, the accepted-token
+ * counts); the meaning taken here:
+ *   - sequence n starts from the state in slot idx[a - 1], with
+ *     idx = state_indices + n * width and a = num_accepted[n] clamped to
+ *     [1, width] (a = 1 when num_accepted is NULL);
+ *   - after its token t it writes the state to slot idx[t].
+ * The starting state is read in full before anything is written, so idx[a-1]
+ * may also be a destination.  width = 1 with num_accepted NULL is the plain
+ * decode step with the state in slot idx[0].
+ *
+ *   problem->total_tokens must equal num_seqs * width.
+ *   q, k          [N * width, H, dk]  qkv_dtype; sequence n's tokens are rows
+ *                 n*width .. n*width + width - 1
+ *   v             [N * width, H, dv]  qkv_dtype
+ *   g, beta       gate NULL: [N * width, H, dk] and [N * width, H] float32;
+ *                 otherwise the raw projections in qkv_dtype, activated as
+ *                 described at kda_gate_t
+ *   state_indices [N, width] int32 (device)
+ *   num_accepted  [N] int32 (device), or NULL
+ *   out           [N * width, H, dv]  out_dtype (written)
+ */
+kda_status_t kda_recurrent_verify(const kda_problem_t *problem, int32_t width, const kda_gate_t *gate,
+                                  const void *q, const void *k, const void *v, const void *g,
+                                  const void *beta, float *state_pool, int32_t num_slots,
+                                  const int32_t *state_indices, const int32_t *num_accepted, void *out,
+                                  void *stream);
 
 #ifdef __cplusplus
 }

@@ -228,3 +228,47 @@ def make_gate(rows: int, num_heads: int, head_k: int, dtype: torch.dtype, *, mu:
     a_log = torch.log(torch.empty(num_heads).uniform_(1.0, 16.0, generator=gen))
     dt_bias = torch.randn(num_heads, head_k, generator=gen) * 0.5
     return GateInputs(raw_g, raw_beta, a_log, dt_bias, lower_bound)
+
+
+@dataclasses.dataclass
+class VerifyInputs:
+    """Verify decode over a state pool.
+
+    q, k: [N, W, H, dk]; v: [N, W, H, dv]; g: [N, W, H, dk] fp32; beta:
+    [N, W, H] fp32; pool: [P, H, dk, dv] fp32; indices: [N, W] int32 (one
+    slot per token, distinct over the whole call, a few replaced by -1 when
+    ``pad`` > 0); accepted: [N] int32 in [1, W].
+    """
+
+    name: str
+    q: torch.Tensor
+    k: torch.Tensor
+    v: torch.Tensor
+    g: torch.Tensor
+    beta: torch.Tensor
+    pool: torch.Tensor
+    indices: torch.Tensor
+    accepted: torch.Tensor
+    scale: float
+
+
+def make_verify(num_seqs: int, width: int, num_heads: int, head_dim: int,
+                dtype: torch.dtype = torch.bfloat16, g_mu: float = 2.0, state_std: float = 0.01,
+                extra_slots: int = 3, pad: int = 0, seed: int = 0, name: str = "verify") -> VerifyInputs:
+    """Draw a verify-decode batch; the pool has N*W + extra_slots slots, the
+    indices are a random injection of the N*W tokens into it."""
+    gen = torch.Generator().manual_seed(seed)
+    shp = (num_seqs, width, num_heads, head_dim)
+    q, k, v = _qkv(gen, shp, shp, dtype)
+    x_g = torch.randn(shp, generator=gen, dtype=torch.float32)
+    x_b = torch.randn((num_seqs, width, num_heads), generator=gen, dtype=torch.float32)
+    g = F.logsigmoid(x_g + g_mu)
+    beta = torch.sigmoid(x_b)
+    P = num_seqs * width + extra_slots
+    pool = torch.randn((P, num_heads, head_dim, head_dim), generator=gen, dtype=torch.float32) * state_std
+    indices = torch.randperm(P, generator=gen)[: num_seqs * width].to(torch.int32).view(num_seqs, width)
+    if pad > 0:
+        flat = indices.view(-1)
+        flat[torch.randperm(flat.numel(), generator=gen)[:pad]] = -1
+    accepted = torch.randint(1, width + 1, (num_seqs,), generator=gen, dtype=torch.int32)
+    return VerifyInputs(name, q, k, v, g, beta, pool, indices, accepted, 1.0 / math.sqrt(head_dim))

@@ -33,7 +33,8 @@ def test_header_declares_the_boundary():
     assert declared_functions() == sorted([
         "kda_abi_version", "kda_status_string", "kda_last_error",
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
-        "kda_chunk_fwd_gated", "kda_recurrent_step_gated"])
+        "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
+        "kda_recurrent_verify"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -231,6 +232,59 @@ def test_gated_entry_points_check_problem_and_pointers():
         assert st == 1, name
     st, msg = _step_gated(_prob(total_tokens=3, num_seqs=2), _gate())
     assert st == 2 and "one token each" in msg
+
+
+def _verify(prob, width, gate=None, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, pool=FAKE, num_slots=4, idx=FAKE, acc=None, out=FAKE)
+    p.update(ptrs)
+    st = lib.kda_recurrent_verify(ctypes.byref(prob), width, None if gate is None else ctypes.byref(gate),
+                                  p["q"], p["k"], p["v"], p["g"], p["beta"], p["pool"], p["num_slots"],
+                                  p["idx"], p["acc"], p["out"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def _pooled(prob, gate=None, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, pool=FAKE, num_slots=4, slots=FAKE, out=FAKE,
+             ws=None, ws_bytes=0)
+    p.update(ptrs)
+    st = lib.kda_chunk_fwd_pooled(ctypes.byref(prob), None if gate is None else ctypes.byref(gate), p["q"],
+                                  p["k"], p["v"], p["g"], p["beta"], p["cu"], p["pool"], p["num_slots"],
+                                  p["slots"], p["out"], p["ws"], p["ws_bytes"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def test_verify_checks_its_arguments():
+    vp = lambda **kw: _prob(**{**dict(total_tokens=12, num_seqs=3), **kw})
+    assert _verify(vp(), 0)[0] == 2 and "width" in _verify(vp(), 0)[1]
+    st, msg = _verify(vp(), 3)
+    assert st == 2 and "num_seqs * width" in msg, (st, msg)
+    st, msg = _verify(vp(), 4, num_slots=-1)
+    assert st == 2 and "num_slots" in msg
+    for name in ("q", "k", "v", "g", "beta", "pool", "idx", "out"):
+        st, _ = _verify(vp(), 4, **{name: None})
+        assert st == 1, name
+    st, msg = _verify(vp(), 4, gate=_gate(has_lower_bound=3))
+    assert st == 2 and "has_lower_bound" in msg
+    st, msg = _verify(vp(head_k=96, head_v=96), 4)
+    assert st == 3 and "head size 96" in msg
+    assert _verify(vp(total_tokens=0, num_seqs=0), 5, q=None, pool=None)[0] == 0
+
+
+def test_pooled_prefill_checks_its_arguments():
+    st, msg = _pooled(_prob(), num_slots=-2)
+    assert st == 2 and "num_slots" in msg
+    for name in ("pool", "slots"):
+        st, msg = _pooled(_prob(), **{name: None})
+        assert st == 1 and "state_pool" in msg, (name, msg)
+    for name in ("q", "k", "v", "g", "beta", "out"):
+        st, _ = _pooled(_prob(), **{name: None})
+        assert st == 1, name
+    st, msg = _pooled(_prob(), gate=_gate(a_log=None))
+    assert st == 1 and "a_log" in msg
+    st, msg = _pooled(_prob(), ws=FAKE, ws_bytes=8)
+    assert st == 4 and "workspace" in msg
 
 
 def test_python_binding_rejects_cpu_tensors():
