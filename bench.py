@@ -178,6 +178,36 @@ def bench_decode(loops: int):
     return dict(x=x, wall=wall, per_launch=per, launches=n, alg_bytes=alg_bytes, num_seqs=N)
 
 
+VERIFY_WIDTH = 4
+
+
+def bench_verify(steps: int, warmup: int):
+    """Verify decode over a state pool: 256 sequences x 4 tokens, H=32, d=128, bf16."""
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+    import kda_workloads as w
+
+    x = w.make_verify(256, VERIFY_WIDTH, 32, 128, torch.bfloat16, g_mu=2.0, extra_slots=0, seed=7,
+                      name="verify_N256_W4_H32_d128")
+    dev = "cuda:0"
+    q, k, v, g, b, idx, acc = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta, x.indices, x.accepted))
+    pool = x.pool.to(dev)
+    out = torch.empty_like(v)
+    stream = torch.cuda.current_stream()
+
+    def one(i):
+        kda.recurrent_verify(q, k, v, g, b, pool, idx, acc, scale=x.scale, out=out)
+
+    for i in range(warmup):
+        one(i)
+    wall, per = time_launches(one, steps, stream)
+    N, W, H = x.q.shape[:3]
+    # per (sequence, head): the starting state read, one state written per token, the token I/O
+    alg_bytes = N * H * ((1 + W) * STATE_BYTES + W * PREFILL_BYTES_PER_TOKEN_HEAD)
+    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=N * W)
+
+
 def cpu_baseline(min_seconds: float = 8.0):
     """The fp64 oracle on the host cores, over whole passes of the same prefill workload."""
     import kda_workloads as w
@@ -237,6 +267,9 @@ def main():
     print(f"prefill: {pf['per_launch'] * 1e6:.1f} us per launch (events), "
           f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
     dc = bench_decode(args.decode_loops)
+    vf = bench_verify(args.steps, args.warmup)
+    print(f"verify decode: {vf['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     gp = bench_prefill_gated(args.steps, args.warmup)
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
@@ -292,6 +325,12 @@ def main():
                                        "traffic": None if g_tr is None else round(g_tr / gp["per_launch"] / 1e9, 2),
                                        "alg_bytes_per_launch": gp["alg_bytes"],
                                        "launch_us": round(gp["per_launch"] * 1e6, 2)}},
+        "verify_decode": {"workload": vf["x"].name, "tokens_per_s": round(vf["tokens"] * args.steps / vf["wall"], 1),
+                          "roofline": {"kernel": "verify_kernel", "bound": "hbm",
+                                       "achieved": round(v_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(v_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                       "alg_bytes_per_launch": vf["alg_bytes"],
+                                       "launch_us": round(vf["per_launch"] * 1e6, 2)}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
