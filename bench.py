@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
 KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
@@ -270,6 +271,7 @@ def main():
     vf = bench_verify(args.steps, args.warmup)
     print(f"verify decode: {vf['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
+    v_tr = measured_traffic("verify_decode")
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     gp = bench_prefill_gated(args.steps, args.warmup)
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
@@ -328,7 +330,8 @@ def main():
         "verify_decode": {"workload": vf["x"].name, "tokens_per_s": round(vf["tokens"] * args.steps / vf["wall"], 1),
                           "roofline": {"kernel": "verify_kernel", "bound": "hbm",
                                        "achieved": round(v_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                       "frac": round(v_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                       "frac": round(v_achieved / HBM_PEAK_GBS, 4),
+                                       "traffic": None if v_tr is None else round(v_tr / vf["per_launch"] / 1e9, 2),
                                        "alg_bytes_per_launch": vf["alg_bytes"],
                                        "launch_us": round(vf["per_launch"] * 1e6, 2)}},
     }
