@@ -44,6 +44,7 @@ class Problem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("qk_l2norm", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32),
+        ("gate_per_head", ctypes.c_int32),
     ]
 
 
@@ -140,11 +141,17 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _problem(T, N, H, dk, dv, qkv_dtype, out_dtype, scale, qk_l2norm) -> Problem:
+def _problem(T, N, H, dk, dv, qkv_dtype, out_dtype, scale, qk_l2norm, gate_per_head=False) -> Problem:
     return Problem(total_tokens=T, num_seqs=N, num_heads=H, head_k=dk, head_v=dv,
                    qkv_dtype=_dtype_code(qkv_dtype), out_dtype=_dtype_code(out_dtype),
                    scale=float(1.0 / math.sqrt(dk) if scale is None else scale),
-                   qk_l2norm=int(bool(qk_l2norm)), chunk_size=64)
+                   qk_l2norm=int(bool(qk_l2norm)), chunk_size=64, gate_per_head=int(bool(gate_per_head)))
+
+
+def _gate_shape(g: torch.Tensor, lead: tuple, dk: int):
+    """(per_head, expected shape) of a gate tensor: lead + (dk,), or lead alone (one decay per head)."""
+    per_head = g.dim() == len(lead)
+    return per_head, lead if per_head else lead + (dk,)
 
 
 def chunk_fwd_workspace_bytes(problem: Problem) -> int:
@@ -180,7 +187,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     _need(q, "q", (T, H, dk), None, dev)
     _need(k, "k", (T, H, dk), q.dtype, dev)
     _need(v, "v", (T, H, dv), q.dtype, dev)
-    _need(g, "g", (T, H, dk), torch.float32, dev)
+    gph, gshape = _gate_shape(g, (T, H), dk)
+    _need(g, "g", gshape, torch.float32, dev)
     _need(beta, "beta", (T, H), torch.float32, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     if initial_state is not None:
@@ -193,7 +201,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -222,23 +230,24 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
         raise KdaArgumentError(2, "tensors must be on a GPU device")
     _need(k, "k", (N, H, dk), q.dtype, dev)
     _need(v, "v", (N, H, dv), q.dtype, dev)
-    _need(g, "g", (N, H, dk), torch.float32, dev)
+    gph, gshape = _gate_shape(g, (N, H), dk)
+    _need(g, "g", gshape, torch.float32, dev)
     _need(beta, "beta", (N, H), torch.float32, dev)
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
     out_dtype = v.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, H, dv), out_dtype, dev)
-    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     _check(_lib.kda_recurrent_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state), _ptr(out), _stream(dev)))
     return out
 
 
 def _gate(a_log: torch.Tensor, dt_bias: torch.Tensor, H: int, dk: int, lower_bound: Optional[float],
-          dev) -> Gate:
+          dev, per_head: bool = False) -> Gate:
     _need(a_log, "a_log", (H,), torch.float32, dev)
-    _need(dt_bias, "dt_bias", (H, dk), torch.float32, dev)
+    _need(dt_bias, "dt_bias", (H,) if per_head else (H, dk), torch.float32, dev)
     return Gate(a_log=a_log.data_ptr(), dt_bias=dt_bias.data_ptr(),
                 has_lower_bound=int(lower_bound is not None),
                 lower_bound=float(0.0 if lower_bound is None else lower_bound))
@@ -271,10 +280,11 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: to
     _need(q, "q", (T, H, dk), None, dev)
     _need(k, "k", (T, H, dk), q.dtype, dev)
     _need(v, "v", (T, H, dv), q.dtype, dev)
-    _need(raw_g, "raw_g", (T, H, dk), q.dtype, dev)
+    gph, gshape = _gate_shape(raw_g, (T, H), dk)
+    _need(raw_g, "raw_g", gshape, q.dtype, dev)
     _need(raw_beta, "raw_beta", (T, H), q.dtype, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
-    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev, gph)
     if initial_state is not None:
         _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
     out_dtype = v.dtype if out_dtype is None else out_dtype
@@ -285,7 +295,7 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: to
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -316,28 +326,29 @@ def recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_
         raise KdaArgumentError(2, "tensors must be on a GPU device")
     _need(k, "k", (N, H, dk), q.dtype, dev)
     _need(v, "v", (N, H, dv), q.dtype, dev)
-    _need(raw_g, "raw_g", (N, H, dk), q.dtype, dev)
+    gph, gshape = _gate_shape(raw_g, (N, H), dk)
+    _need(raw_g, "raw_g", gshape, q.dtype, dev)
     _need(raw_beta, "raw_beta", (N, H), q.dtype, dev)
     _need(state, "state", (N, H, dk, dv), torch.float32, dev)
-    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+    gate = _gate(a_log, dt_bias, H, dk, lower_bound, dev, gph)
     out_dtype = v.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, H, dv), out_dtype, dev)
-    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     _check(_lib.kda_recurrent_step_gated(ctypes.byref(prob), ctypes.byref(gate), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(raw_g), _ptr(raw_beta), _ptr(state), _ptr(out), _stream(dev)))
     return out
 
 
-def _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev):
+def _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev, per_head=False):
     if a_log is None:
         if dt_bias is not None or lower_bound is not None:
             raise KdaArgumentError(1, "dt_bias and lower_bound need a_log")
         return None
     if dt_bias is None:
         raise KdaArgumentError(1, "a_log needs dt_bias")
-    return _gate(a_log, dt_bias, H, dk, lower_bound, dev)
+    return _gate(a_log, dt_bias, H, dk, lower_bound, dev, per_head)
 
 
 def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
@@ -366,12 +377,13 @@ def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if cu_seqlens is None:
         cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
     N = cu_seqlens.numel() - 1
-    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev)
+    gph, gshape = _gate_shape(g, (T, H), dk)
+    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev, gph)
     gdt = torch.float32 if gate is None else q.dtype
     _need(q, "q", (T, H, dk), None, dev)
     _need(k, "k", (T, H, dk), q.dtype, dev)
     _need(v, "v", (T, H, dv), q.dtype, dev)
-    _need(g, "g", (T, H, dk), gdt, dev)
+    _need(g, "g", gshape, gdt, dev)
     _need(beta, "beta", (T, H), gdt, dev)
     _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
     if state_pool.dim() != 4:
@@ -383,7 +395,7 @@ def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if out is None:
         out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (T, H, dv), out_dtype, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -416,11 +428,12 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     dev = q.device
     if dev.type != "cuda":
         raise KdaArgumentError(2, "tensors must be on a GPU device")
-    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev)
+    gph, gshape = _gate_shape(g, (N, W, H), dk)
+    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev, gph)
     gdt = torch.float32 if gate is None else q.dtype
     _need(k, "k", (N, W, H, dk), q.dtype, dev)
     _need(v, "v", (N, W, H, dv), q.dtype, dev)
-    _need(g, "g", (N, W, H, dk), gdt, dev)
+    _need(g, "g", gshape, gdt, dev)
     _need(beta, "beta", (N, W, H), gdt, dev)
     if state_pool.dim() != 4:
         raise KdaArgumentError(2, f"state_pool must be [P, H, dk, dv], got {tuple(state_pool.shape)}")
@@ -433,7 +446,7 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if out is None:
         out = torch.empty((N, W, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, W, H, dv), out_dtype, dev)
-    prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm)
+    prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
     _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, None if gate is None else ctypes.byref(gate), _ptr(q),
                                      _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
                                      _ptr(state_indices), _ptr(num_accepted), _ptr(out), _stream(dev)))

@@ -58,6 +58,8 @@ kda_status_t check_problem(const kda_problem_t* p, const char* what) {
         return fail(KDA_ERR_UNSUPPORTED, "%s: out_dtype %d", what, p->out_dtype);
     if (p->qk_l2norm != 0 && p->qk_l2norm != 1)
         return fail(KDA_ERR_BAD_SHAPE, "%s: qk_l2norm must be 0 or 1", what);
+    if (p->gate_per_head != 0 && p->gate_per_head != 1)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: gate_per_head must be 0 or 1", what);
     // Row counts that index int32 offsets inside kernels stay well within range.
     if (p->total_tokens > (int64_t(1) << 40) || int64_t(p->num_seqs) * p->num_heads > (int64_t(1) << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
@@ -110,6 +112,7 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
     a.g = g;
     a.beta = beta;
     a.gate = gp;
+    a.gate_per_head = p->gate_per_head;
     a.cu_seqlens = cu_seqlens;
     a.initial_state = initial_state;
     a.out = out;
@@ -148,6 +151,7 @@ kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const
     a.g = g;
     a.beta = beta;
     a.gate = gp;
+    a.gate_per_head = p->gate_per_head;
     a.state = state;
     a.out = out;
     a.num_seqs = p->num_seqs;
@@ -290,6 +294,7 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     a.g = g;
     a.beta = beta;
     a.gate = gp;
+    a.gate_per_head = p->gate_per_head;
     a.pool = state_pool;
     a.num_slots = num_slots;
     a.indices = state_indices;

@@ -28,7 +28,7 @@ namespace kda {
 template <int D, typename TIn, typename TOut, bool GATED>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, float* __restrict__ state,
+    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ state,
     TOut* __restrict__ out, int num_heads, float scale, int l2norm) {
     constexpr int NCG = D / 4;      // column groups of four
     constexpr int NRG = 256 / NCG;  // row groups
@@ -54,13 +54,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         const size_t off = static_cast<size_t>(pair) * D + tid;
         sq[tid] = to_f32(q[off]);
         sk[tid] = to_f32(k[off]);
+        // one decay per head: every channel reads the head's value
+        const size_t goff = gph ? static_cast<size_t>(pair) : off;
         float gv;
         if constexpr (GATED) {
             const int h = pair % num_heads;
-            gv = gate_g(to_f32(static_cast<const TIn*>(g)[off]), gp.dt_bias[h * D + tid], gate_exp(gp.a_log[h]),
-                        gp.lower_bound, gp.has_lower_bound);
+            gv = gate_g(to_f32(static_cast<const TIn*>(g)[goff]), gp.dt_bias[gph ? h : h * D + tid],
+                        gate_exp(gp.a_log[h]), gp.lower_bound, gp.has_lower_bound);
         } else {
-            gv = static_cast<const float*>(g)[off];
+            gv = static_cast<const float*>(g)[goff];
         }
         se[tid] = fast_exp2(gv * kLog2e);
     }
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 template <int D, typename TIn, typename TOut, bool GATED>
 __global__ __launch_bounds__(256) void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, float* __restrict__ pool,
+    const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ pool,
     int num_slots, const int32_t* __restrict__ indices, const int32_t* __restrict__ accepted,
     TOut* __restrict__ out, int num_heads, int width, float scale, int l2norm) {
     constexpr int NCG = D / 4;
@@ -188,12 +190,13 @@ __global__ __launch_bounds__(256) void verify_kernel(
             const size_t off = tok * D + tid;
             sq[tid] = to_f32(q[off]);
             sk[tid] = to_f32(k[off]);
+            const size_t goff = gph ? tok : off;
             float gv;
             if constexpr (GATED)
-                gv = gate_g(to_f32(static_cast<const TIn*>(g)[off]), gp.dt_bias[h * D + tid], gate_exp(gp.a_log[h]),
-                            gp.lower_bound, gp.has_lower_bound);
+                gv = gate_g(to_f32(static_cast<const TIn*>(g)[goff]), gp.dt_bias[gph ? h : h * D + tid],
+                            gate_exp(gp.a_log[h]), gp.lower_bound, gp.has_lower_bound);
             else
-                gv = static_cast<const float*>(g)[off];
+                gv = static_cast<const float*>(g)[goff];
             se[tid] = fast_exp2(gv * kLog2e);
         }
         __syncthreads();
@@ -271,11 +274,11 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     const TIn* v = static_cast<const TIn*>(a.v);
     if (a.gate.a_log)
         verify_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
             a.num_heads, a.width, a.scale, a.l2norm);
     else
         verify_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
             a.num_heads, a.width, a.scale, a.l2norm);
     return hipGetLastError();
 }
@@ -299,10 +302,12 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const TIn* v = static_cast<const TIn*>(a.v);
     if (a.gate.a_log)
         decode_step_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.state, static_cast<TOut*>(a.out), a.num_heads, a.scale, a.l2norm);
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out), a.num_heads,
+            a.scale, a.l2norm);
     else
         decode_step_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.state, static_cast<TOut*>(a.out), a.num_heads, a.scale, a.l2norm);
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out), a.num_heads,
+            a.scale, a.l2norm);
     return hipGetLastError();
 }
 

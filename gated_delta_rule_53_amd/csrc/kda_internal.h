@@ -19,6 +19,7 @@ struct DecodeArgs {
     const void* g;
     const void* beta;
     GateParams gate;
+    int gate_per_head;  // g (or the raw gate) is [rows, H]: one decay per head
     float* state;
     void* out;
     int num_seqs;
@@ -38,6 +39,7 @@ struct VerifyArgs {
     const void* g;
     const void* beta;
     GateParams gate;
+    int gate_per_head;
     float* pool;
     int num_slots;
     const int32_t* indices;   // [num_seqs, width]
@@ -60,6 +62,7 @@ struct PrefillArgs {
     const void* g;
     const void* beta;
     GateParams gate;
+    int gate_per_head;
     const int32_t* cu_seqlens;
     const float* initial_state;
     void* out;

@@ -51,7 +51,7 @@ __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2
 template <int D, typename TIn, typename TOut, bool GATED>
 __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
-    const void* __restrict__ g_in, const void* __restrict__ beta_in, GateParams gp,
+    const void* __restrict__ g_in, const void* __restrict__ beta_in, GateParams gp, int gph,
     const int32_t* __restrict__ cu_seqlens, const float* initial_state, TOut* __restrict__ out,
     float* final_state, const int32_t* __restrict__ slots, int num_slots, int64_t total_tokens, int num_seqs,
     int num_heads, float scale, int l2norm) {
@@ -124,7 +124,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     if constexpr (GATED) {
         ga = gate_exp(gp.a_log[h]);
 #pragma unroll
-        for (int i = 0; i < CPT; ++i) gbias[i] = gp.dt_bias[h * D + CPT * pc + i];
+        for (int i = 0; i < CPT; ++i) gbias[i] = gp.dt_bias[gph ? h : h * D + CPT * pc + i];
     }
     int valid_rows = 0;  // rows of the prefetched chunk inside the sequence
     alignas(16) TIn pv[8];
@@ -138,7 +138,13 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 const size_t off = (static_cast<size_t>(c0 + r) * num_heads + h) * D + CPT * pc;
                 load_vec(pk[j], k + off);
                 load_vec(pqv[j], q + off);
-                load_vec(pg[j], g + off);
+                if (gph) {  // one decay per head, the same for every channel
+                    const GT gs = g[static_cast<size_t>(c0 + r) * num_heads + h];
+#pragma unroll
+                    for (int i = 0; i < CPT; ++i) pg[j][i] = gs;
+                } else {
+                    load_vec(pg[j], g + off);
+                }
             } else {
 #pragma unroll
                 for (int i = 0; i < CPT; ++i) {
@@ -448,11 +454,11 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     const TIn* v = static_cast<const TIn*>(a.v);
     if (a.gate.a_log)
         prefill_chunk_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
             a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
     else
         prefill_chunk_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
+            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
             a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
     return hipGetLastError();
 }

@@ -212,7 +212,7 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 template <bool GATED>
 __global__ __launch_bounds__(PNT) void prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const void* __restrict__ g_in,
-    const void* __restrict__ beta_in, GateParams gp, const int32_t* __restrict__ cu_seqlens,
+    const void* __restrict__ beta_in, GateParams gp, int gph, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
     float scale, int l2norm) {
     const float* __restrict__ g = static_cast<const float*>(g_in);
@@ -251,11 +251,24 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         if (r < L) {
             pk = *reinterpret_cast<const uint4*>(k + base + off);
             pq = *reinterpret_cast<const uint4*>(q + base + off);
+            // one decay per head: the row's value for all eight channels
+            const size_t hoff = static_cast<size_t>(start + r) * num_heads + h;
             if constexpr (GATED) {
-                pgr = *reinterpret_cast<const uint4*>(graw + base + off);
+                if (gph) {
+                    const uint32_t w = graw[hoff].bits * 0x10001u;
+                    pgr = uint4{w, w, w, w};
+                } else {
+                    pgr = *reinterpret_cast<const uint4*>(graw + base + off);
+                }
             } else {
-                pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
-                pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
+                if (gph) {
+                    const float gs = g[hoff];
+                    pg0 = floatx4{gs, gs, gs, gs};
+                    pg1 = pg0;
+                } else {
+                    pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
+                    pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
+                }
             }
         } else {
             pk = uint4{0, 0, 0, 0};
@@ -295,8 +308,15 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         // the totals of the 16 waves through LDS
         floatx8 gr;
         if constexpr (GATED) {
-            const floatx4 b0 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc);
-            const floatx4 b1 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc + 4);
+            floatx4 b0, b1;
+            if (gph) {
+                const float bs = gp.dt_bias[h];
+                b0 = floatx4{bs, bs, bs, bs};
+                b1 = b0;
+            } else {
+                b0 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc);
+                b1 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc + 4);
+            }
             const float a = gate_exp(gp.a_log[h]);
             const floatx8 x = unpack8(pgr);
             const float bias[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
@@ -1160,10 +1180,10 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
         const bf16_t* q = static_cast<const bf16_t*>(a.q);
         const bf16_t* k = static_cast<const bf16_t*>(a.k);
         if (a.gate.a_log)
-            prep_kernel<true><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets,
+            prep_kernel<true><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, offsets,
                                                              records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
         else
-            prep_kernel<false><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets,
+            prep_kernel<false><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, offsets,
                                                               records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
         e = hipGetLastError();
         if (e != hipSuccess) return e;

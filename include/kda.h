@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -83,6 +83,10 @@ typedef struct kda_problem {
     float scale;          /* multiplies q after its L2 norm; 1/sqrt(dk) by convention     */
     int32_t qk_l2norm;    /* 1: L2-normalise q and k inside the kernel; 0: use as given   */
     int32_t chunk_size;   /* prefill chunk length; 64 only (0 selects 64)                 */
+    int32_t gate_per_head; /* 0: g (or the raw gate) has one value per key channel,
+                              [rows, H, dk]; 1: one value per head, [rows, H], the same
+                              decay for every channel (the Gated DeltaNet case); the gated
+                              calls then take dt_bias as [H]                               */
 } kda_problem_t;
 
 /*
@@ -103,7 +107,7 @@ typedef struct kda_problem {
  */
 typedef struct kda_gate {
     const float *a_log;      /* [H] float32 (device): the gate scale is exp(a_log[h])   */
-    const float *dt_bias;    /* [H, dk] float32 (device)                                */
+    const float *dt_bias;    /* [H, dk] float32 (device); [H] with gate_per_head        */
     int32_t has_lower_bound; /* 0: softplus gate; 1: bounded sigmoid gate               */
     float lower_bound;       /* used when has_lower_bound == 1: finite and <= 0        */
 } kda_gate_t;
@@ -146,7 +150,8 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
  *
  *   q, k           [T, H, dk]  qkv_dtype
  *   v              [T, H, dv]  qkv_dtype
- *   g              [T, H, dk]  float32, log-decay per key channel (<= 0)
+ *   g              [T, H, dk]  float32, log-decay per key channel (<= 0); [T, H] with
+ *                  problem->gate_per_head
  *   beta           [T, H]      float32, in [0, 1]
  *   cu_seqlens     [N + 1]     int32 (device): 0 = cu[0] <= cu[1] <= ... <= cu[N] = T.
  *                  Sequence n is rows cu[n] .. cu[n+1]-1.  Zero-length sequences are
@@ -188,7 +193,7 @@ kda_status_t kda_chunk_fwd_gated(const kda_problem_t *problem, const kda_gate_t 
  *
  *   q, k    [N, H, dk]  qkv_dtype     (problem->total_tokens must equal N)
  *   v       [N, H, dv]  qkv_dtype
- *   g       [N, H, dk]  float32
+ *   g       [N, H, dk]  float32 ([N, H] with problem->gate_per_head)
  *   beta    [N, H]      float32
  *   state   [N, H, dk, dv] float32, read and overwritten
  *   out     [N, H, dv]  out_dtype (written)

@@ -220,14 +220,23 @@ class GateInputs:
 
 
 def make_gate(rows: int, num_heads: int, head_k: int, dtype: torch.dtype, *, mu: float = -5.0,
-              lower_bound: Optional[float] = None, seed: int = 0, lead: tuple = ()) -> GateInputs:
-    """Draw raw gate inputs of ``lead + (rows, num_heads, head_k)``."""
+              lower_bound: Optional[float] = None, seed: int = 0, lead: tuple = (),
+              per_head: bool = False) -> GateInputs:
+    """Draw raw gate inputs of ``lead + (rows, num_heads, head_k)`` (``lead + (rows,
+    num_heads)`` and dt_bias [H] with ``per_head``: one decay per head)."""
     gen = torch.Generator().manual_seed(seed)
-    raw_g = (torch.randn(*lead, rows, num_heads, head_k, generator=gen) * 0.5 + mu).to(dtype)
+    ch = () if per_head else (head_k,)
+    raw_g = (torch.randn(*lead, rows, num_heads, *ch, generator=gen) * 0.5 + mu).to(dtype)
     raw_beta = torch.randn(*lead, rows, num_heads, generator=gen).to(dtype)
     a_log = torch.log(torch.empty(num_heads).uniform_(1.0, 16.0, generator=gen))
-    dt_bias = torch.randn(num_heads, head_k, generator=gen) * 0.5
+    dt_bias = torch.randn(num_heads, *ch, generator=gen) * 0.5
     return GateInputs(raw_g, raw_beta, a_log, dt_bias, lower_bound)
+
+
+def per_head_decay(shape: tuple, g_mu: float = 2.0, seed: int = 0) -> torch.Tensor:
+    """One log-decay per (token, head): logsigmoid(N(g_mu, 1)) of the given shape, fp32."""
+    gen = torch.Generator().manual_seed(seed)
+    return F.logsigmoid(torch.randn(shape, generator=gen, dtype=torch.float32) + g_mu)
 
 
 @dataclasses.dataclass

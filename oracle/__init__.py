@@ -91,13 +91,17 @@ def forward(q, k, v, g, beta, cu_seqlens, initial_state=None, scale: Optional[fl
             lib=None) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Packed-varlen KDA forward, fp64, token by token.
 
-    q, k: [T, H, dk]; v: [T, H, dv]; g: [T, H, dk]; beta: [T, H];
-    cu_seqlens: [N+1]; initial_state: [N, H, dk, dv] or None.
+    q, k: [T, H, dk]; v: [T, H, dv]; g: [T, H, dk], or [T, H] for one decay
+    per head; beta: [T, H]; cu_seqlens: [N+1]; initial_state: [N, H, dk, dv] or None.
     Returns (out [T, H, dv] float64, final_state [N, H, dk, dv] float64 or None).
     ``lib`` selects another compiled copy of the oracle (the default is the
     one built from ``kda_oracle.c``).
     """
     qf, kf, vf, gf, bf = (_f32(t) for t in (q, k, v, g, beta))
+    if gf.ndim == 2:
+        # one log-decay per (token, head), the same for every key channel: the
+        # scalar gate of Gated DeltaNet, a special case of the per-channel decay
+        gf = np.ascontiguousarray(np.broadcast_to(gf[:, :, None], qf.shape))
     cu = np.ascontiguousarray(np.asarray(
         cu_seqlens.cpu().numpy() if hasattr(cu_seqlens, "cpu") else cu_seqlens, dtype=np.int64))
     T, H, dk = qf.shape

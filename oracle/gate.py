@@ -35,9 +35,14 @@ def sigmoid(z: np.ndarray) -> np.ndarray:
 
 
 def activate(raw_g, raw_beta, a_log, dt_bias, lower_bound: Optional[float] = None) -> Tuple[np.ndarray, np.ndarray]:
-    """(g, beta) from raw_g [..., H, dk], raw_beta [..., H], a_log [H], dt_bias [H, dk]."""
+    """(g, beta) from raw_g [..., H, dk], raw_beta [..., H], a_log [H], dt_bias [H, dk].
+
+    One decay per head (the Gated DeltaNet case): raw_g [..., H] with dt_bias [H].
+    """
     x = _f64(raw_g)
-    scale = np.exp(_f64(a_log))[:, None]   # [H, 1]: one gate scale per head
+    per_head = np.ndim(_f64(dt_bias)) == 1
+    # one gate scale per head: [H] against per-head inputs, [H, 1] against channels
+    scale = np.exp(_f64(a_log)) if per_head else np.exp(_f64(a_log))[:, None]
     u = x + _f64(dt_bias)                  # broadcast over the leading token axes
     if lower_bound is None:
         g = -scale * softplus(u)

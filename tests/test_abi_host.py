@@ -54,10 +54,10 @@ def test_gate_struct_layout():
 
 
 def test_problem_struct_layout_matches_header():
-    # int64 first, then nine 4-byte fields: 8 + 36 = 44, padded to 48.
+    # int64 first, then ten 4-byte fields: 8 + 40 = 48.
     assert ctypes.sizeof(Problem) == 48
     assert Problem.total_tokens.offset == 0 and Problem.num_seqs.offset == 8
-    assert Problem.chunk_size.offset == 40
+    assert Problem.chunk_size.offset == 40 and Problem.gate_per_head.offset == 44
 
 
 def test_status_strings():
@@ -108,6 +108,7 @@ def _step(prob, **ptrs):
     (dict(out_dtype=2), 3, "out_dtype"),
     (dict(qk_l2norm=3), 2, "qk_l2norm"),
     (dict(chunk_size=32), 3, "chunk_size"),
+    (dict(gate_per_head=2), 2, "gate_per_head"),
 ])
 def test_chunk_fwd_rejects_bad_problem(kw, status, needle):
     st, msg = _chunk(_prob(**kw))

@@ -94,3 +94,39 @@ def test_bf16_raw_inputs_are_taken_exactly():
     exact = raw.double().numpy()
     np.testing.assert_allclose(g, -np.logaddexp(0.0, exact), rtol=1e-15)
     np.testing.assert_allclose(b, sp.expit(beta.double().numpy()), rtol=1e-15)
+
+
+def test_per_head_activation_uses_one_scale_and_bias_per_head():
+    # One decay per head (the Gated DeltaNet case): raw_g [rows, H], dt_bias [H].
+    gen = np.random.default_rng(5)
+    H, rows = 4, 9
+    raw_g = gen.standard_normal((rows, H))
+    raw_b = gen.standard_normal((rows, H))
+    a_log = np.log(gen.uniform(1.0, 16.0, H))
+    dt_bias = gen.standard_normal(H)
+    g, b = G.activate(raw_g, raw_b, a_log, dt_bias)
+    want = -np.exp(a_log)[None, :] * np.logaddexp(0.0, raw_g + dt_bias[None, :])
+    np.testing.assert_allclose(g, want, rtol=1e-14)
+    np.testing.assert_allclose(b, sp.expit(raw_b), rtol=1e-14)
+    g2, _ = G.activate(raw_g, raw_b, a_log, dt_bias, lower_bound=-3.0)
+    np.testing.assert_allclose(g2, -3.0 * sp.expit(np.exp(a_log)[None, :] * (raw_g + dt_bias[None, :])), rtol=1e-14)
+
+
+def test_per_head_decay_without_updates_is_a_scalar_decay():
+    # beta = 0: the state only decays, by e^{G_t} with G_t the running sum of
+    # the head's scalar log-decay, so o_t = e^{G_t} S0^T q_hat_t.
+    import oracle
+    gen = np.random.default_rng(8)
+    T, H, d = 6, 2, 8
+    q = gen.standard_normal((T, H, d)).astype(np.float32)
+    k = gen.standard_normal((T, H, d)).astype(np.float32)
+    v = gen.standard_normal((T, H, d)).astype(np.float32)
+    g = -gen.uniform(0.0, 0.5, (T, H)).astype(np.float32)
+    s0 = gen.standard_normal((1, H, d, d)).astype(np.float32)
+    out, fs = oracle.forward(q, k, v, g, np.zeros((T, H), np.float32), [0, T], s0, scale=0.3)
+    G_t = np.cumsum(g.astype(np.float64), axis=0)                      # [T, H]
+    q64 = q.astype(np.float64)
+    qh = 0.3 * q64 / np.sqrt(np.sum(q64 ** 2, -1, keepdims=True) + 1e-6)
+    want = np.exp(G_t)[:, :, None] * np.einsum("hcd,thc->thd", s0[0].astype(np.float64), qh)
+    np.testing.assert_allclose(out, want, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fs[0], np.exp(G_t[-1])[:, None, None] * s0[0], rtol=1e-12, atol=1e-14)
