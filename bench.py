@@ -84,24 +84,29 @@ def time_launches(fn, n: int, stream):
     return wall, per
 
 
-def bench_prefill(steps: int, warmup: int):
+PER_HEAD_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 4 + 4 + 128 * 2   # g is one fp32 per (token, head)
+
+
+def bench_prefill(steps: int, warmup: int, per_head: bool = False):
+    """kda_chunk_fwd on the T=4096, H=32, d=128 workload; per_head: g [T, H] (one decay per head)."""
     import torch
 
     import gated_delta_rule_53_amd as kda
     import kda_workloads as w
 
     x = w.prefill_4k()
+    g_in = w.per_head_decay((x.total_tokens, x.num_heads), 3.0, seed=1) if per_head else x.g
     dev = "cuda:0"
     copies = []
     for _ in range(3):
-        copies.append(dict(q=x.q.to(dev), k=x.k.to(dev), v=x.v.to(dev), g=x.g.to(dev),
+        copies.append(dict(q=x.q.to(dev), k=x.k.to(dev), v=x.v.to(dev), g=g_in.to(dev),
                            beta=x.beta.to(dev), cu=x.cu_seqlens.to(dev),
                            s0=x.initial_state.to(dev),
                            out=torch.empty_like(x.v, device=dev),
                            fs=torch.empty_like(x.initial_state, device=dev)))
     prob = kda.Problem(total_tokens=x.total_tokens, num_seqs=x.num_seqs, num_heads=x.num_heads,
                        head_k=x.head_k, head_v=x.head_v, qkv_dtype=1, out_dtype=1,
-                       scale=x.scale, qk_l2norm=1, chunk_size=64)
+                       scale=x.scale, qk_l2norm=1, chunk_size=64, gate_per_head=int(per_head))
     workspace = torch.empty(max(kda.chunk_fwd_workspace_bytes(prob), 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -114,7 +119,8 @@ def bench_prefill(steps: int, warmup: int):
         step(i)
     wall, per = time_launches(step, steps, stream)
     T, H = x.total_tokens, x.num_heads
-    alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + x.num_seqs * H * 2 * STATE_BYTES
+    per_token = PER_HEAD_BYTES_PER_TOKEN_HEAD if per_head else PREFILL_BYTES_PER_TOKEN_HEAD
+    alg_bytes = T * H * per_token + x.num_seqs * H * 2 * STATE_BYTES
     return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T,
                 workspace_bytes=workspace.numel())
 
@@ -269,6 +275,9 @@ def main():
           f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
     dc = bench_decode(args.decode_loops)
     vf = bench_verify(args.steps, args.warmup)
+    ph = bench_prefill(args.steps, args.warmup, per_head=True)
+    print(f"per-head prefill: {ph['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    ph_achieved = ph["alg_bytes"] / ph["per_launch"] / 1e9
     print(f"verify decode: {vf['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     v_tr = measured_traffic("verify_decode")
@@ -327,6 +336,13 @@ def main():
                                        "traffic": None if g_tr is None else round(g_tr / gp["per_launch"] / 1e9, 2),
                                        "alg_bytes_per_launch": gp["alg_bytes"],
                                        "launch_us": round(gp["per_launch"] * 1e6, 2)}},
+        "per_head_prefill": {"workload": ph["x"].name + "_g_per_head",
+                             "tokens_per_s": round(ph["tokens"] * args.steps / ph["wall"], 1),
+                             "roofline": {"kernel": "kda_chunk_fwd (gate_per_head) = " + " + ".join(PREFILL_KERNELS),
+                                          "bound": "hbm", "achieved": round(ph_achieved, 2), "peak": HBM_PEAK_GBS,
+                                          "unit": "GB/s", "frac": round(ph_achieved / HBM_PEAK_GBS, 4),
+                                          "traffic": None, "alg_bytes_per_launch": ph["alg_bytes"],
+                                          "launch_us": round(ph["per_launch"] * 1e6, 2)}},
         "verify_decode": {"workload": vf["x"].name, "tokens_per_s": round(vf["tokens"] * args.steps / vf["wall"], 1),
                           "roofline": {"kernel": "verify_kernel", "bound": "hbm",
                                        "achieved": round(v_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
