@@ -62,7 +62,7 @@ class Gate(ctypes.Structure):
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
-            f"{_LIB_PATH} is missing: build it with `python -m gated_delta_rule_53_amd.build` "
+            f"{_LIB_PATH} is missing: build it with `python gated_delta_rule_53_amd/build.py` "
             "(hipcc, gfx950).  There is no fallback implementation.")
     lib = ctypes.CDLL(_LIB_PATH)
     P, vp, fp, sz = ctypes.POINTER(Problem), ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t

@@ -1,6 +1,6 @@
 """Build libkda.so (HIP, gfx950) in-tree with hipcc.
 
-Usage: ``python -m gated_delta_rule_53_amd.build`` or ``build()`` from Python.
+Usage: ``python gated_delta_rule_53_amd/build.py`` or ``build()`` from Python.
 """
 from __future__ import annotations
 
