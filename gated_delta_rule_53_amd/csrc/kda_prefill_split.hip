@@ -122,10 +122,30 @@ __host__ __device__ constexpr int tri_R(int b) { return b < 2 ? b : 2 + ((b - 2)
 __host__ __device__ constexpr int tri_s(int b) { return b < 2 ? 0 : (b - 2) & 1; }
 
 // (R, I) block of A and P computed by waves 1-10 of prep_kernel (one each).
-__constant__ int8_t kPrepUnit[16][2] = {
+// The table only feeds constant evaluation: the kernel reads it as two packed
+// immediates, so selecting a wave's block costs scalar shifts and no memory
+// load (a load here would also wait on the next item's prefetch in flight).
+constexpr int8_t kPrepUnit[16][2] = {
     {-1, -1}, {1, 0}, {3, 3}, {2, 0}, {2, 2}, {2, 1}, {1, 1}, {3, 0},
     {0, 0}, {3, 1}, {3, 2}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1}, {-1, -1},
 };
+constexpr uint32_t pack_prep_unit(int col) {
+    uint32_t r = 0;
+    for (int w = 0; w < 16; ++w) r |= static_cast<uint32_t>(kPrepUnit[w][col] & 3) << (2 * w);
+    return r;
+}
+constexpr uint32_t kPrepUnitR = pack_prep_unit(0), kPrepUnitI = pack_prep_unit(1);
+constexpr bool prep_unit_packing_ok() {
+    for (int w = 0; w < 16; ++w) {
+        const bool has = w >= 1 && w <= 10;
+        if (has != (kPrepUnit[w][0] >= 0)) return false;
+        if (has && (static_cast<int>((kPrepUnitR >> (2 * w)) & 3) != kPrepUnit[w][0] ||
+                    static_cast<int>((kPrepUnitI >> (2 * w)) & 3) != kPrepUnit[w][1]))
+            return false;
+    }
+    return true;
+}
+static_assert(prep_unit_packing_ok(), "waves 1-10 own one block each");
 
 __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* rec, int base, int unit, int ns,
                                                          int s, int hl, int lane) {
@@ -209,10 +229,10 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 // --------------------------------------------------------------------------
 // With GATED, g and beta are the raw gate and raw beta (bf16), activated as
 // each item is consumed; rows past a sequence's end get g = beta = 0.
-template <bool GATED>
+template <bool GATED, bool GPH>
 __global__ __launch_bounds__(PNT) void prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const void* __restrict__ g_in,
-    const void* __restrict__ beta_in, GateParams gp, int gph, const int32_t* __restrict__ cu_seqlens,
+    const void* __restrict__ beta_in, GateParams gp, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
     float scale, int l2norm) {
     const float* __restrict__ g = static_cast<const float*>(g_in);
@@ -232,60 +252,48 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int n_chunks = offsets[num_seqs];
     const int items = n_chunks * num_heads;
-    const int row_stride = num_heads * D;
 
     // Prefetch registers: row tid/16, channels 8(tid%16) .. +7 of k, q, g; beta.
-    // Gated: the raw gate row in pgr and the item's valid length in pL.
+    // Gated: the raw gate row in pgr.  One decay per head (GPH): the row's one
+    // value in pgs (raw bf16 bits in pgs_raw when gated).  pL: the item's valid
+    // length.  The loads are unconditional (rows past the chunk's end read its
+    // last row, always in bounds) and every value is masked or activated where
+    // it is consumed, so no wait for a load in flight is ever forced here.
     uint4 pk, pq, pgr = {0u, 0u, 0u, 0u};
     floatx4 pg0 = {0.f, 0.f, 0.f, 0.f}, pg1 = {0.f, 0.f, 0.f, 0.f};
-    float pb = 0.f;
+    float pb = 0.f, pgs = 0.f;
+    uint32_t pgs_raw = 0, pb_raw = 0;
     int pL = 0;
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
         const int n = find_seq(offsets, num_seqs, cg);
         const int64_t start = cu_seqlens[n] + static_cast<int64_t>(C) * (cg - offsets[n]);
         const int L = static_cast<int>(min64(C, cu_seqlens[n + 1] - start));
-        const size_t base = (static_cast<size_t>(start) * num_heads + h) * D;
         const int r = tid >> 4, cc = tid & 15;
-        const int off = r * row_stride + 8 * cc;
-        if (r < L) {
-            pk = *reinterpret_cast<const uint4*>(k + base + off);
-            pq = *reinterpret_cast<const uint4*>(q + base + off);
-            // one decay per head: the row's value for all eight channels
-            const size_t hoff = static_cast<size_t>(start + r) * num_heads + h;
-            if constexpr (GATED) {
-                if (gph) {
-                    const uint32_t w = graw[hoff].bits * 0x10001u;
-                    pgr = uint4{w, w, w, w};
-                } else {
-                    pgr = *reinterpret_cast<const uint4*>(graw + base + off);
-                }
-            } else {
-                if (gph) {
-                    const float gs = g[hoff];
-                    pg0 = floatx4{gs, gs, gs, gs};
-                    pg1 = pg0;
-                } else {
-                    pg0 = *reinterpret_cast<const floatx4*>(g + base + off);
-                    pg1 = *reinterpret_cast<const floatx4*>(g + base + off + 4);
-                }
-            }
+        const int rr = max(min(r, L - 1), 0);
+        const size_t row = static_cast<size_t>(start + rr) * num_heads + h;
+        const size_t off = row * D + 8 * cc;
+        pk = *reinterpret_cast<const uint4*>(k + off);
+        pq = *reinterpret_cast<const uint4*>(q + off);
+        if constexpr (GATED) {
+            if constexpr (GPH)
+                pgs_raw = graw[row].bits;
+            else
+                pgr = *reinterpret_cast<const uint4*>(graw + off);
         } else {
-            pk = uint4{0, 0, 0, 0};
-            pq = uint4{0, 0, 0, 0};
-            if constexpr (GATED) {
-                pgr = uint4{0, 0, 0, 0};
+            if constexpr (GPH) {
+                pgs = g[row];
             } else {
-                pg0 = floatx4{0.f, 0.f, 0.f, 0.f};
-                pg1 = floatx4{0.f, 0.f, 0.f, 0.f};
+                pg0 = *reinterpret_cast<const floatx4*>(g + off);
+                pg1 = *reinterpret_cast<const floatx4*>(g + off + 4);
             }
         }
         if (tid < C) {
-            const size_t bi = static_cast<size_t>(start + tid) * num_heads + h;
+            const size_t bi = static_cast<size_t>(start + max(min(tid, L - 1), 0)) * num_heads + h;
             if constexpr (GATED)
-                pb = tid < L ? gate_sigmoid(to_f32(braw[bi])) : 0.f;
+                pb_raw = braw[bi].bits;
             else
-                pb = tid < L ? beta[bi] : 0.f;
+                pb = beta[bi];
         }
         pL = L;
     };
@@ -303,28 +311,33 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         unsigned char* rec = records + (static_cast<size_t>(cg) * num_heads + h) * REC_BYTES;
 
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
-        const floatx8 kf = unpack8(pk), qf = unpack8(pq);
+        const bool live = rp < pL;  // a row past the chunk's end enters as zeros
+        const floatx8 zero8 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        const floatx8 kf = live ? unpack8(pk) : zero8, qf = live ? unpack8(pq) : zero8;
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
         floatx8 gr;
         if constexpr (GATED) {
-            floatx4 b0, b1;
-            if (gph) {
-                const float bs = gp.dt_bias[h];
-                b0 = floatx4{bs, bs, bs, bs};
-                b1 = b0;
-            } else {
-                b0 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc);
-                b1 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc + 4);
-            }
             const float a = gate_exp(gp.a_log[h]);
-            const floatx8 x = unpack8(pgr);
-            const float bias[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+            if constexpr (GPH) {
+                const float x0 = __uint_as_float(pgs_raw << 16);
+                const float gv = live ? gate_g(x0, gp.dt_bias[h], a, gp.lower_bound, gp.has_lower_bound) : 0.f;
+                gr = floatx8{gv, gv, gv, gv, gv, gv, gv, gv};
+            } else {
+                const floatx8 x = unpack8(pgr);
+                const floatx4 b0 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc);
+                const floatx4 b1 = *reinterpret_cast<const floatx4*>(gp.dt_bias + h * D + 8 * cc + 4);
+                const float bias[8] = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
 #pragma unroll
-            for (int i = 0; i < 8; ++i)
-                gr[i] = rp < pL ? gate_g(x[i], bias[i], a, gp.lower_bound, gp.has_lower_bound) : 0.f;
+                for (int i = 0; i < 8; ++i)
+                    gr[i] = live ? gate_g(x[i], bias[i], a, gp.lower_bound, gp.has_lower_bound) : 0.f;
+            }
         } else {
-            gr = floatx8{pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
+            if constexpr (GPH)
+                gr = floatx8{pgs, pgs, pgs, pgs, pgs, pgs, pgs, pgs};
+            else
+                gr = floatx8{pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
+            if (!live) gr = zero8;
         }
         floatx8 incl = gr;
 #pragma unroll
@@ -372,7 +385,14 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                 srq[rp] = (l2norm ? rsqrtf(sq + kNormEps) : 1.f) * scale;
             }
         }
-        if (tid < C) sbeta[tid] = pb;
+        if (tid < C) {
+            float bv;
+            if constexpr (GATED)
+                bv = gate_sigmoid(__uint_as_float(pb_raw << 16));
+            else
+                bv = pb;
+            sbeta[tid] = tid < pL ? bv : 0.f;
+        }
         lds_barrier();
         // G_r - G_31 for this row
         floatx8 cm;
@@ -407,7 +427,9 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         KDA_PHASE_MARK(0);
 
         // ======== phase 2: A' and P' blocks (K = 128 channels), one per wave 1-10 ========
-        const int uR = kPrepUnit[wave][0], uI = kPrepUnit[wave][1];
+        const bool has_unit = wave >= 1 && wave <= 10;
+        const int uR = has_unit ? static_cast<int>((kPrepUnitR >> (2 * wave)) & 3) : -1;
+        const int uI = has_unit ? static_cast<int>((kPrepUnitI >> (2 * wave)) & 3) : -1;
         floatx4 pacc = {0.f, 0.f, 0.f, 0.f};
         if (uR >= 0) {
             const int ar = (16 * uR + l16) * SW, br = (16 * uI + l16) * SW;
@@ -1179,12 +1201,10 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     if (prep_grid > 0) {
         const bf16_t* q = static_cast<const bf16_t*>(a.q);
         const bf16_t* k = static_cast<const bf16_t*>(a.k);
-        if (a.gate.a_log)
-            prep_kernel<true><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, offsets,
-                                                             records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
-        else
-            prep_kernel<false><<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, offsets,
-                                                              records, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+        auto* kern = a.gate.a_log ? (a.gate_per_head ? prep_kernel<true, true> : prep_kernel<true, false>)
+                                  : (a.gate_per_head ? prep_kernel<false, true> : prep_kernel<false, false>);
+        kern<<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets, records, a.num_seqs,
+                                            a.num_heads, a.scale, a.l2norm);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
