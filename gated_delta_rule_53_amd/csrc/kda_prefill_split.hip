@@ -97,9 +97,11 @@ static_assert(P_R3_END >= P_KIL + PW, "region 3 size");
 constexpr int P_PH = P_R3_END, P_PL = P_PH + PN;                // P' [64][SN]
 constexpr int P_ATH = P_PL + PN, P_ATL = P_ATH + 6 * BLK;       // A'^T blocks [16][24]
 constexpr int P_LDT = P_ATL + 6 * BLK;                          // L' diagonal blocks, transposed, fp32
-constexpr int P_XDH = P_LDT + 4 * 16 * LDS_STR * 4;             // X_RR [4][16][24] bf16
+// X_RR and X_RR diag(rk^2 beta) are stored transposed, block R at R * BLK:
+// row c holds column c of the block (written by one lane as two 16-byte stores).
+constexpr int P_XDH = P_LDT + 4 * 16 * LDS_STR * 4;             // X_RR^T [4][16][24] bf16
 constexpr int P_XDL = P_XDH + 4 * BLK;
-constexpr int P_XFH = P_XDL + 4 * BLK;                          // X_RR diag(rk^2 beta)
+constexpr int P_XFH = P_XDL + 4 * BLK;                          // (X_RR diag(rk^2 beta))^T
 constexpr int P_XFL = P_XFH + 4 * BLK;
 constexpr int P_RK = P_XFL + 4 * BLK;                           // fp32 [64]
 constexpr int P_RQ = P_RK + C * 4;
@@ -495,16 +497,29 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             }
             const int r = 16 * l4 + l16;  // the column's own row in the chunk
             const float sphi = sbeta[r] * srk[r] * srk[r];
+            // column l16 of block l4 is row l16 of the transposed block: 16
+            // consecutive bf16 per plane, hi = RNE(x) and lo = RNE(x - hi)
+            uint32_t xh[8], xl[8], fh[8], fl[8];
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const int o = ((l4 * 16 + m) * WSTR + l16) * 2;
-                const float xv = x[m], xf = x[m] * sphi;
-                const __bf16 hi = static_cast<__bf16>(xv), fh = static_cast<__bf16>(xf);
-                *reinterpret_cast<__bf16*>(smem + P_XDH + o) = hi;
-                *reinterpret_cast<__bf16*>(smem + P_XDL + o) = static_cast<__bf16>(xv - static_cast<float>(hi));
-                *reinterpret_cast<__bf16*>(smem + P_XFH + o) = fh;
-                *reinterpret_cast<__bf16*>(smem + P_XFL + o) = static_cast<__bf16>(xf - static_cast<float>(fh));
+            for (int i = 0; i < 8; ++i) {
+                const float a = x[2 * i], b = x[2 * i + 1];
+                const uint32_t h = pack_bf16x2(a, b);
+                xh[i] = h;
+                xl[i] = pack_bf16x2(a - __uint_as_float(h << 16), b - __uint_as_float(h & 0xffff0000u));
+                const float fa = a * sphi, fb = b * sphi;
+                const uint32_t hf = pack_bf16x2(fa, fb);
+                fh[i] = hf;
+                fl[i] = pack_bf16x2(fa - __uint_as_float(hf << 16), fb - __uint_as_float(hf & 0xffff0000u));
             }
+            const int o = (l4 * 16 + l16) * WSTR * 2;
+            *reinterpret_cast<uint4*>(smem + P_XDH + o) = uint4{xh[0], xh[1], xh[2], xh[3]};
+            *reinterpret_cast<uint4*>(smem + P_XDH + o + 16) = uint4{xh[4], xh[5], xh[6], xh[7]};
+            *reinterpret_cast<uint4*>(smem + P_XDL + o) = uint4{xl[0], xl[1], xl[2], xl[3]};
+            *reinterpret_cast<uint4*>(smem + P_XDL + o + 16) = uint4{xl[4], xl[5], xl[6], xl[7]};
+            *reinterpret_cast<uint4*>(smem + P_XFH + o) = uint4{fh[0], fh[1], fh[2], fh[3]};
+            *reinterpret_cast<uint4*>(smem + P_XFH + o + 16) = uint4{fh[4], fh[5], fh[6], fh[7]};
+            *reinterpret_cast<uint4*>(smem + P_XFL + o) = uint4{fl[0], fl[1], fl[2], fl[3]};
+            *reinterpret_cast<uint4*>(smem + P_XFL + o + 16) = uint4{fl[4], fl[5], fl[6], fl[7]};
         } else {
             if (uR >= 0) {
                 // P' from this wave's accumulator of phase 2
@@ -566,11 +581,14 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         if (wave < 6) {
             const int R = wave < 1 ? 1 : wave < 3 ? 2 : 3;
             const bool ok = l4 < 2;
-            const int xo = ((R * 16 + l16) * WSTR + 8 * l4) * 2;
+            // X_RR[l16][8 l4 .. +7] = column l16 of the transposed block (K past 16 reads as zero)
+            const int xr = ok ? 8 * l4 : 0;
+            const bf16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+            const bf16x8 xh8 = col8_tr(smem, P_XDH + R * BLK, WSTR, xr, 0, l16);
+            const bf16x8 xl8 = col8_tr(smem, P_XDL + R * BLK, WSTR, xr, 0, l16);
             const int bo = ((wave * 16 + l16) * WSTR + 8 * l4) * 2;
             floatx4 w = {0.f, 0.f, 0.f, 0.f};
-            w = mma3(ld8_if(smem, P_XDH + xo, ok), ld8_if(smem, P_XDL + xo, ok), ld8_if(smem, P_ATH + bo, ok),
-                     ld8_if(smem, P_ATL + bo, ok), w);
+            w = mma3(ok ? xh8 : z8, ok ? xl8 : z8, ld8_if(smem, P_ATH + bo, ok), ld8_if(smem, P_ATL + bo, ok), w);
             bf16x4 hi, lo;
             split4(-w, hi, lo);
 #pragma unroll
@@ -587,63 +605,70 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         // Waves 0-7: column tile t = wave of Psi'; waves 8-11: column tile
         // t = wave - 8 of X'.  Step R: out_R = rhs_R + sum_{J<R} W_RJ out_J,
         // with out kept transposed in LDS (each wave reads only its own rows).
-        if (wave < 8) {
+        // Every term has K = 16, so two of them share one 32-wide product:
+        // lanes of groups 0-1 supply block J and groups 2-3 block J+1 (W_RJ and
+        // W_R,J+1 are adjacent, and so are the rows of out_J and out_J+1).
+        // A lone term masks the upper half of K.
+        if (wave < 12) {
             const bool ok = l4 < 2;
-            const int c0 = 16 * wave;
-            const float em = sEm[c0 + l16];
+            const int xr = ok ? 8 * l4 : 0;
+            const bf16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
+            const floatx4 zero4 = {0.f, 0.f, 0.f, 0.f};
+            const bool psi = wave < 8;
+            const int t = psi ? wave : wave - 8;
+            // out^T planes and the first step this wave solves
+            const int oh = psi ? P_PTH : P_XTH, ol = psi ? P_PTL : P_XTL;
+            const int orow = 16 * t + l16;  // the wave's own row of out^T
+            const int j0 = psi ? 0 : t;
+            floatx4 rhs[4];
+            if (psi) {
+                // rhs_R = (X_RR diag(rk^2 beta)) Kg_R[:, tile] e^{G_31}[col], independent of the substitution
+                const float em = sEm[16 * t + l16];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) {
-                // rhs: (X_RR diag(rk^2 beta)) Kg_R[:, tile] e^{G_31}[col]
-                const int xo = ((R * 16 + l16) * WSTR + 8 * l4) * 2;
-                // rows past 16R + 15 (lanes with l4 >= 2) read other LDS data and are zeroed
-                const bf16x8 z8 = {0, 0, 0, 0, 0, 0, 0, 0};
-                const bf16x8 kgh8 = col8_tr(smem, P_KGH, SW, 16 * R + 8 * l4, c0, l16);
-                const bf16x8 kgl8 = col8_tr(smem, P_KGL, SW, 16 * R + 8 * l4, c0, l16);
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                acc = mma3(ld8_if(smem, P_XFH + xo, ok), ld8_if(smem, P_XFL + xo, ok), ok ? kgh8 : z8, ok ? kgl8 : z8,
-                           acc);
-                acc *= em;
-#pragma unroll
-                for (int J = 0; J < R; ++J) {
-                    const int wo = ((pair_index(R, J) * 16 + l16) * WSTR + 8 * l4) * 2;
-                    const int po = ((c0 + l16) * SN + 16 * J + 8 * l4) * 2;
-                    acc = mma3(ld8_if(smem, P_WH + wo, ok), ld8_if(smem, P_WL + wo, ok), ld8_if(smem, P_PTH + po, ok),
-                               ld8_if(smem, P_PTL + po, ok), acc);
+                for (int R = 0; R < 4; ++R) {
+                    // rows past 16R + 15 (lanes with l4 >= 2) read other LDS data and are zeroed
+                    const bf16x8 xfh8 = col8_tr(smem, P_XFH + R * BLK, WSTR, xr, 0, l16);
+                    const bf16x8 xfl8 = col8_tr(smem, P_XFL + R * BLK, WSTR, xr, 0, l16);
+                    const bf16x8 kgh8 = col8_tr(smem, P_KGH, SW, 16 * R + 8 * l4, 16 * t, l16);
+                    const bf16x8 kgl8 = col8_tr(smem, P_KGL, SW, 16 * R + 8 * l4, 16 * t, l16);
+                    rhs[R] = mma3(ok ? xfh8 : z8, ok ? xfl8 : z8, ok ? kgh8 : z8, ok ? kgl8 : z8, zero4) * em;
                 }
-                bf16x4 hi, lo;
-                split4(acc, hi, lo);
-                const int oo = ((c0 + l16) * SN + 16 * R + 4 * l4) * 2;
-                *reinterpret_cast<bf16x4*>(smem + P_PTH + oo) = hi;
-                *reinterpret_cast<bf16x4*>(smem + P_PTL + oo) = lo;
-                asm volatile("" ::: "memory");
+            } else {
+                // X'_tt = X_tt, columns scaled by rk beta (the scan multiplies this X' by V directly):
+                // X_tt[4 l4 + j][l16] is row l16 of the transposed block
+                const float cs = srk[16 * t + l16] * sbeta[16 * t + l16];
+                const int o = ((t * 16 + l16) * WSTR + 4 * l4) * 2;
+                const bf16x4 xh4 = ld4(smem, P_XDH + o), xl4 = ld4(smem, P_XDL + o);
+#pragma unroll
+                for (int R = 0; R < 4; ++R) rhs[R] = zero4;
+                floatx4 d;
+#pragma unroll
+                for (int jj = 0; jj < 4; ++jj) d[jj] = (static_cast<float>(xh4[jj]) + static_cast<float>(xl4[jj])) * cs;
+#pragma unroll
+                for (int R = 0; R < 4; ++R)
+                    if (R == t) rhs[R] = d;
             }
-        } else if (wave < 12) {
-            const bool ok = l4 < 2;
-            const int t = wave - 8;
-            // columns scaled by rk beta: the scan multiplies this X' by V directly
-            const float cs = srk[16 * t + l16] * sbeta[16 * t + l16];
 #pragma unroll
             for (int R = 0; R < 4; ++R) {
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-                if (R == t) {
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int o = ((R * 16 + 4 * l4 + j) * WSTR + l16) * 2;
-                        acc[j] = (static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDH + o)) +
-                                  static_cast<float>(*reinterpret_cast<const __bf16*>(smem + P_XDL + o))) * cs;
-                    }
+                // X' waves: blocks R < t of the tile are the upper triangle and are stored as zeros
+                floatx4 acc = rhs[R];
+                int J = j0;
+                for (; J + 1 < R; J += 2) {
+                    const int wo = ((pair_index(R, J + (l4 >> 1)) * 16 + l16) * WSTR + 8 * (l4 & 1)) * 2;
+                    const int po = (orow * SN + 16 * J + 8 * l4) * 2;
+                    acc = mma3(ld8(smem, P_WH + wo), ld8(smem, P_WL + wo), ld8(smem, oh + po), ld8(smem, ol + po), acc);
                 }
-                for (int J = t; J < R; ++J) {
+                if (J < R) {
                     const int wo = ((pair_index(R, J) * 16 + l16) * WSTR + 8 * l4) * 2;
-                    const int xo2 = ((16 * t + l16) * SN + 16 * J + 8 * l4) * 2;
-                    acc = mma3(ld8_if(smem, P_WH + wo, ok), ld8_if(smem, P_WL + wo, ok),
-                               ld8_if(smem, P_XTH + xo2, ok), ld8_if(smem, P_XTL + xo2, ok), acc);
+                    const int po = (orow * SN + 16 * J + 8 * l4) * 2;
+                    acc = mma3(ld8_if(smem, P_WH + wo, ok), ld8_if(smem, P_WL + wo, ok), ld8_if(smem, oh + po, ok),
+                               ld8_if(smem, ol + po, ok), acc);
                 }
                 bf16x4 hi, lo;
                 split4(acc, hi, lo);
-                const int oo = ((16 * t + l16) * SN + 16 * R + 4 * l4) * 2;
-                *reinterpret_cast<bf16x4*>(smem + P_XTH + oo) = hi;
-                *reinterpret_cast<bf16x4*>(smem + P_XTL + oo) = lo;
+                const int oo = (orow * SN + 16 * R + 4 * l4) * 2;
+                *reinterpret_cast<bf16x4*>(smem + oh + oo) = hi;
+                *reinterpret_cast<bf16x4*>(smem + ol + oo) = lo;
                 asm volatile("" ::: "memory");
             }
         }
