@@ -303,6 +303,41 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     // reads first are the ones written last, still in the last-level cache.
     if (static_cast<int>(blockIdx.x) < items) fetch(items - 1 - static_cast<int>(blockIdx.x), threadIdx.x);
 
+    // -Psi', X', P' fragments of an item out of LDS (K indices in accumulator
+    // order).  Called at the top of the next item, once its prefetched inputs
+    // are in registers: the stores are then issued after that prefetch, and
+    // waiting for the prefetch never waits for them (loads and stores retire
+    // in issue order).  The last item's fragments go out after the loop.
+    auto frags_out = [&](unsigned char* rec, int tid) {
+        for (int f = tid; f < 34 * 64; f += PNT) {
+            const int fr = f >> 6, ln = f & 63;
+            const int li = ln & 15, ka = 4 * (ln >> 4);
+            if (fr < 16) {  // -Psi' [R][s], fp16: -Psi'[16R + li][32s + k] = -Psi'^T[32s + k][16R + li]
+                const int R = fr >> 2, s = fr & 3, r0 = 32 * s + ka;
+                const floatx8 x = bf8_to_f(col8_tr2(smem, P_PTH, SN, r0, r0 + 16, 16 * R, li)) +
+                                  bf8_to_f(col8_tr2(smem, P_PTL, SN, r0, r0 + 16, 16 * R, li));
+                *reinterpret_cast<halfx8*>(rec + REC_NPSI + fr * FRAG + ln * 16) = __builtin_convertvector(-x, halfx8);
+            } else if (fr < 28) {  // X' diag(rk beta) [tri][hl], bf16: X'^T[32s + k][16R + li]
+                const int f2 = fr - 16, b = f2 >> 1, hl = f2 & 1;
+                const int R = tri_R(b), r0 = 32 * tri_s(b) + ka;
+                *reinterpret_cast<bf16x8*>(rec + REC_X + f2 * FRAG + ln * 16) =
+                    col8_tr2(smem, hl ? P_XTL : P_XTH, SN, r0, r0 + 16, 16 * R, li);
+            } else {  // P' [tri], fp16, from the row-major hi/lo planes
+                const int b = fr - 28, R = tri_R(b);
+                const int o = ((16 * R + li) * SN + 32 * tri_s(b) + ka) * 2;
+                const bf16x4 h0 = ld4(smem, P_PH + o), h1 = ld4(smem, P_PH + o + 32);
+                const bf16x4 q0 = ld4(smem, P_PL + o), q1 = ld4(smem, P_PL + o + 32);
+                floatx8 x;
+    #pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    x[i] = static_cast<float>(h0[i]) + static_cast<float>(q0[i]);
+                    x[4 + i] = static_cast<float>(h1[i]) + static_cast<float>(q1[i]);
+                }
+                *reinterpret_cast<halfx8*>(rec + REC_P + b * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
+            }
+        }
+    };
+    unsigned char* prev_rec = nullptr;  // the item whose fragments are still in LDS
     for (int it = blockIdx.x; it < items; it += gridDim.x) {
         const int item = items - 1 - it;
         const int lane = opaque(static_cast<int>(threadIdx.x) & 63);
@@ -353,6 +388,9 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc) = floatx4{incl[0], incl[1], incl[2], incl[3]};
             *reinterpret_cast<floatx4*>(sWT + wave * D + 8 * cc + 4) = floatx4{incl[4], incl[5], incl[6], incl[7]};
         }
+        // the previous item's fragments; the barrier below also ends their LDS reads
+        // (the wave totals live in the X_RR planes, which they do not read)
+        if (prev_rec) frags_out(prev_rec, tid);
         lds_barrier();
         // Channel threads turn the wave totals of channel c into offsets in
         // place: with P_w the sum of the totals of waves 0 .. w-1, entry (w, c)
@@ -674,38 +712,9 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         }
         lds_barrier();
         KDA_PHASE_MARK(4);
-
-        // ======== phase 6: -Psi', X', P' fragments out (K indices in accumulator order) ========
-        for (int f = tid; f < 34 * 64; f += PNT) {
-            const int fr = f >> 6, ln = f & 63;
-            const int li = ln & 15, ka = 4 * (ln >> 4);
-            if (fr < 16) {  // -Psi' [R][s], fp16: -Psi'[16R + li][32s + k] = -Psi'^T[32s + k][16R + li]
-                const int R = fr >> 2, s = fr & 3, r0 = 32 * s + ka;
-                const floatx8 x = bf8_to_f(col8_tr2(smem, P_PTH, SN, r0, r0 + 16, 16 * R, li)) +
-                                  bf8_to_f(col8_tr2(smem, P_PTL, SN, r0, r0 + 16, 16 * R, li));
-                *reinterpret_cast<halfx8*>(rec + REC_NPSI + fr * FRAG + ln * 16) = __builtin_convertvector(-x, halfx8);
-            } else if (fr < 28) {  // X' diag(rk beta) [tri][hl], bf16: X'^T[32s + k][16R + li]
-                const int f2 = fr - 16, b = f2 >> 1, hl = f2 & 1;
-                const int R = tri_R(b), r0 = 32 * tri_s(b) + ka;
-                *reinterpret_cast<bf16x8*>(rec + REC_X + f2 * FRAG + ln * 16) =
-                    col8_tr2(smem, hl ? P_XTL : P_XTH, SN, r0, r0 + 16, 16 * R, li);
-            } else {  // P' [tri], fp16, from the row-major hi/lo planes
-                const int b = fr - 28, R = tri_R(b);
-                const int o = ((16 * R + li) * SN + 32 * tri_s(b) + ka) * 2;
-                const bf16x4 h0 = ld4(smem, P_PH + o), h1 = ld4(smem, P_PH + o + 32);
-                const bf16x4 q0 = ld4(smem, P_PL + o), q1 = ld4(smem, P_PL + o + 32);
-                floatx8 x;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    x[i] = static_cast<float>(h0[i]) + static_cast<float>(q0[i]);
-                    x[4 + i] = static_cast<float>(h1[i]) + static_cast<float>(q1[i]);
-                }
-                *reinterpret_cast<halfx8*>(rec + REC_P + b * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
-            }
-        }
-        lds_barrier();
-        KDA_PHASE_MARK(5);
+        prev_rec = rec;
     }
+    if (prev_rec) frags_out(prev_rec, static_cast<int>(threadIdx.x));
     KDA_PHASE_END;
 }
 
