@@ -45,6 +45,7 @@ KERNEL_SOURCES = {
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
 KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
@@ -278,6 +279,7 @@ def main():
     ph = bench_prefill(args.steps, args.warmup, per_head=True)
     print(f"per-head prefill: {ph['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     ph_achieved = ph["alg_bytes"] / ph["per_launch"] / 1e9
+    ph_tr = measured_traffic("per_head_prefill")
     print(f"verify decode: {vf['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     v_tr = measured_traffic("verify_decode")
@@ -316,7 +318,7 @@ def main():
         "roofline": {"kernel": "kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), "bound": "hbm",
                      "achieved": round(achieved, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if tr is None else round(tr / pf["per_launch"] / 1e9, 2),
+                     "traffic": None if tr is None else round(tr / pf["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": tr,
                      "alg_bytes_per_launch": pf["alg_bytes"],
                      "launch_us": round(pf["per_launch"] * 1e6, 2),
                      "workspace_bytes": pf["workspace_bytes"]},
@@ -325,7 +327,7 @@ def main():
                    "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
                                 "achieved": round(d_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                 "frac": round(d_achieved / HBM_PEAK_GBS, 4),
-                                "traffic": None if d_tr is None else round(d_tr / dc["per_launch"] / 1e9, 2),
+                                "traffic": None if d_tr is None else round(d_tr / dc["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": d_tr,
                                 "alg_bytes_per_launch": dc["alg_bytes"],
                                 "launch_us": round(dc["per_launch"] * 1e6, 2)}},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
@@ -333,7 +335,7 @@ def main():
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),
                                        "bound": "hbm", "achieved": round(g_achieved, 2), "peak": HBM_PEAK_GBS,
                                        "unit": "GB/s", "frac": round(g_achieved / HBM_PEAK_GBS, 4),
-                                       "traffic": None if g_tr is None else round(g_tr / gp["per_launch"] / 1e9, 2),
+                                       "traffic": None if g_tr is None else round(g_tr / gp["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": g_tr,
                                        "alg_bytes_per_launch": gp["alg_bytes"],
                                        "launch_us": round(gp["per_launch"] * 1e6, 2)}},
         "per_head_prefill": {"workload": ph["x"].name + "_g_per_head",
@@ -341,13 +343,14 @@ def main():
                              "roofline": {"kernel": "kda_chunk_fwd (gate_per_head) = " + " + ".join(PREFILL_KERNELS),
                                           "bound": "hbm", "achieved": round(ph_achieved, 2), "peak": HBM_PEAK_GBS,
                                           "unit": "GB/s", "frac": round(ph_achieved / HBM_PEAK_GBS, 4),
-                                          "traffic": None, "alg_bytes_per_launch": ph["alg_bytes"],
+                                          "traffic": None if ph_tr is None else round(ph_tr / ph["per_launch"] / 1e9, 2),
+                                          "traffic_bytes_per_launch": ph_tr, "alg_bytes_per_launch": ph["alg_bytes"],
                                           "launch_us": round(ph["per_launch"] * 1e6, 2)}},
         "verify_decode": {"workload": vf["x"].name, "tokens_per_s": round(vf["tokens"] * args.steps / vf["wall"], 1),
                           "roofline": {"kernel": "verify_kernel", "bound": "hbm",
                                        "achieved": round(v_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                                        "frac": round(v_achieved / HBM_PEAK_GBS, 4),
-                                       "traffic": None if v_tr is None else round(v_tr / vf["per_launch"] / 1e9, 2),
+                                       "traffic": None if v_tr is None else round(v_tr / vf["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": v_tr,
                                        "alg_bytes_per_launch": vf["alg_bytes"],
                                        "launch_us": round(vf["per_launch"] * 1e6, 2)}},
     }
