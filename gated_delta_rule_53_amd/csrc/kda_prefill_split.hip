@@ -258,44 +258,44 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     // Prefetch registers: row tid/16, channels 8(tid%16) .. +7 of k, q, g; beta.
     // Gated: the raw gate row in pgr.  One decay per head (GPH): the row's one
     // value in pgs (raw bf16 bits in pgs_raw when gated).  pL: the item's valid
-    // length.  The loads are unconditional (rows past the chunk's end read its
-    // last row, always in bounds) and every value is masked or activated where
-    // it is consumed, so no wait for a load in flight is ever forced here.
+    // length.  Buffer loads over the chunk's valid rows: rows past its end read
+    // as zero with no branch, and nothing here waits for a load in flight (the
+    // gated values are activated, and masked, where they are consumed).
     uint4 pk, pq, pgr = {0u, 0u, 0u, 0u};
     floatx4 pg0 = {0.f, 0.f, 0.f, 0.f}, pg1 = {0.f, 0.f, 0.f, 0.f};
     float pb = 0.f, pgs = 0.f;
     uint32_t pgs_raw = 0, pb_raw = 0;
     int pL = 0;
+    const int row_bytes = num_heads * D * 2;  // one token's q or k row of all heads, bf16
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
         const int n = find_seq(offsets, num_seqs, cg);
         const int64_t start = cu_seqlens[n] + static_cast<int64_t>(C) * (cg - offsets[n]);
-        const int L = static_cast<int>(min64(C, cu_seqlens[n + 1] - start));
+        const int L = max(static_cast<int>(min64(C, cu_seqlens[n + 1] - start)), 0);
         const int r = tid >> 4, cc = tid & 15;
-        const int rr = max(min(r, L - 1), 0);
-        const size_t row = static_cast<size_t>(start + rr) * num_heads + h;
-        const size_t off = row * D + 8 * cc;
-        pk = *reinterpret_cast<const uint4*>(k + off);
-        pq = *reinterpret_cast<const uint4*>(q + off);
+        const size_t head0 = static_cast<size_t>(start) * num_heads + h;  // (first row, head)
+        const int voff = r * row_bytes + 16 * cc;
+        pk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(k + head0 * D, L * row_bytes), voff, 0, 0));
+        pq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(q + head0 * D, L * row_bytes), voff, 0, 0));
         if constexpr (GATED) {
             if constexpr (GPH)
-                pgs_raw = graw[row].bits;
+                pgs_raw = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(graw + head0, L * num_heads * 2), r * num_heads * 2, 0, 0);
             else
-                pgr = *reinterpret_cast<const uint4*>(graw + off);
+                pgr = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(graw + head0 * D, L * row_bytes), voff, 0, 0));
         } else {
             if constexpr (GPH) {
-                pgs = g[row];
+                pgs = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(g + head0, L * num_heads * 4), r * num_heads * 4, 0, 0));
             } else {
-                pg0 = *reinterpret_cast<const floatx4*>(g + off);
-                pg1 = *reinterpret_cast<const floatx4*>(g + off + 4);
+                const auto gr_ = buffer_rsrc(g + head0 * D, 2 * L * row_bytes);
+                pg0 = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(gr_, 2 * voff, 0, 0));
+                pg1 = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(gr_, 2 * voff + 16, 0, 0));
             }
         }
         if (tid < C) {
-            const size_t bi = static_cast<size_t>(start + max(min(tid, L - 1), 0)) * num_heads + h;
             if constexpr (GATED)
-                pb_raw = braw[bi].bits;
+                pb_raw = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(braw + head0, L * num_heads * 2), tid * num_heads * 2, 0, 0);
             else
-                pb = beta[bi];
+                pb = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(beta + head0, L * num_heads * 4), tid * num_heads * 4, 0, 0));
         }
         pL = L;
     };
@@ -348,13 +348,13 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         unsigned char* rec = records + (static_cast<size_t>(cg) * num_heads + h) * REC_BYTES;
 
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
-        const bool live = rp < pL;  // a row past the chunk's end enters as zeros
-        const floatx8 zero8 = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        const floatx8 kf = live ? unpack8(pk) : zero8, qf = live ? unpack8(pq) : zero8;
+        // rows past the chunk's end were loaded as zeros; only activated gates need a mask
+        const floatx8 kf = unpack8(pk), qf = unpack8(pq);
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
         floatx8 gr;
         if constexpr (GATED) {
+            const bool live = rp < pL;
             const float a = gate_exp(gp.a_log[h]);
             if constexpr (GPH) {
                 const float x0 = __uint_as_float(pgs_raw << 16);
@@ -374,7 +374,6 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                 gr = floatx8{pgs, pgs, pgs, pgs, pgs, pgs, pgs, pgs};
             else
                 gr = floatx8{pg0[0], pg0[1], pg0[2], pg0[3], pg1[0], pg1[1], pg1[2], pg1[3]};
-            if (!live) gr = zero8;
         }
         floatx8 incl = gr;
 #pragma unroll
