@@ -55,6 +55,19 @@ def test_prefill_ragged(d, dtype):
     _check_prefill(x)
 
 
+@pytest.mark.parametrize("d", [64, 128])
+def test_prefill_many_short_sequences(d):
+    """1,500 sequences of 0-70 tokens: more sequences than the device-side chunk
+    map sorts (it then keeps their order and sums chunk counts over two passes),
+    many empty sequences, and more state tiles than compute units (the d=128
+    scan then takes two value tiles per workgroup)."""
+    gen = torch.Generator().manual_seed(23)
+    lens = torch.randint(0, 71, (1500,), generator=gen).tolist()
+    lens[:3] = [0, 64, 65]
+    x = w.make_prefill(lens, 2, d, torch.bfloat16, g_mu=2.0, seed=24, name=f"many_short_d{d}")
+    _check_prefill(x)
+
+
 def test_prefill_without_initial_state():
     x = w.make_prefill([97, 256], 2, 128, torch.bfloat16, g_mu=3.0, state_std=None, seed=12)
     _check_prefill(x, with_state=False)
