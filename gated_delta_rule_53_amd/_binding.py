@@ -45,6 +45,7 @@ class Problem(ctypes.Structure):
         ("qk_l2norm", ctypes.c_int32),
         ("chunk_size", ctypes.c_int32),
         ("gate_per_head", ctypes.c_int32),
+        ("state_layout", ctypes.c_int32),
     ]
 
 
@@ -141,11 +142,23 @@ def _stream(device: torch.device) -> ctypes.c_void_p:
     return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
 
 
-def _problem(T, N, H, dk, dv, qkv_dtype, out_dtype, scale, qk_l2norm, gate_per_head=False) -> Problem:
+# State block layouts (kda_problem_t.state_layout): S[dk][dv], or its transpose.
+STATE_LAYOUTS = {"dk_dv": 0, "dv_dk": 1}
+
+
+def _layout_code(state_layout: str) -> int:
+    if state_layout not in STATE_LAYOUTS:
+        raise KdaArgumentError(2, f"state_layout must be one of {sorted(STATE_LAYOUTS)}, got {state_layout!r}")
+    return STATE_LAYOUTS[state_layout]
+
+
+def _problem(T, N, H, dk, dv, qkv_dtype, out_dtype, scale, qk_l2norm, gate_per_head=False,
+             state_layout: str = "dk_dv") -> Problem:
     return Problem(total_tokens=T, num_seqs=N, num_heads=H, head_k=dk, head_v=dv,
                    qkv_dtype=_dtype_code(qkv_dtype), out_dtype=_dtype_code(out_dtype),
                    scale=float(1.0 / math.sqrt(dk) if scale is None else scale),
-                   qk_l2norm=int(bool(qk_l2norm)), chunk_size=64, gate_per_head=int(bool(gate_per_head)))
+                   qk_l2norm=int(bool(qk_l2norm)), chunk_size=64, gate_per_head=int(bool(gate_per_head)),
+                   state_layout=_layout_code(state_layout))
 
 
 def _gate_shape(g: torch.Tensor, lead: tuple, dk: int):
@@ -161,6 +174,7 @@ def chunk_fwd_workspace_bytes(problem: Problem) -> int:
 def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
               beta: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
               initial_state: Optional[torch.Tensor] = None, *, scale: Optional[float] = None,
+              state_layout: str = "dk_dv",
               qk_l2norm: bool = True, out_dtype: Optional[torch.dtype] = None,
               output_final_state: bool = True, out: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None,
@@ -173,6 +187,8 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     float32 or None.  Returns (out [T, H, dv] in ``out_dtype`` (default: v's
     dtype), final_state [N, H, dk, dv] float32 or None).  Runs on the current
     stream of q's device.  ``final_state`` may be ``initial_state`` itself.
+    ``state_layout="dv_dk"`` takes and returns every state block transposed,
+    [..., dv, dk] (kda_problem_t.state_layout; the same for every call below).
     """
     if q.dim() != 3:
         raise KdaArgumentError(2, f"q must be [T, H, dk], got {tuple(q.shape)}")
@@ -201,7 +217,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -214,6 +230,7 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
                    beta: torch.Tensor, state: torch.Tensor, *, scale: Optional[float] = None,
+                   state_layout: str = "dk_dv",
                    qk_l2norm: bool = True, out_dtype: Optional[torch.dtype] = None,
                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """One decode step for N sequences (``kda_recurrent_step``); ``state`` is updated in place.
@@ -238,7 +255,7 @@ def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.T
     if out is None:
         out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, H, dv), out_dtype, dev)
-    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     _check(_lib.kda_recurrent_step(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g),
                                    _ptr(beta), _ptr(state), _ptr(out), _stream(dev)))
     return out
@@ -257,7 +274,7 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: to
                     raw_beta: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
                     cu_seqlens: Optional[torch.Tensor] = None,
                     initial_state: Optional[torch.Tensor] = None, *, lower_bound: Optional[float] = None,
-                    scale: Optional[float] = None, qk_l2norm: bool = True,
+                    scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
                     out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
                     out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
                     workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
@@ -295,7 +312,7 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: to
         final_state = torch.empty((N, H, dk, dv), dtype=torch.float32, device=dev)
     if final_state is not None:
         _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -309,7 +326,7 @@ def chunk_fwd_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: to
 def recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_g: torch.Tensor,
                          raw_beta: torch.Tensor, a_log: torch.Tensor, dt_bias: torch.Tensor,
                          state: torch.Tensor, *, lower_bound: Optional[float] = None,
-                         scale: Optional[float] = None, qk_l2norm: bool = True,
+                         scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
                          out_dtype: Optional[torch.dtype] = None,
                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """``recurrent_step`` with the gate activation fused in (``kda_recurrent_step_gated``).
@@ -335,7 +352,7 @@ def recurrent_step_gated(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, raw_
     if out is None:
         out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, H, dv), out_dtype, dev)
-    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     _check(_lib.kda_recurrent_step_gated(ctypes.byref(prob), ctypes.byref(gate), _ptr(q), _ptr(k), _ptr(v),
                                          _ptr(raw_g), _ptr(raw_beta), _ptr(state), _ptr(out), _stream(dev)))
     return out
@@ -355,7 +372,7 @@ def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
                      beta: torch.Tensor, state_pool: torch.Tensor, state_slots: torch.Tensor,
                      cu_seqlens: Optional[torch.Tensor] = None, *, a_log: Optional[torch.Tensor] = None,
                      dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
-                     scale: Optional[float] = None, qk_l2norm: bool = True,
+                     scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Chunked prefill with the states in a slot pool (``kda_chunk_fwd_pooled``).
@@ -395,7 +412,7 @@ def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if out is None:
         out = torch.empty((T, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (T, H, dv), out_dtype, dev)
-    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     ws_bytes = chunk_fwd_workspace_bytes(prob)
     if ws_bytes and workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
@@ -410,7 +427,7 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
                      beta: torch.Tensor, state_pool: torch.Tensor, state_indices: torch.Tensor,
                      num_accepted: Optional[torch.Tensor] = None, *, a_log: Optional[torch.Tensor] = None,
                      dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
-                     scale: Optional[float] = None, qk_l2norm: bool = True,
+                     scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
                      out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
     """Multi-token verify decode over a slot pool (``kda_recurrent_verify``).
 
@@ -446,7 +463,7 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     if out is None:
         out = torch.empty((N, W, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, W, H, dv), out_dtype, dev)
-    prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph)
+    prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
     _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, None if gate is None else ctypes.byref(gate), _ptr(q),
                                      _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
                                      _ptr(state_indices), _ptr(num_accepted), _ptr(out), _stream(dev)))

@@ -60,6 +60,8 @@ kda_status_t check_problem(const kda_problem_t* p, const char* what) {
         return fail(KDA_ERR_BAD_SHAPE, "%s: qk_l2norm must be 0 or 1", what);
     if (p->gate_per_head != 0 && p->gate_per_head != 1)
         return fail(KDA_ERR_BAD_SHAPE, "%s: gate_per_head must be 0 or 1", what);
+    if (p->state_layout != KDA_STATE_DK_DV && p->state_layout != KDA_STATE_DV_DK)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: state_layout must be KDA_STATE_DK_DV (0) or KDA_STATE_DV_DK (1)", what);
     // Row counts that index int32 offsets inside kernels stay well within range.
     if (p->total_tokens > (int64_t(1) << 40) || int64_t(p->num_seqs) * p->num_heads > (int64_t(1) << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
@@ -113,6 +115,7 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
     a.beta = beta;
     a.gate = gp;
     a.gate_per_head = p->gate_per_head;
+    a.state_trans = p->state_layout == KDA_STATE_DV_DK;
     a.cu_seqlens = cu_seqlens;
     a.initial_state = initial_state;
     a.out = out;
@@ -152,6 +155,7 @@ kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const
     a.beta = beta;
     a.gate = gp;
     a.gate_per_head = p->gate_per_head;
+    a.state_trans = p->state_layout == KDA_STATE_DV_DK;
     a.state = state;
     a.out = out;
     a.num_seqs = p->num_seqs;
@@ -295,6 +299,7 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     a.beta = beta;
     a.gate = gp;
     a.gate_per_head = p->gate_per_head;
+    a.state_trans = p->state_layout == KDA_STATE_DV_DK;
     a.pool = state_pool;
     a.num_slots = num_slots;
     a.indices = state_indices;

@@ -117,6 +117,12 @@ __device__ inline bool state_block(const int32_t* slots, int num_slots, int n, i
     return true;
 }
 
+// Element (r, c) of a state block, r a key channel and c a value channel:
+// S[dk][dv] (c contiguous), or its transpose S^T[dv][dk] (r contiguous).
+__device__ __forceinline__ size_t state_elem(int r, int c, int d, int trans) {
+    return trans ? static_cast<size_t>(c) * d + r : static_cast<size_t>(r) * d + c;
+}
+
 // Phase timing for kernel tuning.  Compiled out unless KDA_PHASE_TIMING is
 // defined; then thread 0 of every workgroup accumulates clock64() deltas
 // between consecutive marks into kda_phase_cycles[mark].

@@ -25,7 +25,17 @@
 
 namespace kda {
 
-template <int D, typename TIn, typename TOut, bool GATED>
+// Sum over the lanes of a group of G consecutive lanes (G a power of two).
+__device__ __forceinline__ float group_sum(float x, int G) {
+    for (int off = 1; off < G; off <<= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+// TRANS: the state block is S^T[dv][dk].  The thread then owns key rows
+// 4cg..4cg+3 of value columns rg, rg+NRG, ...: the same float4 addresses, and
+// each column's contraction over the key rows is a sum over the NCG lanes of
+// one lane group, with no exchange between waves.
+template <int D, typename TIn, typename TOut, bool GATED, bool TRANS>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ state,
@@ -83,59 +93,82 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     const float rq = (l2norm ? rsqrtf(aq + kNormEps) : 1.f) * scale;
     const float rk = l2norm ? rsqrtf(ak + kNormEps) : 1.f;
 
-    // Decay, then the two partial contractions over this thread's rows.
-    floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + NRG * i;
-        s[i] *= se[r];
-        pu += sk[r] * s[i];
-        pp += sq[r] * s[i];
-    }
-    // Lanes of one wave that share cg differ by multiples of NCG.
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        pu[j] = wave_sum_from(pu[j], NCG);
-        pp[j] = wave_sum_from(pp[j], NCG);
-    }
-    if (lane < NCG) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            red[wave][lane][j] = pu[j];
-            red[wave][lane][4 + j] = pp[j];
-        }
-    }
-    __syncthreads();
-    floatx4 u, p;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
-        p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
-    }
-
-    const size_t voff = static_cast<size_t>(pair) * D + 4 * cg;
-    float b;
-    if constexpr (GATED)
-        b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[pair]));
-    else
-        b = static_cast<const float*>(beta)[pair];
-    floatx4 delta;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
-
-    // The state is not read again in this step: non-temporal stores stream it
-    // out without keeping it in the caches (measured ~25 % more HBM throughput
-    // than plain stores for this read-then-write pattern).
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-        const int r = rg + NRG * i;
-        s[i] += (rk * sk[r]) * delta;
-        __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
-    }
-    if (rg == 0) {
+    if constexpr (TRANS) {
+        const floatx4 e4 = {se[4 * cg], se[4 * cg + 1], se[4 * cg + 2], se[4 * cg + 3]};
+        const floatx4 k4 = {sk[4 * cg], sk[4 * cg + 1], sk[4 * cg + 2], sk[4 * cg + 3]};
+        const floatx4 q4 = {sq[4 * cg], sq[4 * cg + 1], sq[4 * cg + 2], sq[4 * cg + 3]};
+        float b;
+        if constexpr (GATED)
+            b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[pair]));
+        else
+            b = static_cast<const float*>(beta)[pair];
         const float kq = rk * rq * aqk;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+        for (int i = 0; i < RPT; ++i) {
+            const int c = rg + NRG * i;
+            s[i] *= e4;
+            const float u = group_sum(s[i][0] * k4[0] + s[i][1] * k4[1] + s[i][2] * k4[2] + s[i][3] * k4[3], NCG) * rk;
+            const float p = group_sum(s[i][0] * q4[0] + s[i][1] * q4[1] + s[i][2] * q4[2] + s[i][3] * q4[3], NCG) * rq;
+            const float delta = b * (to_f32(v[static_cast<size_t>(pair) * D + c]) - u);
+            s[i] += (rk * delta) * k4;
+            __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + c * D + 4 * cg));
+            if (cg == 0) out[static_cast<size_t>(pair) * D + c] = from_f32<TOut>(p + kq * delta);
+        }
+    } else {
+        // Decay, then the two partial contractions over this thread's rows.
+        floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + NRG * i;
+            s[i] *= se[r];
+            pu += sk[r] * s[i];
+            pp += sq[r] * s[i];
+        }
+        // Lanes of one wave that share cg differ by multiples of NCG.
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            pu[j] = wave_sum_from(pu[j], NCG);
+            pp[j] = wave_sum_from(pp[j], NCG);
+        }
+        if (lane < NCG) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                red[wave][lane][j] = pu[j];
+                red[wave][lane][4 + j] = pp[j];
+            }
+        }
+        __syncthreads();
+        floatx4 u, p;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
+            p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
+        }
+
+        const size_t voff = static_cast<size_t>(pair) * D + 4 * cg;
+        float b;
+        if constexpr (GATED)
+            b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[pair]));
+        else
+            b = static_cast<const float*>(beta)[pair];
+        floatx4 delta;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
+
+        // The state is not read again in this step: non-temporal stores stream it
+        // out without keeping it in the caches (measured ~25 % more HBM throughput
+        // than plain stores for this read-then-write pattern).
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+            const int r = rg + NRG * i;
+            s[i] += (rk * sk[r]) * delta;
+            __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
+        }
+        if (rg == 0) {
+            const float kq = rk * rq * aqk;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+        }
     }
 }
 
@@ -147,7 +180,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // [0, num_slots) reads as the zero state and is not written.  The whole
 // starting state is read before anything is written, so idx[a-1] may also
 // appear among the destinations.  Each token is the decode step above.
-template <int D, typename TIn, typename TOut, bool GATED>
+template <int D, typename TIn, typename TOut, bool GATED, bool TRANS>
 __global__ __launch_bounds__(256) void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ pool,
@@ -213,53 +246,79 @@ __global__ __launch_bounds__(256) void verify_kernel(
         aqk = wave_sum_from(aqk, 1);
         const float rq = (l2norm ? rsqrtf(aq + kNormEps) : 1.f) * scale;
         const float rk = l2norm ? rsqrtf(ak + kNormEps) : 1.f;
-        floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (TRANS) {
+            const floatx4 e4 = {se[4 * cg], se[4 * cg + 1], se[4 * cg + 2], se[4 * cg + 3]};
+            const floatx4 k4 = {sk[4 * cg], sk[4 * cg + 1], sk[4 * cg + 2], sk[4 * cg + 3]};
+            const floatx4 q4 = {sq[4 * cg], sq[4 * cg + 1], sq[4 * cg + 2], sq[4 * cg + 3]};
+            float b;
+            if constexpr (GATED)
+                b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
+            else
+                b = static_cast<const float*>(beta)[tok];
+            const float kq = rk * rq * aqk;
+            float* S = slot_ptr(idx[t]);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + NRG * i;
-            s[i] *= se[r];
-            pu += sk[r] * s[i];
-            pp += sq[r] * s[i];
-        }
+            for (int i = 0; i < RPT; ++i) {
+                const int c = rg + NRG * i;
+                s[i] *= e4;
+                const float u =
+                    group_sum(s[i][0] * k4[0] + s[i][1] * k4[1] + s[i][2] * k4[2] + s[i][3] * k4[3], NCG) * rk;
+                const float p =
+                    group_sum(s[i][0] * q4[0] + s[i][1] * q4[1] + s[i][2] * q4[2] + s[i][3] * q4[3], NCG) * rq;
+                const float delta = b * (to_f32(v[tok * D + c]) - u);
+                s[i] += (rk * delta) * k4;
+                if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + c * D + 4 * cg));
+                if (cg == 0) out[tok * D + c] = from_f32<TOut>(p + kq * delta);
+            }
+        } else {
+            floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            pu[j] = wave_sum_from(pu[j], NCG);
-            pp[j] = wave_sum_from(pp[j], NCG);
-        }
-        if (lane < NCG) {
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rg + NRG * i;
+                s[i] *= se[r];
+                pu += sk[r] * s[i];
+                pp += sq[r] * s[i];
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                red[wave][lane][j] = pu[j];
-                red[wave][lane][4 + j] = pp[j];
+                pu[j] = wave_sum_from(pu[j], NCG);
+                pp[j] = wave_sum_from(pp[j], NCG);
             }
-        }
-        __syncthreads();
-        floatx4 u, p;
+            if (lane < NCG) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
-            p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
-        }
-        float b;
-        if constexpr (GATED)
-            b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
-        else
-            b = static_cast<const float*>(beta)[tok];
-        const size_t voff = tok * D + 4 * cg;
-        floatx4 delta;
+                for (int j = 0; j < 4; ++j) {
+                    red[wave][lane][j] = pu[j];
+                    red[wave][lane][4 + j] = pp[j];
+                }
+            }
+            __syncthreads();
+            floatx4 u, p;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
-        float* S = slot_ptr(idx[t]);
+            for (int j = 0; j < 4; ++j) {
+                u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
+                p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
+            }
+            float b;
+            if constexpr (GATED)
+                b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
+            else
+                b = static_cast<const float*>(beta)[tok];
+            const size_t voff = tok * D + 4 * cg;
+            floatx4 delta;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-            const int r = rg + NRG * i;
-            s[i] += (rk * sk[r]) * delta;
-            if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
-        }
-        if (rg == 0) {
-            const float kq = rk * rq * aqk;
+            for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
+            float* S = slot_ptr(idx[t]);
 #pragma unroll
-            for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+            for (int i = 0; i < RPT; ++i) {
+                const int r = rg + NRG * i;
+                s[i] += (rk * sk[r]) * delta;
+                if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
+            }
+            if (rg == 0) {
+                const float kq = rk * rq * aqk;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+            }
         }
         // sq, sk, se and red are rewritten by the next token
         __syncthreads();
@@ -272,14 +331,10 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     const TIn* q = static_cast<const TIn*>(a.q);
     const TIn* k = static_cast<const TIn*>(a.k);
     const TIn* v = static_cast<const TIn*>(a.v);
-    if (a.gate.a_log)
-        verify_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
-            a.num_heads, a.width, a.scale, a.l2norm);
-    else
-        verify_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices, a.accepted, static_cast<TOut*>(a.out),
-            a.num_heads, a.width, a.scale, a.l2norm);
+    auto* kern = a.gate.a_log ? (a.state_trans ? verify_kernel<D, TIn, TOut, true, true> : verify_kernel<D, TIn, TOut, true, false>)
+                              : (a.state_trans ? verify_kernel<D, TIn, TOut, false, true> : verify_kernel<D, TIn, TOut, false, false>);
+    kern<<<grid, 256, 0, stream>>>(q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices,
+                                   a.accepted, static_cast<TOut*>(a.out), a.num_heads, a.width, a.scale, a.l2norm);
     return hipGetLastError();
 }
 
@@ -300,14 +355,11 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const TIn* q = static_cast<const TIn*>(a.q);
     const TIn* k = static_cast<const TIn*>(a.k);
     const TIn* v = static_cast<const TIn*>(a.v);
-    if (a.gate.a_log)
-        decode_step_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out), a.num_heads,
-            a.scale, a.l2norm);
-    else
-        decode_step_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
-            q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out), a.num_heads,
-            a.scale, a.l2norm);
+    auto* kern = a.gate.a_log
+                     ? (a.state_trans ? decode_step_kernel<D, TIn, TOut, true, true> : decode_step_kernel<D, TIn, TOut, true, false>)
+                     : (a.state_trans ? decode_step_kernel<D, TIn, TOut, false, true> : decode_step_kernel<D, TIn, TOut, false, false>);
+    kern<<<grid, 256, 0, stream>>>(q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out),
+                                   a.num_heads, a.scale, a.l2norm);
     return hipGetLastError();
 }
 

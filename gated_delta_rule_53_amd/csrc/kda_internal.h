@@ -20,6 +20,7 @@ struct DecodeArgs {
     const void* beta;
     GateParams gate;
     int gate_per_head;  // g (or the raw gate) is [rows, H]: one decay per head
+    int state_trans;    // state blocks are S^T [dv][dk]
     float* state;
     void* out;
     int num_seqs;
@@ -40,6 +41,7 @@ struct VerifyArgs {
     const void* beta;
     GateParams gate;
     int gate_per_head;
+    int state_trans;
     float* pool;
     int num_slots;
     const int32_t* indices;   // [num_seqs, width]
@@ -63,6 +65,7 @@ struct PrefillArgs {
     const void* beta;
     GateParams gate;
     int gate_per_head;
+    int state_trans;
     const int32_t* cu_seqlens;
     const float* initial_state;
     void* out;

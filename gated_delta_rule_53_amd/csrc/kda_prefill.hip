@@ -54,7 +54,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
     const void* __restrict__ g_in, const void* __restrict__ beta_in, GateParams gp, int gph,
     const int32_t* __restrict__ cu_seqlens, const float* initial_state, TOut* __restrict__ out,
     float* final_state, const int32_t* __restrict__ slots, int num_slots, int64_t total_tokens, int num_seqs,
-    int num_heads, float scale, int l2norm) {
+    int num_heads, float scale, int l2norm, int state_trans) {
     using GT = typename std::conditional<GATED, TIn, float>::type;  // element type of g and beta
     const GT* __restrict__ g = static_cast<const GT*>(g_in);
     const GT* __restrict__ beta = static_cast<const GT*>(beta_in);
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int c = 16 * cb + 4 * l4 + j;
-            const float s = init ? init[head_state + c * D + col0 + l16] : 0.f;
+            const float s = init ? init[head_state + state_elem(c, col0 + l16, D, state_trans)] : 0.f;
             Sacc[b][j] = s;
             sS[c * kDVT + l16] = s;
         }
@@ -437,7 +437,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             const int cb = wave * CBW + b;
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                fin[head_state + (16 * cb + 4 * l4 + j) * D + col0 + l16] = Sacc[b][j];
+                fin[head_state + state_elem(16 * cb + 4 * l4 + j, col0 + l16, D, state_trans)] = Sacc[b][j];
         }
     }
     KDA_PHASE_END;
@@ -455,11 +455,13 @@ static hipError_t launch_prefill_t(const PrefillArgs& a, hipStream_t stream) {
     if (a.gate.a_log)
         prefill_chunk_kernel<D, TIn, TOut, true><<<grid, 256, 0, stream>>>(
             q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
-            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm,
+            a.state_trans);
     else
         prefill_chunk_kernel<D, TIn, TOut, false><<<grid, 256, 0, stream>>>(
             q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.cu_seqlens, a.initial_state, static_cast<TOut*>(a.out),
-            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm);
+            a.final_state, a.slots, a.num_slots, a.total_tokens, a.num_seqs, a.num_heads, a.scale, a.l2norm,
+            a.state_trans);
     return hipGetLastError();
 }
 

@@ -766,7 +766,8 @@ template <typename TOut, int NT>
 __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state, TOut* __restrict__ out,
-    float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs, int num_heads) {
+    float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs, int num_heads,
+    int state_trans) {
     __shared__ __align__(16) unsigned char lds_sb[3 * SB_BYTES];
     using SS = ScanShape<NT>;
     constexpr int DG_GL = SS::DG_GL, DG_SLOT = SS::DG_SLOT, XCH_SLOT = SS::XCH_SLOT;
@@ -816,7 +817,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
             for (int w = 0; w < 8; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    S[w][j] = init[head_state + (16 * w + 4 * g + j) * D + col0 + l16];
+                    S[w][j] = init[head_state + state_elem(16 * w + 4 * g + j, col0 + l16, D, state_trans)];
         }
         // Step j from state buffer sb (chunk j mod 3) and slots of parity p.
         // D = Delta0 - Psi' S runs K block by K block (32 rows of S each): the
@@ -910,7 +911,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
             for (int w = 0; w < 8; ++w)
 #pragma unroll
                 for (int j = 0; j < 4; ++j)
-                    fin[head_state + (16 * w + 4 * g + j) * D + col0 + l16] = S[w][j];
+                    fin[head_state + state_elem(16 * w + 4 * g + j, col0 + l16, D, state_trans)] = S[w][j];
         }
     } else if (wave == NT + 2) {
         // ================= state-copy wave =================
@@ -1249,11 +1250,13 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     if (pairs)
         scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
-            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads);
+            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
+            a.state_trans);
     else
         scan_kernel<TOut, 1><<<groups * ScanShape<1>::UNITS, ScanShape<1>::THREADS, 0, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
-            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads);
+            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
+            a.state_trans);
     return hipGetLastError();
 }
 

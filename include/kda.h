@@ -54,7 +54,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -87,7 +87,16 @@ typedef struct kda_problem {
                               [rows, H, dk]; 1: one value per head, [rows, H], the same
                               decay for every channel (the Gated DeltaNet case); the gated
                               calls then take dt_bias as [H]                               */
+    int32_t state_layout; /* KDA_STATE_DK_DV (0): every state block (initial, final, decode
+                              state, pool slot) is S[dk][dv], dv contiguous; KDA_STATE_DV_DK
+                              (1): the transpose S^T[dv][dk], dk contiguous, the layout of
+                              the Ascend model file's recurrent cache (`_prefill_flash_kda`
+                              reads and scatters it per request).  Same values either way;
+                              only the element order within a block changes.  ABI 5.     */
 } kda_problem_t;
+
+#define KDA_STATE_DK_DV 0
+#define KDA_STATE_DV_DK 1
 
 /*
  * Gate parameters of the *_gated entry points, which take the raw gate and
@@ -158,9 +167,9 @@ size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
  *                  allowed (their final state is their initial state).  Entries outside
  *                  [0, T] or decreasing pairs make that sequence empty; they never cause
  *                  an out-of-bounds access.
- *   initial_state  [N, H, dk, dv] float32, or NULL for zeros
+ *   initial_state  [N, H, dk, dv] float32 ([N, H, dv, dk] with KDA_STATE_DV_DK), or NULL for zeros
  *   out            [T, H, dv]  out_dtype (written)
- *   final_state    [N, H, dk, dv] float32 (written), or NULL to skip.  May alias
+ *   final_state    [N, H, dk, dv] float32 (layout as initial_state; written), or NULL to skip.  May alias
  *                  initial_state exactly (same pointer); partial overlap is undefined.
  *   workspace      device buffer of at least kda_chunk_fwd_workspace_bytes(problem)
  *                  bytes, or NULL when that is 0.  Contents need not be initialised.
@@ -195,7 +204,7 @@ kda_status_t kda_chunk_fwd_gated(const kda_problem_t *problem, const kda_gate_t 
  *   v       [N, H, dv]  qkv_dtype
  *   g       [N, H, dk]  float32 ([N, H] with problem->gate_per_head)
  *   beta    [N, H]      float32
- *   state   [N, H, dk, dv] float32, read and overwritten
+ *   state   [N, H, dk, dv] float32 ([N, H, dv, dk] with KDA_STATE_DV_DK), read and overwritten
  *   out     [N, H, dv]  out_dtype (written)
  *   stream  a hipStream_t (NULL: the default stream)
  */
@@ -219,7 +228,8 @@ kda_status_t kda_recurrent_step_gated(const kda_problem_t *problem, const kda_ga
  * index per token (`ssm_state_indices`, checked against the fixed "Verify"
  * width) and the number of accepted tokens (`num_accepted_tokens`).
  *
- *   state_pool   [num_slots, H, dk, dv] float32 (device), read and written.
+ *   state_pool   [num_slots, H, dk, dv] float32 (device; [num_slots, H, dv, dk] with
+ *                KDA_STATE_DV_DK), read and written.
  *   A slot index outside [0, num_slots) names no slot: such a state reads as
  *   zero and is not written.  Slots named by different sequences of one call
  *   must be distinct (otherwise the result is undefined).

@@ -53,11 +53,34 @@ def test_gate_struct_layout():
     assert kda.Gate.has_lower_bound.offset == 16 and kda.Gate.lower_bound.offset == 20
 
 
-def test_problem_struct_layout_matches_header():
-    # int64 first, then ten 4-byte fields: 8 + 40 = 48.
-    assert ctypes.sizeof(Problem) == 48
-    assert Problem.total_tokens.offset == 0 and Problem.num_seqs.offset == 8
-    assert Problem.chunk_size.offset == 40 and Problem.gate_per_head.offset == 44
+def _c_layout(struct: str, fields):
+    """sizeof and offsetof of the header's struct, as the C compiler lays it out."""
+    import shutil
+    import subprocess
+    import tempfile
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    lines = ["#include <stdio.h>", "#include <stddef.h>", '#include "kda.h"', "int main(void) {",
+             f'    printf("%zu\\n", sizeof({struct}));']
+    lines += [f'    printf("%zu\\n", offsetof({struct}, {f}));' for f in fields]
+    lines += ["    return 0;", "}"]
+    with tempfile.TemporaryDirectory() as d:
+        src, exe = os.path.join(d, "layout.c"), os.path.join(d, "layout")
+        open(src, "w").write("\n".join(lines) + "\n")
+        subprocess.run([cc, "-I", os.path.dirname(HEADER), src, "-o", exe], check=True)
+        vals = [int(x) for x in subprocess.run([exe], check=True, capture_output=True, text=True).stdout.split()]
+    return vals[0], dict(zip(fields, vals[1:]))
+
+
+@pytest.mark.parametrize("cls,struct", [(Problem, "kda_problem_t"), (kda.Gate, "kda_gate_t")])
+def test_struct_layout_matches_header(cls, struct):
+    """The ctypes mirrors match the C compiler's layout of include/kda.h, field by field."""
+    fields = [f for f, _ in cls._fields_]
+    size, offs = _c_layout(struct, fields)
+    assert ctypes.sizeof(cls) == size
+    for f in fields:
+        assert getattr(cls, f).offset == offs[f], f
 
 
 def test_status_strings():
@@ -109,6 +132,8 @@ def _step(prob, **ptrs):
     (dict(qk_l2norm=3), 2, "qk_l2norm"),
     (dict(chunk_size=32), 3, "chunk_size"),
     (dict(gate_per_head=2), 2, "gate_per_head"),
+    (dict(state_layout=2), 2, "state_layout"),
+    (dict(state_layout=-1), 2, "state_layout"),
 ])
 def test_chunk_fwd_rejects_bad_problem(kw, status, needle):
     st, msg = _chunk(_prob(**kw))
@@ -304,3 +329,10 @@ def test_product_package_does_not_reference_the_oracle():
             if f.endswith((".py", ".hip", ".h", ".cpp")):
                 text = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in text.lower(), f"{f} mentions the oracle"
+
+
+def test_binding_rejects_unknown_state_layout():
+    from gated_delta_rule_53_amd._binding import KdaArgumentError, _layout_code
+    assert _layout_code("dk_dv") == 0 and _layout_code("dv_dk") == 1
+    with pytest.raises(KdaArgumentError):
+        _layout_code("transposed")
