@@ -160,7 +160,8 @@ def bench_prefill_gated(steps: int, warmup: int):
     return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T)
 
 
-def bench_decode(loops: int):
+def bench_decode(loops: int, state_layout: str = "dk_dv"):
+    """kda_recurrent_step, 256 sequences x 64 steps; state_layout "dv_dk" keeps the states transposed."""
     import torch
 
     import gated_delta_rule_53_amd as kda
@@ -170,12 +171,14 @@ def bench_decode(loops: int):
     dev = "cuda:0"
     q, k, v, g, b = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta))
     st = x.initial_state.to(dev)
+    if state_layout == "dv_dk":
+        st = st.transpose(-1, -2).contiguous()
     out = torch.empty_like(v[0])
     stream = torch.cuda.current_stream()
 
     def one(i):
         t = i % x.steps
-        kda.recurrent_step(q[t], k[t], v[t], g[t], b[t], st, scale=x.scale, out=out)
+        kda.recurrent_step(q[t], k[t], v[t], g[t], b[t], st, scale=x.scale, out=out, state_layout=state_layout)
 
     for i in range(x.steps):  # warm-up pass over all 64 steps
         one(i)
@@ -275,6 +278,10 @@ def main():
     print(f"prefill: {pf['per_launch'] * 1e6:.1f} us per launch (events), "
           f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
     dc = bench_decode(args.decode_loops)
+    dt = bench_decode(1, state_layout="dv_dk")
+    print(f"decode, transposed states: {dt['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr,
+          flush=True)
+    dt_achieved = dt["alg_bytes"] / dt["per_launch"] / 1e9
     vf = bench_verify(args.steps, args.warmup)
     ph = bench_prefill(args.steps, args.warmup, per_head=True)
     print(f"per-head prefill: {ph['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
@@ -330,6 +337,13 @@ def main():
                                 "traffic": None if d_tr is None else round(d_tr / dc["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": d_tr,
                                 "alg_bytes_per_launch": dc["alg_bytes"],
                                 "launch_us": round(dc["per_launch"] * 1e6, 2)}},
+        "decode_dv_dk": {"workload": dt["x"].name + "_state_dv_dk",
+                         "steps_per_s": round(dt["launches"] / dt["wall"], 1),
+                         "roofline": {"kernel": "decode_step_kernel (state_layout dv_dk)", "bound": "hbm",
+                                      "achieved": round(dt_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": round(dt_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                      "alg_bytes_per_launch": dt["alg_bytes"],
+                                      "launch_us": round(dt["per_launch"] * 1e6, 2)}},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
                           "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),
