@@ -65,17 +65,17 @@ constexpr int FRAG = 1024;
 // state side (S, D) is an fp16 hi/lo pair.  fp16 keeps 11 significant bits,
 // and every one of these operands is bounded: Qg' by |q_hat|, P' by
 // |q_hat||k_hat|, Ke = k e^{G_last - G} by |k|, Psi' by the scaled inverse.
-// X' diag(rk beta), which multiplies the bf16 values V, stays a bf16 hi/lo
-// pair.
+// X' diag(rk beta) is single fp16 too; the scan multiplies it by V taken to
+// fp16 (exact for bf16 values in fp16's normal range).
 // X' and P' are lower triangular: only the six (R, s) blocks with
 // 32 s <= 16 R + 15 are stored (tri_block).
 constexpr int REC_NPSI = 0;                   // -Psi' : [R 4][s 4] fragments, fp16
 constexpr int REC_QG = 16 * FRAG;             // Qg'   : [R 4][s 4], fp16
 constexpr int REC_KE = 32 * FRAG;             // Ke^T  : [channel block 8][s 2], fp16
-constexpr int REC_X = 48 * FRAG;              // X' diag(rk beta) : [tri 6][hi/lo], bf16
-constexpr int REC_P = 60 * FRAG;              // P'    : [tri 6], fp16
-constexpr int REC_VEC = 66 * FRAG;            // fp32 e^{G_last}[128]
-constexpr int REC_BYTES = REC_VEC + D * 4;    // 68096
+constexpr int REC_X = 48 * FRAG;              // X' diag(rk beta) : [tri 6], fp16
+constexpr int REC_P = 54 * FRAG;              // P'    : [tri 6], fp16
+constexpr int REC_VEC = 60 * FRAG;            // fp32 e^{G_last}[128]
+constexpr int REC_BYTES = REC_VEC + D * 4;    // 61952
 
 // ---- prep_kernel LDS map (bytes) ----
 constexpr int PW = C * SW * 2;                 // 17408: [64][SW] bf16
@@ -309,7 +309,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     // waiting for the prefetch never waits for them (loads and stores retire
     // in issue order).  The last item's fragments go out after the loop.
     auto frags_out = [&](unsigned char* rec, int tid) {
-        for (int f = tid; f < 34 * 64; f += PNT) {
+        for (int f = tid; f < 28 * 64; f += PNT) {
             const int fr = f >> 6, ln = f & 63;
             const int li = ln & 15, ka = 4 * (ln >> 4);
             if (fr < 16) {  // -Psi' [R][s], fp16: -Psi'[16R + li][32s + k] = -Psi'^T[32s + k][16R + li]
@@ -317,13 +317,14 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                 const floatx8 x = bf8_to_f(col8_tr2(smem, P_PTH, SN, r0, r0 + 16, 16 * R, li)) +
                                   bf8_to_f(col8_tr2(smem, P_PTL, SN, r0, r0 + 16, 16 * R, li));
                 *reinterpret_cast<halfx8*>(rec + REC_NPSI + fr * FRAG + ln * 16) = __builtin_convertvector(-x, halfx8);
-            } else if (fr < 28) {  // X' diag(rk beta) [tri][hl], bf16: X'^T[32s + k][16R + li]
-                const int f2 = fr - 16, b = f2 >> 1, hl = f2 & 1;
+            } else if (fr < 22) {  // X' diag(rk beta) [tri], fp16: X'^T[32s + k][16R + li]
+                const int b = fr - 16;
                 const int R = tri_R(b), r0 = 32 * tri_s(b) + ka;
-                *reinterpret_cast<bf16x8*>(rec + REC_X + f2 * FRAG + ln * 16) =
-                    col8_tr2(smem, hl ? P_XTL : P_XTH, SN, r0, r0 + 16, 16 * R, li);
+                const floatx8 x = bf8_to_f(col8_tr2(smem, P_XTH, SN, r0, r0 + 16, 16 * R, li)) +
+                                  bf8_to_f(col8_tr2(smem, P_XTL, SN, r0, r0 + 16, 16 * R, li));
+                *reinterpret_cast<halfx8*>(rec + REC_X + b * FRAG + ln * 16) = __builtin_convertvector(x, halfx8);
             } else {  // P' [tri], fp16, from the row-major hi/lo planes
-                const int b = fr - 28, R = tri_R(b);
+                const int b = fr - 22, R = tri_R(b);
                 const int o = ((16 * R + li) * SN + 32 * tri_s(b) + ka) * 2;
                 const bf16x4 h0 = ld4(smem, P_PH + o), h1 = ld4(smem, P_PH + o + 32);
                 const bf16x4 q0 = ld4(smem, P_PL + o), q1 = ld4(smem, P_PL + o + 32);
@@ -735,7 +736,7 @@ constexpr int SB_KE = 16 * FRAG;               // Ke^T [w 8][s 2]
 // LDS regions, each its own array: the compiler then sees that the direct
 // loads into one region do not write the others, and waits only where needed.
 constexpr int SB_BYTES = 32 * FRAG;            // one of three state buffers (chunk mod 3)
-constexpr int XV_X = 0, XV_V = 12 * FRAG;      // X' buffers: X' [tri 6][hl 2], V rows [64][16 NT] bf16,
+constexpr int XV_X = 0, XV_V = 6 * FRAG;       // X' buffers: X' [tri 6] fp16, V rows [64][16 NT] bf16,
                                                // then e^{G_last} [128] fp32 (the copy fills 1 KiB)
 constexpr int DG_D = 0;                        // two slots: Delta0 of tile t (accumulator layout) at 4t fragments,
                                                // then e^{G_last} [128] fp32
@@ -988,18 +989,15 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     } else if (wave == NT) {
         // ================= Delta0 wave =================
         // X', V rows and e^{G_last} of chunk j into X' buffer xb.
-        const int xrot = unit % 3;
+        const int xrot = unit % 6;
         auto fetch_xv = [&](int xb, int j, int lane) {
             lds_u8* xv = (lds_u8*)(xb ? lds_xv1 : lds_xv0);
             const unsigned char* rec = rec_of(j) + lane * 16;
-            // three 4 KiB groups, in an order rotated by the unit
+            // six 1 KiB fragments, in an order rotated by the unit
 #pragma unroll
-            for (int i = 0; i < 3; ++i) {
-                const int f = 4 * ((i + xrot) % 3);
+            for (int i = 0; i < 6; ++i) {
+                const int f = (i + xrot) % 6;
                 copy16_to_lds<0>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
-                copy16_to_lds<1024>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
-                copy16_to_lds<2048>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
-                copy16_to_lds<3072>(rec + REC_X + f * FRAG, xv + XV_X + f * FRAG);
             }
             // V rows of the unit's 16 NT columns, 2 NT lanes per row (8 columns
             // each), 32 / NT rows per copy; rows past the chunk's end read as zero
@@ -1023,11 +1021,12 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
                 *reinterpret_cast<const floatx2*>(xv + SS::XV_GL + lane * 8);
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                bf16x8 vb[2];
+                halfx8 vb[2];
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
                     const int r0 = 32 * s + 4 * g;
-                    vb[s] = col8_tr2(xv, XV_V, NT * DVT, r0, r0 + 16, DVT * t, l16);
+                    vb[s] = __builtin_convertvector(bf8_to_f(col8_tr2(xv, XV_V, NT * DVT, r0, r0 + 16, DVT * t, l16)),
+                                                    halfx8);
                 }
                 floatx4 Dm[4];
 #pragma unroll
@@ -1035,11 +1034,9 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
 #pragma unroll
                 for (int s = 0; s < 2; ++s)
 #pragma unroll
-                    for (int hl = 0; hl < 2; ++hl)
-#pragma unroll
-                        for (int m = 0; m < 4; ++m)
-                            if (s < (m < 2 ? 1 : 2))
-                                Dm[m] = mma(ld8(xv, XV_X + (2 * tri_block(m, s) + hl) * FRAG + lo16), vb[s], Dm[m]);
+                    for (int m = 0; m < 4; ++m)
+                        if (s < (m < 2 ? 1 : 2))
+                            Dm[m] = mmah(ldh8(xv, XV_X + tri_block(m, s) * FRAG + lo16), vb[s], Dm[m]);
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
                     *reinterpret_cast<floatx4*>(dg + DG_D + (4 * t + m) * FRAG + lo16) = Dm[m];

@@ -139,8 +139,8 @@ const char *kda_last_error(void);
  * the workspace, then a short scan carries the state across chunks.  The size
  * is 4 * (2N + 1) bytes (chunk offsets and the order the scan takes the
  * sequences in) rounded up to a multiple of 256, plus
- * 68096 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 1 KiB per
- * token and head).  Other configurations keep everything on chip and need 0.
+ * 61952 bytes per (chunk, head) for ceil(T / 64) + N chunks (about 0.95 KiB
+ * per token and head).  Other configurations keep everything on chip and need 0.
  */
 size_t kda_chunk_fwd_workspace_bytes(const kda_problem_t *problem);
 

@@ -156,7 +156,7 @@ def test_chunk_fwd_empty_batch_is_a_noop():
 
 
 # bytes of one (chunk, head) record of the two-pass bf16 path
-REC_BYTES = 68096
+REC_BYTES = 61952
 
 
 def test_workspace_query():
