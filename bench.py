@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
 KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
@@ -282,6 +283,7 @@ def main():
     print(f"decode, transposed states: {dt['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr,
           flush=True)
     dt_achieved = dt["alg_bytes"] / dt["per_launch"] / 1e9
+    dt_tr = measured_traffic("decode_dv_dk")
     vf = bench_verify(args.steps, args.warmup)
     ph = bench_prefill(args.steps, args.warmup, per_head=True)
     print(f"per-head prefill: {ph['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
@@ -341,7 +343,9 @@ def main():
                          "steps_per_s": round(dt["launches"] / dt["wall"], 1),
                          "roofline": {"kernel": "decode_step_kernel (state_layout dv_dk)", "bound": "hbm",
                                       "achieved": round(dt_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                      "frac": round(dt_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                      "frac": round(dt_achieved / HBM_PEAK_GBS, 4),
+                                      "traffic": None if dt_tr is None else round(dt_tr / dt["per_launch"] / 1e9, 2),
+                                      "traffic_bytes_per_launch": dt_tr,
                                       "alg_bytes_per_launch": dt["alg_bytes"],
                                       "launch_us": round(dt["per_launch"] * 1e6, 2)}},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
