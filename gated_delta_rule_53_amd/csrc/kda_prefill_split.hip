@@ -748,9 +748,9 @@ constexpr int XCH_TILE = 6 * FRAG;
 
 template <int NT>
 struct ScanShape {
-    // With one tile the X' buffer is doubled, so the Delta0 wave forms Delta0
-    // from a copy made a whole chunk earlier; with two there is no room.
-    static constexpr int XVB = NT == 1 ? 2 : 1;
+    // X' buffers: with one tile three, so the Delta0 wave forms Delta0 from a
+    // copy requested two chunks earlier; with two tiles two (one chunk earlier).
+    static constexpr int XVB = NT == 1 ? 3 : 2;
     static constexpr int XV_GL = XV_V + C * NT * DVT * 2;
     static constexpr int XV_BYTES = XV_GL + FRAG;
     static constexpr int DG_GL = NT * 4 * FRAG;
@@ -775,7 +775,8 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
     // the X' buffers are separate arrays, so the compiler sees that a copy
     // into one does not write what is being read from the other
     __shared__ __align__(16) unsigned char lds_xv0[SS::XV_BYTES];
-    __shared__ __align__(16) unsigned char lds_xv1[SS::XVB == 2 ? SS::XV_BYTES : 16];
+    __shared__ __align__(16) unsigned char lds_xv1[SS::XV_BYTES];
+    __shared__ __align__(16) unsigned char lds_xv2[SS::XVB == 3 ? SS::XV_BYTES : 16];
     __shared__ __align__(16) unsigned char lds_dg[2 * DG_SLOT];
     __shared__ __align__(16) unsigned char lds_xch[2 * XCH_SLOT];
     __shared__ __align__(16) unsigned char lds_touch[256];  // sink of the L2 touches, never read
@@ -991,7 +992,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         // X', V rows and e^{G_last} of chunk j into X' buffer xb.
         const int xrot = unit % 6;
         auto fetch_xv = [&](int xb, int j, int lane) {
-            lds_u8* xv = (lds_u8*)(xb ? lds_xv1 : lds_xv0);
+            lds_u8* xv = (lds_u8*)(xb == 0 ? lds_xv0 : xb == 1 ? lds_xv1 : lds_xv2);
             const unsigned char* rec = rec_of(j) + lane * 16;
             // six 1 KiB fragments, in an order rotated by the unit
 #pragma unroll
@@ -1014,7 +1015,7 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         // Delta0 = X' diag(rk beta) V of every tile from X' buffer xb into slot
         // p, and e^{G_last} along with it.
         auto delta0 = [&](int xb, int p, int lane) {
-            const unsigned char* xv = xb ? lds_xv1 : lds_xv0;
+            const unsigned char* xv = xb == 0 ? lds_xv0 : xb == 1 ? lds_xv1 : lds_xv2;
             const int l16 = lane & 15, g = lane >> 4, lo16 = lane * 16;
             unsigned char* dg = lds_dg + p * DG_SLOT;
             *reinterpret_cast<floatx2*>(dg + DG_GL + lane * 8) =
@@ -1044,56 +1045,53 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
         };
         // Chunks 0 and 1 before the first barrier; then in step j (while the
         // state wave runs chunk j+1) chunk j+2 into slot j mod 2, last read by
-        // the state wave in step j.  With two X' buffers chunk j+2 was copied
-        // in step j-1 (into buffer j mod 2), and chunk j+3 is requested once
-        // its Delta0 is formed, into the buffer chunk j+1 has left.
-        if constexpr (SS::XVB == 2) {
+        // the state wave in step j.  Chunk c's X', V rows and e^{G_last} are in
+        // X' buffer c mod XVB.  With three buffers chunk j+2 was requested in
+        // step j-2 and chunk j+4 is requested once chunk j+2's Delta0 is
+        // formed, into the buffer chunk j+1 has left; with two, chunk j+2 was
+        // requested in step j-1 and chunk j+3 follows.  Past the end the last
+        // chunk is requested again into a buffer that is not read any more (no
+        // branch, so no join merges the copies' wait state).  Requesting before
+        // forming Delta0 was measured slower: the copies then meet the output
+        // wave's loads in the memory queue.
+        constexpr int XVB = SS::XVB;
+        constexpr int XV_COPIES = 6 + 2 * NT + 1;  // copy instructions per fetch_xv
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                if (j < nc) fetch_xv(j, j, lane0);
-            wait_vmcnt<0>();
+        for (int j = 0; j < XVB; ++j)
+            if (j < nc) fetch_xv(j, j, lane0);
+        wait_vmcnt<0>();
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-                if (j < nc) delta0(j, j, lane0);
-            // the reads of buffer 0 are done before the copy into it is issued
-            __builtin_amdgcn_s_waitcnt(0xC07F);
-            if (2 < nc) fetch_xv(0, 2, lane0);
-        } else {
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                if (j < nc) {
-                    fetch_xv(0, j, lane0);
-                    wait_vmcnt<0>();
-                    delta0(0, j, lane0);
-                }
-            }
-        }
+        for (int j = 0; j < 2; ++j)
+            if (j < nc) delta0(j, j, lane0);
+        // the reads of buffer 0 are done before the copy into it is issued
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        if (XVB < nc) fetch_xv(0, XVB, lane0);
         lds_barrier();
-        auto step = [&](int p, int lane, int j) {
+        // step j with its buffers as constants: Delta0 of chunk j+2 from buffer
+        // (j+2) mod XVB, then chunk j+XVB+1 requested into buffer (j+1) mod XVB
+        auto step = [&](int p, int lane, int j, int rb, int wb) {
             if (j + 2 < nc) {
-                if constexpr (SS::XVB == 2) {
-                    // Form chunk j+2's Delta0, then request chunk j+3 (past the end,
-                    // the last chunk again: the buffer it lands in is not read any
-                    // more; no branch, so no join merges the copies' wait state).
-                    // Requesting first was measured slower: the copies then meet
-                    // the output wave's loads in the memory queue.
+                if constexpr (XVB == 3)
+                    wait_vmcnt<XV_COPIES>();
+                else
                     wait_vmcnt<0>();
-                    delta0(p, p, lane);
-                    fetch_xv(1 - p, min(j + 3, nc - 1), lane);
-                } else {
-                    fetch_xv(0, j + 2, lane);
-                    wait_vmcnt<0>();
-                    delta0(0, p, lane);
-                }
+                delta0(rb, p, lane);
+                fetch_xv(wb, min(j + XVB + 1, nc - 1), lane);
             }
         };
-        for (int j = 0; j < nc; j += 2) {
+        constexpr int U = 2 * XVB;  // steps per loop pass: slot parity and buffer index both repeat
+        const int nce = (nc + 1) & ~1;  // barriers the other waves run after the first
+        for (int j = 0; j < nce; j += U) {
             const int lane = opaque(lane0);
-            lds_barrier();
-            step(0, lane, j);
-            lds_barrier();
-            step(1, lane, j + 1);
+#pragma unroll
+            for (int k = 0; k < U; ++k) {
+                if (j + k < nce) {
+                    lds_barrier();
+                    step(k & 1, lane, j + k, (k + 2) % XVB, (k + 1) % XVB);
+                }
+            }
         }
+        wait_vmcnt<0>();
     } else {
         // ================= output wave =================
         struct Ops {
