@@ -190,6 +190,36 @@ def bench_decode(loops: int, state_layout: str = "dk_dv"):
     return dict(x=x, wall=wall, per_launch=per, launches=n, alg_bytes=alg_bytes, num_seqs=N)
 
 
+EPILOGUE_BYTES_PER_ROW = 3 * 128 * 2   # o and gate read, y written, bf16
+
+
+def bench_epilogue(steps: int, warmup: int):
+    """kda_gated_rmsnorm on the core's output shape: T=4096, H=32, dv=128, bf16 in and out."""
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+
+    T, H, dv = 4096, 32, 128
+    gen = torch.Generator().manual_seed(3)
+    dev = "cuda:0"
+    copies = []
+    for _ in range(3):
+        copies.append(dict(o=torch.randn((T, H, dv), generator=gen).to(torch.bfloat16).to(dev),
+                           g=torch.randn((T, H, dv), generator=gen).to(torch.bfloat16).to(dev),
+                           y=torch.empty((T, H, dv), dtype=torch.bfloat16, device=dev)))
+    w = torch.ones(dv, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def one(i):
+        c = copies[i % 3]
+        kda.gated_rmsnorm(c["o"], c["g"], w, eps=1e-6, out=c["y"])
+
+    for i in range(warmup):
+        one(i)
+    wall, per = time_launches(one, steps, stream)
+    return dict(wall=wall, per_launch=per, alg_bytes=T * H * EPILOGUE_BYTES_PER_ROW, tokens=T)
+
+
 VERIFY_WIDTH = 4
 
 
@@ -293,6 +323,9 @@ def main():
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     v_tr = measured_traffic("verify_decode")
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    ep = bench_epilogue(args.steps, args.warmup)
+    print(f"gated rmsnorm epilogue: {ep['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    ep_achieved = ep["alg_bytes"] / ep["per_launch"] / 1e9
     gp = bench_prefill_gated(args.steps, args.warmup)
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     g_achieved = gp["alg_bytes"] / gp["per_launch"] / 1e9
@@ -348,6 +381,13 @@ def main():
                                       "traffic_bytes_per_launch": dt_tr,
                                       "alg_bytes_per_launch": dt["alg_bytes"],
                                       "launch_us": round(dt["per_launch"] * 1e6, 2)}},
+        "epilogue": {"workload": "gated_rmsnorm_T4096_H32_dv128_bf16",
+                     "tokens_per_s": round(ep["tokens"] * args.steps / ep["wall"], 1),
+                     "roofline": {"kernel": "gated_rmsnorm_kernel", "bound": "hbm",
+                                  "achieved": round(ep_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(ep_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "alg_bytes_per_launch": ep["alg_bytes"],
+                                  "launch_us": round(ep["per_launch"] * 1e6, 2)}},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
                           "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),

@@ -21,6 +21,7 @@ from ._binding import (  # noqa: F401
     chunk_fwd_gated,
     chunk_fwd_pooled,
     chunk_fwd_workspace_bytes,
+    gated_rmsnorm,
     library_path,
     raw_library,
     recurrent_step,
@@ -35,6 +36,7 @@ __all__ = [
     "recurrent_step_gated",
     "chunk_fwd_pooled",
     "recurrent_verify",
+    "gated_rmsnorm",
     "Gate",
     "chunk_fwd_workspace_bytes",
     "abi_version",

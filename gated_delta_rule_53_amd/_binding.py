@@ -89,6 +89,8 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_pooled.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [P, i32, G, vp, vp, vp, vp, vp, fp, i32, vp, vp, vp, vp]
     lib.kda_recurrent_verify.restype = ctypes.c_int
+    lib.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, fp, ctypes.c_float, vp, vp]
+    lib.kda_gated_rmsnorm.restype = ctypes.c_int
     return lib
 
 
@@ -467,4 +469,31 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, None if gate is None else ctypes.byref(gate), _ptr(q),
                                      _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
                                      _ptr(state_indices), _ptr(num_accepted), _ptr(out), _stream(dev)))
+    return out
+
+
+def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, eps: float = 1e-6,
+                  out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Output epilogue (``kda_gated_rmsnorm``): o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate).
+
+    o, gate [..., dv] (float32 or bfloat16, one dtype, same shape); weight [dv]
+    float32.  Returns out [..., dv] in ``out_dtype`` (default: o's dtype);
+    ``out`` may be ``o`` itself when the dtypes match.
+    """
+    dev = o.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    if o.dim() < 1:
+        raise KdaArgumentError(2, "o must have a trailing value dimension")
+    dv = o.shape[-1]
+    _need(o, "o", tuple(o.shape), None, dev)
+    _need(gate, "gate", tuple(o.shape), o.dtype, dev)
+    _need(weight, "weight", (dv,), torch.float32, dev)
+    out_dtype = o.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty(o.shape, dtype=out_dtype, device=dev)
+    _need(out, "out", tuple(o.shape), out_dtype, dev)
+    rows = o.numel() // dv if dv else 0
+    _check(_lib.kda_gated_rmsnorm(rows, dv, _dtype_code(o.dtype), _dtype_code(out_dtype), _ptr(o), _ptr(gate),
+                                  _ptr(weight), float(eps), _ptr(out), _stream(dev)))
     return out

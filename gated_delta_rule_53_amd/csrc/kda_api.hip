@@ -317,4 +317,37 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     return finish(kda::launch_verify(a, s), s, what);
 }
 
+kda_status_t kda_gated_rmsnorm(int64_t rows, int32_t head_v, int32_t in_dtype, int32_t out_dtype, const void* o,
+                               const void* gate, const float* weight, float eps, void* out, void* stream) {
+    const char* what = "kda_gated_rmsnorm";
+    if (rows < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: rows = %lld < 0", what, (long long)rows);
+    if (head_v != 64 && head_v != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: head_v %d (supported: 64, 128)", what, head_v);
+    if (in_dtype != KDA_F32 && in_dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: in_dtype %d", what, in_dtype);
+    if (out_dtype != KDA_F32 && out_dtype != KDA_BF16)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: out_dtype %d", what, out_dtype);
+    if (!(eps >= 0.f && eps < 1e30f)) return fail(KDA_ERR_BAD_SHAPE, "%s: eps must be finite and >= 0", what);
+    if (rows > (int64_t(1) << 40)) return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    if (rows == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!o || !gate || !weight || !out)
+        return fail(KDA_ERR_NULL_POINTER, "%s: o, gate, weight and out are required", what);
+    if (out == o && in_dtype != out_dtype)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: out may be o only with out_dtype == in_dtype", what);
+    kda::EpilogueArgs a{};
+    a.o = o;
+    a.gate = gate;
+    a.weight = weight;
+    a.eps = eps;
+    a.out = out;
+    a.rows = rows;
+    a.head_v = head_v;
+    a.in_bf16 = in_dtype == KDA_BF16;
+    a.out_bf16 = out_dtype == KDA_BF16;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_gated_rmsnorm(a, s), s, what);
+}
+
 }  // extern "C"

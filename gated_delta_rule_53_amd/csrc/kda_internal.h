@@ -85,7 +85,21 @@ struct PrefillArgs {
     int l2norm;
 };
 
+// Output epilogue: gated RMSNorm over rows of head_v values.
+struct EpilogueArgs {
+    const void* o;
+    const void* gate;
+    const float* weight;
+    float eps;
+    void* out;
+    int64_t rows;
+    int head_v;
+    bool in_bf16;
+    bool out_bf16;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_gated_rmsnorm(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // fp32 q/k/v, or dk = dv = 64: one workgroup per (sequence, head, 16-column
 // tile) carries the state through the chunks with everything on chip.

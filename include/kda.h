@@ -279,6 +279,30 @@ kda_status_t kda_recurrent_verify(const kda_problem_t *problem, int32_t width, c
                                   const int32_t *state_indices, const int32_t *num_accepted, void *out,
                                   void *stream);
 
+/*
+ * Output epilogue of the layer: gated RMSNorm over the value channels.  The
+ * Ascend model file's attention output path (`_project_out`, with the
+ * `KimiRMSNorm` o_norm over head_dim) maps each (token, head) row of the core
+ * output o, of length dv, to
+ *     y = o / sqrt(mean(o^2) + eps) * weight * sigmoid(gate)
+ * with eps inside the root, one weight per value channel and the output-gate
+ * projection `gate` of the same shape as o.  Computed in float32 and rounded
+ * once to out_dtype (the page rounds its intermediate products to the
+ * activation dtype; that is not modelled).
+ *
+ *   rows      number of (token, head) rows: T * H (>= 0; 0 is a no-op)
+ *   head_v    dv, 64 or 128
+ *   in_dtype  kda_dtype_t of o and gate; out_dtype that of out
+ *   o, gate   [rows, dv] (i.e. [T, H, dv] contiguous), device
+ *   weight    [dv] float32, device
+ *   eps       finite, >= 0 (the layer's rms_norm_eps)
+ *   out       [rows, dv] out_dtype, device; may be o itself when out_dtype ==
+ *             in_dtype (each row is read in full before it is written)
+ * Errors: KDA_ERR_BAD_SHAPE / _UNSUPPORTED / _NULL_POINTER before any launch.
+ */
+kda_status_t kda_gated_rmsnorm(int64_t rows, int32_t head_v, int32_t in_dtype, int32_t out_dtype, const void *o,
+                               const void *gate, const float *weight, float eps, void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

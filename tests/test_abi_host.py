@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "kda_abi_version", "kda_status_string", "kda_last_error",
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
-        "kda_recurrent_verify"])
+        "kda_recurrent_verify", "kda_gated_rmsnorm"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -336,3 +336,31 @@ def test_binding_rejects_unknown_state_layout():
     assert _layout_code("dk_dv") == 0 and _layout_code("dv_dk") == 1
     with pytest.raises(KdaArgumentError):
         _layout_code("transposed")
+
+
+def _norm(rows=8, head_v=128, in_dtype=1, out_dtype=0, o=FAKE, gate=FAKE, weight=FAKE, eps=1e-6, out=None):
+    lib = kda.raw_library()
+    out = ctypes.c_void_p(0x2000) if out is None else out
+    st = lib.kda_gated_rmsnorm(rows, head_v, in_dtype, out_dtype, o, gate, weight, eps, out, None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(rows=-1), 2, "rows"),
+    (dict(head_v=96), 3, "head_v 96"),
+    (dict(in_dtype=5), 3, "in_dtype"),
+    (dict(out_dtype=5), 3, "out_dtype"),
+    (dict(eps=-1.0), 2, "eps"),
+    (dict(eps=float("nan")), 2, "eps"),
+    (dict(gate=None), 1, "required"),
+    (dict(weight=None), 1, "required"),
+    (dict(out=FAKE, in_dtype=1, out_dtype=0), 2, "out may be o"),
+])
+def test_gated_rmsnorm_rejects_before_launch(kw, status, needle):
+    st, msg = _norm(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_gated_rmsnorm_zero_rows_is_a_noop():
+    st, msg = _norm(rows=0, o=None, gate=None, weight=None, out=None)
+    assert st == 0 and msg == ""
