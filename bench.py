@@ -220,6 +220,35 @@ def bench_epilogue(steps: int, warmup: int):
     return dict(wall=wall, per_launch=per, alg_bytes=T * H * EPILOGUE_BYTES_PER_ROW, tokens=T)
 
 
+def bench_conv(steps: int, warmup: int):
+    """kda_short_conv on the fused q/k/v projection of the prefill workload: T=4096,
+    C = 3 * 32 * 128, 4 taps, bf16, SiLU, one request with a starting state."""
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+
+    T, C, K = 4096, 3 * 32 * 128, 4
+    gen = torch.Generator().manual_seed(4)
+    dev = "cuda:0"
+    copies = [dict(x=torch.randn((T, C), generator=gen).to(torch.bfloat16).to(dev),
+                   y=torch.empty((T, C), dtype=torch.bfloat16, device=dev)) for _ in range(3)]
+    w = (torch.randn((K, C), generator=gen) * 0.5).to(torch.bfloat16).to(dev)
+    cu = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    s0 = torch.zeros((1, K - 1, C), dtype=torch.bfloat16, device=dev)
+    s1 = torch.empty_like(s0)
+    stream = torch.cuda.current_stream()
+
+    def one(i):
+        c = copies[i % 3]
+        kda.short_conv(c["x"], w, cu, s0, out=c["y"], final_state=s1)
+
+    for i in range(warmup):
+        one(i)
+    wall, per = time_launches(one, steps, stream)
+    # x read and y written once; weights and states are negligible
+    return dict(wall=wall, per_launch=per, alg_bytes=2 * T * C * 2, tokens=T)
+
+
 VERIFY_WIDTH = 4
 
 
@@ -323,6 +352,9 @@ def main():
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     v_tr = measured_traffic("verify_decode")
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    cv = bench_conv(args.steps, args.warmup)
+    print(f"short conv prologue: {cv['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
+    cv_achieved = cv["alg_bytes"] / cv["per_launch"] / 1e9
     ep = bench_epilogue(args.steps, args.warmup)
     print(f"gated rmsnorm epilogue: {ep['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     ep_achieved = ep["alg_bytes"] / ep["per_launch"] / 1e9
@@ -381,6 +413,13 @@ def main():
                                       "traffic_bytes_per_launch": dt_tr,
                                       "alg_bytes_per_launch": dt["alg_bytes"],
                                       "launch_us": round(dt["per_launch"] * 1e6, 2)}},
+        "prologue": {"workload": "short_conv_T4096_C12288_K4_bf16_silu",
+                     "tokens_per_s": round(cv["tokens"] * args.steps / cv["wall"], 1),
+                     "roofline": {"kernel": "short_conv_kernel", "bound": "hbm",
+                                  "achieved": round(cv_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                  "frac": round(cv_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "alg_bytes_per_launch": cv["alg_bytes"],
+                                  "launch_us": round(cv["per_launch"] * 1e6, 2)}},
         "epilogue": {"workload": "gated_rmsnorm_T4096_H32_dv128_bf16",
                      "tokens_per_s": round(ep["tokens"] * args.steps / ep["wall"], 1),
                      "roofline": {"kernel": "gated_rmsnorm_kernel", "bound": "hbm",

@@ -23,6 +23,7 @@ from ._binding import (  # noqa: F401
     chunk_fwd_workspace_bytes,
     gated_rmsnorm,
     library_path,
+    short_conv,
     raw_library,
     recurrent_step,
     recurrent_step_gated,
@@ -37,6 +38,7 @@ __all__ = [
     "chunk_fwd_pooled",
     "recurrent_verify",
     "gated_rmsnorm",
+    "short_conv",
     "Gate",
     "chunk_fwd_workspace_bytes",
     "abi_version",

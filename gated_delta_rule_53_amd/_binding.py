@@ -91,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.kda_recurrent_verify.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, fp, ctypes.c_float, vp, vp]
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
+    lib.kda_short_conv.argtypes = [i32, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
+    lib.kda_short_conv.restype = ctypes.c_int
     return lib
 
 
@@ -497,3 +499,41 @@ def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, 
     _check(_lib.kda_gated_rmsnorm(rows, dv, _dtype_code(o.dtype), _dtype_code(out_dtype), _ptr(o), _ptr(gate),
                                   _ptr(weight), float(eps), _ptr(out), _stream(dev)))
     return out
+
+
+def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None,
+               state: Optional[torch.Tensor] = None, *, silu: bool = True, output_final_state: bool = True,
+               out: Optional[torch.Tensor] = None,
+               final_state: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Short causal convolution before the core (``kda_short_conv``).
+
+    x [T, C] (float32 or bfloat16); weight [K, C] in x's dtype; cu_seqlens
+    [N+1] int32 (None: one request of T tokens); state [N, K-1, C] in x's
+    dtype or None (zeros).  Returns (y [T, C], final state [N, K-1, C] or
+    None).  ``final_state`` may be ``state`` itself when T == N (decode).
+    """
+    dev = x.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    if x.dim() != 2 or weight.dim() != 2:
+        raise KdaArgumentError(2, "x must be [T, C] and weight [K, C]")
+    T, C = x.shape
+    K = weight.shape[0]
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = cu_seqlens.numel() - 1
+    _need(x, "x", (T, C), None, dev)
+    _need(weight, "weight", (K, C), x.dtype, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if state is not None:
+        _need(state, "state", (N, K - 1, C), x.dtype, dev)
+    if out is None:
+        out = torch.empty_like(x)
+    _need(out, "out", (T, C), x.dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, K - 1, C), dtype=x.dtype, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, K - 1, C), x.dtype, dev)
+    _check(_lib.kda_short_conv(N, T, C, K, _dtype_code(x.dtype), int(bool(silu)), _ptr(x), _ptr(weight),
+                               _ptr(cu_seqlens), _ptr(state), _ptr(final_state), _ptr(out), _stream(dev)))
+    return out, final_state

@@ -14,7 +14,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libkda.so")
 
-SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_split.hip", "kda_epilogue.hip"]
+SOURCES = ["kda_api.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_split.hip", "kda_epilogue.hip",
+           "kda_conv.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

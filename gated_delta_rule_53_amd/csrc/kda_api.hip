@@ -317,6 +317,50 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     return finish(kda::launch_verify(a, s), s, what);
 }
 
+kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t channels, int32_t kernel_size,
+                            int32_t dtype, int32_t silu, const void* x, const void* weight,
+                            const int32_t* cu_seqlens, const void* state_in, void* state_out, void* y,
+                            void* stream) {
+    const char* what = "kda_short_conv";
+    if (num_seqs < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: num_seqs = %d < 0", what, num_seqs);
+    if (total_tokens < 0) return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld < 0", what, (long long)total_tokens);
+    if (channels < 8 || channels % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: channels = %d (a positive multiple of 8)", what, channels);
+    if (kernel_size < 1 || kernel_size > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d (supported: 1 to 4)", what, kernel_size);
+    if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d", what, dtype);
+    if (silu != 0 && silu != 1) return fail(KDA_ERR_BAD_SHAPE, "%s: silu must be 0 or 1", what);
+    if (total_tokens > (int64_t(1) << 40) || int64_t(channels) * 8 > (int64_t(1) << 40))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    if (num_seqs == 0) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    if (!cu_seqlens || !weight || (total_tokens > 0 && (!x || !y)))
+        return fail(KDA_ERR_NULL_POINTER, "%s: cu_seqlens, weight, x and y are required", what);
+    if (state_out && state_in == state_out && total_tokens != num_seqs)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: state_out may be state_in only with one token per request", what);
+    if (total_tokens == 0 && !state_out) {
+        g_last_error[0] = '\0';
+        return KDA_OK;
+    }
+    kda::ConvArgs a{};
+    a.x = x;
+    a.weight = weight;
+    a.cu_seqlens = cu_seqlens;
+    a.state_in = state_in;
+    a.state_out = state_out;
+    a.y = y;
+    a.total_tokens = total_tokens;
+    a.num_seqs = num_seqs;
+    a.channels = channels;
+    a.kernel_size = kernel_size;
+    a.bf16 = dtype == KDA_BF16;
+    a.silu = silu == 1;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_short_conv(a, s), s, what);
+}
+
 kda_status_t kda_gated_rmsnorm(int64_t rows, int32_t head_v, int32_t in_dtype, int32_t out_dtype, const void* o,
                                const void* gate, const float* weight, float eps, void* out, void* stream) {
     const char* what = "kda_gated_rmsnorm";

@@ -1,0 +1,192 @@
+// Short causal convolution before the core (the Ascend model file's
+// `KimiShortConvolution`): a depthwise causal convolution over the fused
+// q/k/v projection, one filter of K taps per channel, run per request with a
+// conv-state cache holding each request's last K - 1 inputs.  With the window
+// w = [state (K - 1 inputs, oldest first), x of the request],
+//
+//   y[t, c] = sum_{j < K} W[j, c] * w[t + j, c],   then optionally y * sigmoid(y),
+//
+// and the request's last K - 1 inputs become its state.  Decode is the same
+// call with one token per request.
+//
+// HBM-bound: every input is read once and every output written once.  Launch:
+// a thread owns eight consecutive channels (one 16-byte load of bf16) of a run
+// of TB tokens, issues the run's loads first and keeps the K - 1 previous
+// inputs in registers; a run that crosses into the next request restarts its
+// window from that request's state.  One extra row of workgroups writes the state of empty requests
+// (their initial state, or zeros).
+#include "kda_common.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int TB = 16;  // tokens per thread
+
+template <typename T>
+__device__ __forceinline__ void load8c(float (&v)[8], const T* p) {
+    T r[8];
+    load_vec<8>(r, p);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = to_f32(r[i]);
+}
+
+template <typename T>
+__device__ __forceinline__ void store8c(T* p, const float (&v)[8]) {
+    T r[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(v[i]);
+    constexpr int BYTES = 8 * static_cast<int>(sizeof(T));
+#pragma unroll
+    for (int i = 0; i < BYTES / 16; ++i) reinterpret_cast<uint4*>(p)[i] = reinterpret_cast<const uint4*>(r)[i];
+}
+
+// The request containing token t: the last n with cu[n] <= t < cu[n + 1] (empty requests skipped).
+__device__ __forceinline__ int request_of(const int32_t* cu, int num_seqs, int64_t t) {
+    int lo = 0, hi = num_seqs;  // cu[lo] <= t < cu[hi]
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid; else hi = mid;
+    }
+    return lo;
+}
+
+}  // namespace
+
+template <int K, typename T, bool SILU>
+__global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x, const T* __restrict__ weight,
+                                                         const int32_t* __restrict__ cu, int num_seqs,
+                                                         const T* state_in, T* state_out, T* __restrict__ y,
+                                                         int64_t total_tokens, int channels, int run_rows) {
+    const int c = (static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x)) * 8;
+    if (c >= channels) return;
+    const size_t C = static_cast<size_t>(channels);
+    constexpr int S = K - 1;  // state length
+    auto soff = [&](int n, int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
+
+    if (static_cast<int>(blockIdx.y) == run_rows) {
+        // empty requests keep their state
+        if (!state_out) return;
+        for (int n = 0; n < num_seqs; ++n) {
+            if (cu[n + 1] != cu[n]) continue;
+#pragma unroll
+            for (int m = 0; m < S; ++m) {
+                float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+                if (state_in) load8c(v, state_in + soff(n, m));
+                store8c(state_out + soff(n, m), v);
+            }
+        }
+        return;
+    }
+
+    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * TB;
+    const int64_t t1 = min(t0 + TB, total_tokens);
+    if (t0 >= t1) return;
+    float w[K][8];
+#pragma unroll
+    for (int j = 0; j < K; ++j) load8c(w[j], weight + static_cast<size_t>(j) * C + c);
+
+    int n = request_of(cu, num_seqs, t0);
+    int64_t start = cu[n], end = cu[n + 1];
+    // win[m]: the input m + 1 steps before the current token (m < S)
+    float win[S > 0 ? S : 1][8];
+    auto fill_window = [&](int64_t t) {
+#pragma unroll
+        for (int m = 0; m < S; ++m) {
+            const int64_t p = t - 1 - m;
+            if (p >= start && p >= 0) {
+                load8c(win[m], x + static_cast<size_t>(p) * C + c);
+            } else {
+                // 1 .. S steps before the request (clamped: cu_seqlens is not checked on the device)
+                const int back = static_cast<int>(min(max(start - p, static_cast<int64_t>(1)), static_cast<int64_t>(S)));
+                if (state_in) {
+                    load8c(win[m], state_in + soff(n, S - back));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) win[m][i] = 0.f;
+                }
+            }
+        }
+    };
+    // the run's inputs, loaded raw before any arithmetic (rows past t1 repeat the last row)
+    T xin[TB][8];
+#pragma unroll
+    for (int u = 0; u < TB; ++u) load_vec<8>(xin[u], x + static_cast<size_t>(min(t0 + u, t1 - 1)) * C + c);
+    fill_window(t0);
+#pragma unroll
+    for (int u = 0; u < TB; ++u) {
+        const int64_t t = t0 + u;
+        if (t >= t1) break;
+        if (t >= end) {
+            // the run enters the next non-empty request
+            n = request_of(cu, num_seqs, t);
+            start = cu[n];
+            end = cu[n + 1];
+            fill_window(t);
+        }
+        float cur[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) cur[i] = to_f32(xin[u][i]);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = w[K - 1][i] * cur[i];
+#pragma unroll
+        for (int m = 0; m < S; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += w[K - 2 - m][i] * win[m][i];
+        if constexpr (SILU) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+        }
+        store8c(y + static_cast<size_t>(t) * C + c, acc);
+        // shift: the current input becomes one step back
+#pragma unroll
+        for (int m = S - 1; m > 0; --m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[m][i] = win[m - 1][i];
+        if constexpr (S > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[0][i] = cur[i];
+        }
+        if (t == end - 1 && state_out) {
+            // the request's last S inputs, oldest first
+#pragma unroll
+            for (int m = 0; m < S; ++m) store8c(state_out + soff(n, m), win[S - 1 - m]);
+        }
+    }
+}
+
+template <int K, typename T>
+static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
+    const int run_rows = static_cast<int>((a.total_tokens + TB - 1) / TB);
+    const dim3 grid(static_cast<unsigned>((a.channels / 8 + 255) / 256), static_cast<unsigned>(run_rows + 1));
+    const T* x = static_cast<const T*>(a.x);
+    const T* w = static_cast<const T*>(a.weight);
+    const T* si = static_cast<const T*>(a.state_in);
+    T* so = static_cast<T*>(a.state_out);
+    T* y = static_cast<T*>(a.y);
+    if (a.silu)
+        short_conv_kernel<K, T, true><<<grid, 256, 0, stream>>>(x, w, a.cu_seqlens, a.num_seqs, si, so, y,
+                                                                 a.total_tokens, a.channels, run_rows);
+    else
+        short_conv_kernel<K, T, false><<<grid, 256, 0, stream>>>(x, w, a.cu_seqlens, a.num_seqs, si, so, y,
+                                                                  a.total_tokens, a.channels, run_rows);
+    return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_conv_t(const ConvArgs& a, hipStream_t stream) {
+    switch (a.kernel_size) {
+        case 1: return launch_conv_kt<1, T>(a, stream);
+        case 2: return launch_conv_kt<2, T>(a, stream);
+        case 3: return launch_conv_kt<3, T>(a, stream);
+        default: return launch_conv_kt<4, T>(a, stream);
+    }
+}
+
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream) {
+    return a.bf16 ? launch_conv_t<bf16_t>(a, stream) : launch_conv_t<float>(a, stream);
+}
+
+}  // namespace kda

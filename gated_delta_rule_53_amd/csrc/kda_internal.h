@@ -98,7 +98,24 @@ struct EpilogueArgs {
     bool out_bf16;
 };
 
+// Short causal convolution over [total_tokens, channels] with per-request states.
+struct ConvArgs {
+    const void* x;
+    const void* weight;       // [kernel_size, channels]
+    const int32_t* cu_seqlens;
+    const void* state_in;     // [num_seqs, kernel_size - 1, channels] or null (zeros)
+    void* state_out;          // same shape, or null
+    void* y;
+    int64_t total_tokens;
+    int num_seqs;
+    int channels;
+    int kernel_size;
+    bool bf16;
+    bool silu;
+};
+
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // fp32 q/k/v, or dk = dv = 64: one workgroup per (sequence, head, 16-column

@@ -280,6 +280,37 @@ kda_status_t kda_recurrent_verify(const kda_problem_t *problem, int32_t width, c
                                   void *stream);
 
 /*
+ * Short causal convolution before the core (the Ascend model file's
+ * `KimiShortConvolution`, run on the fused q/k/v projection): a depthwise
+ * causal convolution, one filter of kernel_size taps per channel, per request,
+ * with a conv-state cache holding each request's last kernel_size - 1 inputs.
+ * With the window w = [state (oldest first), the request's inputs],
+ *     y[t, c] = sum_{j < K} weight[j, c] * w[t + j, c]     (the last tap meets the current input)
+ * then, with silu = 1, y * sigmoid(y).  The request's last K - 1 inputs (its
+ * state followed by its inputs when it is shorter) become its final state; an
+ * empty request keeps its state.  Decode is the same call with one token per
+ * request (total_tokens == num_seqs).
+ *
+ *   num_seqs, total_tokens   N >= 0 requests, T >= 0 tokens (N = 0: no-op)
+ *   channels      C, a positive multiple of 8 (e.g. 3 * H * d for fused q/k/v)
+ *   kernel_size   K, 1 to 4
+ *   dtype         kda_dtype_t of x, weight, the states and y
+ *   silu          1: apply y * sigmoid(y); 0: none (the page passes the operator
+ *                 no activation argument, so both are offered)
+ *   x             [T, C] device; cu_seqlens [N + 1] int32 device, 0 = cu[0] <= ... <= cu[N] = T
+ *   weight        [K, C] device (tap-major, the layout the page builds for its operator)
+ *   state_in      [N, K - 1, C] device, or NULL for zeros
+ *   state_out     [N, K - 1, C] device (written), or NULL to skip; may be state_in
+ *                 only when total_tokens == num_seqs
+ *   y             [T, C] device (written)
+ * All device pointers 16-byte aligned.  Errors are found on the host before any launch.
+ */
+kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t channels, int32_t kernel_size,
+                            int32_t dtype, int32_t silu, const void *x, const void *weight,
+                            const int32_t *cu_seqlens, const void *state_in, void *state_out, void *y,
+                            void *stream);
+
+/*
  * Output epilogue of the layer: gated RMSNorm over the value channels.  The
  * Ascend model file's attention output path (`_project_out`, with the
  * `KimiRMSNorm` o_norm over head_dim) maps each (token, head) row of the core

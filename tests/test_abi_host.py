@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "kda_abi_version", "kda_status_string", "kda_last_error",
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
-        "kda_recurrent_verify", "kda_gated_rmsnorm"])
+        "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -363,4 +363,36 @@ def test_gated_rmsnorm_rejects_before_launch(kw, status, needle):
 
 def test_gated_rmsnorm_zero_rows_is_a_noop():
     st, msg = _norm(rows=0, o=None, gate=None, weight=None, out=None)
+    assert st == 0 and msg == ""
+
+
+def _conv(num_seqs=2, total_tokens=10, channels=64, kernel_size=4, dtype=1, silu=1, x=FAKE, weight=FAKE, cu=FAKE,
+          state_in=None, state_out=None, y=FAKE):
+    lib = kda.raw_library()
+    st = lib.kda_short_conv(num_seqs, total_tokens, channels, kernel_size, dtype, silu, x, weight, cu, state_in,
+                            state_out, y, None)
+    return st, lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,needle", [
+    (dict(num_seqs=-1), 2, "num_seqs"),
+    (dict(total_tokens=-1), 2, "total_tokens"),
+    (dict(channels=12), 3, "channels"),
+    (dict(channels=0), 3, "channels"),
+    (dict(kernel_size=5), 3, "kernel_size"),
+    (dict(kernel_size=0), 3, "kernel_size"),
+    (dict(dtype=4), 3, "dtype"),
+    (dict(silu=2), 2, "silu"),
+    (dict(weight=None), 1, "required"),
+    (dict(cu=None), 1, "required"),
+    (dict(y=None), 1, "required"),
+    (dict(state_in=FAKE, state_out=FAKE), 2, "one token per request"),
+])
+def test_short_conv_rejects_before_launch(kw, status, needle):
+    st, msg = _conv(**kw)
+    assert st == status and needle in msg, (st, msg)
+
+
+def test_short_conv_empty_batch_is_a_noop():
+    st, msg = _conv(num_seqs=0, total_tokens=0, x=None, weight=None, cu=None, y=None)
     assert st == 0 and msg == ""
