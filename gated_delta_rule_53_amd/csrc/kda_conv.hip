@@ -22,7 +22,7 @@ namespace kda {
 
 namespace {
 
-constexpr int TB = 16;  // tokens per thread
+constexpr int TB = 8;  // tokens per thread (8 measured best of 8 / 16 / 32 on the bench shape)
 
 template <typename T>
 __device__ __forceinline__ void load8c(float (&v)[8], const T* p) {
@@ -38,8 +38,11 @@ __device__ __forceinline__ void store8c(T* p, const float (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(v[i]);
     constexpr int BYTES = 8 * static_cast<int>(sizeof(T));
+    // non-temporal: nothing here reads y back (measured 57.7 -> 48.3 us on the bench shape)
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 #pragma unroll
-    for (int i = 0; i < BYTES / 16; ++i) reinterpret_cast<uint4*>(p)[i] = reinterpret_cast<const uint4*>(r)[i];
+    for (int i = 0; i < BYTES / 16; ++i)
+        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(r)[i], reinterpret_cast<u32x4*>(p) + i);
 }
 
 // The request containing token t: the last n with cu[n] <= t < cu[n + 1] (empty requests skipped).
