@@ -48,6 +48,8 @@ KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["prologue"] = ["gated_delta_rule_53_amd/csrc/kda_conv.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
+KERNEL_SOURCES["epilogue"] = ["gated_delta_rule_53_amd/csrc/kda_epilogue.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
@@ -355,9 +357,11 @@ def main():
     cv = bench_conv(args.steps, args.warmup)
     print(f"short conv prologue: {cv['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     cv_achieved = cv["alg_bytes"] / cv["per_launch"] / 1e9
+    cv_tr = measured_traffic("prologue")
     ep = bench_epilogue(args.steps, args.warmup)
     print(f"gated rmsnorm epilogue: {ep['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     ep_achieved = ep["alg_bytes"] / ep["per_launch"] / 1e9
+    ep_tr = measured_traffic("epilogue")
     gp = bench_prefill_gated(args.steps, args.warmup)
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     g_achieved = gp["alg_bytes"] / gp["per_launch"] / 1e9
@@ -417,14 +421,18 @@ def main():
                      "tokens_per_s": round(cv["tokens"] * args.steps / cv["wall"], 1),
                      "roofline": {"kernel": "short_conv_kernel", "bound": "hbm",
                                   "achieved": round(cv_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(cv_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "frac": round(cv_achieved / HBM_PEAK_GBS, 4),
+                                  "traffic": None if cv_tr is None else round(cv_tr / cv["per_launch"] / 1e9, 2),
+                                  "traffic_bytes_per_launch": cv_tr,
                                   "alg_bytes_per_launch": cv["alg_bytes"],
                                   "launch_us": round(cv["per_launch"] * 1e6, 2)}},
         "epilogue": {"workload": "gated_rmsnorm_T4096_H32_dv128_bf16",
                      "tokens_per_s": round(ep["tokens"] * args.steps / ep["wall"], 1),
                      "roofline": {"kernel": "gated_rmsnorm_kernel", "bound": "hbm",
                                   "achieved": round(ep_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                                  "frac": round(ep_achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                                  "frac": round(ep_achieved / HBM_PEAK_GBS, 4),
+                                  "traffic": None if ep_tr is None else round(ep_tr / ep["per_launch"] / 1e9, 2),
+                                  "traffic_bytes_per_launch": ep_tr,
                                   "alg_bytes_per_launch": ep["alg_bytes"],
                                   "launch_us": round(ep["per_launch"] * 1e6, 2)}},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
