@@ -27,6 +27,7 @@ from ._binding import (  # noqa: F401
     raw_library,
     recurrent_step,
     recurrent_step_gated,
+    recurrent_step_normed,
     recurrent_verify,
 )
 
@@ -35,6 +36,7 @@ __all__ = [
     "chunk_fwd_gated",
     "recurrent_step",
     "recurrent_step_gated",
+    "recurrent_step_normed",
     "chunk_fwd_pooled",
     "recurrent_verify",
     "gated_rmsnorm",

@@ -93,6 +93,8 @@ def _load() -> ctypes.CDLL:
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [i32, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
     lib.kda_short_conv.restype = ctypes.c_int
+    lib.kda_recurrent_step_normed.argtypes = [P, G, vp, vp, vp, vp, vp, fp, vp, fp, ctypes.c_float, vp, vp]
+    lib.kda_recurrent_step_normed.restype = ctypes.c_int
     return lib
 
 
@@ -537,3 +539,47 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch
     _check(_lib.kda_short_conv(N, T, C, K, _dtype_code(x.dtype), int(bool(silu)), _ptr(x), _ptr(weight),
                                _ptr(cu_seqlens), _ptr(state), _ptr(final_state), _ptr(out), _stream(dev)))
     return out, final_state
+
+
+def recurrent_step_normed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                          beta: torch.Tensor, state: torch.Tensor, out_gate: torch.Tensor,
+                          norm_weight: torch.Tensor, *, norm_eps: float = 1e-6,
+                          a_log: Optional[torch.Tensor] = None, dt_bias: Optional[torch.Tensor] = None,
+                          lower_bound: Optional[float] = None, scale: Optional[float] = None,
+                          state_layout: str = "dk_dv", qk_l2norm: bool = True,
+                          out_dtype: Optional[torch.dtype] = None,
+                          out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """One decode step with the output epilogue fused (``kda_recurrent_step_normed``).
+
+    As ``recurrent_step`` (or ``recurrent_step_gated`` when ``a_log`` and
+    ``dt_bias`` are given, g and beta then being the raw projections), but the
+    returned rows are o / sqrt(mean(o^2) + norm_eps) * norm_weight *
+    sigmoid(out_gate); out_gate [N, H, dv] in q's dtype, norm_weight [dv] float32.
+    """
+    if q.dim() != 3:
+        raise KdaArgumentError(2, f"q must be [N, H, dk], got {tuple(q.shape)}")
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    _need(k, "k", (N, H, dk), q.dtype, dev)
+    _need(v, "v", (N, H, dv), q.dtype, dev)
+    gph, gshape = _gate_shape(g, (N, H), dk)
+    gate = _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev, gph)
+    gdt = torch.float32 if gate is None else q.dtype
+    _need(g, "g", gshape, gdt, dev)
+    _need(beta, "beta", (N, H), gdt, dev)
+    _need(state, "state", (N, H, dk, dv), torch.float32, dev)
+    _need(out_gate, "out_gate", (N, H, dv), q.dtype, dev)
+    _need(norm_weight, "norm_weight", (dv,), torch.float32, dev)
+    out_dtype = v.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((N, H, dv), dtype=out_dtype, device=dev)
+    _need(out, "out", (N, H, dv), out_dtype, dev)
+    prob = _problem(N, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
+    _check(_lib.kda_recurrent_step_normed(ctypes.byref(prob), None if gate is None else ctypes.byref(gate),
+                                          _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state),
+                                          _ptr(out_gate), _ptr(norm_weight), float(norm_eps), _ptr(out),
+                                          _stream(dev)))
+    return out

@@ -137,7 +137,8 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
 
 kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const kda::GateParams& gp,
                                  const void* q, const void* k, const void* v, const void* g,
-                                 const void* beta, float* state, void* out, void* stream) {
+                                 const void* beta, float* state, void* out, void* stream,
+                                 const kda::NormParams& norm = kda::NormParams{}) {
     if (p->total_tokens != p->num_seqs)
         return fail(KDA_ERR_BAD_SHAPE, "%s: total_tokens = %lld must equal num_seqs = %d (one token each)",
                     what, (long long)p->total_tokens, p->num_seqs);
@@ -156,6 +157,7 @@ kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const
     a.gate = gp;
     a.gate_per_head = p->gate_per_head;
     a.state_trans = p->state_layout == KDA_STATE_DV_DK;
+    a.norm = norm;
     a.state = state;
     a.out = out;
     a.num_seqs = p->num_seqs;
@@ -248,6 +250,23 @@ kda_status_t kda_recurrent_step_gated(const kda_problem_t* p, const kda_gate_t* 
     st = check_gate(gate, what, gp);
     if (st != KDA_OK) return st;
     return recurrent_step_impl(what, p, gp, q, k, v, raw_g, raw_beta, state, out, stream);
+}
+
+kda_status_t kda_recurrent_step_normed(const kda_problem_t* p, const kda_gate_t* gate, const void* q,
+                                      const void* k, const void* v, const void* g, const void* beta, float* state,
+                                      const void* out_gate, const float* norm_weight, float norm_eps, void* out,
+                                      void* stream) {
+    const char* what = "kda_recurrent_step_normed";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    const kda::GateParams gp = optional_gate(gate, what, st);
+    if (st != KDA_OK) return st;
+    if (!(norm_eps >= 0.f && norm_eps < 1e30f))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: norm_eps must be finite and >= 0", what);
+    if (p->num_seqs > 0 && (!out_gate || !norm_weight))
+        return fail(KDA_ERR_NULL_POINTER, "%s: out_gate and norm_weight are required", what);
+    return recurrent_step_impl(what, p, gp, q, k, v, g, beta, state, out, stream,
+                               kda::NormParams{out_gate, norm_weight, norm_eps});
 }
 
 kda_status_t kda_chunk_fwd_pooled(const kda_problem_t* p, const kda_gate_t* gate, const void* q, const void* k,

@@ -20,6 +20,8 @@
 // Launch: one 256-thread workgroup per (sequence, head).  Thread (cg, rg)
 // owns value columns 4cg..4cg+3 of rows rg, rg+NRG, ...: every load and store
 // of the state is a float4, and a wave touches whole 512-byte rows.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -35,11 +37,16 @@ __device__ __forceinline__ float group_sum(float x, int G) {
 // 4cg..4cg+3 of value columns rg, rg+NRG, ...: the same float4 addresses, and
 // each column's contraction over the key rows is a sum over the NCG lanes of
 // one lane group, with no exchange between waves.
-template <int D, typename TIn, typename TOut, bool GATED, bool TRANS>
+// NORM: the output epilogue is applied before anything is written: the
+// step's output row (all dv values of one (sequence, head), which this
+// workgroup holds) goes through LDS to wave 0, which writes
+// o / sqrt(mean(o^2) + eps) * weight * sigmoid(out_gate) (the Ascend model
+// file's `_project_out` norm and gate), so o itself never reaches HBM.
+template <int D, typename TIn, typename TOut, bool GATED, bool TRANS, bool NORM>
 __global__ __launch_bounds__(256) void decode_step_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ state,
-    TOut* __restrict__ out, int num_heads, float scale, int l2norm) {
+    TOut* __restrict__ out, int num_heads, float scale, int l2norm, NormParams np) {
     constexpr int NCG = D / 4;      // column groups of four
     constexpr int NRG = 256 / NCG;  // row groups
     constexpr int RPT = D / NRG;    // rows per thread
@@ -60,6 +67,7 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 
     __shared__ float sq[D], sk[D], se[D];
     __shared__ float red[4][NCG][8];
+    __shared__ float so[NORM ? D : 1];  // the output row on its way to the epilogue
     if (tid < D) {
         const size_t off = static_cast<size_t>(pair) * D + tid;
         sq[tid] = to_f32(q[off]);
@@ -112,7 +120,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
             const float delta = b * (to_f32(v[static_cast<size_t>(pair) * D + c]) - u);
             s[i] += (rk * delta) * k4;
             __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + c * D + 4 * cg));
-            if (cg == 0) out[static_cast<size_t>(pair) * D + c] = from_f32<TOut>(p + kq * delta);
+            if (cg == 0) {
+                if constexpr (NORM)
+                    so[c] = p + kq * delta;
+                else
+                    out[static_cast<size_t>(pair) * D + c] = from_f32<TOut>(p + kq * delta);
+            }
         }
     } else {
         // Decay, then the two partial contractions over this thread's rows.
@@ -167,7 +180,27 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
         if (rg == 0) {
             const float kq = rk * rq * aqk;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+            for (int j = 0; j < 4; ++j) {
+                if constexpr (NORM)
+                    so[4 * cg + j] = p[j] + kq * delta[j];
+                else
+                    out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+            }
+        }
+    }
+    if constexpr (NORM) {
+        __syncthreads();
+        if (wave == 0) {
+            float ss = 0.f;
+#pragma unroll
+            for (int c = lane; c < D; c += 64) ss += so[c] * so[c];
+            ss = wave_sum_from(ss, 1);
+            const float r = rsqrtf(ss * (1.f / D) + np.eps);
+            const TIn* og = static_cast<const TIn*>(np.gate) + static_cast<size_t>(pair) * D;
+#pragma unroll
+            for (int c = lane; c < D; c += 64)
+                out[static_cast<size_t>(pair) * D + c] =
+                    from_f32<TOut>(so[c] * r * np.weight[c] * gate_sigmoid(to_f32(og[c])));
         }
     }
 }
@@ -355,11 +388,16 @@ static hipError_t launch_decode_t(const DecodeArgs& a, hipStream_t stream) {
     const TIn* q = static_cast<const TIn*>(a.q);
     const TIn* k = static_cast<const TIn*>(a.k);
     const TIn* v = static_cast<const TIn*>(a.v);
-    auto* kern = a.gate.a_log
-                     ? (a.state_trans ? decode_step_kernel<D, TIn, TOut, true, true> : decode_step_kernel<D, TIn, TOut, true, false>)
-                     : (a.state_trans ? decode_step_kernel<D, TIn, TOut, false, true> : decode_step_kernel<D, TIn, TOut, false, false>);
+    auto pick = [&](auto norm) {
+        constexpr bool N = decltype(norm)::value;
+        return a.gate.a_log ? (a.state_trans ? decode_step_kernel<D, TIn, TOut, true, true, N>
+                                             : decode_step_kernel<D, TIn, TOut, true, false, N>)
+                            : (a.state_trans ? decode_step_kernel<D, TIn, TOut, false, true, N>
+                                             : decode_step_kernel<D, TIn, TOut, false, false, N>);
+    };
+    auto* kern = a.norm.gate ? pick(std::true_type{}) : pick(std::false_type{});
     kern<<<grid, 256, 0, stream>>>(q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.state, static_cast<TOut*>(a.out),
-                                   a.num_heads, a.scale, a.l2norm);
+                                   a.num_heads, a.scale, a.l2norm, a.norm);
     return hipGetLastError();
 }
 

@@ -12,6 +12,14 @@ namespace kda {
 // g and beta are float32 when gate.a_log is null; otherwise they are the raw
 // gate [rows, H, dk] and raw beta [rows, H] in the q/k/v dtype, activated in
 // the kernels.
+// Output epilogue fused into decode: out = o / sqrt(mean(o^2) + eps) * weight
+// * sigmoid(gate); gate null means none.
+struct NormParams {
+    const void* gate;      // [rows, H, dv] in the q/k/v dtype
+    const float* weight;   // [dv]
+    float eps;
+};
+
 struct DecodeArgs {
     const void* q;
     const void* k;
@@ -21,6 +29,7 @@ struct DecodeArgs {
     GateParams gate;
     int gate_per_head;  // g (or the raw gate) is [rows, H]: one decay per head
     int state_trans;    // state blocks are S^T [dv][dk]
+    NormParams norm;
     float* state;
     void* out;
     int num_seqs;

@@ -280,6 +280,25 @@ kda_status_t kda_recurrent_verify(const kda_problem_t *problem, int32_t width, c
                                   void *stream);
 
 /*
+ * kda_recurrent_step (or, with gate non-NULL, kda_recurrent_step_gated) with
+ * the layer's output epilogue fused: the workgroup of a (sequence, head) holds
+ * its whole output row, so
+ *     out = o / sqrt(mean(o^2) + norm_eps) * norm_weight * sigmoid(out_gate)
+ * is written in place of o, which never reaches memory (the Ascend model
+ * file's `_project_out` norm and gate; see kda_gated_rmsnorm).
+ *
+ *   gate        NULL: g and beta are activated float32 values; otherwise the raw
+ *               projections as for kda_recurrent_step_gated
+ *   out_gate    [N, H, dv] in qkv_dtype (device)
+ *   norm_weight [dv] float32 (device); norm_eps finite, >= 0
+ * Everything else as kda_recurrent_step.
+ */
+kda_status_t kda_recurrent_step_normed(const kda_problem_t *problem, const kda_gate_t *gate, const void *q,
+                                      const void *k, const void *v, const void *g, const void *beta,
+                                      float *state, const void *out_gate, const float *norm_weight,
+                                      float norm_eps, void *out, void *stream);
+
+/*
  * Short causal convolution before the core (the Ascend model file's
  * `KimiShortConvolution`, run on the fused q/k/v projection): a depthwise
  * causal convolution, one filter of kernel_size taps per channel, per request,

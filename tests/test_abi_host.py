@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "kda_abi_version", "kda_status_string", "kda_last_error",
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
-        "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv"])
+        "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv", "kda_recurrent_step_normed"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -396,3 +396,18 @@ def test_short_conv_rejects_before_launch(kw, status, needle):
 def test_short_conv_empty_batch_is_a_noop():
     st, msg = _conv(num_seqs=0, total_tokens=0, x=None, weight=None, cu=None, y=None)
     assert st == 0 and msg == ""
+
+
+def test_recurrent_step_normed_rejects_before_launch():
+    lib = kda.raw_library()
+    p = _prob(total_tokens=4, num_seqs=4)
+    st = lib.kda_recurrent_step_normed(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                       1e-6, FAKE, None)
+    assert st == 1 and "out_gate" in lib.kda_last_error().decode()
+    st = lib.kda_recurrent_step_normed(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       -1.0, FAKE, None)
+    assert st == 2 and "norm_eps" in lib.kda_last_error().decode()
+    p = _prob(total_tokens=5, num_seqs=4)
+    st = lib.kda_recurrent_step_normed(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                       1e-6, FAKE, None)
+    assert st == 2 and "one token each" in lib.kda_last_error().decode()
