@@ -39,6 +39,9 @@ kda_status_t finish(hipError_t launch, hipStream_t stream, const char* what) {
     return KDA_OK;
 }
 
+// Vector loads and stores of 16 bytes: a null pointer passes (it is checked where it is required).
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
 // Checks shared by both entry points.  Returns KDA_OK or the first violation.
 kda_status_t check_problem(const kda_problem_t* p, const char* what) {
     if (!p) return fail(KDA_ERR_NULL_POINTER, "%s: problem is NULL", what);
@@ -349,8 +352,11 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t chan
         return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d (supported: 1 to 4)", what, kernel_size);
     if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d", what, dtype);
     if (silu != 0 && silu != 1) return fail(KDA_ERR_BAD_SHAPE, "%s: silu must be 0 or 1", what);
-    if (total_tokens > (int64_t(1) << 40) || int64_t(channels) * 8 > (int64_t(1) << 40))
+    // grid: one workgroup per 8 tokens (x) and per 2048 channels (y)
+    if (total_tokens > (int64_t(1) << 33) || channels > (1 << 26))
         return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    if (!aligned16(x) || !aligned16(weight) || !aligned16(state_in) || !aligned16(state_out) || !aligned16(y))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: x, weight, states and y must be 16-byte aligned", what);
     if (num_seqs == 0) {
         g_last_error[0] = '\0';
         return KDA_OK;
@@ -390,7 +396,10 @@ kda_status_t kda_gated_rmsnorm(int64_t rows, int32_t head_v, int32_t in_dtype, i
     if (out_dtype != KDA_F32 && out_dtype != KDA_BF16)
         return fail(KDA_ERR_UNSUPPORTED, "%s: out_dtype %d", what, out_dtype);
     if (!(eps >= 0.f && eps < 1e30f)) return fail(KDA_ERR_BAD_SHAPE, "%s: eps must be finite and >= 0", what);
-    if (rows > (int64_t(1) << 40)) return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    // grid: one workgroup per 64 rows (dv = 128) or 128 (dv = 64)
+    if (rows > (int64_t(1) << 36)) return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    if (!aligned16(o) || !aligned16(gate) || !aligned16(weight) || !aligned16(out))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: o, gate, weight and out must be 16-byte aligned", what);
     if (rows == 0) {
         g_last_error[0] = '\0';
         return KDA_OK;

@@ -61,14 +61,15 @@ template <int K, typename T, bool SILU>
 __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x, const T* __restrict__ weight,
                                                          const int32_t* __restrict__ cu, int num_seqs,
                                                          const T* state_in, T* state_out, T* __restrict__ y,
-                                                         int64_t total_tokens, int channels, int run_rows) {
-    const int c = (static_cast<int>(blockIdx.x) * 256 + static_cast<int>(threadIdx.x)) * 8;
+                                                         int64_t total_tokens, int channels, int64_t run_rows) {
+    // blockIdx.x: run of TB tokens (the last one writes empty requests' states); blockIdx.y: 2048 channels
+    const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
     if (c >= channels) return;
     const size_t C = static_cast<size_t>(channels);
     constexpr int S = K - 1;  // state length
     auto soff = [&](int n, int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
 
-    if (static_cast<int>(blockIdx.y) == run_rows) {
+    if (static_cast<int64_t>(blockIdx.x) == run_rows) {
         // empty requests keep their state
         if (!state_out) return;
         for (int n = 0; n < num_seqs; ++n) {
@@ -83,7 +84,7 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
         return;
     }
 
-    const int64_t t0 = static_cast<int64_t>(blockIdx.y) * TB;
+    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
     const int64_t t1 = min(t0 + TB, total_tokens);
     if (t0 >= t1) return;
     float w[K][8];
@@ -162,8 +163,8 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
 
 template <int K, typename T>
 static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
-    const int run_rows = static_cast<int>((a.total_tokens + TB - 1) / TB);
-    const dim3 grid(static_cast<unsigned>((a.channels / 8 + 255) / 256), static_cast<unsigned>(run_rows + 1));
+    const int64_t run_rows = (a.total_tokens + TB - 1) / TB;
+    const dim3 grid(static_cast<unsigned>(run_rows + 1), static_cast<unsigned>((a.channels / 8 + 255) / 256));
     const T* x = static_cast<const T*>(a.x);
     const T* w = static_cast<const T*>(a.weight);
     const T* si = static_cast<const T*>(a.state_in);

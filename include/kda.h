@@ -322,7 +322,8 @@ kda_status_t kda_recurrent_step_normed(const kda_problem_t *problem, const kda_g
  *   state_out     [N, K - 1, C] device (written), or NULL to skip; may be state_in
  *                 only when total_tokens == num_seqs
  *   y             [T, C] device (written)
- * All device pointers 16-byte aligned.  Errors are found on the host before any launch.
+ * All device pointers 16-byte aligned (KDA_ERR_BAD_SHAPE otherwise); T <= 2^33,
+ * C <= 2^26.  Errors are found on the host before any launch.
  */
 kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t channels, int32_t kernel_size,
                             int32_t dtype, int32_t silu, const void *x, const void *weight,
@@ -348,6 +349,7 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t chan
  *   eps       finite, >= 0 (the layer's rms_norm_eps)
  *   out       [rows, dv] out_dtype, device; may be o itself when out_dtype ==
  *             in_dtype (each row is read in full before it is written)
+ * All pointers 16-byte aligned (KDA_ERR_BAD_SHAPE otherwise).
  * Errors: KDA_ERR_BAD_SHAPE / _UNSUPPORTED / _NULL_POINTER before any launch.
  */
 kda_status_t kda_gated_rmsnorm(int64_t rows, int32_t head_v, int32_t in_dtype, int32_t out_dtype, const void *o,

@@ -355,6 +355,7 @@ def _norm(rows=8, head_v=128, in_dtype=1, out_dtype=0, o=FAKE, gate=FAKE, weight
     (dict(gate=None), 1, "required"),
     (dict(weight=None), 1, "required"),
     (dict(out=FAKE, in_dtype=1, out_dtype=0), 2, "out may be o"),
+    (dict(gate=ctypes.c_void_p(0x1004)), 2, "16-byte aligned"),
 ])
 def test_gated_rmsnorm_rejects_before_launch(kw, status, needle):
     st, msg = _norm(**kw)
@@ -387,6 +388,7 @@ def _conv(num_seqs=2, total_tokens=10, channels=64, kernel_size=4, dtype=1, silu
     (dict(cu=None), 1, "required"),
     (dict(y=None), 1, "required"),
     (dict(state_in=FAKE, state_out=FAKE), 2, "one token per request"),
+    (dict(x=ctypes.c_void_p(0x1008)), 2, "16-byte aligned"),
 ])
 def test_short_conv_rejects_before_launch(kw, status, needle):
     st, msg = _conv(**kw)
