@@ -875,6 +875,15 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
                 for (int m = 0; m < 4; ++m) fa[m] = fb[m];
                 sh = shn;
                 sl = sln;
+                // A wave hides only about two of its own VALU instructions
+                // under each MFMA: spread the split and the decay over the
+                // block's eight products, reads first.
+                __builtin_amdgcn_sched_group_barrier(0x100, 10, 0);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                    __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);
+                }
                 __builtin_amdgcn_sched_barrier(0);
             }
             KDA_PHASE_MARK(8);
