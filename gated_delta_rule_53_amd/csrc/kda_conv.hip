@@ -62,14 +62,20 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
                                                          const int32_t* __restrict__ cu, int num_seqs,
                                                          const T* state_in, T* state_out, T* __restrict__ y,
                                                          int64_t total_tokens, int channels, int64_t run_rows) {
-    // blockIdx.x: run of TB tokens (the last one writes empty requests' states); blockIdx.y: 2048 channels
+    // blockIdx.y: 2048 channels.  blockIdx.x: a run of TB tokens (run run_rows
+    // writes empty requests' states).  Workgroup ids are dealt to the eight
+    // XCDs in turn, so XCD k (ids = k mod 8) takes the runs [k per, (k+1) per)
+    // in order: the K - 1 rows before a run were fetched into that XCD's L2
+    // by the run before it.
+    const int64_t per = (run_rows + 8) / 8;
+    const int64_t run = static_cast<int64_t>(blockIdx.x & 7) * per + (blockIdx.x >> 3);
     const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
-    if (c >= channels) return;
+    if (c >= channels || run > run_rows) return;
     const size_t C = static_cast<size_t>(channels);
     constexpr int S = K - 1;  // state length
     auto soff = [&](int n, int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
 
-    if (static_cast<int64_t>(blockIdx.x) == run_rows) {
+    if (run == run_rows) {
         // empty requests keep their state
         if (!state_out) return;
         for (int n = 0; n < num_seqs; ++n) {
@@ -84,7 +90,7 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
         return;
     }
 
-    const int64_t t0 = static_cast<int64_t>(blockIdx.x) * TB;
+    const int64_t t0 = run * TB;
     const int64_t t1 = min(t0 + TB, total_tokens);
     if (t0 >= t1) return;
     float w[K][8];
@@ -164,7 +170,8 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
 template <int K, typename T>
 static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
     const int64_t run_rows = (a.total_tokens + TB - 1) / TB;
-    const dim3 grid(static_cast<unsigned>(run_rows + 1), static_cast<unsigned>((a.channels / 8 + 255) / 256));
+    const int64_t per = (run_rows + 8) / 8;  // runs per XCD: 8 per >= run_rows + 1
+    const dim3 grid(static_cast<unsigned>(8 * per), static_cast<unsigned>((a.channels / 8 + 255) / 256));
     const T* x = static_cast<const T*>(a.x);
     const T* w = static_cast<const T*>(a.weight);
     const T* si = static_cast<const T*>(a.state_in);
