@@ -3,9 +3,9 @@
 Outputs: fp32 inputs within 1e-5 of max|oracle|; bf16 outputs (rounded once)
 within one bf16 ulp of each oracle value plus 1e-6 of max|oracle|.  Final
 states are copies of stored inputs and must match exactly.  Cases: requests
-shorter than the filter, empty requests, runs of 16 tokens that cross request
+shorter than the filter, empty requests, runs of 8 tokens that cross request
 boundaries, all filter lengths, with and without a starting state, SiLU on and
-off, decode in place (one token per request), and a split run equal to the
+off, two channel blocks with a few hundred runs, decode in place (one token per request), and a split run equal to the
 whole run bit for bit.
 """
 import numpy as np
@@ -59,6 +59,20 @@ def test_short_conv_matches_oracle(K, dtype, silu, with_state):
     torch.cuda.synchronize()
     ref, ref_s = conv.short_conv(x, w, cu.numpy(), None if s0 is None else s0, silu=silu)
     _check(y, ys if K > 1 else None, ref, ref_s, dtype)
+
+
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+def test_short_conv_two_channel_blocks_many_runs(dtype):
+    """C = 2304 spans two 2048-channel workgroup columns; 3,034 tokens are 380 runs of 8,
+    dealt to the eight XCDs in contiguous ranges, with request boundaries inside runs."""
+    import gated_delta_rule_53_amd as kda
+    lens = [700, 0, 1, 1500, 33, 800]
+    x, w, cu, s0 = _inputs(lens, 2304, 4, dtype, seed=91)
+    announce(f"short_conv C=2304 T={sum(lens)} {dtype}")
+    y, ys = kda.short_conv(dev(x), dev(w), dev(cu), dev(s0), silu=True)
+    torch.cuda.synchronize()
+    ref, ref_s = conv.short_conv(x, w, cu.numpy(), s0, silu=True)
+    _check(y, ys, ref, ref_s, dtype)
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
