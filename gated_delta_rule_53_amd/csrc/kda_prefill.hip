@@ -24,7 +24,11 @@
 //   * exp(G[r]-G[i]) is factored through the start s_B of 16-token blocks:
 //     row side k[r] exp(G[r]-G[s_R]) (<= 1), column side k[i] exp(G[s_I]-G[i])
 //     (>= 1, bounded by one block's decay) and a per-channel block factor
-//     exp(G[s_R]-G[s_I]) (<= 1).  All contractions then run on MFMA.
+//     exp(G[s_R]-G[s_I]) (<= 1).  All contractions then run on MFMA.  A chunk
+//     in which some block's decay exceeds kRefSpan (the column side would
+//     leave the float range) forms A and P exactly instead: for each column
+//     i the vector k[i] exp(G[r]-G[i]) is carried down the rows by products
+//     of exp(g[r]) <= 1, and the state update takes k exp(G[last]-G) directly.
 //   * The state tile lives in MFMA accumulators across the whole chunk chain;
 //     a copy in LDS feeds the (Gamma*K) S and (Gamma*Q) S products.
 //   * A tail chunk is masked, not padded: rows past the sequence end read as
@@ -41,6 +45,9 @@ namespace {
 constexpr int kC = 64;     // chunk length
 constexpr int kDVT = 16;   // value columns per workgroup
 constexpr int kSC = kC + 2;  // LDS row stride of 64x64 matrices (floats)
+// Largest decay (natural log) one 16-token block may span on the factored
+// path: exp(60) is well inside the float32 range.
+constexpr float kRefSpan = 60.f;
 
 __device__ __forceinline__ int pair_index(int R, int I) { return R * (R - 1) / 2 + I; }
 
@@ -233,6 +240,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         }
         __syncthreads();
         KDA_PHASE_MARK(4);
+        int unsafe = 0;
         {
             float carry = 0.f;
             for (int s = 0; s < seg; ++s) carry += sCarry[s * D + c];
@@ -242,9 +250,68 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             for (int i = 0; i < SEGLEN; ++i)
                 if (((seg * SEGLEN + i) & 15) == 0) sB[((seg * SEGLEN + i) >> 4) * D + c] = Gv[i];
             if (seg == NSEG - 1) sGLlog[c] = Gv[SEGLEN - 1];
+            // segments hold whole 16-token blocks: the column-side exponent
+            // G[s_R] - G[r] of every row is known here (NaN counts as unsafe)
+            static_assert(SEGLEN % 16 == 0, "segments of whole blocks");
+#pragma unroll
+            for (int i = 0; i < SEGLEN; ++i)
+                unsafe |= !(Gv[i & ~15] - Gv[i] <= kRefSpan * kLog2e);
         }
-        __syncthreads();
+        // every thread learns whether any channel of the chunk is out of range
+        const bool exact = __syncthreads_or(unsafe) != 0;
         KDA_PHASE_MARK(5);
+        if (exact) {
+            // sKi holds g (log2 units): turn it into e^g in place
+#pragma unroll
+            for (int i = 0; i < SEGLEN; ++i) {
+                float* p = &sKi[(seg * SEGLEN + i) * SD + c];
+                *p = fast_exp2(*p);
+            }
+            __syncthreads();
+            // thread (column i, part): channels part, part + 4, ...; z = k_hat[i]
+            // exp(G[r] - G[i]) per channel, carried from row i down the rows.
+            // With D = 128 the channels go in two passes of 16, to keep z in
+            // registers next to the prefetched chunk; the first pass leaves
+            // its partial sums in sL and sP.
+            constexpr int CH = D / 4, CHP = CH > 16 ? 16 : CH, NP = CH / CHP;
+            const int ic = tid >> 2, part = tid & 3;
+            const float rki = srk[ic];
+            for (int hp = 0; hp < NP; ++hp) {
+                float z[CHP];
+#pragma unroll
+                for (int m = 0; m < CHP; ++m) z[m] = 0.f;
+                for (int r = 0; r < kC; ++r) {
+                    float a = 0.f, p = 0.f;
+#pragma unroll
+                    for (int m = 0; m < CHP; ++m) {
+                        const int o = r * SD + 4 * (hp * CHP + m) + part;
+                        const float kr = sKl[o];
+                        z[m] = r == ic ? kr * rki : z[m] * sKi[o];
+                        a += kr * z[m];
+                        p += sQl[o] * z[m];
+                    }
+                    a += __shfl_xor(a, 1, 64);
+                    a += __shfl_xor(a, 2, 64);
+                    p += __shfl_xor(p, 1, 64);
+                    p += __shfl_xor(p, 2, 64);
+                    if (part == 0) {
+                        const int o = r * kSC + ic;
+                        if (hp > 0) {
+                            a += sL[o];
+                            p += sP[o];
+                        }
+                        if (hp + 1 < NP) {
+                            sL[o] = a;
+                            sP[o] = p;
+                        } else {
+                            sL[o] = ic < r ? sbeta[r] * srk[r] * a : (ic == r ? 1.f : 0.f);
+                            sP[o] = ic <= r ? srq[r] * p : 0.f;
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+        }
 
         // ---- scaled operands and per-channel block factors ----
 #pragma unroll
@@ -254,7 +321,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
             const float kk = sKl[r * SD + c] * srk[r];
             const float qq = sQl[r * SD + c] * srq[r];
             const float e = fast_exp2(Gv[i] - Bv);
-            const float einv = fast_exp2(Bv - Gv[i]);
+            // exact path: k exp(G[last] - G), for the state update only
+            const float einv = fast_exp2(exact ? sGLlog[c] - Gv[i] : Bv - Gv[i]);
             sKl[r * SD + c] = kk * e;
             sQl[r * SD + c] = qq * e;
             sKi[r * SD + c] = kk * einv;
@@ -270,7 +338,7 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
         if (seg == NSEG - 1) {
             const float gl = sGLlog[c];
 #pragma unroll
-            for (int R = 0; R < 4; ++R) sFL[R * D + c] = fast_exp2(gl - sB[R * D + c]);
+            for (int R = 0; R < 4; ++R) sFL[R * D + c] = exact ? 1.f : fast_exp2(gl - sB[R * D + c]);
             sGL[c] = fast_exp2(gl);
         }
         __syncthreads();
@@ -288,8 +356,8 @@ __global__ __launch_bounds__(256) void prefill_chunk_kernel(
                 Oq = mfma_f32_16x16x4(sQl[r * SD + cc] * gam, bS, Oq);
             }
         }
-        // ---- A and P, block pairs (R, I <= R) spread over the waves ----
-        for (int pi = wave; pi < 10; pi += 4) {
+        // ---- A and P, block pairs (R, I <= R) spread over the waves (exact path: done) ----
+        for (int pi = exact ? 10 : wave; pi < 10; pi += 4) {
             const int R = pi < 1 ? 0 : pi < 3 ? 1 : pi < 6 ? 2 : 3;
             const int I = pi - R * (R + 1) / 2;
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};

@@ -109,10 +109,21 @@ constexpr int P_BETA = P_RQ + C * 4;
 constexpr int P_EM = P_BETA + C * 4;                            // fp32 [128] e^{G_31}
 constexpr int P_EL = P_EM + D * 4;                              // e^{G_last - G_31}
 constexpr int P_GL = P_EL + D * 4;                              // e^{G_last}
-constexpr int P_LDS = P_GL + D * 4;
+constexpr int P_G31 = P_GL + D * 4;                             // fp32 [128] G_31 (natural log)
+constexpr int P_GLL = P_G31 + D * 4;                            // fp32 [128] G_last (natural log)
+constexpr int P_FLAG = P_GLL + D * 4;                           // int: the item takes the exact path
+constexpr int P_LDS = P_FLAG + 16;
 static_assert(P_LDS <= 160 * 1024, "prep LDS budget");
 constexpr int P_WT = P_XDH;                                     // 16 wave totals [16][128] fp32 (phase 1 only)
 static_assert(16 * D * 4 <= 4 * 4 * BLK, "wave totals alias X_RR and X_RR diag(rk^2 beta)");
+// Exact path (a chunk whose decay is too strong for the reference token):
+// raw k, q and e^g of every row, fp32 [64][128], in regions 1-3 before the
+// planes are formed there.
+constexpr int P_GK = 0, P_GQ = C * D * 4, P_GE = 2 * C * D * 4;
+static_assert(P_GE + C * D * 4 <= P_R3_END && P_R3_END <= P_PH, "exact-path arrays fit below P'");
+// Largest |G_r - G_31| (natural log) the reference-token factors may span:
+// e^{60} and e^{-60} are well inside the float32 and bf16 normal range.
+constexpr float kRefSpan = 60.f;
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -152,6 +163,84 @@ static_assert(prep_unit_packing_ok(), "waves 1-10 own one block each");
 __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* rec, int base, int unit, int ns,
                                                          int s, int hl, int lane) {
     return rec + base + ((unit * ns + s) * 2 + hl) * FRAG + lane * 16;
+}
+
+// Exact A' and P' of one (chunk, head), for chunks whose decay is too strong
+// to factor through the reference token.  Raw k, q and e^g of every row are
+// in LDS (fp32 [64][128]).  For column i the per-channel vector
+// z = k_i e^{G_r - G_i} is carried down the rows by z <- z e^{g_r}, starting
+// from z = k_i at row i: every factor is at most 1, so nothing overflows
+// however strong the decay (tiny products underflow towards zero, as the
+// exact values do).  Then, with the same scalings as the MFMA path,
+//   A'[r][i] = beta_r rk_r^2 (k_r . z)   (i < r),   P'[r][i] = rq_r (q_r . z)   (i <= r),
+// written where that path leaves them: A' diagonal blocks in fp32 and the
+// other A' blocks as bf16 hi/lo (both transposed), P' as bf16 hi/lo
+// row-major.  Entries above the diagonal are not written: the inverses do
+// not read them and the P' planes are cleared beforehand.
+// Lane (l4, l16) takes column i = 4 pw + l4 and channels 8 l16 .. 8 l16 + 7;
+// the 16 lanes of a DPP row reduce the dot products over the channels.
+__device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16, int l4) {
+    const float* gk = reinterpret_cast<const float*>(smem + P_GK);
+    const float* gq = reinterpret_cast<const float*>(smem + P_GQ);
+    const float* ge = reinterpret_cast<const float*>(smem + P_GE);
+    const float* srk = reinterpret_cast<const float*>(smem + P_RK);
+    const float* srq = reinterpret_cast<const float*>(smem + P_RQ);
+    const float* sbeta = reinterpret_cast<const float*>(smem + P_BETA);
+    // Column group pw starts at row 4 pw.  The four waves sharing a SIMD
+    // (wave mod 4) get groups whose row counts add up to the same total.
+    const int pw = ((wave >> 2) & 1) ? (wave ^ 3) : wave;
+    const int r0 = 4 * pw, i = r0 + l4, co = 8 * l16;
+    auto row8 = [&](const float* base, int r) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(base + r * D + co);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(base + r * D + co + 4);
+        return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    };
+    const floatx8 ki = row8(gk, i);
+    floatx8 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float av = 0.f, pv = 0.f;  // lane l16 keeps the sums of row 16 (r / 16) + l16
+    // Row r of the sums: z is born at r == i (the first four rows of the
+    // group), decayed by e^{g_r} afterwards; a 16-row batch ends at r % 16 == 15.
+    auto step = [&](int r, bool birth) {
+        const floatx8 er = row8(ge, r);
+        if (birth) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) z[c] = r == i ? ki[c] : z[c] * er[c];
+        } else {
+            z *= er;
+        }
+        const floatx8 kr = row8(gk, r), qr = row8(gq, r);
+        float a = 0.f, p = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            a += kr[c] * z[c];
+            p += qr[c] * z[c];
+        }
+        a = row16_sum(a);
+        p = row16_sum(p);
+        av = l16 == (r & 15) ? a : av;
+        pv = l16 == (r & 15) ? p : pv;
+        if ((r & 15) != 15) return;
+        const int rr = (r & ~15) + l16;
+        if (rr < i) return;
+        uint32_t h, l;
+        split2(srq[rr] * pv, 0.f, h, l);
+        *reinterpret_cast<uint16_t*>(smem + P_PH + (rr * SN + i) * 2) = static_cast<uint16_t>(h);
+        *reinterpret_cast<uint16_t*>(smem + P_PL + (rr * SN + i) * 2) = static_cast<uint16_t>(l);
+        if (rr == i) return;
+        const float rk = srk[rr];
+        const float av_s = sbeta[rr] * rk * rk * av;
+        const int R = rr >> 4, I = i >> 4;
+        if (R == I) {
+            *reinterpret_cast<float*>(smem + P_LDT + ((R * 16 + (i & 15)) * LDS_STR + (rr & 15)) * 4) = av_s;
+        } else {
+            split2(av_s, 0.f, h, l);
+            const int o = ((pair_index(R, I) * 16 + (i & 15)) * WSTR + (rr & 15)) * 2;
+            *reinterpret_cast<uint16_t*>(smem + P_ATH + o) = static_cast<uint16_t>(h);
+            *reinterpret_cast<uint16_t*>(smem + P_ATL + o) = static_cast<uint16_t>(l);
+        }
+    };
+    for (int r = r0; r < r0 + 4; ++r) step(r, true);
+    for (int r = r0 + 4; r < C; ++r) step(r, false);
 }
 
 // Sequence of chunk cg: the last n with offsets[n] <= cg (empty sequences are skipped).
@@ -249,6 +338,9 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     float* sEm = reinterpret_cast<float*>(smem + P_EM);
     float* sEL = reinterpret_cast<float*>(smem + P_EL);
     float* sGL = reinterpret_cast<float*>(smem + P_GL);
+    float* sG31 = reinterpret_cast<float*>(smem + P_G31);
+    float* sGLL = reinterpret_cast<float*>(smem + P_GLL);
+    int* sFlag = reinterpret_cast<int*>(smem + P_FLAG);
 
     KDA_PHASE_BEGIN
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -350,6 +442,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
 
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
         // rows past the chunk's end were loaded as zeros; only activated gates need a mask
+        if (tid == 0) *sFlag = 0;  // last read after the previous item's second barrier
         const floatx8 kf = unpack8(pk), qf = unpack8(pq);
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
@@ -410,6 +503,11 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             sEm[tid] = fast_exp2(pre[8] * kLog2e);
             sEL[tid] = fast_exp2((pre[16] - pre[8]) * kLog2e);
             sGL[tid] = fast_exp2(pre[16] * kLog2e);
+            sG31[tid] = pre[8];
+            sGLL[tid] = pre[16];
+            // With g <= 0, G_r - G_31 lies in [pre[16] - pre[8], -pre[8]]; past
+            // kRefSpan the chunk takes the exact path (a NaN sum does too).
+            if (!(-pre[8] <= kRefSpan && pre[8] - pre[16] <= kRefSpan)) *sFlag = 1;
         }
         {
             float sk = 0.f, sq = 0.f;
@@ -434,21 +532,14 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             sbeta[tid] = tid < pL ? bv : 0.f;
         }
         lds_barrier();
-        // G_r - G_31 for this row
-        floatx8 cm;
-        {
-            const floatx4 a = *reinterpret_cast<const floatx4*>(sWT + wave * D + 8 * cc);
-            const floatx4 b = *reinterpret_cast<const floatx4*>(sWT + wave * D + 8 * cc + 4);
-            cm = floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-        }
-        const floatx8 d = (cm + incl) * kLog2e;
-        {
+        // Operand planes: Kg = k e^{d}, Qg = q e^{d}, Ki = k e^{dt} (bf16 hi/lo).
+        auto planes = [&](const floatx8& d, const floatx8& dt) {
             const int o = (rp * SW + 8 * cc) * 2;
             floatx8 e, ei;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 e[i] = fast_exp2(d[i]);
-                ei[i] = fast_exp2(-d[i]);
+                ei[i] = fast_exp2(dt[i]);
             }
             bf16x8 hi, lo;
             split8(kf * e, hi, lo);
@@ -460,6 +551,49 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             split8(kf * ei, hi, lo);
             *reinterpret_cast<bf16x8*>(smem + P_KIH + o) = hi;
             *reinterpret_cast<bf16x8*>(smem + P_KIL + o) = lo;
+        };
+        // G_r - G_31 for this row
+        auto offsets8 = [&](const float* base) {
+            const floatx4 a = *reinterpret_cast<const floatx4*>(base);
+            const floatx4 b = *reinterpret_cast<const floatx4*>(base + 4);
+            return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+        };
+        // Decay too strong for the reference token somewhere in the chunk:
+        // A' and P' come from exact_ap, and the planes take the chunk's start
+        // (Kg, Qg) and end (Ki) as references, every factor at most 1, with
+        // e^{G_31} and e^{G_last - G_31} replaced by 1 downstream.
+        const bool exact = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(sFlag)) != 0;
+        if (exact) {
+            const int o = rp * D + 8 * cc;
+            floatx8 eg;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) eg[i] = fast_exp2(gr[i] * kLog2e);
+            float* gk = reinterpret_cast<float*>(smem + P_GK);
+            float* gq = reinterpret_cast<float*>(smem + P_GQ);
+            float* ge = reinterpret_cast<float*>(smem + P_GE);
+            *reinterpret_cast<floatx4*>(gk + o) = floatx4{kf[0], kf[1], kf[2], kf[3]};
+            *reinterpret_cast<floatx4*>(gk + o + 4) = floatx4{kf[4], kf[5], kf[6], kf[7]};
+            *reinterpret_cast<floatx4*>(gq + o) = floatx4{qf[0], qf[1], qf[2], qf[3]};
+            *reinterpret_cast<floatx4*>(gq + o + 4) = floatx4{qf[4], qf[5], qf[6], qf[7]};
+            *reinterpret_cast<floatx4*>(ge + o) = floatx4{eg[0], eg[1], eg[2], eg[3]};
+            *reinterpret_cast<floatx4*>(ge + o + 4) = floatx4{eg[4], eg[5], eg[6], eg[7]};
+            // P' planes (hi and lo, adjacent) cleared: exact_ap writes i <= r only
+            static_assert(P_PL == P_PH + PN && 2 * PN % 16 == 0, "P' planes adjacent");
+            for (int u = tid; u < 2 * PN / 16; u += PNT)
+                *reinterpret_cast<uint4*>(smem + P_PH + 16 * u) = uint4{0u, 0u, 0u, 0u};
+            if (tid < D) {
+                sEm[tid] = 1.f;
+                sEL[tid] = 1.f;
+            }
+            lds_barrier();
+            exact_ap(smem, wave, l16, l4);
+            lds_barrier();
+            // d = G_r (from the chunk's start), dt = G_last - G_r
+            const floatx8 dl = offsets8(sWT + wave * D + 8 * cc) + incl + offsets8(sG31 + 8 * cc);
+            planes(dl * kLog2e, (offsets8(sGLL + 8 * cc) - dl) * kLog2e);
+        } else {
+            const floatx8 d = (offsets8(sWT + wave * D + 8 * cc) + incl) * kLog2e;
+            planes(d, -d);
         }
         // the next item's loads fly from here on
         if (it + static_cast<int>(gridDim.x) < items) fetch(items - 1 - (it + static_cast<int>(gridDim.x)), tid);
@@ -471,7 +605,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         const int uR = has_unit ? static_cast<int>((kPrepUnitR >> (2 * wave)) & 3) : -1;
         const int uI = has_unit ? static_cast<int>((kPrepUnitI >> (2 * wave)) & 3) : -1;
         floatx4 pacc = {0.f, 0.f, 0.f, 0.f};
-        if (uR >= 0) {
+        if (uR >= 0 && !exact) {
             const int ar = (16 * uR + l16) * SW, br = (16 * uI + l16) * SW;
             floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -560,14 +694,16 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             *reinterpret_cast<uint4*>(smem + P_XFL + o + 16) = uint4{fl[4], fl[5], fl[6], fl[7]};
         } else {
             if (uR >= 0) {
-                // P' from this wave's accumulator of phase 2
-                bf16x4 hi, lo;
-                split4(pacc, hi, lo);
+                // P' from this wave's accumulator of phase 2 (exact path: in place already)
+                if (!exact) {
+                    bf16x4 hi, lo;
+                    split4(pacc, hi, lo);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int o = ((16 * uR + 4 * l4 + j) * SN + 16 * uI + l16) * 2;
-                    *reinterpret_cast<__bf16*>(smem + P_PH + o) = hi[j];
-                    *reinterpret_cast<__bf16*>(smem + P_PL + o) = lo[j];
+                    for (int j = 0; j < 4; ++j) {
+                        const int o = ((16 * uR + 4 * l4 + j) * SN + 16 * uI + l16) * 2;
+                        *reinterpret_cast<__bf16*>(smem + P_PH + o) = hi[j];
+                        *reinterpret_cast<__bf16*>(smem + P_PL + o) = lo[j];
+                    }
                 }
             } else if (wave == 15) {
                 // blocks (0,1) and (2,3) lie in the K range of 32-wide steps and read as zero

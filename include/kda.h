@@ -27,15 +27,16 @@
  *     and leave every output untouched.  KDA_ERR_HIP reports a failed launch.
  *     kda_last_error() gives a human-readable detail for the calling thread.
  *   - NaN or Inf inputs propagate into the outputs; they are not checked.
- *   - The numeric domain of the chunked kernel: g must be finite and <= 0,
- *     and the chunk form factors exp(G_r - G_i) (G: cumulative sum of g inside
- *     a chunk) through a reference token, so partial sums of g around it must
- *     stay above -80 per channel (exp(80) is near the float32 limit).  With
- *     bf16 q/k/v and dk = 128 the reference is the chunk's token 31: the sums
- *     over the chunk's tokens 1..31 and over its tokens 32..63 must be >= -80.
- *     Otherwise the reference is the start of each aligned 16-token block and
- *     the sum over every such block must be >= -80.  Chunks are counted from
- *     the start of each sequence.  Decode has no such limit.
+ *   - The numeric domain of the chunked kernel: g must be finite and <= 0;
+ *     any such g is handled, however strong the decay.  The chunk form needs
+ *     exp(G_r - G_i) for i <= r (G: cumulative sum of g inside a chunk of 64
+ *     tokens, counted from the start of each sequence).  A chunk and head
+ *     whose partial sums of g stay within 60 of a reference token (with bf16
+ *     q/k/v and dk = 128: the chunk's token 31; otherwise the start of each
+ *     aligned 16-token block) factors it through that token onto MFMA; one
+ *     whose decay is steeper takes an exact path that carries
+ *     k_i exp(G_r - G_i) down the rows as products of exp(g) <= 1 (more
+ *     work per chunk than the factored path).  Decode has no such split.
  *   - With bf16 q/k/v and dk = 128 the chunk pass carries the state and the
  *     per-chunk operands through fp16 (11 significant bits, largest finite
  *     value 65504): |k|, |v| and the entries of the state must stay well

@@ -221,15 +221,22 @@ class GateInputs:
 
 def make_gate(rows: int, num_heads: int, head_k: int, dtype: torch.dtype, *, mu: float = -5.0,
               lower_bound: Optional[float] = None, seed: int = 0, lead: tuple = (),
-              per_head: bool = False) -> GateInputs:
+              per_head: bool = False, std: float = 0.5, dt_std: float = 0.5,
+              a_log_value: Optional[float] = None) -> GateInputs:
     """Draw raw gate inputs of ``lead + (rows, num_heads, head_k)`` (``lead + (rows,
-    num_heads)`` and dt_bias [H] with ``per_head``: one decay per head)."""
+    num_heads)`` and dt_bias [H] with ``per_head``: one decay per head).
+
+    raw gate ~ N(mu, std**2); dt_bias ~ N(0, dt_std**2) (``dt_std=0`` gives the
+    zero bias); ``a_log_value`` replaces every head's log(U(1, 16)) draw by one
+    value (the draw still happens, so the other tensors do not change)."""
     gen = torch.Generator().manual_seed(seed)
     ch = () if per_head else (head_k,)
-    raw_g = (torch.randn(*lead, rows, num_heads, *ch, generator=gen) * 0.5 + mu).to(dtype)
+    raw_g = (torch.randn(*lead, rows, num_heads, *ch, generator=gen) * std + mu).to(dtype)
     raw_beta = torch.randn(*lead, rows, num_heads, generator=gen).to(dtype)
     a_log = torch.log(torch.empty(num_heads).uniform_(1.0, 16.0, generator=gen))
-    dt_bias = torch.randn(num_heads, *ch, generator=gen) * 0.5
+    if a_log_value is not None:
+        a_log = torch.full((num_heads,), float(a_log_value))
+    dt_bias = torch.randn(num_heads, *ch, generator=gen) * dt_std
     return GateInputs(raw_g, raw_beta, a_log, dt_bias, lower_bound)
 
 

@@ -186,21 +186,34 @@ def test_prefill_varlen8_workload():
     _check_prefill(w.varlen8())
 
 
-def test_prefill_long_128k_workload_sampled_heads():
-    """T=131072, H=32, d=128: the GPU runs every head; heads 0, 13 and 31 are
-    checked element by element against the oracle (every token, whole state)."""
+def test_prefill_long_128k_workload():
+    """T=131072, H=32, d=128: every output and the whole final state of all 32
+    heads against the oracle.  The oracle runs over groups of 16 heads (heads
+    are independent) to bound host memory; the error metric is taken over the
+    whole tensors: max over groups of max|gpu - oracle|, over max|oracle|."""
     x = w.long_128k()
-    announce(f"prefill {x.name} (all heads on GPU, 3 heads checked)")
+    announce(f"prefill {x.name} (all heads)")
     out, fs = prefill_on_gpu(x, out_dtype=torch.float32, with_state=False)
-    heads = [0, 13, 31]
-    sl = lambda t: t[:, heads].contiguous()
-    ref_o, ref_s = oracle.forward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), x.cu_seqlens,
-                                  None, scale=x.scale)
-    eo = rel_err(out[:, heads], ref_o)
-    es = rel_err(fs[:, heads], ref_s)
-    print(f"  err out {eo:.3e} state {es:.3e}")
-    assert eo <= 2e-3 and es <= 2e-3
     assert bool(torch.isfinite(out).all()) and bool(torch.isfinite(fs).all())
+    out_c, fs_c = out.cpu(), fs.cpu()
+    del out, fs
+    err_o = err_s = den_o = den_s = 0.0
+    H, G = x.num_heads, 16
+    for h0 in range(0, H, G):
+        sl = lambda t: t[:, h0:h0 + G].contiguous()
+        ro, rs = oracle.forward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), x.cu_seqlens,
+                                None, scale=x.scale)
+        go = out_c[:, h0:h0 + G].double().numpy()
+        gs = fs_c[:, h0:h0 + G].double().numpy()
+        err_o = max(err_o, float(np.abs(go - ro).max()))
+        err_s = max(err_s, float(np.abs(gs - rs).max()))
+        den_o = max(den_o, float(np.abs(ro).max()))
+        den_s = max(den_s, float(np.abs(rs).max()))
+        print(f"  heads {h0}..{h0 + G - 1} checked", flush=True)
+        del ro, rs, go, gs
+    eo, es = err_o / den_o, err_s / den_s
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
 
 
 # ------------------------------------------------------------------ decode
