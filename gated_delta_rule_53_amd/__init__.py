@@ -19,6 +19,7 @@ from ._binding import (  # noqa: F401
     abi_version,
     chunk_fwd,
     chunk_fwd_gated,
+    chunk_fwd_noalloc,
     chunk_fwd_pooled,
     chunk_fwd_workspace_bytes,
     gated_rmsnorm,
@@ -34,6 +35,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "chunk_fwd",
     "chunk_fwd_gated",
+    "chunk_fwd_noalloc",
     "recurrent_step",
     "recurrent_step_gated",
     "recurrent_step_normed",

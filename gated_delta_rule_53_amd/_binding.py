@@ -77,6 +77,8 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_workspace_bytes.restype = sz
     lib.kda_chunk_fwd.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp, sz, vp]
     lib.kda_chunk_fwd.restype = ctypes.c_int
+    lib.kda_chunk_fwd_noalloc.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, vp, fp, vp]
+    lib.kda_chunk_fwd_noalloc.restype = ctypes.c_int
     lib.kda_recurrent_step.argtypes = [P, vp, vp, vp, fp, fp, fp, vp, vp]
     lib.kda_recurrent_step.restype = ctypes.c_int
     G = ctypes.POINTER(Gate)
@@ -232,6 +234,48 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
                               _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
                               _ptr(workspace), ws_len, _stream(dev)))
     return out, final_state
+
+
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_fwd_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                      beta: torch.Tensor, cu_seqlens: torch.Tensor, initial_state: Optional[torch.Tensor],
+                      out: torch.Tensor, final_state: Optional[torch.Tensor], *, scale: Optional[float] = None,
+                      state_layout: str = "dk_dv", qk_l2norm: bool = True) -> None:
+    """``kda_chunk_fwd_noalloc``: chunk_fwd with no workspace and no allocation.
+
+    For callers that cannot allocate device memory (graph capture, serving
+    loops): every tensor, ``out`` and ``final_state`` included, comes from
+    the caller, and the library's own 128 MiB device array serves as the
+    workspace.  Problems needing more workspace than that are rejected.
+    Calls that overlap in time on one GPU share that array and race.
+    Arguments as for ``chunk_fwd``; ``out`` gives the output dtype.
+    """
+    if q.dim() != 3:
+        raise KdaArgumentError(2, f"q must be [T, H, dk], got {tuple(q.shape)}")
+    T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    N = cu_seqlens.numel() - 1
+    _need(q, "q", (T, H, dk), None, dev)
+    _need(k, "k", (T, H, dk), q.dtype, dev)
+    _need(v, "v", (T, H, dv), q.dtype, dev)
+    gph, gshape = _gate_shape(g, (T, H), dk)
+    _need(g, "g", gshape, torch.float32, dev)
+    _need(beta, "beta", (T, H), torch.float32, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, dk, dv), torch.float32, dev)
+    _need(out, "out", (T, H, dv), out.dtype, dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, dk, dv), torch.float32, dev)
+    prob = _problem(T, N, H, dk, dv, q.dtype, out.dtype, scale, qk_l2norm, gph, state_layout)
+    _check(_lib.kda_chunk_fwd_noalloc(ctypes.byref(prob), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+                                      _ptr(cu_seqlens), _ptr(initial_state), _ptr(out), _ptr(final_state),
+                                      _stream(dev)))
 
 
 def recurrent_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

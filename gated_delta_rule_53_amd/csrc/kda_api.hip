@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "kda.h"
 #include "kda_internal.h"
@@ -37,6 +38,35 @@ kda_status_t finish(hipError_t launch, hipStream_t stream, const char* what) {
     }
     g_last_error[0] = '\0';
     return KDA_OK;
+}
+
+// ---- workspace of kda_chunk_fwd_noalloc ----
+// A file-scope device array: every GPU the library runs on holds its own copy,
+// at its own address, until the process ends.  In host code `scratch` is only
+// a stand-in for the symbol; the device address comes from
+// hipGetSymbolAddress, looked up once per device (with that device current)
+// and kept in g_scratch_ptr.  Only those addresses are ever passed to kernels.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+hipError_t scratch_address(void** out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return e;
+        if (!p) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
 }
 
 // Vector loads and stores of 16 bytes: a null pointer passes (it is checked where it is required).
@@ -86,11 +116,15 @@ kda_status_t check_gate(const kda_gate_t* gate, const char* what, kda::GateParam
     return KDA_OK;
 }
 
+// Workspace of one prefill call: the caller's buffer, or (noalloc) the library's scratch array.
+enum class Workspace { kCaller, kScratch };
+
 kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda::GateParams& gp,
                             const void* q, const void* k, const void* v, const void* g, const void* beta,
                             const int32_t* cu_seqlens, const float* initial_state, void* out,
                             float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                            const int32_t* slots = nullptr, int num_slots = 0) {
+                            const int32_t* slots = nullptr, int num_slots = 0,
+                            Workspace ws_kind = Workspace::kCaller) {
     if (p->chunk_size != 0 && p->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
     if (p->num_seqs == 0) {
@@ -105,11 +139,24 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
         return KDA_OK;
     }
     const size_t need = kda_chunk_fwd_workspace_bytes(p);
-    if (workspace_bytes < need)
-        return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
-    if (need > 0 && !workspace) return fail(KDA_ERR_NULL_POINTER, "%s: workspace is NULL", what);
+    if (ws_kind == Workspace::kScratch) {
+        if (need > KDA_NOALLOC_SCRATCH_BYTES)
+            return fail(KDA_ERR_UNSUPPORTED, "%s: the problem needs %zu bytes of workspace; the library's scratch "
+                        "holds %zu (use kda_chunk_fwd with a workspace)", what, need,
+                        static_cast<size_t>(KDA_NOALLOC_SCRATCH_BYTES));
+    } else {
+        if (workspace_bytes < need)
+            return fail(KDA_ERR_WORKSPACE, "%s: workspace %zu < %zu bytes", what, workspace_bytes, need);
+        if (need > 0 && !workspace) return fail(KDA_ERR_NULL_POINTER, "%s: workspace is NULL", what);
+    }
     if (need > 0 && ((p->total_tokens + 63) / 64 + p->num_seqs) * int64_t(p->num_heads) > (int64_t(1) << 31) - 1)
         return fail(KDA_ERR_UNSUPPORTED, "%s: too many (chunk, head) pairs", what);
+    if (ws_kind == Workspace::kScratch && need > 0) {
+        // every argument is valid: only now touch the device
+        const hipError_t e = scratch_address(&workspace);
+        if (e != hipSuccess)
+            return fail(KDA_ERR_HIP, "%s: address of the library's scratch: %s", what, hipGetErrorString(e));
+    }
     kda::PrefillArgs a{};
     a.q = q;
     a.k = k;
@@ -218,6 +265,16 @@ kda_status_t kda_chunk_fwd(const kda_problem_t* p, const void* q, const void* k,
     if (st != KDA_OK) return st;
     return chunk_fwd_impl(what, p, kda::GateParams{}, q, k, v, g, beta, cu_seqlens, initial_state, out,
                           final_state, workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t* p, const void* q, const void* k, const void* v,
+                                   const float* g, const float* beta, const int32_t* cu_seqlens,
+                                   const float* initial_state, void* out, float* final_state, void* stream) {
+    const char* what = "kda_chunk_fwd_noalloc";
+    const kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    return chunk_fwd_impl(what, p, kda::GateParams{}, q, k, v, g, beta, cu_seqlens, initial_state, out,
+                          final_state, nullptr, 0, stream, nullptr, 0, Workspace::kScratch);
 }
 
 kda_status_t kda_chunk_fwd_gated(const kda_problem_t* p, const kda_gate_t* gate, const void* q, const void* k,

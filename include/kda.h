@@ -21,8 +21,9 @@
  * Conventions for every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller, row-major
  *     and densely packed, innermost dimension last.  The library allocates
- *     nothing, keeps no state between calls and never synchronises `stream`:
- *     work is enqueued on it and the call returns.
+ *     nothing, keeps no state between calls (kda_chunk_fwd_noalloc's device
+ *     array aside) and never synchronises `stream`: work is enqueued on it and
+ *     the call returns.
  *   - Argument errors are detected on the host before anything is enqueued
  *     and leave every output untouched.  KDA_ERR_HIP reports a failed launch.
  *     kda_last_error() gives a human-readable detail for the calling thread.
@@ -181,6 +182,31 @@ kda_status_t kda_chunk_fwd(const kda_problem_t *problem, const void *q, const vo
                            const int32_t *cu_seqlens, const float *initial_state, void *out,
                            float *final_state, void *workspace, size_t workspace_bytes,
                            void *stream);
+
+/*
+ * kda_chunk_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Same computation, arguments and results
+ * as kda_chunk_fwd (the same kernels run); the caller still provides q, k,
+ * v, g, beta, cu_seqlens, the states and out.
+ *
+ * The two-pass path's workspace is a device array inside the library,
+ * KDA_NOALLOC_SCRATCH_BYTES (128 MiB) on every GPU the library runs on, held
+ * until the process ends.  A problem with kda_chunk_fwd_workspace_bytes(problem)
+ * above that ((ceil(T / 64) + N) * H beyond about 2,166: one sequence of up to
+ * 4,224 tokens at H = 32, or 34,560 at H = 4, fits) fails with
+ * KDA_ERR_UNSUPPORTED before anything is enqueued.  No call allocates or frees memory; the first call on
+ * each GPU looks up the array's device address (hipGetSymbolAddress), and a
+ * failure there is KDA_ERR_HIP.  Nothing in the array needs to start at zero:
+ * each call writes what it reads.  Every call on one GPU shares that GPU's
+ * array, so calls that overlap in time on one GPU (two streams, or two host
+ * threads) race and give undefined results: serialise them.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+kda_status_t kda_chunk_fwd_noalloc(const kda_problem_t *problem, const void *q, const void *k,
+                                   const void *v, const float *g, const float *beta,
+                                   const int32_t *cu_seqlens, const float *initial_state, void *out,
+                                   float *final_state, void *stream);
 
 /*
  * kda_chunk_fwd with the gate activation fused in: raw_g [T, H, dk] and

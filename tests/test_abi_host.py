@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
         "kda_abi_version", "kda_status_string", "kda_last_error",
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
-        "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv", "kda_recurrent_step_normed"])
+        "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv", "kda_recurrent_step_normed",
+        "kda_chunk_fwd_noalloc"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -181,6 +182,45 @@ def test_workspace_is_checked():
     assert st == 4 and "workspace" in msg, (st, msg)
     st, msg = _chunk(_prob(), ws=None, ws_bytes=need)
     assert st == 1 and "workspace" in msg, (st, msg)
+
+
+def _noalloc(prob, **ptrs):
+    lib = kda.raw_library()
+    p = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fs=None)
+    p.update(ptrs)
+    st = lib.kda_chunk_fwd_noalloc(None if prob is None else ctypes.byref(prob), p["q"], p["k"], p["v"],
+                                   p["g"], p["beta"], p["cu"], p["s0"], p["out"], p["fs"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def test_noalloc_checks_like_chunk_fwd():
+    assert _noalloc(None)[0] == 1
+    for kw, status, needle in [(dict(num_seqs=-1), 2, "num_seqs"), (dict(head_k=96, head_v=96), 3, "head size"),
+                               (dict(chunk_size=32), 3, "chunk_size")]:
+        st, msg = _noalloc(_prob(**kw))
+        assert st == status and needle in msg and "noalloc" in msg, (st, msg)
+    for name in ("q", "k", "v", "g", "beta", "out", "cu"):
+        st, msg = _noalloc(_prob(), **{name: None})
+        assert st == 1, name
+    st, msg = _noalloc(_prob(num_seqs=0, total_tokens=0), q=None, k=None, v=None, g=None, beta=None, cu=None,
+                       out=None)
+    assert st == 0 and msg == ""
+
+
+def test_noalloc_rejects_problems_beyond_its_scratch():
+    """The library's array holds 128 MiB: one sequence of 4,224 tokens at H = 32
+    fits, 4,225 does not (before any HIP call, so this runs without a GPU)."""
+    lib = kda.raw_library()
+    limit = 128 << 20
+    fits = _prob(total_tokens=4224, num_seqs=1, num_heads=32)
+    over = _prob(total_tokens=4225, num_seqs=1, num_heads=32)
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(fits)) <= limit
+    assert lib.kda_chunk_fwd_workspace_bytes(ctypes.byref(over)) > limit
+    st, msg = _noalloc(over)
+    assert st == 3 and "scratch" in msg, (st, msg)
+    assert kda._binding.NOALLOC_SCRATCH_BYTES == limit
+    m = re.search(r"#define KDA_NOALLOC_SCRATCH_BYTES \(\(size_t\)128 << 20\)", open(HEADER).read())
+    assert m is not None
 
 
 @pytest.mark.parametrize("kw,status,needle", [
