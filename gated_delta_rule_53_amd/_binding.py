@@ -195,6 +195,10 @@ def chunk_fwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor
     float32 or None.  Returns (out [T, H, dv] in ``out_dtype`` (default: v's
     dtype), final_state [N, H, dk, dv] float32 or None).  Runs on the current
     stream of q's device.  ``final_state`` may be ``initial_state`` itself.
+    ``cu_seqlens=None`` builds [0, T] on the device, and the workspace (if
+    not given) and the outputs (if not given) are allocated, on every call:
+    under graph capture or in allocation-free loops pass them all (or use
+    ``chunk_fwd_noalloc``).
     ``state_layout="dv_dk"`` takes and returns every state block transposed,
     [..., dv, dk] (kda_problem_t.state_layout; the same for every call below).
     """
@@ -432,7 +436,8 @@ def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     there; a slot outside [0, P) starts from zero and is not written.  Without
     a_log, g [T, H, dk] and beta [T, H] are float32; with a_log (and dt_bias,
     lower_bound as for ``chunk_fwd_gated``) they are the raw projections in
-    q's dtype.  Returns out.
+    q's dtype.  Returns out.  cu_seqlens, out and workspace: as for
+    ``chunk_fwd`` (built or allocated on every call when not given).
     """
     if q.dim() != 3:
         raise KdaArgumentError(2, f"q must be [T, H, dk], got {tuple(q.shape)}")
@@ -556,7 +561,10 @@ def short_conv(x: torch.Tensor, weight: torch.Tensor, cu_seqlens: Optional[torch
     x [T, C] (float32 or bfloat16); weight [K, C] in x's dtype; cu_seqlens
     [N+1] int32 (None: one request of T tokens); state [N, K-1, C] in x's
     dtype or None (zeros).  Returns (y [T, C], final state [N, K-1, C] or
-    None).  ``final_state`` may be ``state`` itself when T == N (decode).
+    None).  ``final_state`` may be ``state`` itself (in place: each request
+    then runs on one thread per 8 channels, which suits decode and short
+    requests).  ``cu_seqlens=None`` builds [0, T] on the device on every call
+    (a host-to-device copy): not for graph capture or allocation-free loops.
     """
     dev = x.device
     if dev.type != "cuda":

@@ -4,6 +4,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <initializer_list>
 #include <mutex>
 
 #include "kda.h"
@@ -71,6 +72,30 @@ hipError_t scratch_address(void** out) {
 
 // Vector loads and stores of 16 bytes: a null pointer passes (it is checked where it is required).
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_to(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; }
+
+// Largest token count of kda_short_conv: 256 * ceil(T / 8) + 2048 work-items along x below 2^32.
+constexpr int64_t kConvMaxTokens = (int64_t(1) << 27) - 1024;
+
+// Alignment the kernels' vector accesses need: q, k, v, out, the states, the
+// workspace and a per-channel g (or raw gate) move in 16-byte pieces; beta,
+// a per-head g and the int32 arrays element by element.  elem: bytes of one
+// g / beta element (4 for float32, 2 for a bf16 raw gate).
+kda_status_t check_alignment(const char* what, const kda_problem_t* p, size_t elem, const void* q,
+                             const void* k, const void* v, const void* g, const void* beta, const void* out,
+                             std::initializer_list<const void*> blocks16,
+                             std::initializer_list<const void*> ints = {}) {
+    bool ok = aligned16(q) && aligned16(k) && aligned16(v) && aligned16(out) && aligned_to(beta, elem) &&
+              (p->gate_per_head ? aligned_to(g, elem) : aligned16(g));
+    for (const void* b : blocks16) ok = ok && aligned16(b);
+    if (!ok)
+        return fail(KDA_ERR_BAD_SHAPE, "%s: q, k, v, out, %sthe state and workspace buffers must be 16-byte "
+                    "aligned, beta%s %zu-byte aligned", what, p->gate_per_head ? "" : "g, ",
+                    p->gate_per_head ? " and g" : "", elem);
+    for (const void* i : ints)
+        if (!aligned_to(i, 4)) return fail(KDA_ERR_BAD_SHAPE, "%s: int32 index arrays must be 4-byte aligned", what);
+    return KDA_OK;
+}
 
 // Checks shared by both entry points.  Returns KDA_OK or the first violation.
 kda_status_t check_problem(const kda_problem_t* p, const char* what) {
@@ -138,6 +163,12 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
         g_last_error[0] = '\0';
         return KDA_OK;
     }
+    {
+        const size_t elem = gp.a_log && p->qkv_dtype == KDA_BF16 ? 2 : 4;
+        const kda_status_t st = check_alignment(what, p, elem, q, k, v, g, beta, out,
+                                                {initial_state, final_state, workspace}, {cu_seqlens, slots});
+        if (st != KDA_OK) return st;
+    }
     const size_t need = kda_chunk_fwd_workspace_bytes(p);
     if (ws_kind == Workspace::kScratch) {
         if (need > KDA_NOALLOC_SCRATCH_BYTES)
@@ -198,6 +229,12 @@ kda_status_t recurrent_step_impl(const char* what, const kda_problem_t* p, const
     }
     if (!q || !k || !v || !g || !beta || !state || !out)
         return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state and out are required", what);
+    {
+        const size_t elem = gp.a_log && p->qkv_dtype == KDA_BF16 ? 2 : 4;
+        const kda_status_t st = check_alignment(what, p, elem, q, k, v, g, beta, out,
+                                                {state, norm.gate, norm.weight});
+        if (st != KDA_OK) return st;
+    }
     kda::DecodeArgs a{};
     a.q = q;
     a.k = k;
@@ -370,6 +407,11 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     if (!q || !k || !v || !g || !beta || !state_pool || !state_indices || !out)
         return fail(KDA_ERR_NULL_POINTER, "%s: q, k, v, g, beta, state_pool, state_indices and out are required",
                     what);
+    {
+        const size_t elem = gp.a_log && p->qkv_dtype == KDA_BF16 ? 2 : 4;
+        st = check_alignment(what, p, elem, q, k, v, g, beta, out, {state_pool}, {state_indices, num_accepted});
+        if (st != KDA_OK) return st;
+    }
     kda::VerifyArgs a{};
     a.q = q;
     a.k = k;
@@ -409,9 +451,11 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t chan
         return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d (supported: 1 to 4)", what, kernel_size);
     if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d", what, dtype);
     if (silu != 0 && silu != 1) return fail(KDA_ERR_BAD_SHAPE, "%s: silu must be 0 or 1", what);
-    // grid: one workgroup per 8 tokens (x) and per 2048 channels (y)
-    if (total_tokens > (int64_t(1) << 33) || channels > (1 << 26))
-        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large", what);
+    // grid: one workgroup of 256 threads per 8 tokens (x; in place: per request) and per 2048
+    // channels (y); the launch's work-item count along x must stay below 2^32
+    if (total_tokens > kConvMaxTokens || channels > (1 << 26) || num_seqs > (1 << 23))
+        return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large (at most %lld tokens, 2^23 requests, 2^26 "
+                    "channels)", what, (long long)kConvMaxTokens);
     if (!aligned16(x) || !aligned16(weight) || !aligned16(state_in) || !aligned16(state_out) || !aligned16(y))
         return fail(KDA_ERR_BAD_SHAPE, "%s: x, weight, states and y must be 16-byte aligned", what);
     if (num_seqs == 0) {
@@ -420,8 +464,6 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t chan
     }
     if (!cu_seqlens || !weight || (total_tokens > 0 && (!x || !y)))
         return fail(KDA_ERR_NULL_POINTER, "%s: cu_seqlens, weight, x and y are required", what);
-    if (state_out && state_in == state_out && total_tokens != num_seqs)
-        return fail(KDA_ERR_BAD_SHAPE, "%s: state_out may be state_in only with one token per request", what);
     if (total_tokens == 0 && !state_out) {
         g_last_error[0] = '\0';
         return KDA_OK;

@@ -15,6 +15,12 @@
 // inputs in registers; a run that crosses into the next request restarts its
 // window from that request's state.  One extra row of workgroups writes the state of empty requests
 // (their initial state, or zeros).
+//
+// In place (state_out == state_in, the decode case): a request's old state
+// could be read by one run while another run writes its new state, so that
+// case has its own launch, request-major: one thread per request and eight
+// channels reads the old state, runs the request's tokens and only then
+// writes the new state.  Empty requests keep their state untouched.
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -167,8 +173,72 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
     }
 }
 
+// In place: blockIdx.x is the request, blockIdx.y 2048 channels.
+template <int K, typename T, bool SILU>
+__global__ __launch_bounds__(256) void short_conv_inplace_kernel(const T* __restrict__ x, const T* __restrict__ weight,
+                                                                 const int32_t* __restrict__ cu, T* state,
+                                                                 T* __restrict__ y, int64_t total_tokens,
+                                                                 int channels) {
+    const int n = static_cast<int>(blockIdx.x);
+    const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
+    if (c >= channels) return;
+    int64_t start = cu[n], end = cu[n + 1];
+    if (start < 0 || end > total_tokens || end < start) end = start;  // malformed: no tokens
+    if (start == end) return;
+    const size_t C = static_cast<size_t>(channels);
+    constexpr int S = K - 1;
+    auto soff = [&](int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
+    float w[K][8];
+#pragma unroll
+    for (int j = 0; j < K; ++j) load8c(w[j], weight + static_cast<size_t>(j) * C + c);
+    // win[m]: the input m + 1 steps back; the old state, newest last
+    float win[S > 0 ? S : 1][8];
+#pragma unroll
+    for (int m = 0; m < S; ++m) load8c(win[m], state + soff(S - 1 - m));
+    for (int64_t t = start; t < end; ++t) {
+        float cur[8];
+        load8c(cur, x + static_cast<size_t>(t) * C + c);
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = w[K - 1][i] * cur[i];
+#pragma unroll
+        for (int m = 0; m < S; ++m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += w[K - 2 - m][i] * win[m][i];
+        if constexpr (SILU) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+        }
+        store8c(y + static_cast<size_t>(t) * C + c, acc);
+#pragma unroll
+        for (int m = S - 1; m > 0; --m)
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[m][i] = win[m - 1][i];
+        if constexpr (S > 0) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) win[0][i] = cur[i];
+        }
+    }
+    // every read of this request's state is done: write the new one, oldest first
+#pragma unroll
+    for (int m = 0; m < S; ++m) store8c(state + soff(m), win[S - 1 - m]);
+}
+
 template <int K, typename T>
 static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
+    if (a.state_out && a.state_out == a.state_in) {
+        const dim3 grid(static_cast<unsigned>(a.num_seqs), static_cast<unsigned>((a.channels / 8 + 255) / 256));
+        T* st = static_cast<T*>(a.state_out);
+        if (a.silu)
+            short_conv_inplace_kernel<K, T, true><<<grid, 256, 0, stream>>>(
+                static_cast<const T*>(a.x), static_cast<const T*>(a.weight), a.cu_seqlens, st,
+                static_cast<T*>(a.y), a.total_tokens, a.channels);
+        else
+            short_conv_inplace_kernel<K, T, false><<<grid, 256, 0, stream>>>(
+                static_cast<const T*>(a.x), static_cast<const T*>(a.weight), a.cu_seqlens, st,
+                static_cast<T*>(a.y), a.total_tokens, a.channels);
+        return hipGetLastError();
+    }
     const int64_t run_rows = (a.total_tokens + TB - 1) / TB;
     const int64_t per = (run_rows + 8) / 8;  // runs per XCD: 8 per >= run_rows + 1
     const dim3 grid(static_cast<unsigned>(8 * per), static_cast<unsigned>((a.channels / 8 + 255) / 256));

@@ -28,6 +28,13 @@
  *     and leave every output untouched.  KDA_ERR_HIP reports a failed launch.
  *     kda_last_error() gives a human-readable detail for the calling thread.
  *   - NaN or Inf inputs propagate into the outputs; they are not checked.
+ *   - Alignment (checked on the host, KDA_ERR_BAD_SHAPE otherwise): q, k, v,
+ *     out, g or the raw gate when it has one value per key channel, every
+ *     state buffer, pool and workspace, and the output gate and norm weight
+ *     must be 16-byte aligned (the kernels move them in 16-byte pieces); beta
+ *     and a per-head g need their element's alignment (4 bytes for float32, 2
+ *     for a bf16 raw input) and the int32 index arrays 4 bytes.  Whole rows
+ *     sliced from a PyTorch allocation meet this.
  *   - The numeric domain of the chunked kernel: g must be finite and <= 0;
  *     any such g is handled, however strong the decay.  The chunk form needs
  *     exp(G_r - G_i) for i <= r (G: cumulative sum of g inside a chunk of 64
@@ -347,10 +354,13 @@ kda_status_t kda_recurrent_step_normed(const kda_problem_t *problem, const kda_g
  *   weight        [K, C] device (tap-major, the layout the page builds for its operator)
  *   state_in      [N, K - 1, C] device, or NULL for zeros
  *   state_out     [N, K - 1, C] device (written), or NULL to skip; may be state_in
- *                 only when total_tokens == num_seqs
+ *                 (in place: every request reads its old state before its new state
+ *                 is written; each request then runs on one thread per 8 channels,
+ *                 token after token, which suits decode and short requests)
  *   y             [T, C] device (written)
- * All device pointers 16-byte aligned (KDA_ERR_BAD_SHAPE otherwise); T <= 2^33,
- * C <= 2^26.  Errors are found on the host before any launch.
+ * All device pointers 16-byte aligned (KDA_ERR_BAD_SHAPE otherwise); T <= 2^27 - 1024,
+ * N <= 2^23, C <= 2^26 (the launch grid's limits).  Errors are found on the host
+ * before any launch.
  */
 kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t channels, int32_t kernel_size,
                             int32_t dtype, int32_t silu, const void *x, const void *weight,

@@ -193,6 +193,43 @@ def _noalloc(prob, **ptrs):
     return st, lib.kda_last_error().decode()
 
 
+MISALIGNED = ctypes.c_void_p(0x1008)  # 8-byte aligned, not 16
+MISALIGNED4 = ctypes.c_void_p(0x1002)  # 2-byte aligned, not 4
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "out", "s0", "fs", "ws"])
+def test_chunk_fwd_rejects_misaligned_vector_operands(name):
+    prob = _prob()
+    need = kda.raw_library().kda_chunk_fwd_workspace_bytes(ctypes.byref(prob))
+    ptrs = dict(ws=FAKE, ws_bytes=need)
+    ptrs[name] = MISALIGNED
+    st, msg = _chunk(prob, **ptrs)
+    assert st == 2 and "16-byte aligned" in msg, (name, st, msg)
+
+
+@pytest.mark.parametrize("name", ["beta", "cu"])
+def test_chunk_fwd_rejects_misaligned_elements(name):
+    prob = _prob()
+    need = kda.raw_library().kda_chunk_fwd_workspace_bytes(ctypes.byref(prob))
+    st, msg = _chunk(prob, ws=FAKE, ws_bytes=need, **{name: MISALIGNED4})
+    assert st == 2 and "aligned" in msg, (name, st, msg)
+
+
+def test_per_head_g_needs_only_element_alignment():
+    """g [T, H] (one decay per head) is read element by element: a 4-byte aligned g
+    passes the alignment check (and the call then fails later, on the host, for
+    want of a workspace)."""
+    prob = _prob(gate_per_head=1)
+    st, msg = _chunk(prob, g=ctypes.c_void_p(0x1004))
+    assert st == 4 and "workspace" in msg, (st, msg)
+
+
+@pytest.mark.parametrize("name", ["q", "k", "v", "g", "state", "out"])
+def test_recurrent_step_rejects_misaligned_vector_operands(name):
+    st, msg = _step(_prob(total_tokens=2, num_seqs=2), **{name: MISALIGNED})
+    assert st == 2 and "16-byte aligned" in msg, (name, st, msg)
+
+
 def test_noalloc_checks_like_chunk_fwd():
     assert _noalloc(None)[0] == 1
     for kw, status, needle in [(dict(num_seqs=-1), 2, "num_seqs"), (dict(head_k=96, head_v=96), 3, "head size"),
@@ -336,6 +373,11 @@ def test_verify_checks_its_arguments():
     st, msg = _verify(vp(head_k=96, head_v=96), 4)
     assert st == 3 and "head size 96" in msg
     assert _verify(vp(total_tokens=0, num_seqs=0), 5, q=None, pool=None)[0] == 0
+    for name in ("q", "pool", "out"):
+        st, msg = _verify(vp(), 4, **{name: MISALIGNED})
+        assert st == 2 and "16-byte aligned" in msg, (name, st, msg)
+    st, msg = _verify(vp(), 4, idx=MISALIGNED4)
+    assert st == 2 and "4-byte aligned" in msg, (st, msg)
 
 
 def test_pooled_prefill_checks_its_arguments():
@@ -427,8 +469,10 @@ def _conv(num_seqs=2, total_tokens=10, channels=64, kernel_size=4, dtype=1, silu
     (dict(weight=None), 1, "required"),
     (dict(cu=None), 1, "required"),
     (dict(y=None), 1, "required"),
-    (dict(state_in=FAKE, state_out=FAKE), 2, "one token per request"),
     (dict(x=ctypes.c_void_p(0x1008)), 2, "16-byte aligned"),
+    # the launch's work-items along x (256 per 8 tokens) stay below 2^32
+    (dict(total_tokens=(1 << 27) - 1023), 3, "too large"),
+    (dict(num_seqs=(1 << 23) + 1), 3, "too large"),
 ])
 def test_short_conv_rejects_before_launch(kw, status, needle):
     st, msg = _conv(**kw)

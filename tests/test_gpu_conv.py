@@ -5,8 +5,8 @@ within one bf16 ulp of each oracle value plus 1e-6 of max|oracle|.  Final
 states are copies of stored inputs and must match exactly.  Cases: requests
 shorter than the filter, empty requests, runs of 8 tokens that cross request
 boundaries, all filter lengths, with and without a starting state, SiLU on and
-off, two channel blocks with a few hundred runs, decode in place (one token per request), and a split run equal to the
-whole run bit for bit.
+off, two channel blocks with a few hundred runs, in place (one token per request, and
+requests of several tokens), and a split run equal to the whole run bit for bit.
 """
 import numpy as np
 import pytest
@@ -88,6 +88,25 @@ def test_short_conv_decode_in_place(dtype):
     ref, ref_s = conv.short_conv(x, w, cu.numpy(), s0, silu=True)
     assert ys.data_ptr() == st.data_ptr()
     _check(y, ys, ref, ref_s, dtype)
+
+
+@pytest.mark.parametrize("lens", [[1, 1, 1, 1, 1, 1, 1, 2, 1, 0], [0, 5, 9, 1, 0, 30, 2, 17]],
+                         ids=["T_eq_N_cross_run", "multi_token"])
+@pytest.mark.parametrize("K", [2, 4])
+def test_short_conv_in_place_any_lengths(lens, K):
+    """In place with requests of several tokens: T == N with a 2-token request
+    across the boundary of two 8-token runs (tokens 7 and 8), and a batch of
+    longer requests; every request reads its old state before its new one is
+    written."""
+    import gated_delta_rule_53_amd as kda
+    x, w, cu, s0 = _inputs(lens, 384, K, torch.float32, seed=7 + K)
+    announce(f"short_conv in place lens={lens} K={K}")
+    st = dev(s0)
+    y, ys = kda.short_conv(dev(x), dev(w), dev(cu), st, final_state=st)
+    torch.cuda.synchronize()
+    ref, ref_s = conv.short_conv(x, w, cu.numpy(), s0, silu=True)
+    assert ys.data_ptr() == st.data_ptr()
+    _check(y, ys, ref, ref_s, torch.float32)
 
 
 def test_short_conv_split_run_equals_whole_run():
