@@ -9,7 +9,10 @@ step so that the 256 MB Infinity Cache cannot serve a step's reads from the
 previous one.
 
 The decode kernel (kda_recurrent_step) is timed on its own workload, 256
-sequences x 64 steps, H=32, d=128, and reported under ``decode``.  The same
+sequences x 64 steps, H=32, d=128, and reported under ``decode``.  The other
+two bf16 prefill workloads are reported under ``varlen8`` (8 packed sequences
+of U{512..8192} tokens) and ``long_128k`` (one sequence of 131,072 tokens),
+each far larger than the Infinity Cache, so one input copy serves.  The same
 prefill workload through the fused-gate entry point (kda_chunk_fwd_gated: raw
 bf16 gate and beta activated in the kernel) is reported under ``gated_prefill``.
 
@@ -33,6 +36,10 @@ sys.path.insert(0, ROOT)
 
 METRIC = "KDA prefill tokens/s + decode steps/s (H=32,d=128) and % of MFMA/HBM roofline"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16/fp16 MFMA
+# Algorithmic flops of the chunked form per (token, head) at C = 64, d = 128:
+# 5 C d + 6 d^2 + (2/3) C^2 with triangles counted at half.
+PREFILL_FLOPS_PER_TOKEN_HEAD = round(5 * 64 * 128 + 6 * 128 * 128 + 2 * 64 * 64 / 3)  # 141,995
 PREFILL_BYTES_PER_TOKEN_HEAD = 3 * 128 * 2 + 128 * 4 + 4 + 128 * 2   # q,k,v bf16; g fp32; beta; out bf16
 STATE_BYTES = 128 * 128 * 4
 DECODE_BYTES_PER_HEAD_STEP = 2 * STATE_BYTES + PREFILL_BYTES_PER_TOKEN_HEAD
@@ -45,6 +52,8 @@ KERNEL_SOURCES = {
     "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
 KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["prefill_varlen8"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["prefill_long128k"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
@@ -127,6 +136,54 @@ def bench_prefill(steps: int, warmup: int, per_head: bool = False):
     alg_bytes = T * H * per_token + x.num_seqs * H * 2 * STATE_BYTES
     return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T,
                 workspace_bytes=workspace.numel())
+
+
+def bench_prefill_workload(x, steps: int, warmup: int):
+    """kda_chunk_fwd on one of the larger bf16 workloads (one input copy: each
+    is several GB, far beyond the 256 MB Infinity Cache)."""
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+
+    dev = "cuda:0"
+    q, k, v, g, b, cu = (t.to(dev) for t in (x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens))
+    s0 = None if x.initial_state is None else x.initial_state.to(dev)
+    out = torch.empty_like(v)
+    fs = torch.empty((x.num_seqs, x.num_heads, x.head_k, x.head_v), device=dev)
+    prob = kda.Problem(total_tokens=x.total_tokens, num_seqs=x.num_seqs, num_heads=x.num_heads,
+                       head_k=x.head_k, head_v=x.head_v, qkv_dtype=1, out_dtype=1,
+                       scale=x.scale, qk_l2norm=1, chunk_size=64)
+    workspace = torch.empty(max(kda.chunk_fwd_workspace_bytes(prob), 1), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kda.chunk_fwd(q, k, v, g, b, cu, s0, scale=x.scale, out=out, final_state=fs, workspace=workspace)
+
+    for i in range(warmup):
+        step(i)
+    wall, per = time_launches(step, steps, stream)
+    T, H, N = x.total_tokens, x.num_heads, x.num_seqs
+    states = (2 if s0 is not None else 1) * N * H * STATE_BYTES
+    alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + states
+    res = dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=T,
+               flops=T * H * PREFILL_FLOPS_PER_TOKEN_HEAD)
+    del q, k, v, g, b, out, fs, workspace
+    torch.cuda.empty_cache()
+    return res
+
+
+def prefill_roofline(kernel: str, r, traffic):
+    """HBM roofline of one prefill call, with the MFMA fraction of the same call beside it."""
+    achieved = r["alg_bytes"] / r["per_launch"] / 1e9
+    tflops = r["flops"] / r["per_launch"] / 1e12
+    return {"kernel": kernel, "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": None if traffic is None else round(traffic / r["per_launch"] / 1e9, 2),
+            "traffic_bytes_per_launch": traffic, "alg_bytes_per_launch": r["alg_bytes"],
+            "launch_us": round(r["per_launch"] * 1e6, 2),
+            "mfma_achieved_tflops": round(tflops, 2), "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
+            "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+            "alg_flops_per_launch": r["flops"]}
 
 
 def bench_prefill_gated(steps: int, warmup: int):
@@ -281,22 +338,68 @@ def bench_verify(steps: int, warmup: int):
     return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=N * W)
 
 
-def cpu_baseline(min_seconds: float = 8.0):
-    """The fp64 oracle on the host cores, over whole passes of the same prefill workload."""
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(min_seconds: float = 8.0, heads: int = 0, threads: int = 0):
+    """The fp64 oracle on the host cores, over whole passes of the same prefill workload
+    (``heads``: only the first so many heads, for a bounded single-core sample;
+    ``threads``: the oracle's OpenMP thread count, 0 for its default)."""
     import kda_workloads as w
     import oracle
+    if threads > 0:
+        oracle.set_threads(threads)
     x = w.prefill_4k()
+    H = x.num_heads if heads <= 0 else heads
+    sl = lambda t: t[:, :H].contiguous()
+    s0 = x.initial_state[:, :H].contiguous()
     passes, t0 = 0, time.perf_counter()
     while True:
-        oracle.forward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, x.initial_state, scale=x.scale)
+        oracle.forward(sl(x.q), sl(x.k), sl(x.v), sl(x.g), sl(x.beta), x.cu_seqlens, s0, scale=x.scale)
         passes += 1
         el = time.perf_counter() - t0
         if el >= min_seconds or passes >= 50:
             break
-    return dict(value=passes * x.total_tokens / el, unit="tokens/s", cores=oracle.threads(),
-                kind="oracle",
-                sample=f"{passes} full pass(es) of prefill_T4096_H32_d128 (fp64 recurrence, "
-                       f"{el:.1f} s wall)")
+    # tokens/s of the whole workload (all 32 heads): heads are independent and equal in work
+    value = passes * x.total_tokens * H / x.num_heads / el
+    return dict(value=value, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+                sample=f"{passes} pass(es) of prefill_T4096_H32_d128 over {H} of {x.num_heads} heads "
+                       f"(fp64 recurrence, {el:.1f} s wall), scaled to all heads")
+
+
+def cpu_baseline_single_core():
+    """The same oracle on one thread, in a child process (its OpenMP pool never grows)."""
+    import subprocess
+    code = ("import json, bench; "
+            "print('CPU1 ' + json.dumps(bench.cpu_baseline(min_seconds=8.0, heads=8, threads=1)))")
+    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
+    for line in res.stdout.splitlines():
+        if line.startswith("CPU1 "):
+            return json.loads(line[5:])
+    return {"error": (res.stderr or res.stdout)[-400:]}
+
+
+def hbm_copy_bandwidth(gib: int = 2, reps: int = 10):
+    """A plain device-to-device copy: the practical HBM rate beside the 8 TB/s peak."""
+    import torch
+    n = gib * (1 << 30) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(2):
+        dst.copy_(src)
+    wall, per = time_launches(lambda i: dst.copy_(src), reps, torch.cuda.current_stream())
+    del src, dst
+    torch.cuda.empty_cache()
+    gbs = 2 * n * 4 / per / 1e9
+    return {"kernel": "torch copy_ (read + write)", "bytes_per_launch": 2 * n * 4, "gbs": round(gbs, 1),
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def copy_calibration(gib: int = 1, reps: int = 4):
@@ -337,8 +440,16 @@ def main():
         return
 
     pf = bench_prefill(args.steps, args.warmup)
+    pf["flops"] = pf["tokens"] * 32 * PREFILL_FLOPS_PER_TOKEN_HEAD
     print(f"prefill: {pf['per_launch'] * 1e6:.1f} us per launch (events), "
           f"{pf['wall'] / args.steps * 1e6:.1f} us per step (wall)", file=sys.stderr, flush=True)
+    import kda_workloads as w
+    v8 = bench_prefill_workload(w.varlen8(), min(args.steps, 10), 1)
+    print(f"varlen8 prefill: {v8['per_launch'] * 1e3:.3f} ms per launch (events)", file=sys.stderr, flush=True)
+    lg = bench_prefill_workload(w.long_128k(), min(args.steps, 5), 1)
+    print(f"long_128k prefill: {lg['per_launch'] * 1e3:.3f} ms per launch (events)", file=sys.stderr, flush=True)
+    cp = hbm_copy_bandwidth()
+    print(f"device copy: {cp['gbs']} GB/s", file=sys.stderr, flush=True)
     dc = bench_decode(args.decode_loops)
     dt = bench_decode(1, state_layout="dv_dk")
     print(f"decode, transposed states: {dt['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr,
@@ -393,13 +504,19 @@ def main():
         "config": {"workload": pf["x"].name, "num_seqs": 1, "seq_len": pf["tokens"],
                    "heads": 32, "head_dim": 128, "chunk": 64, "qkv": "bf16", "g_beta": "f32",
                    "state": "f32", "out": "bf16", "input_copies_rotated": 3},
-        "roofline": {"kernel": "kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), "bound": "hbm",
-                     "achieved": round(achieved, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None if tr is None else round(tr / pf["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": tr,
-                     "alg_bytes_per_launch": pf["alg_bytes"],
-                     "launch_us": round(pf["per_launch"] * 1e6, 2),
+        "roofline": {**prefill_roofline("kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), pf, tr),
                      "workspace_bytes": pf["workspace_bytes"]},
+        "hbm_copy": cp,
+        "varlen8": {"workload": v8["x"].name, "tokens": v8["tokens"], "num_seqs": v8["x"].num_seqs,
+                    "tokens_per_s": round(v8["tokens"] / v8["per_launch"], 1),
+                    "ms_per_call": round(v8["per_launch"] * 1e3, 4),
+                    "roofline": prefill_roofline("kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), v8,
+                                                 measured_traffic("prefill_varlen8"))},
+        "long_128k": {"workload": lg["x"].name, "tokens": lg["tokens"],
+                      "tokens_per_s": round(lg["tokens"] / lg["per_launch"], 1),
+                      "ms_per_call": round(lg["per_launch"] * 1e3, 4), "target_ms": 2.0,
+                      "roofline": prefill_roofline("kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), lg,
+                                                   measured_traffic("prefill_long128k"))},
         "decode": {"workload": dc["x"].name, "steps_per_s": round(decode_steps_per_s, 1),
                    "tokens_per_s": round(decode_steps_per_s * dc["num_seqs"], 1),
                    "roofline": {"kernel": "decode_step_kernel", "bound": "hbm",
@@ -461,6 +578,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()
+        line["cpu_baseline"]["model"] = cpu_model()
+        line["cpu_baseline"]["single_core"] = cpu_baseline_single_core()
     print(json.dumps(line), flush=True)
 
 

@@ -54,6 +54,8 @@ def load(path: str):
     lib.kda_oracle_forward.restype = ctypes.c_int
     lib.kda_oracle_threads.argtypes = []
     lib.kda_oracle_threads.restype = ctypes.c_int
+    lib.kda_oracle_set_threads.argtypes = [ctypes.c_int]
+    lib.kda_oracle_set_threads.restype = None
     return lib
 
 
@@ -69,6 +71,11 @@ def _load():
 def threads() -> int:
     """OpenMP threads the C oracle uses."""
     return int(_load().kda_oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Use n OpenMP threads in later calls (the results do not depend on it)."""
+    _load().kda_oracle_set_threads(int(n))
 
 
 def _f32(x) -> np.ndarray:

@@ -53,6 +53,15 @@ int kda_oracle_threads(void) {
 #endif
 }
 
+/* Threads for later calls (n >= 1); the result never depends on it. */
+void kda_oracle_set_threads(int n) {
+#ifdef _OPENMP
+    if (n >= 1) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 /* One (sequence, head) pair, tokens [t0, t1).  S is dk*dv doubles, row-major
  * S[c*dv + j] (key channel c, value channel j).  Work vectors: qf, kf (dk),
  * u (dv). */
