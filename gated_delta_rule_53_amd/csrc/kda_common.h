@@ -127,11 +127,14 @@ __device__ __forceinline__ size_t state_elem(int r, int c, int d, int trans) {
 // defined; then thread 0 of every workgroup accumulates clock64() deltas
 // between consecutive marks into kda_phase_cycles[mark].
 #ifdef KDA_PHASE_TIMING
+#ifndef KDA_PHASE_TID
+#define KDA_PHASE_TID 0  // the thread that records (its wave's timeline)
+#endif
 __device__ unsigned long long kda_phase_cycles[32];
 #define KDA_PHASE_BEGIN long long kda_phase_t = clock64(); long long kda_phase_acc[32] = {0};
 #define KDA_PHASE_MARK(i)                                  \
     do {                                                   \
-        if (threadIdx.x == 0) {                            \
+        if (threadIdx.x == KDA_PHASE_TID) {                \
             const long long kda_now = clock64();           \
             kda_phase_acc[i] += kda_now - kda_phase_t;     \
             kda_phase_t = kda_now;                         \
@@ -139,7 +142,7 @@ __device__ unsigned long long kda_phase_cycles[32];
     } while (0)
 #define KDA_PHASE_END                                                          \
     do {                                                                       \
-        if (threadIdx.x == 0)                                                  \
+        if (threadIdx.x == KDA_PHASE_TID)                                      \
             for (int kda_i = 0; kda_i < 32; ++kda_i)                           \
                 if (kda_phase_acc[kda_i])                                      \
                     atomicAdd(&kda_phase_cycles[kda_i], (unsigned long long)kda_phase_acc[kda_i]); \

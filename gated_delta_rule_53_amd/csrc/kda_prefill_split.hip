@@ -1333,6 +1333,357 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
 }
 
 // --------------------------------------------------------------------------
+// ---- chain_kernel: four waves per (sequence, head, 16-column value tile) ----
+// Wave m (0..3) owns the state rows 32m .. 32m+31 of the tile (two 16x16
+// accumulator tiles) and the 16 token rows 16m .. 16m+15 of D and of the
+// output.  Per chunk, with every operand in registers (loaded straight from
+// the record one chunk ahead, no LDS staging):
+//   1. the wave's S rows go to LDS as fp16 hi/lo B operands (K block m);
+//      barrier;
+//   2. all of S is read back; D_m = Delta0_m - Psi'[m,:] S (Delta0_m =
+//      X'[m,:] diag(rk beta) V, V from LDS) and O^T_m = S^T Qg'[m,:]^T;
+//   3. D_m goes to LDS as hi/lo (half of a 32-token K block); barrier;
+//   4. all of D is read back; S <- diag(e^{G_last}) S + Ke^T D for the
+//      wave's rows, O^T_m += D^T P'[m,:]^T, and the output rows are stored.
+// Two barriers per chunk; each wave issues at most 24 MFMAs per chunk.
+// A fifth wave pulls the record and the V rows of the chunk TOUCH_AHEAD steps
+// ahead into L2 (one 4-byte load per 128-byte line, into an LDS sink; the
+// eight units of a chain take every eighth line each), so the four waves'
+// loads, requested one chunk ahead, find their lines in L2 instead of HBM.
+// It also copies each chunk's V rows into LDS, two chunks ahead.  The four
+// waves issue only their register loads and output stores: a direct-to-LDS
+// copy among them would make the compiler wait for it before LDS reads, and
+// any branch around a memory operation makes it count conservatively.
+// Measured (config 2, per chunk, clock64 in wave 0): about 2.4k cycles,
+// against 2.5k for scan_kernel with one tile per workgroup.
+constexpr int CH_SX_BYTES = 8 * FRAG;    // S: K block s, hi/lo -> (2 s + hl) fragments
+constexpr int CH_DX_BYTES = 4 * FRAG;    // D: K block s, hi/lo -> (2 s + hl) fragments
+constexpr int CH_VBYTES = C * DVT * 2;   // V rows of a chunk, [64][16] bf16 (three buffers)
+constexpr int CH_SINK = 256;             // sink of the touch wave's loads
+// two workgroups with 64 KiB of padding each exceed 160 KiB
+constexpr int CH_LDS = CH_SX_BYTES + CH_DX_BYTES + 3 * CH_VBYTES + CH_SINK;
+static_assert(2 * (CH_LDS + 64 * 1024) > 160 * 1024, "padding keeps one workgroup per CU");
+
+constexpr int CH_THREADS = 320;           // four state waves and the touch wave
+constexpr int TOUCH_AHEAD = 6;
+
+template <typename TOut>
+__global__ __launch_bounds__(CH_THREADS) void chain_kernel(
+    const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state,
+    TOut* __restrict__ out, float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs,
+    int num_heads, int state_trans) {
+    __shared__ __align__(16) unsigned char lds_sx[CH_SX_BYTES];
+    __shared__ __align__(16) unsigned char lds_dx[CH_DX_BYTES];
+    __shared__ __align__(16) unsigned char lds_vb[3 * CH_VBYTES];  // chunk j's V rows in buffer j mod 3
+    __shared__ __align__(16) unsigned char lds_sink[CH_SINK];  // never read
+    extern __shared__ __align__(16) unsigned char lds_pad[];  // sized at launch to keep one workgroup per CU
+    (void)lds_pad;
+    // Workgroup id -> (chain rank, unit): the eight units of a chain share
+    // id mod 8, so they run on one XCD and read the chain's records through
+    // one L2 (as in scan_kernel).
+    const int id = static_cast<int>(blockIdx.x);
+    const int crank = (id / 64) * 8 + (id & 7);
+    const int unit = (id >> 3) & 7;
+    if (crank >= num_seqs * num_heads) return;
+    const int n = order[crank / num_heads], h = crank % num_heads;
+    const int m = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int lane0 = static_cast<int>(threadIdx.x) & 63;
+    const int col0 = unit * DVT;
+    const int c_begin = offsets[n], c_end = offsets[n + 1];
+    const int nc = c_end - c_begin;
+    const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
+    const int row_stride = num_heads * D;
+    size_t head_state = 0;
+    const bool has_state = state_block(slots, num_slots, n, h, num_heads, D, head_state);
+    const float* init = has_state ? initial_state : nullptr;
+    float* fin = has_state ? final_state : nullptr;
+    auto rec_of = [&](int j) { return records + (static_cast<size_t>(c_begin + j) * num_heads + h) * REC_BYTES; };
+    auto tok_of = [&](int j) { return t_first + static_cast<int64_t>(C) * j; };
+    auto len_of = [&](int j) { return static_cast<int>(min64(C, t_last - tok_of(j))); };
+    const int ns = m < 2 ? 1 : 2;  // 32-token K blocks of the triangular X' and P' rows of block m
+
+    // output rows 16 r .. 16 r + 15 of chunk j (the tile of wave r), L of the
+    // chunk's rows valid: lane (g, l16) holds token 16 r + l16, columns 4g .. 4g+3
+    auto store_o = [&](const floatx4& O, int r, int j, int L, int lane) {
+        const int l16 = lane & 15, g = lane >> 4;
+        const int out_bytes = L * row_stride * static_cast<int>(sizeof(TOut));
+        const auto orr = buffer_rsrc(out + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0, out_bytes);
+        const int off = ((16 * r + l16) * row_stride + 4 * g) * static_cast<int>(sizeof(TOut));
+        if constexpr (sizeof(TOut) == 4) {
+            typedef int intx4 __attribute__((ext_vector_type(4)));
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, O), orr, off, 0, 0);
+        } else {
+            typedef int intx2 __attribute__((ext_vector_type(2)));
+            const intx2 pk = {static_cast<int>(pack_bf16x2(O[0], O[1])), static_cast<int>(pack_bf16x2(O[2], O[3]))};
+            __builtin_amdgcn_raw_buffer_store_b64(pk, orr, off, 0, 0);
+        }
+    };
+
+    // V rows of chunk j (64 rows of the unit's 16 columns) into V buffer j & 1:
+    // copy k, lane l: row 32 k + l / 2, columns 8 (l & 1) .. +7; rows past the
+    // chunk's end read as zero.
+    auto copy_v = [&](int j, unsigned char* vbuf, int lane) {
+        const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0,
+                                    len_of(j) * row_stride * 2);
+#pragma unroll
+        for (int k = 0; k < 2; ++k)
+            copy16_to_lds_buf(vr, ((32 * k + (lane >> 1)) * row_stride + 8 * (lane & 1)) * 2,
+                              (lds_u8*)vbuf + k * 32 * DVT * 2);
+    };
+    if (m == 4) {
+        // ---- touch wave: chunk j + TOUCH_AHEAD into L2 during step j ----
+        lds_u8* sink = (lds_u8*)lds_sink;
+        constexpr int REC_LINES = (REC_BYTES + 127) / 128;  // 484
+        auto touch = [&](int j, int lane) {
+            const int i = unit + 8 * lane;  // this unit's lines: unit, unit + 8, ...
+            // record lines (lanes past its end fall outside the range and access nothing)
+            copy4_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), i < REC_LINES ? 128 * i : REC_BYTES, sink);
+            // V: the chunk's rows of this head, 256 bytes = 2 lines each
+            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D,
+                                        len_of(j) * row_stride * 2);
+            copy4_to_lds_buf(vr, ((i >> 1) * row_stride + 64 * (i & 1)) * 2, sink);
+        };
+        // Chunks past the last are clamped to it, so every step issues the
+        // same operations (the clamped ones hit lines already in L2).
+        const int lane = lane0;
+        if (nc > 0) {
+            copy_v(0, lds_vb, lane);
+            copy_v(min(1, nc - 1), lds_vb + CH_VBYTES, lane);
+#pragma unroll
+            for (int j = 2; j < TOUCH_AHEAD; ++j) touch(min(j, nc - 1), lane);
+            static_assert(2 + 2 * (TOUCH_AHEAD - 2) == 10, "ops after chunk 0's copies");
+            wait_vmcnt<2 + 2 * (TOUCH_AHEAD - 2)>();
+        }
+        // Only the V copy goes between the two barriers (so this wave reaches
+        // the second one on time); the touches and the stores of chunk j - 1's
+        // output rows follow it, while the other waves update the state.
+        // Chunk j + 2's V rows are copied during step j into the buffer chunk
+        // j - 1 left; per step this wave issues 2 copies and 2 touches, so
+        // before step j's first barrier chunk j's copies are the ops older
+        // than the last 6 (step 1: the last 10; step 0: the last 10).
+        auto vbuf = [&](int j) { return lds_vb + (j % 3) * CH_VBYTES; };
+        KDA_PHASE_BEGIN
+        for (int j = 0; j < nc; ++j) {
+            if (j == 1)
+                wait_vmcnt<10>();
+            else if (j > 1)
+                wait_vmcnt<6>();
+            KDA_PHASE_MARK(24);
+            lds_barrier();
+            KDA_PHASE_MARK(25);
+            const int jv = min(j + 2, nc - 1);
+            copy_v(jv, vbuf(jv), lane);
+            KDA_PHASE_MARK(26);
+            lds_barrier();
+            KDA_PHASE_MARK(27);
+            touch(min(j + TOUCH_AHEAD, nc - 1), lane);
+            KDA_PHASE_MARK(28);
+        }
+        KDA_PHASE_END;
+
+        wait_vmcnt<0>();
+        return;
+    }
+
+
+    KDA_PHASE_BEGIN
+    // state rows 32m + 4g + j (tile 0) and 32m + 16 + 4g + j (tile 1), column col0 + l16
+    floatx4 S[2];
+    {
+        const int l16 = lane0 & 15, g = lane0 >> 4;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                S[a][j] = init ? init[head_state + state_elem(32 * m + 16 * a + 4 * g + j, col0 + l16, D, state_trans)]
+                               : 0.f;
+    }
+
+    // The operands of chunk j, wave m: -Psi'[m][s], Qg'[m][s] (s = 0..3), Ke^T
+    // of channel blocks 2m, 2m+1 (K blocks 0, 1), X' and P' blocks (m, s <
+    // ns; a second, unused copy of block (m, 0) when ns = 1, so every wave
+    // issues the same loads), e^{G_last} of the wave's state rows.
+    struct Ops {
+        uint4 np[4], qg[4], ke[4], x[2], p[2];
+        floatx4 gl[2];
+    };
+    // The loads come in three groups, each issued between the MFMAs of one
+    // part of the step (a wave issues in order and would otherwise stall on
+    // the memory queue before its products), in the order the next chunk
+    // uses them: X', -Psi' (D); Qg' (output); Ke^T, e^{G_last}, P' (update).
+    // X' and P' block (m, 1) exists for m >= 2 only: for m < 2 it is read
+    // at an offset past the record's range, which returns zeros (no branch,
+    // no mask written over a register with a load in flight).
+    const int blk1_off = ns > 1 ? 0 : REC_BYTES;
+    auto tri_load = [&](const __amdgpu_buffer_rsrc_t& rr, int base, int s_, int lane) {
+        const int off = s_ == 0 ? base + tri_block(m, 0) * FRAG + lane * 16
+                                : base + tri_block(m, 1) * FRAG + lane * 16 + blk1_off;
+        return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rr, off, 0, 0));
+    };
+    auto load_a = [&](Ops& o, const unsigned char* rec, const __amdgpu_buffer_rsrc_t& rr, int i, int lane) {
+        if (i < 2) {
+            o.x[i] = tri_load(rr, REC_X, i, lane);
+        } else {
+            o.np[i - 2] = *reinterpret_cast<const uint4*>(rec + REC_NPSI + (4 * m + i - 2) * FRAG);
+        }
+    };
+    auto load_b = [&](Ops& o, const unsigned char* rec, int i) {  // i = 0 .. 3
+        o.qg[i] = *reinterpret_cast<const uint4*>(rec + REC_QG + (4 * m + i) * FRAG);
+    };
+    auto load_c = [&](Ops& o, const unsigned char* rec, const unsigned char* vec, const __amdgpu_buffer_rsrc_t& rr,
+                      int i, int lane) {  // i = 0 .. 7
+        if (i < 4) {
+            o.ke[i] = *reinterpret_cast<const uint4*>(rec + REC_KE + ((2 * m + (i >> 1)) * 2 + (i & 1)) * FRAG);
+        } else if (i < 6) {
+            o.gl[i - 4] = *reinterpret_cast<const floatx4*>(vec + 16 * (i - 4) * 4);
+        } else {
+            o.p[i - 6] = tri_load(rr, REC_P, i - 6, lane);
+        }
+    };
+    auto load = [&](Ops& o, int j, int lane) {
+        const unsigned char* rec = rec_of(j) + lane * 16;
+        const unsigned char* vec = rec_of(j) + REC_VEC + (32 * m + 4 * (lane >> 4)) * 4;
+        const auto rr = buffer_rsrc(rec_of(j), REC_BYTES);
+#pragma unroll
+        for (int i = 0; i < 6; ++i) load_a(o, rec, rr, i, lane);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) load_b(o, rec, i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) load_c(o, rec, vec, rr, i, lane);
+    };
+    // One chunk with its operands in cur; the next chunk's go into nxt, in
+    // three groups between this chunk's products (18 loads; the compiler
+    // waits for each where it is used).
+    auto step = [&](Ops& cur, Ops& nxt, int j, floatx4& O, int& L, int lane) {
+        const unsigned char* vb_cur = lds_vb + (j % 3) * CH_VBYTES;
+        const int lo16 = lane * 16, l16 = lane & 15, g = lane >> 4;
+        const int jn = min(j + 1, nc - 1);
+        const unsigned char* nrec = rec_of(jn) + lane * 16;
+        const unsigned char* nvec = rec_of(jn) + REC_VEC + (32 * m + 4 * g) * 4;
+        const auto nrr = buffer_rsrc(rec_of(jn), REC_BYTES);
+        // (1) this wave's rows of S into LDS as the B operand of K block m
+        {
+            halfx8 sh, sl;
+            split8h(S[0], S[1], sh, sl);
+            *reinterpret_cast<halfx8*>(lds_sx + (2 * m) * FRAG + lo16) = sh;
+            *reinterpret_cast<halfx8*>(lds_sx + (2 * m + 1) * FRAG + lo16) = sl;
+        }
+        KDA_PHASE_MARK(16);
+        KDA_PHASE_MARK(17);
+        lds_barrier();
+        KDA_PHASE_MARK(18);
+        // (2) S (all 128 rows) back as B operands; V rows of this chunk as B operands
+        halfx8 shs[4], sls[4], vb[2];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            shs[s] = ldh8(lds_sx, (2 * s) * FRAG + lo16);
+            sls[s] = ldh8(lds_sx, (2 * s + 1) * FRAG + lo16);
+        }
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            const int r0 = 32 * s + 4 * g;
+            vb[s] = __builtin_convertvector(
+                bf8_to_f(col8_tr2(vb_cur, 0, DVT, r0, r0 + 16, 0, l16)), halfx8);
+        }
+        // the products of D, each followed by one load of the next chunk (pinned order)
+        floatx4 Dm = mmah(as_halfx8(cur.x[0]), vb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(nxt, nrec, nrr, 0, lane);
+        __builtin_amdgcn_sched_barrier(0);
+        Dm = mmah(as_halfx8(cur.x[1]), vb[1], Dm);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(nxt, nrec, nrr, 1, lane);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            Dm = mmah(as_halfx8(cur.np[s]), shs[s], Dm);
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(nxt, nrec, nrr, 2 + s, lane);
+            __builtin_amdgcn_sched_barrier(0);
+            Dm = mmah(as_halfx8(cur.np[s]), sls[s], Dm);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        // (3) D_m into LDS: rows 16m .. 16m+15 are half (m & 1) of K block m >> 1
+        {
+            halfx4 dh, dl;
+            split4h(Dm, dh, dl);
+            const int o = (2 * (m >> 1)) * FRAG + lo16 + 8 * (m & 1);
+            *reinterpret_cast<halfx4*>(lds_dx + o) = dh;
+            *reinterpret_cast<halfx4*>(lds_dx + o + FRAG) = dl;
+        }
+        O = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+            O = mmah(shs[s], as_halfx8(cur.qg[s]), O);
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(nxt, nrec, s);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        L = len_of(j);
+        KDA_PHASE_MARK(19);
+        lds_barrier();
+        KDA_PHASE_MARK(20);
+        // (4) D back; state update of the wave's rows; output
+        halfx8 dh[2], dl[2];
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
+            dh[s] = ldh8(lds_dx, (2 * s) * FRAG + lo16);
+            dl[s] = ldh8(lds_dx, (2 * s + 1) * FRAG + lo16);
+        }
+        S[0] *= cur.gl[0];
+        S[1] *= cur.gl[1];
+        // the update's products and the output's, each followed by one load of the next chunk
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int a = 0; a < 2; ++a) {
+                S[a] = mmah(as_halfx8(cur.ke[2 * a + s]), dh[s], S[a]);
+                __builtin_amdgcn_sched_barrier(0);
+                load_c(nxt, nrec, nvec, nrr, 2 * s + a, lane);
+                __builtin_amdgcn_sched_barrier(0);
+                S[a] = mmah(as_halfx8(cur.ke[2 * a + s]), dl[s], S[a]);
+                __builtin_amdgcn_sched_barrier(0);
+                load_c(nxt, nrec, nvec, nrr, 4 + 2 * s + a, lane);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        O = mmah(dh[0], as_halfx8(cur.p[0]), O);
+        O = mmah(dh[1], as_halfx8(cur.p[1]), O);
+        store_o(O, m, j, L, lane);
+        KDA_PHASE_MARK(21);
+        (void)l16;
+    };
+
+    if (nc > 0) {
+        Ops B0, B1;
+        floatx4 O = {0.f, 0.f, 0.f, 0.f};
+        int L = 0;
+        load(B0, 0, lane0);
+        // Needed by the first step anyway; waiting here also keeps the
+        // compiler's count at the loop head to what the loop itself issues
+        // (it merges the entry path into every iteration).
+        wait_vmcnt<0>();
+        int j = 0;
+        for (; j + 1 < nc; j += 2) {
+            const int lane = opaque(lane0);
+            step(B0, B1, j, O, L, lane);
+            step(B1, B0, j + 1, O, L, lane);
+        }
+        if (j < nc) step(B0, B1, j, O, L, opaque(lane0));
+        wait_vmcnt<0>();
+    }
+    if (fin) {
+        const int l16 = lane0 & 15, g = lane0 >> 4;
+#pragma unroll
+        for (int a = 0; a < 2; ++a)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                fin[head_state + state_elem(32 * m + 16 * a + 4 * g + j, col0 + l16, D, state_trans)] = S[a][j];
+    }
+    KDA_PHASE_END;
+}
+
+// --------------------------------------------------------------------------
 
 bool split_prefill_applies(const PrefillArgs& a) { return a.qkv_bf16 && a.head_dim == D; }
 
@@ -1383,20 +1734,24 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
         if (e != hipSuccess) return e;
     }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
-    // One tile per workgroup while every tile has a compute unit of its own
-    // (the chunk chain is then the limit); two when tiles outnumber them.
-    const bool pairs = static_cast<size_t>(chains) * (D / DVT) > static_cast<size_t>(device_cu_count());
     const unsigned groups = (chains + 7u) & ~7u;
-    if (pairs)
-        scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(
+    // While every 16-column tile has a compute unit of its own, the chunk
+    // chain's latency is the limit: chain_kernel (four waves share a tile's
+    // chain; 64 KiB of LDS padding keeps one workgroup per CU).  When tiles
+    // outnumber CUs, throughput is: scan_kernel with two tiles per workgroup
+    // reads each record once for both.
+    const bool pairs = static_cast<size_t>(chains) * (D / DVT) > static_cast<size_t>(device_cu_count());
+    if (!pairs) {
+        chain_kernel<TOut><<<groups * 8, CH_THREADS, 64 * 1024, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
             a.state_trans);
-    else
-        scan_kernel<TOut, 1><<<groups * ScanShape<1>::UNITS, ScanShape<1>::THREADS, 0, stream>>>(
-            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
-            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
-            a.state_trans);
+        return hipGetLastError();
+    }
+    scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(
+        static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+        static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
+        a.state_trans);
     return hipGetLastError();
 }
 
