@@ -56,6 +56,7 @@ KERNEL_SOURCES["prefill_varlen8"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["prefill_long128k"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
+KERNEL_SOURCES["verify_normed"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["prologue"] = ["gated_delta_rule_53_amd/csrc/kda_conv.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
 KERNEL_SOURCES["epilogue"] = ["gated_delta_rule_53_amd/csrc/kda_epilogue.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
@@ -311,8 +312,12 @@ def bench_conv(steps: int, warmup: int):
 VERIFY_WIDTH = 4
 
 
-def bench_verify(steps: int, warmup: int):
-    """Verify decode over a state pool: 256 sequences x 4 tokens, H=32, d=128, bf16."""
+def bench_verify(steps: int, warmup: int, normed: bool = False):
+    """Verify decode over a state pool: 256 sequences x 4 tokens, H=32, d=128, bf16.
+
+    normed: kda_recurrent_verify_normed (gated RMSNorm fused); the unfused pair
+    (kda_recurrent_verify, then kda_gated_rmsnorm on its bf16 output) is timed
+    beside it."""
     import torch
 
     import gated_delta_rule_53_amd as kda
@@ -325,17 +330,37 @@ def bench_verify(steps: int, warmup: int):
     pool = x.pool.to(dev)
     out = torch.empty_like(v)
     stream = torch.cuda.current_stream()
+    gen = torch.Generator().manual_seed(8)
+    og = torch.randn(tuple(v.shape), generator=gen).to(torch.bfloat16).to(dev)
+    nw = (1.0 + 0.1 * torch.randn((v.shape[-1],), generator=gen)).to(dev)
+    y = torch.empty_like(v)
 
     def one(i):
+        if normed:
+            kda.recurrent_verify_normed(q, k, v, g, b, pool, idx, og, nw, acc, scale=x.scale, out=out)
+        else:
+            kda.recurrent_verify(q, k, v, g, b, pool, idx, acc, scale=x.scale, out=out)
+
+    def unfused(i):
         kda.recurrent_verify(q, k, v, g, b, pool, idx, acc, scale=x.scale, out=out)
+        kda.gated_rmsnorm(out, og, nw, eps=1e-6, out=y)
 
     for i in range(warmup):
         one(i)
     wall, per = time_launches(one, steps, stream)
     N, W, H = x.q.shape[:3]
+    dv = x.v.shape[-1]
     # per (sequence, head): the starting state read, one state written per token, the token I/O
-    alg_bytes = N * H * ((1 + W) * STATE_BYTES + W * PREFILL_BYTES_PER_TOKEN_HEAD)
-    return dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=N * W)
+    # (normed: plus the output-gate row each token reads)
+    alg_bytes = N * H * ((1 + W) * STATE_BYTES + W * PREFILL_BYTES_PER_TOKEN_HEAD + (W * dv * 2 if normed else 0))
+    res = dict(x=x, wall=wall, per_launch=per, alg_bytes=alg_bytes, tokens=N * W)
+    if normed:
+        for i in range(warmup):
+            unfused(i)
+        _, per_u = time_launches(unfused, steps, stream)
+        # the unfused pair also writes o and reads it back: two more bf16 rows per token-head
+        res.update(per_launch_unfused=per_u, alg_bytes_unfused=alg_bytes + 2 * N * W * H * dv * 2)
+    return res
 
 
 def cpu_model() -> str:
@@ -464,6 +489,11 @@ def main():
     print(f"verify decode: {vf['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     v_achieved = vf["alg_bytes"] / vf["per_launch"] / 1e9
     v_tr = measured_traffic("verify_decode")
+    vn = bench_verify(args.steps, args.warmup, normed=True)
+    print(f"verify decode + fused gated rmsnorm: {vn['per_launch'] * 1e6:.1f} us per launch; unfused pair "
+          f"{vn['per_launch_unfused'] * 1e6:.1f} us (events)", file=sys.stderr, flush=True)
+    vn_achieved = vn["alg_bytes"] / vn["per_launch"] / 1e9
+    vn_tr = measured_traffic("verify_normed")
     print(f"decode: {dc['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     cv = bench_conv(args.steps, args.warmup)
     print(f"short conv prologue: {cv['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
@@ -575,6 +605,16 @@ def main():
                                        "traffic": None if v_tr is None else round(v_tr / vf["per_launch"] / 1e9, 2), "traffic_bytes_per_launch": v_tr,
                                        "alg_bytes_per_launch": vf["alg_bytes"],
                                        "launch_us": round(vf["per_launch"] * 1e6, 2)}},
+        "verify_normed": {"workload": vn["x"].name + "_gated_rmsnorm",
+                          "tokens_per_s": round(vn["tokens"] * args.steps / vn["wall"], 1),
+                          "unfused_us": round(vn["per_launch_unfused"] * 1e6, 2),
+                          "unfused_alg_bytes": vn["alg_bytes_unfused"],
+                          "roofline": {"kernel": "verify_kernel (NORM)", "bound": "hbm",
+                                       "achieved": round(vn_achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                       "frac": round(vn_achieved / HBM_PEAK_GBS, 4),
+                                       "traffic": None if vn_tr is None else round(vn_tr / vn["per_launch"] / 1e9, 2),
+                                       "traffic_bytes_per_launch": vn_tr, "alg_bytes_per_launch": vn["alg_bytes"],
+                                       "launch_us": round(vn["per_launch"] * 1e6, 2)}},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline()

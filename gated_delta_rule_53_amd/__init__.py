@@ -30,6 +30,7 @@ from ._binding import (  # noqa: F401
     recurrent_step_gated,
     recurrent_step_normed,
     recurrent_verify,
+    recurrent_verify_normed,
 )
 
 __all__ = [
@@ -41,6 +42,7 @@ __all__ = [
     "recurrent_step_normed",
     "chunk_fwd_pooled",
     "recurrent_verify",
+    "recurrent_verify_normed",
     "gated_rmsnorm",
     "short_conv",
     "Gate",

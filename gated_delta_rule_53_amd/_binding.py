@@ -91,6 +91,9 @@ def _load() -> ctypes.CDLL:
     lib.kda_chunk_fwd_pooled.restype = ctypes.c_int
     lib.kda_recurrent_verify.argtypes = [P, i32, G, vp, vp, vp, vp, vp, fp, i32, vp, vp, vp, vp]
     lib.kda_recurrent_verify.restype = ctypes.c_int
+    lib.kda_recurrent_verify_normed.argtypes = [P, i32, G, vp, vp, vp, vp, vp, fp, i32, vp, vp, vp, fp,
+                                                ctypes.c_float, vp, vp]
+    lib.kda_recurrent_verify_normed.restype = ctypes.c_int
     lib.kda_gated_rmsnorm.argtypes = [ctypes.c_int64, i32, i32, i32, vp, vp, fp, ctypes.c_float, vp, vp]
     lib.kda_gated_rmsnorm.restype = ctypes.c_int
     lib.kda_short_conv.argtypes = [i32, ctypes.c_int64, i32, i32, i32, i32, vp, vp, vp, vp, vp, vp, vp]
@@ -483,7 +486,9 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
                      num_accepted: Optional[torch.Tensor] = None, *, a_log: Optional[torch.Tensor] = None,
                      dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
                      scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
-                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+                     out_dtype: Optional[torch.dtype] = None, out: Optional[torch.Tensor] = None,
+                     out_gate: Optional[torch.Tensor] = None, norm_weight: Optional[torch.Tensor] = None,
+                     norm_eps: float = 1e-6) -> torch.Tensor:
     """Multi-token verify decode over a slot pool (``kda_recurrent_verify``).
 
     q, k [N, W, H, dk]; v [N, W, H, dv]; g, beta [N, W, H, dk], [N, W, H]
@@ -492,6 +497,10 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     state_indices[n, a-1] (a = num_accepted[n] clamped to [1, W], 1 without
     num_accepted) and writes its state after token t to slot
     state_indices[n, t].  Returns out [N, W, H, dv].
+
+    With out_gate [N, W, H, dv] (q's dtype) and norm_weight [dv] float32 the
+    output epilogue is fused (``kda_recurrent_verify_normed``): the returned
+    rows are o / sqrt(mean(o^2) + norm_eps) * norm_weight * sigmoid(out_gate).
     """
     if q.dim() != 4:
         raise KdaArgumentError(2, f"q must be [N, W, H, dk], got {tuple(q.shape)}")
@@ -514,15 +523,43 @@ def recurrent_verify(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch
     _need(state_indices, "state_indices", (N, W), torch.int32, dev)
     if num_accepted is not None:
         _need(num_accepted, "num_accepted", (N,), torch.int32, dev)
+    normed = out_gate is not None or norm_weight is not None
+    if normed:
+        if out_gate is None or norm_weight is None:
+            raise KdaArgumentError(2, "out_gate and norm_weight go together")
+        _need(out_gate, "out_gate", (N, W, H, dv), q.dtype, dev)
+        _need(norm_weight, "norm_weight", (dv,), torch.float32, dev)
     out_dtype = v.dtype if out_dtype is None else out_dtype
     if out is None:
         out = torch.empty((N, W, H, dv), dtype=out_dtype, device=dev)
     _need(out, "out", (N, W, H, dv), out_dtype, dev)
     prob = _problem(N * W, N, H, dk, dv, q.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
-    _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, None if gate is None else ctypes.byref(gate), _ptr(q),
-                                     _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_pool), P,
-                                     _ptr(state_indices), _ptr(num_accepted), _ptr(out), _stream(dev)))
+    gp = None if gate is None else ctypes.byref(gate)
+    if normed:
+        _check(_lib.kda_recurrent_verify_normed(ctypes.byref(prob), W, gp, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                                _ptr(beta), _ptr(state_pool), P, _ptr(state_indices),
+                                                _ptr(num_accepted), _ptr(out_gate), _ptr(norm_weight),
+                                                float(norm_eps), _ptr(out), _stream(dev)))
+    else:
+        _check(_lib.kda_recurrent_verify(ctypes.byref(prob), W, gp, _ptr(q), _ptr(k), _ptr(v), _ptr(g),
+                                         _ptr(beta), _ptr(state_pool), P, _ptr(state_indices),
+                                         _ptr(num_accepted), _ptr(out), _stream(dev)))
     return out
+
+
+def recurrent_verify_normed(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,
+                            beta: torch.Tensor, state_pool: torch.Tensor, state_indices: torch.Tensor,
+                            out_gate: torch.Tensor, norm_weight: torch.Tensor,
+                            num_accepted: Optional[torch.Tensor] = None, *, norm_eps: float = 1e-6,
+                            **kwargs) -> torch.Tensor:
+    """Verify decode with the output epilogue fused (``kda_recurrent_verify_normed``).
+
+    As ``recurrent_verify`` (same keyword arguments), but each returned row is
+    o / sqrt(mean(o^2) + norm_eps) * norm_weight * sigmoid(out_gate), with
+    out_gate [N, W, H, dv] in q's dtype and norm_weight [dv] float32.
+    """
+    return recurrent_verify(q, k, v, g, beta, state_pool, state_indices, num_accepted, out_gate=out_gate,
+                            norm_weight=norm_weight, norm_eps=norm_eps, **kwargs)
 
 
 def gated_rmsnorm(o: torch.Tensor, gate: torch.Tensor, weight: torch.Tensor, *, eps: float = 1e-6,

@@ -384,11 +384,11 @@ kda_status_t kda_chunk_fwd_pooled(const kda_problem_t* p, const kda_gate_t* gate
                           workspace_bytes, stream, state_slots, num_slots);
 }
 
-kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const kda_gate_t* gate, const void* q,
-                                  const void* k, const void* v, const void* g, const void* beta,
-                                  float* state_pool, int32_t num_slots, const int32_t* state_indices,
-                                  const int32_t* num_accepted, void* out, void* stream) {
-    const char* what = "kda_recurrent_verify";
+static kda_status_t verify_impl(const char* what, const kda_problem_t* p, int32_t width, const kda_gate_t* gate,
+                                const void* q, const void* k, const void* v, const void* g, const void* beta,
+                                float* state_pool, int32_t num_slots, const int32_t* state_indices,
+                                const int32_t* num_accepted, void* out, void* stream,
+                                const kda::NormParams& norm = kda::NormParams{}) {
     kda_status_t st = check_problem(p, what);
     if (st != KDA_OK) return st;
     const kda::GateParams gp = optional_gate(gate, what, st);
@@ -409,7 +409,8 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
                     what);
     {
         const size_t elem = gp.a_log && p->qkv_dtype == KDA_BF16 ? 2 : 4;
-        st = check_alignment(what, p, elem, q, k, v, g, beta, out, {state_pool}, {state_indices, num_accepted});
+        st = check_alignment(what, p, elem, q, k, v, g, beta, out, {state_pool, norm.gate, norm.weight},
+                             {state_indices, num_accepted});
         if (st != KDA_OK) return st;
     }
     kda::VerifyArgs a{};
@@ -425,6 +426,7 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     a.num_slots = num_slots;
     a.indices = state_indices;
     a.accepted = num_accepted;
+    a.norm = norm;
     a.out = out;
     a.num_seqs = p->num_seqs;
     a.width = width;
@@ -436,6 +438,29 @@ kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const k
     a.l2norm = p->qk_l2norm;
     hipStream_t s = static_cast<hipStream_t>(stream);
     return finish(kda::launch_verify(a, s), s, what);
+}
+
+kda_status_t kda_recurrent_verify(const kda_problem_t* p, int32_t width, const kda_gate_t* gate, const void* q,
+                                  const void* k, const void* v, const void* g, const void* beta,
+                                  float* state_pool, int32_t num_slots, const int32_t* state_indices,
+                                  const int32_t* num_accepted, void* out, void* stream) {
+    return verify_impl("kda_recurrent_verify", p, width, gate, q, k, v, g, beta, state_pool, num_slots,
+                       state_indices, num_accepted, out, stream);
+}
+
+kda_status_t kda_recurrent_verify_normed(const kda_problem_t* p, int32_t width, const kda_gate_t* gate,
+                                         const void* q, const void* k, const void* v, const void* g,
+                                         const void* beta, float* state_pool, int32_t num_slots,
+                                         const int32_t* state_indices, const int32_t* num_accepted,
+                                         const void* out_gate, const float* norm_weight, float norm_eps, void* out,
+                                         void* stream) {
+    const char* what = "kda_recurrent_verify_normed";
+    if (!(norm_eps >= 0.f && norm_eps < 1e30f))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: norm_eps must be finite and >= 0", what);
+    if (p && p->num_seqs > 0 && (!out_gate || !norm_weight))
+        return fail(KDA_ERR_NULL_POINTER, "%s: out_gate and norm_weight are required", what);
+    return verify_impl(what, p, width, gate, q, k, v, g, beta, state_pool, num_slots, state_indices, num_accepted,
+                       out, stream, kda::NormParams{out_gate, norm_weight, norm_eps});
 }
 
 kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t channels, int32_t kernel_size,

@@ -213,12 +213,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // [0, num_slots) reads as the zero state and is not written.  The whole
 // starting state is read before anything is written, so idx[a-1] may also
 // appear among the destinations.  Each token is the decode step above.
-template <int D, typename TIn, typename TOut, bool GATED, bool TRANS>
+// NORM: each token's output row goes through LDS to wave 0, which writes the
+// gated RMSNorm of it (as in decode_step_kernel) while the other waves load
+// the next token: o itself never reaches HBM.
+template <int D, typename TIn, typename TOut, bool GATED, bool TRANS, bool NORM>
 __global__ __launch_bounds__(256) void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
     const void* __restrict__ g, const void* __restrict__ beta, GateParams gp, int gph, float* __restrict__ pool,
     int num_slots, const int32_t* __restrict__ indices, const int32_t* __restrict__ accepted,
-    TOut* __restrict__ out, int num_heads, int width, float scale, int l2norm) {
+    TOut* __restrict__ out, int num_heads, int width, float scale, int l2norm, NormParams np) {
     constexpr int NCG = D / 4;
     constexpr int NRG = 256 / NCG;
     constexpr int RPT = D / NRG;
@@ -249,6 +252,7 @@ __global__ __launch_bounds__(256) void verify_kernel(
 
     __shared__ float sq[D], sk[D], se[D];
     __shared__ float red[4][NCG][8];
+    __shared__ float so[NORM ? D : 1];  // the token's output row on its way to the epilogue
     for (int t = 0; t < width; ++t) {
         const size_t row = static_cast<size_t>(n) * width + t;  // token row
         const size_t tok = row * num_heads + h;                  // (token, head)
@@ -301,7 +305,12 @@ __global__ __launch_bounds__(256) void verify_kernel(
                 const float delta = b * (to_f32(v[tok * D + c]) - u);
                 s[i] += (rk * delta) * k4;
                 if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + c * D + 4 * cg));
-                if (cg == 0) out[tok * D + c] = from_f32<TOut>(p + kq * delta);
+                if (cg == 0) {
+                    if constexpr (NORM)
+                        so[c] = p + kq * delta;
+                    else
+                        out[tok * D + c] = from_f32<TOut>(p + kq * delta);
+                }
             }
         } else {
             floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
@@ -350,11 +359,31 @@ __global__ __launch_bounds__(256) void verify_kernel(
             if (rg == 0) {
                 const float kq = rk * rq * aqk;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+                for (int j = 0; j < 4; ++j) {
+                    if constexpr (NORM)
+                        so[4 * cg + j] = p[j] + kq * delta[j];
+                    else
+                        out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+                }
             }
         }
         // sq, sk, se and red are rewritten by the next token
         __syncthreads();
+        if constexpr (NORM) {
+            // so is rewritten only after the next token's first barrier, which
+            // wave 0 reaches once it has read it here
+            if (wave == 0) {
+                float ss = 0.f;
+#pragma unroll
+                for (int c = lane; c < D; c += 64) ss += so[c] * so[c];
+                ss = wave_sum_from(ss, 1);
+                const float r = rsqrtf(ss * (1.f / D) + np.eps);
+                const TIn* og = static_cast<const TIn*>(np.gate) + tok * D;
+#pragma unroll
+                for (int c = lane; c < D; c += 64)
+                    out[tok * D + c] = from_f32<TOut>(so[c] * r * np.weight[c] * gate_sigmoid(to_f32(og[c])));
+            }
+        }
     }
 }
 
@@ -364,10 +393,17 @@ static hipError_t launch_verify_t(const VerifyArgs& a, hipStream_t stream) {
     const TIn* q = static_cast<const TIn*>(a.q);
     const TIn* k = static_cast<const TIn*>(a.k);
     const TIn* v = static_cast<const TIn*>(a.v);
-    auto* kern = a.gate.a_log ? (a.state_trans ? verify_kernel<D, TIn, TOut, true, true> : verify_kernel<D, TIn, TOut, true, false>)
-                              : (a.state_trans ? verify_kernel<D, TIn, TOut, false, true> : verify_kernel<D, TIn, TOut, false, false>);
+    auto pick = [&](auto norm) {
+        constexpr bool N = decltype(norm)::value;
+        return a.gate.a_log ? (a.state_trans ? verify_kernel<D, TIn, TOut, true, true, N>
+                                             : verify_kernel<D, TIn, TOut, true, false, N>)
+                            : (a.state_trans ? verify_kernel<D, TIn, TOut, false, true, N>
+                                             : verify_kernel<D, TIn, TOut, false, false, N>);
+    };
+    auto* kern = a.norm.gate ? pick(std::true_type{}) : pick(std::false_type{});
     kern<<<grid, 256, 0, stream>>>(q, k, v, a.g, a.beta, a.gate, a.gate_per_head, a.pool, a.num_slots, a.indices,
-                                   a.accepted, static_cast<TOut*>(a.out), a.num_heads, a.width, a.scale, a.l2norm);
+                                   a.accepted, static_cast<TOut*>(a.out), a.num_heads, a.width, a.scale, a.l2norm,
+                                   a.norm);
     return hipGetLastError();
 }
 

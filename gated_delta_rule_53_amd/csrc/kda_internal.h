@@ -55,6 +55,7 @@ struct VerifyArgs {
     int num_slots;
     const int32_t* indices;   // [num_seqs, width]
     const int32_t* accepted;  // [num_seqs] or null
+    NormParams norm;          // fused output epilogue (norm.gate null: none)
     void* out;
     int num_seqs;
     int width;

@@ -314,6 +314,26 @@ kda_status_t kda_recurrent_verify(const kda_problem_t *problem, int32_t width, c
                                   void *stream);
 
 /*
+ * kda_recurrent_verify with the layer's output epilogue fused, as
+ * kda_recurrent_step_normed does for one token: the workgroup of a (sequence,
+ * head) holds each token's whole output row, and writes
+ *     out = o / sqrt(mean(o^2) + norm_eps) * norm_weight * sigmoid(out_gate)
+ * in place of o, which never reaches memory (the Ascend model file's
+ * `_project_out` norm and gate).  The states written are those of
+ * kda_recurrent_verify, bit for bit.
+ *
+ *   out_gate    [N * width, H, dv] in qkv_dtype (device, 16-byte aligned)
+ *   norm_weight [dv] float32 (device, 16-byte aligned); norm_eps finite, >= 0
+ * Everything else as kda_recurrent_verify.
+ */
+kda_status_t kda_recurrent_verify_normed(const kda_problem_t *problem, int32_t width, const kda_gate_t *gate,
+                                         const void *q, const void *k, const void *v, const void *g,
+                                         const void *beta, float *state_pool, int32_t num_slots,
+                                         const int32_t *state_indices, const int32_t *num_accepted,
+                                         const void *out_gate, const float *norm_weight, float norm_eps,
+                                         void *out, void *stream);
+
+/*
  * kda_recurrent_step (or, with gate non-NULL, kda_recurrent_step_gated) with
  * the layer's output epilogue fused: the workgroup of a (sequence, head) holds
  * its whole output row, so

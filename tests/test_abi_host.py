@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
         "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv", "kda_recurrent_step_normed",
-        "kda_chunk_fwd_noalloc"])
+        "kda_chunk_fwd_noalloc", "kda_recurrent_verify_normed"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -497,3 +497,22 @@ def test_recurrent_step_normed_rejects_before_launch():
     st = lib.kda_recurrent_step_normed(ctypes.byref(p), None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
                                        1e-6, FAKE, None)
     assert st == 2 and "one token each" in lib.kda_last_error().decode()
+
+
+def test_recurrent_verify_normed_rejects_before_launch():
+    lib = kda.raw_library()
+    p = _prob(total_tokens=12, num_seqs=3)
+    call = lambda prob, width, og, nw, eps: lib.kda_recurrent_verify_normed(
+        ctypes.byref(prob), width, None, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 8, FAKE, None, og, nw, eps, FAKE, None)
+    assert call(p, 4, None, FAKE, 1e-6) == 1 and "out_gate" in lib.kda_last_error().decode()
+    assert call(p, 4, FAKE, None, 1e-6) == 1 and "norm_weight" in lib.kda_last_error().decode()
+    assert call(p, 4, FAKE, FAKE, -1.0) == 2 and "norm_eps" in lib.kda_last_error().decode()
+    assert call(p, 4, FAKE, FAKE, float("nan")) == 2 and "norm_eps" in lib.kda_last_error().decode()
+    # the checks of kda_recurrent_verify apply as well
+    assert call(p, 3, FAKE, FAKE, 1e-6) == 2 and "num_seqs * width" in lib.kda_last_error().decode()
+    st = call(p, 4, MISALIGNED, FAKE, 1e-6)
+    assert st == 2 and "16-byte aligned" in lib.kda_last_error().decode()
+    st = call(p, 4, FAKE, MISALIGNED, 1e-6)
+    assert st == 2 and "16-byte aligned" in lib.kda_last_error().decode()
+    # an empty batch needs no epilogue operands
+    assert call(_prob(total_tokens=0, num_seqs=0), 4, None, None, 1e-6) == 0

@@ -147,3 +147,49 @@ def test_prefill_pooled_gated():
     es = _check_pool(pool, rp, pool_in.numpy(), [3, 0], tol)
     print(f"  err out {eo:.3e} state {es:.3e} (tol {tol:.0e})")
     assert eo <= tol, eo
+
+
+# (N, W, H, d, dtype, state layout, raw gate)
+VERIFY_NORMED_CASES = [
+    (8, 4, 4, 128, torch.bfloat16, "dk_dv", False),
+    (5, 3, 2, 64, torch.float32, "dv_dk", False),
+    (4, 2, 2, 128, torch.bfloat16, "dv_dk", True),
+    (3, 5, 2, 64, torch.bfloat16, "dk_dv", True),
+]
+
+
+@pytest.mark.parametrize("N,W,H,d,dtype,layout,raw", VERIFY_NORMED_CASES)
+def test_verify_normed(N, W, H, d, dtype, layout, raw):
+    """Verify decode with the output epilogue fused: outputs against the slot
+    oracle followed by the epilogue oracle; the pool must equal the plain
+    verify call's pool bit for bit (the same state arithmetic)."""
+    import gated_delta_rule_53_amd as kda
+    from oracle import epilogue
+    x = w.make_verify(N, W, H, d, dtype, g_mu=2.0, pad=1, seed=53 + N + W)
+    gen = torch.Generator().manual_seed(54 + d)
+    og = torch.randn((N, W, H, d), generator=gen).to(dtype)
+    nw = 1.0 + 0.1 * torch.randn((d,), generator=gen)
+    announce(f"verify normed N={N} W={W} H={H} d={d} {dtype} layout={layout} raw_gate={raw}")
+    pool_in = x.pool if layout == "dk_dv" else x.pool.transpose(-1, -2).contiguous()
+    if raw:
+        gi = w.make_gate(W, H, d, dtype, mu=-5.0, seed=55, lead=(N,))
+        g_in, b_in = gi.raw_g, gi.raw_beta
+        kw = dict(a_log=dev(gi.a_log), dt_bias=dev(gi.dt_bias))
+        g_act, b_act = ogate.activate(gi.raw_g, gi.raw_beta, gi.a_log, gi.dt_bias, None)
+    else:
+        g_in, b_in, kw = x.g, x.beta, {}
+        g_act, b_act = x.g, x.beta
+    common = dict(scale=x.scale, state_layout=layout, out_dtype=torch.float32, **kw)
+    pool, pool_plain = dev(pool_in.clone()), dev(pool_in.clone())
+    args = (dev(x.q), dev(x.k), dev(x.v), dev(g_in), dev(b_in))
+    y = kda.recurrent_verify_normed(*args, pool, dev(x.indices), dev(og), dev(nw), dev(x.accepted),
+                                    norm_eps=1e-6, **common)
+    kda.recurrent_verify(*args, pool_plain, dev(x.indices), dev(x.accepted), **common)
+    torch.cuda.synchronize()
+    assert torch.equal(pool, pool_plain)
+    ro, _ = oslots.verify(x.q, x.k, x.v, g_act, b_act, x.pool.double().numpy(), x.indices.numpy(),
+                          x.accepted.numpy(), x.scale)
+    ref = epilogue.gated_rmsnorm(ro, og, nw, 1e-6)
+    err = rel_err(y, ref)
+    print(f"  err {err:.3e}")
+    assert err <= tol_for(dtype), err
