@@ -55,6 +55,7 @@ KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["prefill_varlen8"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["prefill_long128k"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["per_head_prefill"] = KERNEL_SOURCES["prefill"]
+KERNEL_SOURCES["prefill_conv"] = KERNEL_SOURCES["prefill"] + ["gated_delta_rule_53_amd/csrc/kda_conv.hip"]
 KERNEL_SOURCES["verify_decode"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["verify_normed"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
@@ -185,6 +186,74 @@ def prefill_roofline(kernel: str, r, traffic):
             "mfma_achieved_tflops": round(tflops, 2), "mfma_peak_tflops": MFMA_BF16_PEAK_TFLOPS,
             "mfma_frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
             "alg_flops_per_launch": r["flops"]}
+
+
+CONV_K = 4
+
+
+def bench_prefill_conv(steps: int, warmup: int):
+    """kda_chunk_fwd_conv (short convolution fused into the prefill's loads) on
+    the T=4096, H=32, d=128 prefill with K=4 and SiLU, beside the unfused pair
+    (kda_short_conv on the fused projection, then kda_chunk_fwd on its split
+    output).  Three input copies in turn, as for the plain prefill."""
+    import torch
+
+    import gated_delta_rule_53_amd as kda
+    import kda_workloads as w
+
+    x = w.make_conv_prefill([4096], 32, 128, CONV_K, seed=0, name="conv_prefill_T4096_H32_d128_K4")
+    dev = "cuda:0"
+    T, _, H, d = x.x.shape
+    C = 3 * H * d
+    copies = []
+    for _ in range(3):
+        copies.append(dict(x=x.x.to(dev), g=x.g.to(dev), b=x.beta.to(dev), s0=x.initial_state.to(dev),
+                           cs=x.conv_state.to(dev), cs_out=torch.empty_like(x.conv_state, device=dev),
+                           out=torch.empty((T, H, d), dtype=torch.bfloat16, device=dev),
+                           fs=torch.empty_like(x.initial_state, device=dev)))
+    w_, cu = x.weight.to(dev), x.cu_seqlens.to(dev)
+    prob = kda.Problem(total_tokens=T, num_seqs=1, num_heads=H, head_k=d, head_v=d, qkv_dtype=1, out_dtype=1,
+                       scale=x.scale, qk_l2norm=1, chunk_size=64)
+    ws = torch.empty(kda.chunk_fwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
+    qkv = [torch.empty((T, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    stream = torch.cuda.current_stream()
+
+    def fused(i):
+        c = copies[i % 3]
+        kda.chunk_fwd_conv(c["x"], c["g"], c["b"], w_, cu, c["s0"], c["cs"], conv_state_out=c["cs_out"],
+                           scale=x.scale, out=c["out"], final_state=c["fs"], workspace=ws)
+
+    # the unfused pair, timed launch by launch (the split of y into contiguous
+    # q, k, v that kda_chunk_fwd takes is left out: done once, outside)
+    def conv_only(i):
+        c = copies[i % 3]
+        kda.short_conv(c["x"].view(T, C), w_, cu, c["cs"], silu=True, out=y, final_state=c["cs_out"])
+
+    def core_only(i):
+        c = copies[i % 3]
+        kda.chunk_fwd(qkv[0], qkv[1], qkv[2], c["g"], c["b"], cu, c["s0"], scale=x.scale, out=c["out"],
+                      final_state=c["fs"], workspace=ws)
+
+    for i in range(warmup):
+        fused(i)
+    wall, per = time_launches(fused, steps, stream)
+    conv_only(0)
+    yv = y.view(T, 3, H, d)
+    for j in range(3):
+        qkv[j].copy_(yv[:, j])
+    for i in range(warmup):
+        conv_only(i)
+        core_only(i)
+    _, per_c = time_launches(conv_only, steps, stream)
+    _, per_p = time_launches(core_only, steps, stream)
+    per_u = per_c + per_p
+    states = 2 * H * STATE_BYTES + 2 * (CONV_K - 1) * C * 2
+    alg_bytes = T * H * PREFILL_BYTES_PER_TOKEN_HEAD + states
+    # the unfused pair also writes the convolved q/k/v and reads them back (the split copy aside)
+    alg_bytes_unfused = alg_bytes + 2 * T * C * 2
+    return dict(x=x, wall=wall, per_launch=per, per_launch_unfused=per_u, alg_bytes=alg_bytes,
+                alg_bytes_unfused=alg_bytes_unfused, tokens=T, flops=T * H * PREFILL_FLOPS_PER_TOKEN_HEAD)
 
 
 def bench_prefill_gated(steps: int, warmup: int):
@@ -507,6 +576,10 @@ def main():
     print(f"gated prefill: {gp['per_launch'] * 1e6:.1f} us per launch (events)", file=sys.stderr, flush=True)
     g_achieved = gp["alg_bytes"] / gp["per_launch"] / 1e9
     g_tr = measured_traffic("gated_prefill")
+    pc = bench_prefill_conv(args.steps, args.warmup)
+    print(f"prefill with fused conv: {pc['per_launch'] * 1e6:.1f} us per launch; unfused conv + prefill "
+          f"{pc['per_launch_unfused'] * 1e6:.1f} us (events)", file=sys.stderr, flush=True)
+    pc_tr = measured_traffic("prefill_conv")
 
     ms_per_step = pf["wall"] / args.steps * 1e3
     tokens_per_s = pf["tokens"] * args.steps / pf["wall"]
@@ -582,6 +655,12 @@ def main():
                                   "traffic_bytes_per_launch": ep_tr,
                                   "alg_bytes_per_launch": ep["alg_bytes"],
                                   "launch_us": round(ep["per_launch"] * 1e6, 2)}},
+        "prefill_conv": {"workload": pc["x"].name + "_silu",
+                         "tokens_per_s": round(pc["tokens"] * args.steps / pc["wall"], 1),
+                         "unfused_us": round(pc["per_launch_unfused"] * 1e6, 2),
+                         "unfused_alg_bytes": pc["alg_bytes_unfused"],
+                         "roofline": prefill_roofline("kda_chunk_fwd_conv = chunk_map_kernel + prep_kernel (CONV) + "
+                                                      "chain_kernel (CONV) + conv_state_kernel", pc, pc_tr)},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
                           "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),

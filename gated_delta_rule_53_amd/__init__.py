@@ -13,11 +13,13 @@ from __future__ import annotations
 from ._binding import (  # noqa: F401
     KDA_BF16,
     KDA_F32,
+    Conv,
     Gate,
     KdaError,
     Problem,
     abi_version,
     chunk_fwd,
+    chunk_fwd_conv,
     chunk_fwd_gated,
     chunk_fwd_noalloc,
     chunk_fwd_pooled,
@@ -36,6 +38,7 @@ from ._binding import (  # noqa: F401
 __all__ = [
     "chunk_fwd",
     "chunk_fwd_gated",
+    "chunk_fwd_conv",
     "chunk_fwd_noalloc",
     "recurrent_step",
     "recurrent_step_gated",
@@ -46,6 +49,7 @@ __all__ = [
     "gated_rmsnorm",
     "short_conv",
     "Gate",
+    "Conv",
     "chunk_fwd_workspace_bytes",
     "abi_version",
     "library_path",

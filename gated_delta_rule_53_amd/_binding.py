@@ -60,6 +60,18 @@ class Gate(ctypes.Structure):
     ]
 
 
+class Conv(ctypes.Structure):
+    """Mirror of ``kda_conv_t``."""
+
+    _fields_ = [
+        ("kernel_size", ctypes.c_int32),
+        ("silu", ctypes.c_int32),
+        ("weight", ctypes.c_void_p),
+        ("state_in", ctypes.c_void_p),
+        ("state_out", ctypes.c_void_p),
+    ]
+
+
 def _load() -> ctypes.CDLL:
     if not os.path.exists(_LIB_PATH):
         raise ImportError(
@@ -84,6 +96,8 @@ def _load() -> ctypes.CDLL:
     G = ctypes.POINTER(Gate)
     lib.kda_chunk_fwd_gated.argtypes = [P, G, vp, vp, vp, vp, vp, vp, fp, vp, fp, vp, sz, vp]
     lib.kda_chunk_fwd_gated.restype = ctypes.c_int
+    lib.kda_chunk_fwd_conv.argtypes = [P, G, ctypes.POINTER(Conv), vp, vp, vp, vp, fp, vp, fp, vp, sz, vp]
+    lib.kda_chunk_fwd_conv.restype = ctypes.c_int
     lib.kda_recurrent_step_gated.argtypes = [P, G, vp, vp, vp, vp, vp, fp, vp, vp]
     lib.kda_recurrent_step_gated.restype = ctypes.c_int
     i32 = ctypes.c_int32
@@ -423,6 +437,74 @@ def _gate_or_none(a_log, dt_bias, H, dk, lower_bound, dev, per_head=False):
     if dt_bias is None:
         raise KdaArgumentError(1, "a_log needs dt_bias")
     return _gate(a_log, dt_bias, H, dk, lower_bound, dev, per_head)
+
+
+def chunk_fwd_conv(qkv: torch.Tensor, g: torch.Tensor, beta: torch.Tensor, conv_weight: torch.Tensor,
+                   cu_seqlens: Optional[torch.Tensor] = None, initial_state: Optional[torch.Tensor] = None,
+                   conv_state: Optional[torch.Tensor] = None, *, silu: bool = True,
+                   conv_state_out: Optional[torch.Tensor] = None, a_log: Optional[torch.Tensor] = None,
+                   dt_bias: Optional[torch.Tensor] = None, lower_bound: Optional[float] = None,
+                   scale: Optional[float] = None, state_layout: str = "dk_dv", qk_l2norm: bool = True,
+                   out_dtype: Optional[torch.dtype] = None, output_final_state: bool = True,
+                   out: Optional[torch.Tensor] = None, final_state: Optional[torch.Tensor] = None,
+                   workspace: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked prefill with the short convolution fused in (``kda_chunk_fwd_conv``).
+
+    qkv [T, 3, H, d] bfloat16, d = 128: the fused q/k/v projection before
+    the convolution; conv_weight [K, 3 H d] bfloat16 (tap-major, K = 1..4);
+    conv_state [N, K-1, 3 H d] bfloat16 or None (zeros); conv_state_out, if
+    given, receives each request's last K-1 inputs (it may be conv_state).
+    g, beta: float32 activated, or the raw projections in bfloat16 with
+    a_log / dt_bias / lower_bound as for ``chunk_fwd_gated``.  The rest as for
+    ``chunk_fwd``.  Equals ``short_conv`` followed by ``chunk_fwd`` on the
+    split output.  Returns (out, final_state).
+    """
+    if qkv.dim() != 4 or qkv.shape[1] != 3:
+        raise KdaArgumentError(2, f"qkv must be [T, 3, H, d], got {tuple(qkv.shape)}")
+    T, _, H, d = qkv.shape
+    dev = qkv.device
+    if dev.type != "cuda":
+        raise KdaArgumentError(2, "tensors must be on a GPU device")
+    if cu_seqlens is None:
+        cu_seqlens = torch.tensor([0, T], dtype=torch.int32, device=dev)
+    N = cu_seqlens.numel() - 1
+    _need(qkv, "qkv", (T, 3, H, d), None, dev)
+    if conv_weight.dim() != 2:
+        raise KdaArgumentError(2, f"conv_weight must be [K, 3 H d], got {tuple(conv_weight.shape)}")
+    K = conv_weight.shape[0]
+    _need(conv_weight, "conv_weight", (K, 3 * H * d), qkv.dtype, dev)
+    for name, st in (("conv_state", conv_state), ("conv_state_out", conv_state_out)):
+        if st is not None:
+            _need(st, name, (N, K - 1, 3 * H * d), qkv.dtype, dev)
+    gph, gshape = _gate_shape(g, (T, H), d)
+    gate = _gate_or_none(a_log, dt_bias, H, d, lower_bound, dev, gph)
+    gdt = torch.float32 if gate is None else qkv.dtype
+    _need(g, "g", gshape, gdt, dev)
+    _need(beta, "beta", (T, H), gdt, dev)
+    _need(cu_seqlens, "cu_seqlens", (N + 1,), torch.int32, dev)
+    if initial_state is not None:
+        _need(initial_state, "initial_state", (N, H, d, d), torch.float32, dev)
+    out_dtype = qkv.dtype if out_dtype is None else out_dtype
+    if out is None:
+        out = torch.empty((T, H, d), dtype=out_dtype, device=dev)
+    _need(out, "out", (T, H, d), out_dtype, dev)
+    if output_final_state and final_state is None:
+        final_state = torch.empty((N, H, d, d), dtype=torch.float32, device=dev)
+    if final_state is not None:
+        _need(final_state, "final_state", (N, H, d, d), torch.float32, dev)
+    prob = _problem(T, N, H, d, d, qkv.dtype, out_dtype, scale, qk_l2norm, gph, state_layout)
+    ws_bytes = chunk_fwd_workspace_bytes(prob)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    ws_len = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    conv = Conv(kernel_size=K, silu=int(bool(silu)), weight=conv_weight.data_ptr(),
+                state_in=None if conv_state is None else conv_state.data_ptr(),
+                state_out=None if conv_state_out is None else conv_state_out.data_ptr())
+    _check(_lib.kda_chunk_fwd_conv(ctypes.byref(prob), None if gate is None else ctypes.byref(gate),
+                                   ctypes.byref(conv), _ptr(qkv), _ptr(g), _ptr(beta), _ptr(cu_seqlens),
+                                   _ptr(initial_state), _ptr(out), _ptr(final_state), _ptr(workspace), ws_len,
+                                   _stream(dev)))
+    return out, final_state
 
 
 def chunk_fwd_pooled(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, g: torch.Tensor,

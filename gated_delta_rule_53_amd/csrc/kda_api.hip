@@ -149,7 +149,8 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
                             const int32_t* cu_seqlens, const float* initial_state, void* out,
                             float* final_state, void* workspace, size_t workspace_bytes, void* stream,
                             const int32_t* slots = nullptr, int num_slots = 0,
-                            Workspace ws_kind = Workspace::kCaller) {
+                            Workspace ws_kind = Workspace::kCaller, const kda::ConvParams* conv = nullptr,
+                            int64_t qkv_row = 0) {
     if (p->chunk_size != 0 && p->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
     if (p->num_seqs == 0) {
@@ -203,6 +204,8 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
     a.final_state = final_state;
     a.slots = slots;
     a.num_slots = num_slots;
+    a.qkv_row = qkv_row > 0 ? qkv_row : int64_t(p->num_heads) * p->head_k;
+    if (conv) a.conv = *conv;
     a.total_tokens = p->total_tokens;
     a.num_seqs = p->num_seqs;
     a.num_heads = p->num_heads;
@@ -326,6 +329,55 @@ kda_status_t kda_chunk_fwd_gated(const kda_problem_t* p, const kda_gate_t* gate,
     if (st != KDA_OK) return st;
     return chunk_fwd_impl(what, p, gp, q, k, v, raw_g, raw_beta, cu_seqlens, initial_state, out, final_state,
                           workspace, workspace_bytes, stream);
+}
+
+kda_status_t kda_chunk_fwd_conv(const kda_problem_t* p, const kda_gate_t* gate, const kda_conv_t* conv,
+                                const void* qkv, const void* g, const void* beta, const int32_t* cu_seqlens,
+                                const float* initial_state, void* out, float* final_state, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+    const char* what = "kda_chunk_fwd_conv";
+    kda_status_t st = check_problem(p, what);
+    if (st != KDA_OK) return st;
+    const kda::GateParams gp = optional_gate(gate, what, st);
+    if (st != KDA_OK) return st;
+    if (!conv) return fail(KDA_ERR_NULL_POINTER, "%s: conv is NULL", what);
+    if (conv->kernel_size < 1 || conv->kernel_size > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d (supported: 1 to 4)", what, conv->kernel_size);
+    if (conv->silu != 0 && conv->silu != 1) return fail(KDA_ERR_BAD_SHAPE, "%s: silu must be 0 or 1", what);
+    if (p->qkv_dtype != KDA_BF16 || p->head_k != 128)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: the convolution is fused into the bf16, d = 128 path only (use "
+                    "kda_short_conv, then kda_chunk_fwd)", what);
+    const int64_t channels = 3 * int64_t(p->num_heads) * p->head_k;
+    if (channels > (1 << 26)) return fail(KDA_ERR_UNSUPPORTED, "%s: too many heads", what);
+    if (!aligned16(conv->weight) || !aligned16(conv->state_in) || !aligned16(conv->state_out))
+        return fail(KDA_ERR_BAD_SHAPE, "%s: the conv weight and states must be 16-byte aligned", what);
+    if (p->num_seqs > 0 && !conv->weight) return fail(KDA_ERR_NULL_POINTER, "%s: conv->weight is NULL", what);
+    if (p->total_tokens > 0 && !qkv) return fail(KDA_ERR_NULL_POINTER, "%s: qkv is NULL", what);
+    const size_t hd = size_t(p->num_heads) * p->head_k;
+    const kda::bf16_t* x = static_cast<const kda::bf16_t*>(qkv);
+    kda::ConvParams cv{};
+    cv.weight = static_cast<const kda::bf16_t*>(conv->weight);
+    cv.state = static_cast<const kda::bf16_t*>(conv->state_in);
+    cv.K = conv->kernel_size;
+    cv.silu = conv->silu;
+    cv.channels = static_cast<int>(channels);
+    st = chunk_fwd_impl(what, p, gp, x, x ? x + hd : nullptr, x ? x + 2 * hd : nullptr, g, beta, cu_seqlens,
+                        initial_state, out, final_state, workspace, workspace_bytes, stream, nullptr, 0,
+                        Workspace::kCaller, &cv, channels);
+    if (st != KDA_OK || !conv->state_out || p->num_seqs == 0 || conv->kernel_size < 2) return st;
+    // the new conv states, after every read of the old ones
+    kda::ConvArgs a{};
+    a.x = qkv;
+    a.cu_seqlens = cu_seqlens;
+    a.state_in = conv->state_in;
+    a.state_out = conv->state_out;
+    a.total_tokens = p->total_tokens;
+    a.num_seqs = p->num_seqs;
+    a.channels = static_cast<int>(channels);
+    a.kernel_size = conv->kernel_size;
+    a.bf16 = true;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    return finish(kda::launch_conv_state(a, s), s, what);
 }
 
 kda_status_t kda_recurrent_step(const kda_problem_t* p, const void* q, const void* k, const void* v,

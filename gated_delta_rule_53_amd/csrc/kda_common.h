@@ -68,6 +68,72 @@ struct GateParams {
     int has_lower_bound;
 };
 
+// Short causal convolution fused into the prefill's q/k/v loads (the Ascend
+// model file's `KimiShortConvolution`, run on the fused q/k/v projection
+// before the core).  Channels of the fused projection: q = [0, H d),
+// k = [H d, 2 H d), v = [2 H d, 3 H d).  weight null: no convolution.
+struct ConvParams {
+    const bf16_t* weight;  // [K, channels], tap-major
+    const bf16_t* state;   // [N, K - 1, channels] (oldest first), or null for zeros
+    int K;                 // 1 .. 4
+    int silu;              // 1: y * sigmoid(y)
+    int channels;          // 3 H d
+};
+
+// The short convolution's arithmetic on bf16 inputs, shared by kda_short_conv
+// and the prefill that fuses it, so both give the same bits.  Four taps (a
+// filter of K < 4 taps is padded at the front with zero taps); per channel
+// c, with x_m the input m steps back and w_t tap t (tap 3 meets x_0):
+//   y = dot(x_0 w_3 + x_1 w_2, on top of x_2 w_1 + x_3 w_0)
+// as two bf16 pair products with float32 accumulation (v_dot2_f32_bf16).
+typedef __bf16 cbf16x2 __attribute__((ext_vector_type(2)));
+
+// (lo half of a, lo half of b) and (hi of a, hi of b) as packed pairs.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x07060302u); }
+
+// The tap pairs of eight channels: a[c] = (w_3, w_2), b[c] = (w_1, w_0).
+struct ConvTaps8 {
+    uint32_t a[8], b[8];
+};
+
+__device__ __forceinline__ uint32_t word_at(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// w[t]: tap t of eight channels (packed bf16, channel 2e in the low half of word e)
+__device__ __forceinline__ ConvTaps8 conv_taps8(const uint4 (&w)[4]) {
+    ConvTaps8 t;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        t.a[2 * e] = pair_lo(word_at(w[3], e), word_at(w[2], e));
+        t.a[2 * e + 1] = pair_hi(word_at(w[3], e), word_at(w[2], e));
+        t.b[2 * e] = pair_lo(word_at(w[1], e), word_at(w[0], e));
+        t.b[2 * e + 1] = pair_hi(word_at(w[1], e), word_at(w[0], e));
+    }
+    return t;
+}
+
+// The convolution (before any activation) of eight channels from their
+// inputs 0 .. 3 steps back: y[2e], y[2e + 1] for the words e in [E0, E1).
+template <int E0 = 0, int E1 = 4>
+__device__ __forceinline__ void conv8_bf16(const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
+                                           const ConvTaps8& t, float (&y)[8]) {
+#pragma unroll
+    for (int e = E0; e < E1; ++e) {
+        const uint32_t a0 = word_at(x0, e), a1 = word_at(x1, e), a2 = word_at(x2, e), a3 = word_at(x3, e);
+        const uint32_t p01[2] = {pair_lo(a0, a1), pair_hi(a0, a1)};
+        const uint32_t p23[2] = {pair_lo(a2, a3), pair_hi(a2, a3)};
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(cbf16x2, p23[h]),
+                                                            __builtin_bit_cast(cbf16x2, t.b[2 * e + h]), 0.f, false);
+            y[2 * e + h] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(cbf16x2, p01[h]),
+                                                           __builtin_bit_cast(cbf16x2, t.a[2 * e + h]), s, false);
+        }
+    }
+}
+
 // e^x and 1/x through the hardware exp2 and reciprocal (about 1 ulp each).
 __device__ __forceinline__ float gate_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
 __device__ __forceinline__ float gate_sigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + gate_exp(-x)); }

@@ -9,6 +9,11 @@
 // and the request's last K - 1 inputs become its state.  Decode is the same
 // call with one token per request.
 //
+// bf16 inputs go through the shared bf16 dot-product arithmetic
+// (conv8_bf16: four taps, two pair products per channel), the same that the
+// prefill applies when it fuses this convolution into its loads; float32
+// inputs through float32 multiply-adds.
+//
 // HBM-bound: every input is read once and every output written once.  Launch:
 // a thread owns eight consecutive channels (one 16-byte load of bf16) of a run
 // of TB tokens, issues the run's loads first and keeps the K - 1 previous
@@ -21,6 +26,8 @@
 // case has its own launch, request-major: one thread per request and eight
 // channels reads the old state, runs the request's tokens and only then
 // writes the new state.  Empty requests keep their state untouched.
+#include <type_traits>
+
 #include "kda_common.h"
 #include "kda_internal.h"
 
@@ -49,6 +56,23 @@ __device__ __forceinline__ void store8c(T* p, const float (&v)[8]) {
 #pragma unroll
     for (int i = 0; i < BYTES / 16; ++i)
         __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(r)[i], reinterpret_cast<u32x4*>(p) + i);
+}
+
+// bf16: the eight channels' raw words, and their non-temporal store.
+__device__ __forceinline__ uint4 load_raw8(const bf16_t* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ void store_raw8(bf16_t* p, const uint4& v) {
+    typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    __builtin_nontemporal_store(u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<u32x4*>(p));
+}
+
+// The tap rows of eight channels padded at the front to four (zero rows).
+template <int K>
+__device__ __forceinline__ ConvTaps8 load_taps8(const bf16_t* weight, size_t C, int c) {
+    uint4 w[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+        w[t] = t < 4 - K ? uint4{0u, 0u, 0u, 0u} : load_raw8(weight + static_cast<size_t>(t - (4 - K)) * C + c);
+    return conv_taps8(w);
 }
 
 // The request containing token t: the last n with cu[n] <= t < cu[n + 1] (empty requests skipped).
@@ -99,76 +123,126 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
     const int64_t t0 = run * TB;
     const int64_t t1 = min(t0 + TB, total_tokens);
     if (t0 >= t1) return;
-    float w[K][8];
-#pragma unroll
-    for (int j = 0; j < K; ++j) load8c(w[j], weight + static_cast<size_t>(j) * C + c);
-
     int n = request_of(cu, num_seqs, t0);
     int64_t start = cu[n], end = cu[n + 1];
-    // win[m]: the input m + 1 steps before the current token (m < S)
-    float win[S > 0 ? S : 1][8];
-    auto fill_window = [&](int64_t t) {
+    // the input p steps before token t is x[t - p], or, before the request,
+    // its state row S - back (1 .. S steps before the request; clamped: cu_seqlens
+    // is not checked on the device); zero without a state
+    auto back_row = [&](int64_t p) {
+        return static_cast<int>(min(max(start - p, static_cast<int64_t>(1)), static_cast<int64_t>(S)));
+    };
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        // bf16: the raw words, through the shared dot-product arithmetic
+        const ConvTaps8 taps = load_taps8<K>(weight, C, c);
+        uint4 win[3] = {};  // win[m]: the input m + 1 steps back (zero past S)
+        auto fill_window = [&](int64_t t) {
 #pragma unroll
-        for (int m = 0; m < S; ++m) {
-            const int64_t p = t - 1 - m;
-            if (p >= start && p >= 0) {
-                load8c(win[m], x + static_cast<size_t>(p) * C + c);
-            } else {
-                // 1 .. S steps before the request (clamped: cu_seqlens is not checked on the device)
-                const int back = static_cast<int>(min(max(start - p, static_cast<int64_t>(1)), static_cast<int64_t>(S)));
-                if (state_in) {
-                    load8c(win[m], state_in + soff(n, S - back));
-                } else {
+            for (int m = 0; m < S; ++m) {
+                const int64_t p = t - 1 - m;
+                if (p >= start && p >= 0)
+                    win[m] = load_raw8(x + static_cast<size_t>(p) * C + c);
+                else
+                    win[m] = state_in ? load_raw8(state_in + soff(n, S - back_row(p))) : uint4{0u, 0u, 0u, 0u};
+            }
+        };
+        uint4 xin[TB];
 #pragma unroll
-                    for (int i = 0; i < 8; ++i) win[m][i] = 0.f;
-                }
+        for (int u = 0; u < TB; ++u) xin[u] = load_raw8(x + static_cast<size_t>(min(t0 + u, t1 - 1)) * C + c);
+        fill_window(t0);
+#pragma unroll
+        for (int u = 0; u < TB; ++u) {
+            const int64_t t = t0 + u;
+            if (t >= t1) break;
+            if (t >= end) {
+                n = request_of(cu, num_seqs, t);
+                start = cu[n];
+                end = cu[n + 1];
+                fill_window(t);
+            }
+            float acc[8];
+            conv8_bf16(xin[u], win[0], win[1], win[2], taps, acc);
+            if constexpr (SILU) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+            }
+            store8c(y + static_cast<size_t>(t) * C + c, acc);
+#pragma unroll
+            for (int m = S - 1; m > 0; --m) win[m] = win[m - 1];
+            if constexpr (S > 0) win[0] = xin[u];
+            if (t == end - 1 && state_out) {
+#pragma unroll
+                for (int m = 0; m < S; ++m) store_raw8(state_out + soff(n, m), win[S - 1 - m]);
             }
         }
-    };
-    // the run's inputs, loaded raw before any arithmetic (rows past t1 repeat the last row)
-    T xin[TB][8];
+        return;
+    } else {
+        float w[K][8];
 #pragma unroll
-    for (int u = 0; u < TB; ++u) load_vec<8>(xin[u], x + static_cast<size_t>(min(t0 + u, t1 - 1)) * C + c);
-    fill_window(t0);
+        for (int j = 0; j < K; ++j) load8c(w[j], weight + static_cast<size_t>(j) * C + c);
+
+        // win[m]: the input m + 1 steps before the current token (m < S)
+        float win[S > 0 ? S : 1][8];
+        auto fill_window = [&](int64_t t) {
 #pragma unroll
-    for (int u = 0; u < TB; ++u) {
-        const int64_t t = t0 + u;
-        if (t >= t1) break;
-        if (t >= end) {
-            // the run enters the next non-empty request
-            n = request_of(cu, num_seqs, t);
-            start = cu[n];
-            end = cu[n + 1];
-            fill_window(t);
-        }
-        float cur[8];
+            for (int m = 0; m < S; ++m) {
+                const int64_t p = t - 1 - m;
+                if (p >= start && p >= 0) {
+                    load8c(win[m], x + static_cast<size_t>(p) * C + c);
+                } else {
+                    if (state_in) {
+                        load8c(win[m], state_in + soff(n, S - back_row(p)));
+                    } else {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) cur[i] = to_f32(xin[u][i]);
-        float acc[8];
+                        for (int i = 0; i < 8; ++i) win[m][i] = 0.f;
+                    }
+                }
+            }
+        };
+        // the run's inputs, loaded raw before any arithmetic (rows past t1 repeat the last row)
+        T xin[TB][8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) acc[i] = w[K - 1][i] * cur[i];
+        for (int u = 0; u < TB; ++u) load_vec<8>(xin[u], x + static_cast<size_t>(min(t0 + u, t1 - 1)) * C + c);
+        fill_window(t0);
 #pragma unroll
-        for (int m = 0; m < S; ++m)
+        for (int u = 0; u < TB; ++u) {
+            const int64_t t = t0 + u;
+            if (t >= t1) break;
+            if (t >= end) {
+                // the run enters the next non-empty request
+                n = request_of(cu, num_seqs, t);
+                start = cu[n];
+                end = cu[n + 1];
+                fill_window(t);
+            }
+            float cur[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] += w[K - 2 - m][i] * win[m][i];
-        if constexpr (SILU) {
+            for (int i = 0; i < 8; ++i) cur[i] = to_f32(xin[u][i]);
+            float acc[8];
 #pragma unroll
-            for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
-        }
-        store8c(y + static_cast<size_t>(t) * C + c, acc);
-        // shift: the current input becomes one step back
+            for (int i = 0; i < 8; ++i) acc[i] = w[K - 1][i] * cur[i];
 #pragma unroll
-        for (int m = S - 1; m > 0; --m)
+            for (int m = 0; m < S; ++m)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) win[m][i] = win[m - 1][i];
-        if constexpr (S > 0) {
+                for (int i = 0; i < 8; ++i) acc[i] += w[K - 2 - m][i] * win[m][i];
+            if constexpr (SILU) {
 #pragma unroll
-            for (int i = 0; i < 8; ++i) win[0][i] = cur[i];
-        }
-        if (t == end - 1 && state_out) {
-            // the request's last S inputs, oldest first
+                for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+            }
+            store8c(y + static_cast<size_t>(t) * C + c, acc);
+            // shift: the current input becomes one step back
 #pragma unroll
-            for (int m = 0; m < S; ++m) store8c(state_out + soff(n, m), win[S - 1 - m]);
+            for (int m = S - 1; m > 0; --m)
+#pragma unroll
+                for (int i = 0; i < 8; ++i) win[m][i] = win[m - 1][i];
+            if constexpr (S > 0) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) win[0][i] = cur[i];
+            }
+            if (t == end - 1 && state_out) {
+                // the request's last S inputs, oldest first
+#pragma unroll
+                for (int m = 0; m < S; ++m) store8c(state_out + soff(n, m), win[S - 1 - m]);
+            }
         }
     }
 }
@@ -188,6 +262,29 @@ __global__ __launch_bounds__(256) void short_conv_inplace_kernel(const T* __rest
     const size_t C = static_cast<size_t>(channels);
     constexpr int S = K - 1;
     auto soff = [&](int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
+    if constexpr (std::is_same<T, bf16_t>::value) {
+        // bf16: the raw words, through the shared dot-product arithmetic
+        const ConvTaps8 taps = load_taps8<K>(weight, C, c);
+        uint4 win[3] = {};  // win[m]: the input m + 1 steps back (zero past S)
+#pragma unroll
+        for (int m = 0; m < S; ++m) win[m] = load_raw8(state + soff(S - 1 - m));
+        for (int64_t t = start; t < end; ++t) {
+            const uint4 cur = load_raw8(x + static_cast<size_t>(t) * C + c);
+            float acc[8];
+            conv8_bf16(cur, win[0], win[1], win[2], taps, acc);
+            if constexpr (SILU) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+            }
+            store8c(y + static_cast<size_t>(t) * C + c, acc);
+#pragma unroll
+            for (int m = S - 1; m > 0; --m) win[m] = win[m - 1];
+            if constexpr (S > 0) win[0] = cur;
+        }
+#pragma unroll
+        for (int m = 0; m < S; ++m) store_raw8(state + soff(m), win[S - 1 - m]);
+        return;
+    }
     float w[K][8];
 #pragma unroll
     for (int j = 0; j < K; ++j) load8c(w[j], weight + static_cast<size_t>(j) * C + c);
@@ -222,6 +319,53 @@ __global__ __launch_bounds__(256) void short_conv_inplace_kernel(const T* __rest
     // every read of this request's state is done: write the new one, oldest first
 #pragma unroll
     for (int m = 0; m < S; ++m) store8c(state + soff(m), win[S - 1 - m]);
+}
+
+// The state update alone, for the prefill with the convolution fused into
+// its loads (which writes no y): blockIdx.x is the request, blockIdx.y 2048
+// channels.  With the window w = [old state, the request's inputs], the new
+// state is w's last K - 1 entries; all of them are read before any is
+// written, so state_out may be state_in.
+template <typename T>
+__global__ __launch_bounds__(256) void conv_state_kernel(const T* __restrict__ x, const int32_t* __restrict__ cu,
+                                                         const T* state_in, T* state_out, int64_t total_tokens,
+                                                         int channels, int K) {
+    const int n = static_cast<int>(blockIdx.x);
+    const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
+    if (c >= channels) return;
+    int64_t start = cu[n], end = cu[n + 1];
+    if (start < 0 || end > total_tokens || end < start) end = start;  // malformed: no tokens
+    const int64_t len = end - start;
+    const size_t C = static_cast<size_t>(channels);
+    const int S = K - 1;
+    float v[3][8];
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        if (m >= S) break;
+        const int64_t i = len + m;  // index into the window
+        if (i >= S) {
+            load8c(v[m], x + static_cast<size_t>(start + i - S) * C + c);
+        } else if (state_in) {
+            load8c(v[m], state_in + (static_cast<size_t>(n) * S + i) * C + c);
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[m][e] = 0.f;
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < 3; ++m) {
+        if (m >= S) break;
+        store8c(state_out + (static_cast<size_t>(n) * S + m) * C + c, v[m]);
+    }
+}
+
+hipError_t launch_conv_state(const ConvArgs& a, hipStream_t stream) {
+    if (a.num_seqs == 0 || a.kernel_size < 2 || !a.state_out) return hipSuccess;
+    const dim3 grid(static_cast<unsigned>(a.num_seqs), static_cast<unsigned>((a.channels / 8 + 255) / 256));
+    conv_state_kernel<bf16_t><<<grid, 256, 0, stream>>>(
+        static_cast<const bf16_t*>(a.x), a.cu_seqlens, static_cast<const bf16_t*>(a.state_in),
+        static_cast<bf16_t*>(a.state_out), a.total_tokens, a.channels, a.kernel_size);
+    return hipGetLastError();
 }
 
 template <int K, typename T>

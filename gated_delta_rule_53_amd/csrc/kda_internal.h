@@ -85,6 +85,11 @@ struct PrefillArgs {
     // outside [0, num_slots) starts from zero and is not written.
     const int32_t* slots;
     int num_slots;
+    // Elements between consecutive tokens of q, k and v (H d for separate
+    // [T, H, d] tensors; 3 H d when they are the column blocks of the fused
+    // projection, as with conv).
+    int64_t qkv_row;
+    ConvParams conv;  // conv.weight null: q, k, v are used as given
     int64_t total_tokens;
     int num_seqs;
     int num_heads;
@@ -126,6 +131,10 @@ struct ConvArgs {
 
 hipError_t launch_decode(const DecodeArgs& a, hipStream_t stream);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t stream);
+// The conv-state update alone (bf16): each request's last K - 1 inputs of x
+// [T, channels] (its old state followed by its inputs when it is shorter)
+// into state_out; state_out may be state_in.
+hipError_t launch_conv_state(const ConvArgs& a, hipStream_t stream);
 hipError_t launch_gated_rmsnorm(const EpilogueArgs& a, hipStream_t stream);
 hipError_t launch_verify(const VerifyArgs& a, hipStream_t stream);
 // fp32 q/k/v, or dk = dv = 64: one workgroup per (sequence, head, 16-column

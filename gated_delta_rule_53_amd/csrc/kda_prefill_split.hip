@@ -38,6 +38,8 @@
 //                     form the output behind them, for all its tiles.
 // Inside prep, operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except
 // k.k in A (inverted afterwards); the 16x16 diagonal inverses are fp32.
+#include <type_traits>
+
 #include "kda_bf16_mfma.h"
 #include "kda_internal.h"
 
@@ -112,7 +114,8 @@ constexpr int P_GL = P_EL + D * 4;                              // e^{G_last}
 constexpr int P_G31 = P_GL + D * 4;                             // fp32 [128] G_31 (natural log)
 constexpr int P_GLL = P_G31 + D * 4;                            // fp32 [128] G_last (natural log)
 constexpr int P_FLAG = P_GLL + D * 4;                           // int: the item takes the exact path
-constexpr int P_LDS = P_FLAG + 16;
+constexpr int P_CW = P_FLAG + 16;                               // conv taps of the item's head: k, q [4][128] bf16
+constexpr int P_LDS = P_CW + 2 * 4 * D * 2;
 static_assert(P_LDS <= 160 * 1024, "prep LDS budget");
 constexpr int P_WT = P_XDH;                                     // 16 wave totals [16][128] fp32 (phase 1 only)
 static_assert(16 * D * 4 <= 4 * 4 * BLK, "wave totals alias X_RR and X_RR diag(rk^2 beta)");
@@ -121,6 +124,10 @@ static_assert(16 * D * 4 <= 4 * 4 * BLK, "wave totals alias X_RR and X_RR diag(r
 // planes are formed there.
 constexpr int P_GK = 0, P_GQ = C * D * 4, P_GE = 2 * C * D * 4;
 static_assert(P_GE + C * D * 4 <= P_R3_END && P_R3_END <= P_PH, "exact-path arrays fit below P'");
+// Fused convolution: the raw k and q rows -4 .. 63 of the chunk (row -4 + i
+// at i * 256 bytes), in region 1 from the top of an item until its planes.
+constexpr int P_CVK = 0, P_CVQ = (C + 4) * D * 2;
+static_assert(P_CVQ + (C + 4) * D * 2 <= P_R2, "raw rows fit in region 1");
 // Largest |G_r - G_31| (natural log) the reference-token factors may span:
 // e^{60} and e^{-60} are well inside the float32 and bf16 normal range.
 constexpr float kRefSpan = 60.f;
@@ -243,6 +250,47 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
     for (int r = r0 + 4; r < C; ++r) step(r, false);
 }
 
+// ---- the short convolution fused into the q/k/v loads ----
+// Its four taps (K < 4: leading taps of weight zero) meet the rows r - 3 ..
+// r of the fused projection; the arithmetic is that of kda_short_conv term
+// for term (the tap that meets row r first, then one fused multiply-add per
+// step back), then y * sigmoid(y) with silu, rounded to bf16 as the
+// standalone convolution's output is, so the core sees the same inputs.
+
+// Lane l gets lane l - 1's words (lane 0 gets lane 63's): a DPP whole-wave rotate.
+__device__ __forceinline__ uint4 ror1_u4(const uint4& v) {
+    constexpr int kWaveRor1 = 0x13C;
+    return uint4{static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v.x), kWaveRor1, 0xF, 0xF, false)),
+                 static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v.y), kWaveRor1, 0xF, 0xF, false)),
+                 static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v.z), kWaveRor1, 0xF, 0xF, false)),
+                 static_cast<unsigned>(__builtin_amdgcn_update_dpp(0, static_cast<int>(v.w), kWaveRor1, 0xF, 0xF, false))};
+}
+
+// x0 .. x3: the eight channels' inputs 0 .. 3 steps back; t: their tap pairs.
+// The convolution of kda_short_conv (conv8_bf16), then silu, rounded to bf16;
+// zero for rows past the chunk's end.
+// Channels 2e, 2e + 1 for the words e in [E0, E1) (the others are left zero).
+template <int E0 = 0, int E1 = 4>
+__device__ __forceinline__ floatx8 conv8(const uint4& x0, const uint4& x1, const uint4& x2, const uint4& x3,
+                                        const ConvTaps8& t, int silu, bool live) {
+    float a[8] = {};
+    conv8_bf16<E0, E1>(x0, x1, x2, x3, t, a);
+    if (silu) {
+#pragma unroll
+        for (int i = 2 * E0; i < 2 * E1; ++i) a[i] *= gate_sigmoid(a[i]);
+    }
+    // bf16 round to nearest even in hardware (the standalone kernel's
+    // software rounding gives the same value for every non-NaN input)
+    floatx8 y = {};
+#pragma unroll
+    for (int i = 2 * E0; i < 2 * E1; i += 2) {
+        const uint32_t p = pack_bf16x2(a[i], a[i + 1]);
+        y[i] = live ? __uint_as_float(p << 16) : 0.f;
+        y[i + 1] = live ? __uint_as_float(p & 0xffff0000u) : 0.f;
+    }
+    return y;
+}
+
 // Sequence of chunk cg: the last n with offsets[n] <= cg (empty sequences are skipped).
 __device__ __forceinline__ int find_seq(const int32_t* offsets, int num_seqs, int cg) {
     int lo = 0, hi = num_seqs;  // offsets[lo] <= cg < offsets[hi]
@@ -320,12 +368,20 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 // --------------------------------------------------------------------------
 // With GATED, g and beta are the raw gate and raw beta (bf16), activated as
 // each item is consumed; rows past a sequence's end get g = beta = 0.
-template <bool GATED, bool GPH>
+// With CONV, q and k are column blocks of the fused projection (qk_row
+// elements per token) before the short convolution, which is applied here:
+// at the top of an item every thread puts its raw k and q row into LDS
+// (region 1, free until the planes), beside the four rows before the chunk
+// (from the previous chunk, or the request's conv state for a sequence's
+// first chunk) and the head's taps, which waves 0-3 fetched with the item's
+// other inputs; after the first barrier each row is convolved from rows
+// r - 3 .. r.
+template <bool GATED, bool GPH, bool CONV>
 __global__ __launch_bounds__(PNT) void prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const void* __restrict__ g_in,
     const void* __restrict__ beta_in, GateParams gp, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
-    float scale, int l2norm) {
+    float scale, int l2norm, int qk_row, ConvParams cv) {
     const float* __restrict__ g = static_cast<const float*>(g_in);
     const float* __restrict__ beta = static_cast<const float*>(beta_in);
     const bf16_t* __restrict__ graw = static_cast<const bf16_t*>(g_in);
@@ -354,11 +410,13 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     // as zero with no branch, and nothing here waits for a load in flight (the
     // gated values are activated, and masked, where they are consumed).
     uint4 pk, pq, pgr = {0u, 0u, 0u, 0u};
+    uint4 pcv = {0u, 0u, 0u, 0u};  // CONV: waves 0, 1: k, q rows -4 .. -1; waves 2, 3: k, q taps
     floatx4 pg0 = {0.f, 0.f, 0.f, 0.f}, pg1 = {0.f, 0.f, 0.f, 0.f};
     float pb = 0.f, pgs = 0.f;
     uint32_t pgs_raw = 0, pb_raw = 0;
     int pL = 0;
-    const int row_bytes = num_heads * D * 2;  // one token's q or k row of all heads, bf16
+    const int row_bytes = num_heads * D * 2;  // one token's g row of all heads, bf16 (twice that in fp32)
+    const int qk_bytes = qk_row * 2;          // one token's q or k row
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
         const int n = find_seq(offsets, num_seqs, cg);
@@ -367,8 +425,41 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         const int r = tid >> 4, cc = tid & 15;
         const size_t head0 = static_cast<size_t>(start) * num_heads + h;  // (first row, head)
         const int voff = r * row_bytes + 16 * cc;
-        pk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(k + head0 * D, L * row_bytes), voff, 0, 0));
-        pq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(q + head0 * D, L * row_bytes), voff, 0, 0));
+        const size_t qk0 = static_cast<size_t>(start) * qk_row + h * D;
+        const int qoff = r * qk_bytes + 16 * cc;
+        pk = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(k + qk0, L * qk_bytes), qoff, 0, 0));
+        pq = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(q + qk0, L * qk_bytes), qoff, 0, 0));
+        if constexpr (CONV) {
+            // lane (l4, cc) of waves 0 and 1: the row -4 + l4 before the chunk
+            // of k and of q: from the previous chunk, or for a sequence's first
+            // chunk the conv state's row K - 5 + l4 (entries past its range, or
+            // with no state, read as zero); of waves 2 and 3: tap l4 of the
+            // head's k and q channels 8 cc .. 8 cc + 7 (taps padded at the front
+            // to four); the other waves read nothing (an empty range)
+            const int l4 = r & 3;
+            const bool first = cg == offsets[n];
+            const int srow_bytes = cv.channels * 2;
+            const bool is_k = (wave & 1) == 0;
+            const int blk = is_k ? num_heads * D : 0;  // channel block of k or q
+            const int s_idx = cv.K - 5 + l4;
+            const int s_range = cv.state ? (cv.K - 1) * srow_bytes : 0;
+            const int tap = l4 - (4 - cv.K);
+            const int w_range = (cv.K - 1) * srow_bytes + D * 2;
+            const bf16_t* xs = is_k ? k : q;
+            const bf16_t* base;
+            int range, off;
+            if (wave < 2) {
+                base = first ? (cv.state ? cv.state + static_cast<size_t>(n) * (cv.K - 1) * cv.channels + blk + h * D : xs)
+                             : xs + qk0 - 4 * static_cast<size_t>(qk_row);
+                range = first ? s_range : 4 * qk_bytes;
+                off = first ? (s_idx >= 0 ? s_idx * srow_bytes + 16 * cc : s_range) : l4 * qk_bytes + 16 * cc;
+            } else {
+                base = wave < 4 ? cv.weight + blk + h * D : xs;
+                range = wave < 4 ? w_range : 0;
+                off = wave < 4 && tap >= 0 ? tap * srow_bytes + 16 * cc : range;
+            }
+            pcv = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(buffer_rsrc(base, range), off, 0, 0));
+        }
         if constexpr (GATED) {
             if constexpr (GPH)
                 pgs_raw = __builtin_amdgcn_raw_buffer_load_b16(buffer_rsrc(graw + head0, L * num_heads * 2), r * num_heads * 2, 0, 0);
@@ -443,7 +534,19 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         // ======== phase 1: norms, cumulative log-decay, operand planes ========
         // rows past the chunk's end were loaded as zeros; only activated gates need a mask
         if (tid == 0) *sFlag = 0;  // last read after the previous item's second barrier
-        const floatx8 kf = unpack8(pk), qf = unpack8(pq);
+        floatx8 kf, qf;
+        if constexpr (CONV) {
+            // raw rows into region 1 (convolved after the first barrier)
+            *reinterpret_cast<uint4*>(smem + P_CVK + (4 + rp) * D * 2 + 16 * cc) = pk;
+            *reinterpret_cast<uint4*>(smem + P_CVQ + (4 + rp) * D * 2 + 16 * cc) = pq;
+            if (wave < 2)
+                *reinterpret_cast<uint4*>(smem + (wave == 0 ? P_CVK : P_CVQ) + l4 * D * 2 + 16 * cc) = pcv;
+            else if (wave < 4)
+                *reinterpret_cast<uint4*>(smem + P_CW + (wave - 2) * 4 * D * 2 + l4 * D * 2 + 16 * cc) = pcv;
+        } else {
+            kf = unpack8(pk);
+            qf = unpack8(pq);
+        }
         // inclusive prefix of g over the wave's four rows (16-lane groups), then
         // the totals of the 16 waves through LDS
         floatx8 gr;
@@ -485,6 +588,21 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         // (the wave totals live in the X_RR planes, which they do not read)
         if (prev_rec) frags_out(prev_rec, tid);
         lds_barrier();
+        if constexpr (CONV) {
+            // row rp from the raw rows rp - 3 .. rp and the head's taps
+            auto conv_rows = [&](int base, int taps, const uint4& own) {
+                uint4 w[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) w[t] = *reinterpret_cast<const uint4*>(smem + taps + t * D * 2 + 16 * cc);
+                const unsigned char* row = smem + base + (4 + rp) * D * 2 + 16 * cc;
+                const uint4 x1 = *reinterpret_cast<const uint4*>(row - D * 2);
+                const uint4 x2 = *reinterpret_cast<const uint4*>(row - 2 * D * 2);
+                const uint4 x3 = *reinterpret_cast<const uint4*>(row - 3 * D * 2);
+                return conv8(own, x1, x2, x3, conv_taps8(w), cv.silu, rp < pL);
+            };
+            kf = conv_rows(P_CVK, P_CW, pk);
+            qf = conv_rows(P_CVQ, P_CW + 4 * D * 2, pq);
+        }
         // Channel threads turn the wave totals of channel c into offsets in
         // place: with P_w the sum of the totals of waves 0 .. w-1, entry (w, c)
         // becomes P_w - P_8, the cumulative g before wave w's first row minus
@@ -1359,20 +1477,24 @@ __global__ __launch_bounds__(ScanShape<NT>::THREADS) void scan_kernel(
 constexpr int CH_SX_BYTES = 8 * FRAG;    // S: K block s, hi/lo -> (2 s + hl) fragments
 constexpr int CH_DX_BYTES = 4 * FRAG;    // D: K block s, hi/lo -> (2 s + hl) fragments
 constexpr int CH_VBYTES = C * DVT * 2;   // V rows of a chunk, [64][16] bf16 (three buffers)
-constexpr int CH_SINK = 256;             // sink of the touch wave's loads
+constexpr int CH_SINK = 1024;            // sink of the touch waves' loads
 // two workgroups with 64 KiB of padding each exceed 160 KiB
 constexpr int CH_LDS = CH_SX_BYTES + CH_DX_BYTES + 3 * CH_VBYTES + CH_SINK;
 static_assert(2 * (CH_LDS + 64 * 1024) > 160 * 1024, "padding keeps one workgroup per CU");
 
 constexpr int CH_THREADS = 320;           // four state waves and the touch wave
+constexpr int CH_THREADS_CONV = 512;      // with the convolution fused: four helper waves
 constexpr int TOUCH_AHEAD = 6;
 
-template <typename TOut>
-__global__ __launch_bounds__(CH_THREADS) void chain_kernel(
+// With CONV, v is the value block of the fused projection (v_row elements
+// per token) before the short convolution, and the touch wave convolves the
+// chunk's V rows instead of copying them (see below).
+template <typename TOut, bool CONV>
+__global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_kernel(
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state,
     TOut* __restrict__ out, float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs,
-    int num_heads, int state_trans) {
+    int num_heads, int state_trans, int v_row, ConvParams cv) {
     __shared__ __align__(16) unsigned char lds_sx[CH_SX_BYTES];
     __shared__ __align__(16) unsigned char lds_dx[CH_DX_BYTES];
     __shared__ __align__(16) unsigned char lds_vb[3 * CH_VBYTES];  // chunk j's V rows in buffer j mod 3
@@ -1423,15 +1545,17 @@ __global__ __launch_bounds__(CH_THREADS) void chain_kernel(
     // V rows of chunk j (64 rows of the unit's 16 columns) into V buffer j & 1:
     // copy k, lane l: row 32 k + l / 2, columns 8 (l & 1) .. +7; rows past the
     // chunk's end read as zero.
+    auto v_rows = [&](int j) {  // the chunk's V rows of this head, v_row elements apart
+        return buffer_rsrc(v + static_cast<size_t>(tok_of(j)) * v_row + h * D + col0, len_of(j) * v_row * 2);
+    };
     auto copy_v = [&](int j, unsigned char* vbuf, int lane) {
-        const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D + col0,
-                                    len_of(j) * row_stride * 2);
+        const auto vr = v_rows(j);
 #pragma unroll
         for (int k = 0; k < 2; ++k)
-            copy16_to_lds_buf(vr, ((32 * k + (lane >> 1)) * row_stride + 8 * (lane & 1)) * 2,
+            copy16_to_lds_buf(vr, ((32 * k + (lane >> 1)) * v_row + 8 * (lane & 1)) * 2,
                               (lds_u8*)vbuf + k * 32 * DVT * 2);
     };
-    if (m == 4) {
+    if (m >= 4) {
         // ---- touch wave: chunk j + TOUCH_AHEAD into L2 during step j ----
         lds_u8* sink = (lds_u8*)lds_sink;
         constexpr int REC_LINES = (REC_BYTES + 127) / 128;  // 484
@@ -1440,13 +1564,152 @@ __global__ __launch_bounds__(CH_THREADS) void chain_kernel(
             // record lines (lanes past its end fall outside the range and access nothing)
             copy4_to_lds_buf(buffer_rsrc(rec_of(j), REC_BYTES), i < REC_LINES ? 128 * i : REC_BYTES, sink);
             // V: the chunk's rows of this head, 256 bytes = 2 lines each
-            const auto vr = buffer_rsrc(v + (static_cast<size_t>(tok_of(j)) * num_heads + h) * D,
-                                        len_of(j) * row_stride * 2);
-            copy4_to_lds_buf(vr, ((i >> 1) * row_stride + 64 * (i & 1)) * 2, sink);
+            const auto vr = buffer_rsrc(v + static_cast<size_t>(tok_of(j)) * v_row + h * D, len_of(j) * v_row * 2);
+            copy4_to_lds_buf(vr, ((i >> 1) * v_row + 64 * (i & 1)) * 2, sink);
         };
         // Chunks past the last are clamped to it, so every step issues the
         // same operations (the clamped ones hit lines already in L2).
         const int lane = lane0;
+        if constexpr (CONV) {
+            // Four helper waves, hi = m - 4, one per SIMD beside a state wave:
+            // lane l convolves row l of a chunk in columns 4 hi .. 4 hi + 3
+            // (words we0 = 2 (hi & 1), we0 + 1 of the 16-byte half hf = hi / 2)
+            // from the raw rows l - 3 .. l (of this chunk in the lanes below,
+            // of the previous chunk, or before a sequence's first chunk its
+            // conv state, in lanes 61 .. 63 of p).  Chunk j + 2 is convolved
+            // into its V buffer during step j (the buffer was last read in
+            // step j - 1): word we0 between the two barriers, we0 + 1 after the
+            // second, while the state waves work; its raw rows were loaded
+            // during step j - 1.  The three raw-row registers rotate by
+            // unrolling, so none waits on a load by being copied.  Helper 1
+            // touches the V lines, the others the record lines.
+            const int hi = m - 4, hf = hi >> 1;
+            uint4 prev, ra, rb, rc, r0;
+            ConvTaps8 taps;
+            {
+                const int wrow = cv.channels * 2, range = (cv.K - 1) * wrow + 32;
+                const auto wr = buffer_rsrc(cv.weight + 2 * num_heads * D + h * D + col0, range);
+                uint4 w[4];
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    const int jt = t - (4 - cv.K);
+                    w[t] = __builtin_bit_cast(
+                        uint4, __builtin_amdgcn_raw_buffer_load_b128(wr, jt >= 0 ? jt * wrow + 16 * hf : range, 0, 0));
+                }
+                taps = conv_taps8(w);
+                const int srow = cv.channels * 2, s_range = cv.state ? (cv.K - 1) * srow : 0;
+                const auto sr = buffer_rsrc(cv.state ? cv.state + static_cast<size_t>(n) * (cv.K - 1) * cv.channels +
+                                                           2 * num_heads * D + h * D + col0
+                                                     : v,
+                                            s_range);
+                const int s_idx = cv.K - 65 + lane;  // lanes 61 .. 63: 3 .. 1 steps before the sequence
+                prev = __builtin_bit_cast(
+                    uint4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_idx >= 0 ? s_idx * srow + 16 * hf : s_range, 0, 0));
+            }
+            auto raw = [&](int j) {
+                return __builtin_bit_cast(uint4,
+                                          __builtin_amdgcn_raw_buffer_load_b128(v_rows(j), lane * v_row * 2 + 16 * hf, 0, 0));
+            };
+            // word e (channels 2e, 2e + 1 of the half) of chunk j's V rows from
+            // its raw rows x and the previous chunk's p
+            auto conv_word = [&](int j, const uint4& x, const uint4& p, auto ew) {
+                constexpr int E = decltype(ew)::value;
+                const bool live = lane < len_of(j);
+                // rows l - 1, l - 2, l - 3 by rotating the wave (lanes 61 .. 63
+                // hand over the previous chunk's rows where the wrap needs them)
+                const uint4 x1 = ror1_u4(lane == 63 ? p : x);
+                const uint4 x2 = ror1_u4(ror1_u4(lane >= 62 ? p : x));
+                const uint4 x3 = ror1_u4(ror1_u4(ror1_u4(lane >= 61 ? p : x)));
+                const floatx8 y = conv8<E, E + 1>(x, x1, x2, x3, taps, cv.silu, live);
+                *reinterpret_cast<uint32_t*>(lds_vb + (j % 3) * CH_VBYTES + lane * DVT * 2 + 16 * hf + 4 * E) =
+                    pack_bf16x2(y[2 * E], y[2 * E + 1]);
+            };
+            using IA = std::integral_constant<int, 0>;
+            using IB = std::integral_constant<int, 1>;
+            using IC = std::integral_constant<int, 2>;
+            using ID = std::integral_constant<int, 3>;
+            // the helper's two words (we0 = 0 or 2, chosen at run time: one
+            // call per case keeps E a constant)
+            auto conv_first = [&](int j, const uint4& x, const uint4& p) {
+                if (hi & 1) conv_word(j, x, p, IC{});
+                else conv_word(j, x, p, IA{});
+            };
+            auto conv_second = [&](int j, const uint4& x, const uint4& p) {
+                if (hi & 1) conv_word(j, x, p, ID{});
+                else conv_word(j, x, p, IB{});
+            };
+            // helper 1 touches V rows of this head (from its first column, 2
+            // lines each), the others record lines: one load, its address
+            // chosen by arithmetic (a branch around it would make the compiler
+            // count loads in flight conservatively)
+            const uint64_t pick = hi == 1 ? 0 : ~uint64_t(0);
+            auto touch_reg = [&](int j) {
+                const int i = unit + 8 * lane;
+                const uint64_t a = reinterpret_cast<uint64_t>(rec_of(j));
+                const uint64_t b = reinterpret_cast<uint64_t>(v + static_cast<size_t>(tok_of(j)) * v_row + h * D);
+                const unsigned char* base = reinterpret_cast<const unsigned char*>((a & pick) | (b & ~pick));
+                const int range = hi != 1 ? REC_BYTES : len_of(j) * v_row * 2;
+                const int off = hi != 1 ? (i < REC_LINES ? 128 * i : REC_BYTES) : ((i >> 1) * v_row + 64 * (i & 1)) * 2;
+                return __builtin_amdgcn_raw_buffer_load_b32(buffer_rsrc(base, range), off, 0, 0);
+            };
+            uint32_t sum = 0, tka = 0, tkb = 0, tkc = 0;
+            if (nc > 0) {
+                // chunks 0 and 1 before the loop; ra, rb: the raw rows of chunks 1, 2
+                r0 = raw(0);
+                ra = raw(min(1, nc - 1));
+                rb = raw(min(2, nc - 1));
+#pragma unroll
+                for (int j = 3; j < TOUCH_AHEAD; ++j) touch(min(j, nc - 1), lane);
+                wait_vmcnt<0>();  // once: the direct-to-LDS touches are done before the loop's LDS writes
+                conv_first(0, r0, prev);
+                conv_second(0, r0, prev);
+                if (nc > 1) {
+                    conv_first(1, ra, r0);
+                    conv_second(1, ra, r0);
+                }
+            }
+            // step j with x1, x2 the raw rows of chunks j + 1, j + 2; x3
+            // receives chunk j + 3's.  Per step: one raw load after the first
+            // barrier, one touch at the end, so chunk j + 2's rows are older
+            // than the last 2 operations once x3 is issued.  A touch's value is
+            // folded in three steps later (the line comes from HBM).  The
+            // scheduling barriers keep each part of the work between its two
+            // barriers.
+            KDA_PHASE_BEGIN
+            auto step_t = [&](int j, const uint4& x1, const uint4& x2, uint4& x3, uint32_t& tk) {
+                KDA_PHASE_MARK(24);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                KDA_PHASE_MARK(25);
+                x3 = raw(min(j + 3, nc - 1));
+                wait_vmcnt<2>();
+                if (j + 2 < nc) conv_first(j + 2, x2, x1);
+                KDA_PHASE_MARK(26);
+                __builtin_amdgcn_sched_barrier(0);
+                lds_barrier();
+                __builtin_amdgcn_sched_barrier(0);
+                KDA_PHASE_MARK(27);
+                if (j + 2 < nc) conv_second(j + 2, x2, x1);
+                KDA_PHASE_MARK(28);
+                sum += tk;
+                tk = touch_reg(min(j + TOUCH_AHEAD, nc - 1));
+                KDA_PHASE_MARK(29);
+            };
+            int j = 0;
+            for (; j + 3 <= nc; j += 3) {
+                step_t(j, ra, rb, rc, tka);
+                step_t(j + 1, rb, rc, ra, tkb);
+                step_t(j + 2, rc, ra, rb, tkc);
+            }
+            if (j < nc) step_t(j, ra, rb, rc, tka);
+            if (j + 1 < nc) step_t(j + 1, rb, rc, ra, tkb);
+            KDA_PHASE_END;
+            wait_vmcnt<0>();
+            sum += tka + tkb + tkc;
+            reinterpret_cast<uint32_t*>(lds_sink)[hi * 64 + lane] = sum;
+            return;
+        }
         if (nc > 0) {
             copy_v(0, lds_vb, lane);
             copy_v(min(1, nc - 1), lds_vb + CH_VBYTES, lane);
@@ -1726,10 +1989,14 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     if (prep_grid > 0) {
         const bf16_t* q = static_cast<const bf16_t*>(a.q);
         const bf16_t* k = static_cast<const bf16_t*>(a.k);
-        auto* kern = a.gate.a_log ? (a.gate_per_head ? prep_kernel<true, true> : prep_kernel<true, false>)
-                                  : (a.gate_per_head ? prep_kernel<false, true> : prep_kernel<false, false>);
+        auto pick = [&](auto conv) {
+            constexpr bool CV = decltype(conv)::value;
+            return a.gate.a_log ? (a.gate_per_head ? prep_kernel<true, true, CV> : prep_kernel<true, false, CV>)
+                                : (a.gate_per_head ? prep_kernel<false, true, CV> : prep_kernel<false, false, CV>);
+        };
+        auto* kern = a.conv.weight ? pick(std::true_type{}) : pick(std::false_type{});
         kern<<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets, records, a.num_seqs,
-                                            a.num_heads, a.scale, a.l2norm);
+                                            a.num_heads, a.scale, a.l2norm, static_cast<int>(a.qkv_row), a.conv);
         e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
@@ -1740,12 +2007,21 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     // chain; 64 KiB of LDS padding keeps one workgroup per CU).  When tiles
     // outnumber CUs, throughput is: scan_kernel with two tiles per workgroup
     // reads each record once for both.
+    // With the convolution fused, chain_kernel (whose touch wave convolves
+    // V) runs in both cases, without the padding when tiles outnumber CUs.
     const bool pairs = static_cast<size_t>(chains) * (D / DVT) > static_cast<size_t>(device_cu_count());
-    if (!pairs) {
-        chain_kernel<TOut><<<groups * 8, CH_THREADS, 64 * 1024, stream>>>(
+    if (a.conv.weight) {
+        chain_kernel<TOut, true><<<groups * 8, CH_THREADS_CONV, pairs ? 0 : 64 * 1024, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
-            a.state_trans);
+            a.state_trans, static_cast<int>(a.qkv_row), a.conv);
+        return hipGetLastError();
+    }
+    if (!pairs) {
+        chain_kernel<TOut, false><<<groups * 8, CH_THREADS, 64 * 1024, stream>>>(
+            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+            static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
+            a.state_trans, static_cast<int>(a.qkv_row), a.conv);
         return hipGetLastError();
     }
     scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(

@@ -63,7 +63,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 typedef enum kda_status {
     KDA_OK = 0,
@@ -227,6 +227,56 @@ kda_status_t kda_chunk_fwd_gated(const kda_problem_t *problem, const kda_gate_t 
                                  const int32_t *cu_seqlens, const float *initial_state, void *out,
                                  float *final_state, void *workspace, size_t workspace_bytes,
                                  void *stream);
+
+/*
+ * Short causal convolution fused into the prefill.  The Ascend model file's
+ * `_forward_core` runs `KimiShortConvolution` over the fused q/k/v
+ * projection before the core; kda_chunk_fwd_conv takes that projection
+ * before the convolution and applies the convolution (with y * sigmoid(y)
+ * when silu = 1) inside the prefill's loads of q, k and v, so the convolved
+ * q/k/v are never written to memory.  The convolution is the one
+ * kda_short_conv computes (same taps, same state convention, same bf16
+ * rounding of its output), so this call's results equal kda_short_conv
+ * followed by kda_chunk_fwd on the split output.
+ *
+ *   kernel_size  K, 1 to 4
+ *   silu         1: y * sigmoid(y) after the convolution; 0: none
+ *   weight       [K, 3 H d] bf16 (device, 16-byte aligned), tap-major as for
+ *                kda_short_conv; channels [0, H d) are q's, then k's, then v's
+ *   state_in     [N, K - 1, 3 H d] bf16 (device, 16-byte aligned): each
+ *                request's last K - 1 inputs before this call, oldest first;
+ *                NULL for zeros
+ *   state_out    [N, K - 1, 3 H d] bf16 (device, 16-byte aligned), written
+ *                after the prefill with each request's last K - 1 inputs (its
+ *                old state followed by its inputs when it is shorter); NULL to
+ *                skip; may equal state_in
+ */
+typedef struct kda_conv {
+    int32_t kernel_size;
+    int32_t silu;
+    const void *weight;
+    const void *state_in;
+    void *state_out;
+} kda_conv_t;
+
+/*
+ * kda_chunk_fwd (gate NULL: g and beta activated, float32) or
+ * kda_chunk_fwd_gated (gate non-NULL: raw projections) with the short
+ * convolution fused in (kda_conv_t above).
+ *
+ *   qkv     [T, 3, H, d] bf16: the fused projection before the convolution
+ *           (q = qkv[:, 0], k = qkv[:, 1], v = qkv[:, 2]), 16-byte aligned
+ *   problem qkv_dtype KDA_BF16 and head_k = head_v = 128 (the Kimi-Linear
+ *           shape); anything else is KDA_ERR_UNSUPPORTED (use kda_short_conv
+ *           and then kda_chunk_fwd)
+ * g, beta, cu_seqlens, the states, out and the workspace (of
+ * kda_chunk_fwd_workspace_bytes bytes) are as for kda_chunk_fwd.  Errors are
+ * found on the host before any launch.
+ */
+kda_status_t kda_chunk_fwd_conv(const kda_problem_t *problem, const kda_gate_t *gate, const kda_conv_t *conv,
+                                const void *qkv, const void *g, const void *beta, const int32_t *cu_seqlens,
+                                const float *initial_state, void *out, float *final_state, void *workspace,
+                                size_t workspace_bytes, void *stream);
 
 /*
  * One decode step: every sequence advances by exactly one token, and its state

@@ -288,3 +288,35 @@ def make_verify(num_seqs: int, width: int, num_heads: int, head_dim: int,
         flat[torch.randperm(flat.numel(), generator=gen)[:pad]] = -1
     accepted = torch.randint(1, width + 1, (num_seqs,), generator=gen, dtype=torch.int32)
     return VerifyInputs(name, q, k, v, g, beta, pool, indices, accepted, 1.0 / math.sqrt(head_dim))
+
+
+@dataclasses.dataclass
+class ConvPrefillInputs:
+    """A prefill whose q, k, v come out of the short convolution: x is the fused
+    projection before it, [T, 3, H, d] (q, k, v blocks); weight [K, 3 H d];
+    conv_state [N, K - 1, 3 H d] or None; the rest as PrefillInputs."""
+
+    name: str
+    x: torch.Tensor
+    weight: torch.Tensor
+    conv_state: Optional[torch.Tensor]
+    g: torch.Tensor
+    beta: torch.Tensor
+    cu_seqlens: torch.Tensor
+    initial_state: Optional[torch.Tensor]
+    scale: float
+
+
+def make_conv_prefill(lengths: List[int], num_heads: int, head_dim: int, kernel_size: int = 4,
+                      dtype: torch.dtype = torch.bfloat16, g_mu: float = 3.0, conv_state: bool = True,
+                      state_std: Optional[float] = 0.01, seed: int = 0,
+                      name: str = "conv_prefill") -> ConvPrefillInputs:
+    """x ~ N(0, 1), conv weight ~ N(0, 0.5^2), conv state ~ N(0, 1) (in dtype);
+    g = logsigmoid(N(g_mu, 1)), beta = sigmoid(N(0, 1)) (float32); S0 ~ N(0, state_std^2)."""
+    base = make_prefill(lengths, num_heads, head_dim, dtype, g_mu=g_mu, state_std=state_std, seed=seed, name=name)
+    gen = torch.Generator().manual_seed(seed + 1000)
+    T, N, C = base.q.shape[0], len(lengths), 3 * num_heads * head_dim
+    x = torch.randn((T, 3, num_heads, head_dim), generator=gen).to(dtype)
+    w = (torch.randn((kernel_size, C), generator=gen) * 0.5).to(dtype)
+    s = torch.randn((N, kernel_size - 1, C), generator=gen).to(dtype) if conv_state else None
+    return ConvPrefillInputs(name, x, w, s, base.g, base.beta, base.cu_seqlens, base.initial_state, base.scale)

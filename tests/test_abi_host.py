@@ -35,7 +35,7 @@ def test_header_declares_the_boundary():
         "kda_chunk_fwd_workspace_bytes", "kda_chunk_fwd", "kda_recurrent_step",
         "kda_chunk_fwd_gated", "kda_recurrent_step_gated", "kda_chunk_fwd_pooled",
         "kda_recurrent_verify", "kda_gated_rmsnorm", "kda_short_conv", "kda_recurrent_step_normed",
-        "kda_chunk_fwd_noalloc", "kda_recurrent_verify_normed"])
+        "kda_chunk_fwd_noalloc", "kda_recurrent_verify_normed", "kda_chunk_fwd_conv"])
 
 
 def test_library_exports_every_declared_symbol():
@@ -74,7 +74,8 @@ def _c_layout(struct: str, fields):
     return vals[0], dict(zip(fields, vals[1:]))
 
 
-@pytest.mark.parametrize("cls,struct", [(Problem, "kda_problem_t"), (kda.Gate, "kda_gate_t")])
+@pytest.mark.parametrize("cls,struct", [(Problem, "kda_problem_t"), (kda.Gate, "kda_gate_t"),
+                                        (kda.Conv, "kda_conv_t")])
 def test_struct_layout_matches_header(cls, struct):
     """The ctypes mirrors match the C compiler's layout of include/kda.h, field by field."""
     fields = [f for f, _ in cls._fields_]
@@ -516,3 +517,44 @@ def test_recurrent_verify_normed_rejects_before_launch():
     assert st == 2 and "16-byte aligned" in lib.kda_last_error().decode()
     # an empty batch needs no epilogue operands
     assert call(_prob(total_tokens=0, num_seqs=0), 4, None, None, 1e-6) == 0
+
+
+def _conv_call(prob, conv, **ptrs):
+    lib = kda.raw_library()
+    p = dict(gate=None, qkv=FAKE, g=FAKE, beta=FAKE, cu=FAKE, s0=None, out=FAKE, fs=None, ws=FAKE,
+             ws_bytes=1 << 40)
+    p.update(ptrs)
+    st = lib.kda_chunk_fwd_conv(ctypes.byref(prob), p["gate"], None if conv is None else ctypes.byref(conv),
+                                p["qkv"], p["g"], p["beta"], p["cu"], p["s0"], p["out"], p["fs"], p["ws"],
+                                p["ws_bytes"], None)
+    return st, lib.kda_last_error().decode()
+
+
+def test_chunk_fwd_conv_rejects_before_launch():
+    ok = lambda **kw: kda.Conv(**{**dict(kernel_size=4, silu=1, weight=0x1000, state_in=None, state_out=None), **kw})
+    st, msg = _conv_call(_prob(), None)
+    assert st == 1 and "conv is NULL" in msg
+    for K in (0, 5):
+        st, msg = _conv_call(_prob(), ok(kernel_size=K))
+        assert st == 3 and "kernel_size" in msg, (K, st, msg)
+    st, msg = _conv_call(_prob(), ok(silu=2))
+    assert st == 2 and "silu" in msg
+    # only the bf16, d = 128 path has the convolution fused
+    for kw in (dict(qkv_dtype=0), dict(head_k=64, head_v=64)):
+        st, msg = _conv_call(_prob(**kw), ok())
+        assert st == 3 and "bf16, d = 128" in msg, (kw, st, msg)
+    for name in ("weight", "state_in", "state_out"):
+        st, msg = _conv_call(_prob(), ok(**{name: 0x1008}))
+        assert st == 2 and "16-byte aligned" in msg, (name, st, msg)
+    st, msg = _conv_call(_prob(), ok(weight=None))
+    assert st == 1 and "weight" in msg
+    st, msg = _conv_call(_prob(), ok(), qkv=None)
+    assert st == 1 and "qkv" in msg
+    st, msg = _conv_call(_prob(), ok(), qkv=MISALIGNED)
+    assert st == 2 and "16-byte aligned" in msg, (st, msg)
+    # the checks of kda_chunk_fwd apply as well
+    st, msg = _conv_call(_prob(), ok(), ws_bytes=16)
+    assert st == 4 and "workspace" in msg, (st, msg)
+    st, msg = _conv_call(_prob(), ok(), gate=ctypes.byref(_gate(has_lower_bound=3)))
+    assert st == 2 and "has_lower_bound" in msg
+    assert _conv_call(_prob(total_tokens=0, num_seqs=0), ok(weight=None), qkv=None)[0] == 0

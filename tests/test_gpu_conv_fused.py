@@ -1,0 +1,215 @@
+"""The prefill with the short convolution fused into its loads (kda_chunk_fwd_conv).
+
+References:
+- the unfused GPU pipeline, kda_short_conv then kda_chunk_fwd (or
+  kda_chunk_fwd_gated) on the split output: the fused call uses the same
+  convolution arithmetic and bf16 rounding and the same state chain, so
+  out, the final state and the conv state must match it bit for bit
+  whenever both run the same chain kernel (every case below but the one
+  with more 16-column tiles than compute units, checked to the oracle bar);
+- the fp64 oracles chained (the Ascend model file's `_forward_core`: the
+  convolution, its output rounded to bf16 as the layer's activations are,
+  then the core; `_project_out` after it): oracle.conv.short_conv,
+  oracle.forward and oracle.epilogue, within 2e-3 of max|oracle|; a bf16
+  output, rounded once, may also differ by half a bf16 ulp of each value
+  (2^-9 |ref|).
+Cases: requests shorter than the filter, empty requests, chunk boundaries,
+every filter length, with and without conv state and SiLU, the conv state
+updated in place, raw gates, both output dtypes and state layouts, many
+chains, and the full 4096-token, 32-head workload.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_workloads as w
+import oracle
+from oracle import conv as oconv
+from oracle import epilogue
+from oracle import gate as ogate
+from tests.gpu_helpers import TOL_BF16, announce, dev, rel_err
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import gated_delta_rule_53_amd  # noqa: F401  (fails loudly if libkda.so is missing)
+    yield
+
+
+def _split(y, H, d):
+    T = y.shape[0]
+    y = y.view(T, 3, H, d)
+    return y[:, 0].contiguous(), y[:, 1].contiguous(), y[:, 2].contiguous()
+
+
+def _s0(x, layout):
+    """The initial state in the layout the call is told (the oracle takes S[dk][dv])."""
+    if x.initial_state is None or layout == "dk_dv":
+        return dev(x.initial_state)
+    return dev(x.initial_state.transpose(-1, -2))
+
+
+def _unfused(x, silu, out_dtype, layout, gate_kw=None, g=None, beta=None):
+    """kda_short_conv, then kda_chunk_fwd(_gated) on its split output."""
+    import gated_delta_rule_53_amd as kda
+    T, _, H, d = x.x.shape
+    y, ys = kda.short_conv(dev(x.x.reshape(T, 3 * H * d)), dev(x.weight), dev(x.cu_seqlens), dev(x.conv_state),
+                           silu=silu)
+    q, k, v = _split(y, H, d)
+    s0 = _s0(x, layout)
+    if gate_kw:
+        out, fs = kda.chunk_fwd_gated(q, k, v, dev(g), dev(beta), cu_seqlens=dev(x.cu_seqlens), initial_state=s0,
+                                      scale=x.scale, out_dtype=out_dtype, state_layout=layout, **gate_kw)
+    else:
+        out, fs = kda.chunk_fwd(q, k, v, dev(x.g), dev(x.beta), dev(x.cu_seqlens), s0, scale=x.scale,
+                                out_dtype=out_dtype, state_layout=layout)
+    return out, fs, ys
+
+
+def _fused(x, silu, out_dtype, layout, gate_kw=None, g=None, beta=None, in_place=False):
+    import gated_delta_rule_53_amd as kda
+    cs = dev(x.conv_state)
+    if in_place:
+        cs_out = cs
+    else:
+        K = x.weight.shape[0]
+        cs_out = torch.empty((len(x.cu_seqlens) - 1, K - 1, x.weight.shape[1]), dtype=x.x.dtype, device="cuda:0")
+    gg = dev(g) if gate_kw else dev(x.g)
+    bb = dev(beta) if gate_kw else dev(x.beta)
+    out, fs = kda.chunk_fwd_conv(dev(x.x), gg, bb, dev(x.weight), dev(x.cu_seqlens), _s0(x, layout), cs,
+                                 silu=silu, conv_state_out=cs_out, scale=x.scale, out_dtype=out_dtype,
+                                 state_layout=layout, **(gate_kw or {}))
+    return out, fs, cs_out
+
+
+def _oracle(x, silu, g=None, beta=None):
+    """conv (fp64) -> bf16 -> forward (fp64); returns (out, final state, conv state)."""
+    T, _, H, d = x.x.shape
+    y, ys = oconv.short_conv(x.x.reshape(T, 3 * H * d), x.weight, x.cu_seqlens.numpy(),
+                             None if x.conv_state is None else x.conv_state, silu=silu)
+    yb = torch.from_numpy(y).to(torch.bfloat16)
+    q, k, v = _split(yb, H, d)
+    o, fs = oracle.forward(q, k, v, x.g if g is None else g, x.beta if beta is None else beta, x.cu_seqlens,
+                           x.initial_state, x.scale)
+    return o, fs, ys
+
+
+def _err(gpu, ref, bf16_out):
+    """max over elements of |gpu - ref| / max|ref|, with half a bf16 ulp of
+    each value taken off first when the output was rounded to bf16."""
+    g = gpu.detach().double().cpu().numpy()
+    ref = np.asarray(ref, dtype=np.float64)
+    assert g.shape == ref.shape
+    d = np.abs(g - ref)
+    if bf16_out:
+        d = np.maximum(d - 2.0 ** -9 * np.abs(ref), 0.0)
+    m = float(np.abs(ref).max())
+    return float(d.max()) / m if m > 0 else float(d.max())
+
+
+def _state_dk_dv(fs, layout):
+    return fs if layout == "dk_dv" else fs.transpose(-1, -2)
+
+
+# (lengths, H, K, silu, conv state, out dtype, state layout)
+CASES = [
+    ([300], 2, 4, True, True, torch.bfloat16, "dk_dv"),
+    ([1, 2, 3, 64, 65, 130], 3, 4, True, True, torch.float32, "dk_dv"),
+    ([0, 70, 0, 3, 128], 2, 4, False, False, torch.bfloat16, "dv_dk"),
+    ([200, 77], 2, 3, True, True, torch.float32, "dk_dv"),
+    ([129, 2], 1, 2, False, True, torch.bfloat16, "dk_dv"),
+    ([100, 5], 2, 1, True, False, torch.float32, "dv_dk"),
+]
+
+
+@pytest.mark.parametrize("lens,H,K,silu,with_cs,out_dtype,layout", CASES)
+def test_fused_conv_equals_unfused_and_oracle(lens, H, K, silu, with_cs, out_dtype, layout):
+    x = w.make_conv_prefill(lens, H, 128, K, conv_state=with_cs, seed=sum(lens) + K)
+    announce(f"conv-fused prefill lens={lens} H={H} K={K} silu={silu} conv_state={with_cs} {out_dtype} {layout}")
+    o1, f1, s1 = _unfused(x, silu, out_dtype, layout)
+    o2, f2, s2 = _fused(x, silu, out_dtype, layout)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    assert torch.equal(f1, f2)
+    if K > 1:
+        assert torch.equal(s1, s2)
+    ro, rf, rs = _oracle(x, silu)
+    eo, es = _err(o2, ro, out_dtype == torch.bfloat16), rel_err(_state_dk_dv(f2, layout), rf)
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+    if K > 1:
+        assert np.array_equal(s2.double().cpu().numpy(), rs)
+
+
+def test_fused_conv_state_in_place():
+    x = w.make_conv_prefill([1, 40, 2, 0, 90], 2, 128, 4, seed=11)
+    announce("conv-fused prefill, conv state updated in place")
+    o1, f1, s1 = _unfused(x, True, torch.float32, "dk_dv")
+    o2, f2, s2 = _fused(x, True, torch.float32, "dk_dv", in_place=True)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("lb", [None, -5.0])
+def test_fused_conv_with_raw_gate(lb):
+    lens, H = [150, 33], 2
+    x = w.make_conv_prefill(lens, H, 128, 4, seed=12)
+    gi = w.make_gate(sum(lens), H, 128, torch.bfloat16, mu=-5.0 if lb is None else -2.0, lower_bound=lb, seed=13)
+    kw = dict(a_log=dev(gi.a_log), dt_bias=dev(gi.dt_bias), lower_bound=lb)
+    announce(f"conv-fused prefill, raw gate lower_bound={lb}")
+    o1, f1, _ = _unfused(x, True, torch.float32, "dk_dv", kw, gi.raw_g, gi.raw_beta)
+    o2, f2, _ = _fused(x, True, torch.float32, "dk_dv", kw, gi.raw_g, gi.raw_beta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    g, b = ogate.activate(gi.raw_g, gi.raw_beta, gi.a_log, gi.dt_bias, lb)
+    ro, rf, _ = _oracle(x, True, g, b)
+    eo, es = rel_err(o2, ro), rel_err(f2, rf)
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_fused_conv_many_chains_and_epilogue():
+    """48 (sequence, head) chains, 384 column tiles: more tiles than compute
+    units (the chain kernel without its one-per-CU padding); the bf16 output
+    through kda_gated_rmsnorm against conv -> forward -> epilogue."""
+    import gated_delta_rule_53_amd as kda
+    lens, H = [300, 200, 150], 16
+    x = w.make_conv_prefill(lens, H, 128, 4, seed=14)
+    announce(f"conv-fused prefill lens={lens} H={H} (tiles > CUs) + gated rmsnorm")
+    o2, f2, _ = _fused(x, True, torch.bfloat16, "dk_dv")
+    gen = torch.Generator().manual_seed(15)
+    og = torch.randn(tuple(o2.shape), generator=gen).to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn((128,), generator=gen)
+    y = kda.gated_rmsnorm(o2, dev(og), dev(nw), eps=1e-6, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ro, rf, _ = _oracle(x, True)
+    ry = epilogue.gated_rmsnorm(ro, og, nw, 1e-6)
+    eo, es, ey = _err(o2, ro, True), rel_err(f2, rf), _err(y, ry, True)
+    print(f"  err out {eo:.3e} state {es:.3e} normed {ey:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16 and ey <= TOL_BF16, (eo, es, ey)
+
+
+def test_fused_conv_4k_workload_equals_unfused():
+    """T = 4096, H = 32, d = 128, K = 4 with SiLU: the whole output and final
+    state bit for bit against the unfused pipeline; output rows sampled
+    against the oracle on two heads."""
+    x = w.make_conv_prefill([4096], 32, 128, 4, seed=16, name="conv_prefill_T4096_H32_d128")
+    announce("conv-fused prefill T=4096 H=32 d=128 K=4")
+    o1, f1, s1 = _unfused(x, True, torch.bfloat16, "dk_dv")
+    o2, f2, s2 = _fused(x, True, torch.bfloat16, "dk_dv")
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2) and torch.equal(s1, s2)
+    # two heads through the oracle (the convolution of all channels, the core on heads 0 and 31)
+    T = 4096
+    y, _ = oconv.short_conv(x.x.reshape(T, 3 * 32 * 128), x.weight, x.cu_seqlens.numpy(), x.conv_state, silu=True)
+    q, k, v = _split(torch.from_numpy(y).to(torch.bfloat16), 32, 128)
+    for h in (0, 31):
+        ro, rf = oracle.forward(q[:, h:h + 1], k[:, h:h + 1], v[:, h:h + 1], x.g[:, h:h + 1], x.beta[:, h:h + 1],
+                                x.cu_seqlens, x.initial_state[:, h:h + 1], x.scale)
+        eo, es = _err(o2[:, h:h + 1], ro, True), rel_err(f2[:, h:h + 1], rf)
+        print(f"  head {h}: err out {eo:.3e} state {es:.3e}")
+        assert eo <= TOL_BF16 and es <= TOL_BF16, (h, eo, es)
