@@ -62,7 +62,10 @@ KERNEL_SOURCES["decode_dv_dk"] = KERNEL_SOURCES["decode"]
 KERNEL_SOURCES["prologue"] = ["gated_delta_rule_53_amd/csrc/kda_conv.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
 KERNEL_SOURCES["epilogue"] = ["gated_delta_rule_53_amd/csrc/kda_epilogue.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"]
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
-PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
+# one chain per (sequence, head, 16-column tile): chain_kernel while every tile
+# has a compute unit, scan_kernel (two tiles per workgroup) beyond that
+PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "chain_kernel"]
+PREFILL_KERNELS_MANY = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
 
 def source_digest(kind: str) -> str:
@@ -463,21 +466,17 @@ def cpu_baseline(min_seconds: float = 8.0, heads: int = 0, threads: int = 0):
             break
     # tokens/s of the whole workload (all 32 heads): heads are independent and equal in work
     value = passes * x.total_tokens * H / x.num_heads / el
-    return dict(value=value, unit="tokens/s", cores=oracle.threads(), kind="oracle",
+    # the oracle's threads each take whole (sequence, head) pairs: at most that many work
+    return dict(value=value, unit="tokens/s", cores=min(oracle.threads(), x.num_seqs * H), kind="oracle",
                 sample=f"{passes} pass(es) of prefill_T4096_H32_d128 over {H} of {x.num_heads} heads "
                        f"(fp64 recurrence, {el:.1f} s wall), scaled to all heads")
 
 
 def cpu_baseline_single_core():
-    """The same oracle on one thread, in a child process (its OpenMP pool never grows)."""
-    import subprocess
-    code = ("import json, bench; "
-            "print('CPU1 ' + json.dumps(bench.cpu_baseline(min_seconds=8.0, heads=8, threads=1)))")
-    res = subprocess.run([sys.executable, "-c", code], cwd=ROOT, capture_output=True, text=True, timeout=600)
-    for line in res.stdout.splitlines():
-        if line.startswith("CPU1 "):
-            return json.loads(line[5:])
-    return {"error": (res.stderr or res.stdout)[-400:]}
+    """The same oracle on one core: one head, so one (sequence, head) pair and
+    one busy thread whatever the OpenMP thread count (set to 16 on the GPU
+    hosts), scaled to all heads."""
+    return cpu_baseline(min_seconds=6.0, heads=1)
 
 
 def hbm_copy_bandwidth(gib: int = 2, reps: int = 10):
@@ -492,8 +491,18 @@ def hbm_copy_bandwidth(gib: int = 2, reps: int = 10):
     del src, dst
     torch.cuda.empty_cache()
     gbs = 2 * n * 4 / per / 1e9
+    # write-only: the rate a store-dominated kernel (verify writes 4 states per read) can reach
+    dst = torch.empty(n, dtype=torch.float32, device="cuda:0")
+    for _ in range(2):
+        dst.zero_()
+    _, per_w = time_launches(lambda i: dst.zero_(), reps, torch.cuda.current_stream())
+    del dst
+    torch.cuda.empty_cache()
+    wgbs = n * 4 / per_w / 1e9
     return {"kernel": "torch copy_ (read + write)", "bytes_per_launch": 2 * n * 4, "gbs": round(gbs, 1),
-            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4)}
+            "frac_of_peak": round(gbs / HBM_PEAK_GBS, 4),
+            "write_only": {"kernel": "torch zero_ (write)", "bytes_per_launch": n * 4, "gbs": round(wgbs, 1),
+                           "frac_of_peak": round(wgbs / HBM_PEAK_GBS, 4)}}
 
 
 def copy_calibration(gib: int = 1, reps: int = 4):
@@ -613,7 +622,7 @@ def main():
         "varlen8": {"workload": v8["x"].name, "tokens": v8["tokens"], "num_seqs": v8["x"].num_seqs,
                     "tokens_per_s": round(v8["tokens"] / v8["per_launch"], 1),
                     "ms_per_call": round(v8["per_launch"] * 1e3, 4),
-                    "roofline": prefill_roofline("kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS), v8,
+                    "roofline": prefill_roofline("kda_chunk_fwd = " + " + ".join(PREFILL_KERNELS_MANY), v8,
                                                  measured_traffic("prefill_varlen8"))},
         "long_128k": {"workload": lg["x"].name, "tokens": lg["tokens"],
                       "tokens_per_s": round(lg["tokens"] / lg["per_launch"], 1),

@@ -213,9 +213,15 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // [0, num_slots) reads as the zero state and is not written.  The whole
 // starting state is read before anything is written, so idx[a-1] may also
 // appear among the destinations.  Each token is the decode step above.
-// NORM: each token's output row goes through LDS to wave 0, which writes the
-// gated RMSNorm of it (as in decode_step_kernel) while the other waves load
-// the next token: o itself never reaches HBM.
+// NORM: each token's output row gets the gated RMSNorm of decode_step_kernel
+// before it is written, so o itself never reaches HBM.  With S[dk][dv] the
+// row already sits in wave 0's first lanes, which apply it in registers;
+// with S^T it goes through LDS to wave 0 after the token's last barrier,
+// while the other waves load the next token.  The token's output-gate row
+// is loaded with its q and k, and the norm weight once, both into LDS, so
+// no global load is waited for there; the gate row alternates between two
+// buffers, since the next token's is stored while wave 0 may still be
+// reading this one's.
 template <int D, typename TIn, typename TOut, bool GATED, bool TRANS, bool NORM>
 __global__ __launch_bounds__(256) void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -253,6 +259,11 @@ __global__ __launch_bounds__(256) void verify_kernel(
     __shared__ float sq[D], sk[D], se[D];
     __shared__ float red[4][NCG][8];
     __shared__ float so[NORM ? D : 1];  // the token's output row on its way to the epilogue
+    __shared__ float sog[NORM ? 2 : 1][NORM ? D : 1];  // sigmoid of the output-gate row of token t in [t & 1]
+    __shared__ float snw[NORM ? D : 1];                 // the norm weight
+    if constexpr (NORM) {
+        if (tid < D) snw[tid] = np.weight[tid];
+    }
     for (int t = 0; t < width; ++t) {
         const size_t row = static_cast<size_t>(n) * width + t;  // token row
         const size_t tok = row * num_heads + h;                  // (token, head)
@@ -260,6 +271,7 @@ __global__ __launch_bounds__(256) void verify_kernel(
             const size_t off = tok * D + tid;
             sq[tid] = to_f32(q[off]);
             sk[tid] = to_f32(k[off]);
+            if constexpr (NORM) sog[t & 1][tid] = gate_sigmoid(to_f32(static_cast<const TIn*>(np.gate)[off]));
             const size_t goff = gph ? tok : off;
             float gv;
             if constexpr (GATED)
@@ -356,20 +368,35 @@ __global__ __launch_bounds__(256) void verify_kernel(
                 s[i] += (rk * sk[r]) * delta;
                 if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
             }
-            if (rg == 0) {
-                const float kq = rk * rq * aqk;
+            const float kq = rk * rq * aqk;
+            if constexpr (NORM) {
+                // the whole output row is in wave 0's first NCG lanes (four
+                // columns each; the other lanes of the wave repeat them): the
+                // epilogue runs there, with no exchange
+                if (wave == 0) {
+                    float ov[4], ss = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    if constexpr (NORM)
-                        so[4 * cg + j] = p[j] + kq * delta[j];
-                    else
-                        out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+                    for (int j = 0; j < 4; ++j) {
+                        ov[j] = p[j] + kq * delta[j];
+                        ss += ov[j] * ov[j];
+                    }
+#pragma unroll
+                    for (int m = 1; m < NCG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                    const float r = rsqrtf(ss * (1.f / D) + np.eps);
+                    if (rg == 0) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j)
+                            out[voff + j] = from_f32<TOut>(ov[j] * r * snw[4 * cg + j] * sog[t & 1][4 * cg + j]);
+                    }
                 }
+            } else if (rg == 0) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
             }
         }
         // sq, sk, se and red are rewritten by the next token
         __syncthreads();
-        if constexpr (NORM) {
+        if constexpr (NORM && TRANS) {
             // so is rewritten only after the next token's first barrier, which
             // wave 0 reaches once it has read it here
             if (wave == 0) {
@@ -378,10 +405,9 @@ __global__ __launch_bounds__(256) void verify_kernel(
                 for (int c = lane; c < D; c += 64) ss += so[c] * so[c];
                 ss = wave_sum_from(ss, 1);
                 const float r = rsqrtf(ss * (1.f / D) + np.eps);
-                const TIn* og = static_cast<const TIn*>(np.gate) + tok * D;
 #pragma unroll
                 for (int c = lane; c < D; c += 64)
-                    out[tok * D + c] = from_f32<TOut>(so[c] * r * np.weight[c] * gate_sigmoid(to_f32(og[c])));
+                    out[tok * D + c] = from_f32<TOut>(so[c] * r * snw[c] * sog[t & 1][c]);
             }
         }
     }

@@ -680,7 +680,10 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
         // A' and P' come from exact_ap, and the planes take the chunk's start
         // (Kg, Qg) and end (Ki) as references, every factor at most 1, with
         // e^{G_31} and e^{G_last - G_31} replaced by 1 downstream.
-        const bool exact = __builtin_amdgcn_readfirstlane(*reinterpret_cast<volatile int*>(sFlag)) != 0;
+        // a plain LDS read (the barrier's memory clobber makes it a fresh one; a
+        // volatile generic pointer would compile to a flat load, which the
+        // compiler waits for together with every vector memory operation in flight)
+        const bool exact = __builtin_amdgcn_readfirstlane(*sFlag) != 0;
         if (exact) {
             const int o = rp * D + 8 * cc;
             floatx8 eg;
