@@ -518,6 +518,28 @@ def copy_calibration(gib: int = 1, reps: int = 4):
                                            "bytes_written_per_launch": n * 4, "launches": reps}}))
 
 
+def _wl(name):
+    import kda_workloads as w
+    return getattr(w, name)()
+
+
+# One leg at a time (--leg), for profiler runs that must see one workload.
+LEGS = {
+    "prefill": lambda a: bench_prefill(a.steps, a.warmup),
+    "prefill_varlen8": lambda a: bench_prefill_workload(_wl("varlen8"), min(a.steps, 10), 1),
+    "prefill_long128k": lambda a: bench_prefill_workload(_wl("long_128k"), min(a.steps, 5), 1),
+    "per_head_prefill": lambda a: bench_prefill(a.steps, a.warmup, per_head=True),
+    "gated_prefill": lambda a: bench_prefill_gated(a.steps, a.warmup),
+    "prefill_conv": lambda a: bench_prefill_conv(a.steps, a.warmup),
+    "decode": lambda a: bench_decode(a.decode_loops),
+    "decode_dv_dk": lambda a: bench_decode(1, state_layout="dv_dk"),
+    "verify_decode": lambda a: bench_verify(a.steps, a.warmup),
+    "verify_normed": lambda a: bench_verify(a.steps, a.warmup, normed=True),
+    "prologue": lambda a: bench_conv(a.steps, a.warmup),
+    "epilogue": lambda a: bench_epilogue(a.steps, a.warmup),
+}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -527,6 +549,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (reference for HBM byte counters)")
+    ap.add_argument("--leg", choices=sorted(LEGS),
+                    help="only run this leg (for per-workload profiler runs); prints its launch time")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported (the KDA core "
@@ -540,6 +564,11 @@ def main():
         sys.exit(1)
     if args.copy_calibration:
         copy_calibration()
+        return
+    if args.leg:
+        r = LEGS[args.leg](args)
+        print(json.dumps({"leg": args.leg, "launch_us": round(r["per_launch"] * 1e6, 2),
+                          "alg_bytes_per_launch": r.get("alg_bytes")}), flush=True)
         return
 
     pf = bench_prefill(args.steps, args.warmup)
