@@ -213,3 +213,27 @@ def test_fused_conv_4k_workload_equals_unfused():
         eo, es = _err(o2[:, h:h + 1], ro, True), rel_err(f2[:, h:h + 1], rf)
         print(f"  head {h}: err out {eo:.3e} state {es:.3e}")
         assert eo <= TOL_BF16 and es <= TOL_BF16, (h, eo, es)
+
+
+def test_fused_conv_with_one_decay_per_head():
+    """gate_per_head (g [T, H]) with the convolution fused: the prep kernel's
+    per-head and conv modes together, against the unfused pair and the oracle
+    (the per-head decay broadcast over the key channels)."""
+    import gated_delta_rule_53_amd as kda
+    lens, H = [130, 61], 2
+    x = w.make_conv_prefill(lens, H, 128, 4, seed=17)
+    gh = w.per_head_decay((sum(lens), H), 3.0, seed=18)
+    announce("conv-fused prefill, one decay per head")
+    T = sum(lens)
+    y, _ = kda.short_conv(dev(x.x.reshape(T, 3 * H * 128)), dev(x.weight), dev(x.cu_seqlens), dev(x.conv_state))
+    q, k, v = _split(y, H, 128)
+    o1, f1 = kda.chunk_fwd(q, k, v, dev(gh), dev(x.beta), dev(x.cu_seqlens), dev(x.initial_state), scale=x.scale,
+                           out_dtype=torch.float32)
+    o2, f2 = kda.chunk_fwd_conv(dev(x.x), dev(gh), dev(x.beta), dev(x.weight), dev(x.cu_seqlens),
+                                dev(x.initial_state), dev(x.conv_state), scale=x.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    ro, rf, _ = _oracle(x, True, gh[..., None].expand(T, H, 128).contiguous(), None)
+    eo, es = rel_err(o2, ro), rel_err(f2, rf)
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
