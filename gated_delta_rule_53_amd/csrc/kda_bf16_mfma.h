@@ -122,14 +122,6 @@ __device__ __forceinline__ bf16x8 col8_tr(const unsigned char* smem, int base, i
     return col8_tr2(smem, base, stride, r0, r0 + 4, c0, l16);
 }
 
-// Two floats to packed bf16 (round to nearest even in hardware): element 0 in
-// the low half.  (Converting a four-wide vector and taking its elements
-// apart is avoided: the compiler at hand keeps only element 0 there.)
-__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-    const floatx2 xv = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(xv, bf16x2v));
-}
-
 // Four bf16 at smem[off_bytes] (8-byte aligned).
 __device__ __forceinline__ bf16x4 ld4(const unsigned char* smem, int off_bytes) {
     return *reinterpret_cast<const bf16x4*>(smem + off_bytes);

@@ -23,13 +23,18 @@ __device__ __forceinline__ float to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x.bits) << 16);
 }
 
-// float -> bf16, round to nearest even; NaN stays a (quiet) NaN.
-__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return bf16_t{static_cast<uint16_t>((u >> 16) | 0x40u)};
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return bf16_t{static_cast<uint16_t>(u >> 16)};
+typedef float cfloatx2 __attribute__((ext_vector_type(2)));
+typedef __bf16 cbf16x2 __attribute__((ext_vector_type(2)));
+
+// Two floats to packed bf16, round to nearest even in hardware (a NaN stays a
+// quiet NaN): a in the low half.  (Converting a four-wide vector and taking
+// its elements apart is avoided: the compiler at hand keeps only element 0
+// there.)
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(cfloatx2{a, b}, cbf16x2));
 }
+
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) { return bf16_t{static_cast<uint16_t>(pack_bf16x2(f, 0.f))}; }
 
 template <typename T>
 __device__ __forceinline__ T from_f32(float x);
@@ -86,7 +91,6 @@ struct ConvParams {
 // c, with x_m the input m steps back and w_t tap t (tap 3 meets x_0):
 //   y = dot(x_0 w_3 + x_1 w_2, on top of x_2 w_1 + x_3 w_0)
 // as two bf16 pair products with float32 accumulation (v_dot2_f32_bf16).
-typedef __bf16 cbf16x2 __attribute__((ext_vector_type(2)));
 
 // (lo half of a, lo half of b) and (hi of a, hi of b) as packed pairs.
 __device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) { return __builtin_amdgcn_perm(b, a, 0x05040100u); }

@@ -16,10 +16,12 @@
 //
 // HBM-bound: every input is read once and every output written once.  Launch:
 // a thread owns eight consecutive channels (one 16-byte load of bf16) of a run
-// of TB tokens, issues the run's loads first and keeps the K - 1 previous
+// of 16 tokens (8 in float32), issues the run's loads first and keeps the K - 1 previous
 // inputs in registers; a run that crosses into the next request restarts its
-// window from that request's state.  One extra row of workgroups writes the state of empty requests
-// (their initial state, or zeros).
+// window from that request's state.  Workgroups take (run, 2048-channel
+// block) pairs with the channel block varying fastest, so the workgroups in
+// flight together read and write whole rows.  One extra run row writes the
+// state of empty requests (their initial state, or zeros).
 //
 // In place (state_out == state_in, the decode case): a request's old state
 // could be read by one run while another run writes its new state, so that
@@ -35,7 +37,12 @@ namespace kda {
 
 namespace {
 
-constexpr int TB = 8;  // tokens per thread (8 measured best of 8 / 16 / 32 on the bench shape)
+// Tokens per thread: 16 for bf16 (best of 4 / 8 / 16 / 32 on a 4096 x 12,288
+// projection), 8 for float32 (twice the registers per token).
+template <typename T>
+constexpr int run_tokens() { return sizeof(T) == 2 ? 16 : 8; }
+// Workgroups per launch at most; more (run, channel block) pairs are taken in turn.
+constexpr int64_t kConvMaxGroups = int64_t(1) << 20;
 
 template <typename T>
 __device__ __forceinline__ void load8c(float (&v)[8], const T* p) {
@@ -45,17 +52,20 @@ __device__ __forceinline__ void load8c(float (&v)[8], const T* p) {
     for (int i = 0; i < 8; ++i) v[i] = to_f32(r[i]);
 }
 
+// Eight channels out, non-temporal: nothing here reads y back (measured
+// 57.7 -> 48.3 us on the bench shape).  bf16: rounded by pairs in hardware.
 template <typename T>
 __device__ __forceinline__ void store8c(T* p, const float (&v)[8]) {
-    T r[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) r[i] = from_f32<T>(v[i]);
-    constexpr int BYTES = 8 * static_cast<int>(sizeof(T));
-    // non-temporal: nothing here reads y back (measured 57.7 -> 48.3 us on the bench shape)
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(T) == 2) {
+        __builtin_nontemporal_store(u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                                          pack_bf16x2(v[6], v[7])},
+                                    reinterpret_cast<u32x4*>(p));
+    } else {
 #pragma unroll
-    for (int i = 0; i < BYTES / 16; ++i)
-        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(r)[i], reinterpret_cast<u32x4*>(p) + i);
+        for (int i = 0; i < 2; ++i)
+            __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(v)[i], reinterpret_cast<u32x4*>(p) + i);
+    }
 }
 
 // bf16: the eight channels' raw words, and their non-temporal store.
@@ -87,20 +97,14 @@ __device__ __forceinline__ int request_of(const int32_t* cu, int num_seqs, int64
 
 }  // namespace
 
+// One run of run_tokens<T>() tokens (run == run_rows: the states of empty requests) in
+// channels c .. c + 7.
 template <int K, typename T, bool SILU>
-__global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x, const T* __restrict__ weight,
-                                                         const int32_t* __restrict__ cu, int num_seqs,
-                                                         const T* state_in, T* state_out, T* __restrict__ y,
-                                                         int64_t total_tokens, int channels, int64_t run_rows) {
-    // blockIdx.y: 2048 channels.  blockIdx.x: a run of TB tokens (run run_rows
-    // writes empty requests' states).  Workgroup ids are dealt to the eight
-    // XCDs in turn, so XCD k (ids = k mod 8) takes the runs [k per, (k+1) per)
-    // in order: the K - 1 rows before a run were fetched into that XCD's L2
-    // by the run before it.
-    const int64_t per = (run_rows + 8) / 8;
-    const int64_t run = static_cast<int64_t>(blockIdx.x & 7) * per + (blockIdx.x >> 3);
-    const int c = (static_cast<int>(blockIdx.y) * 256 + static_cast<int>(threadIdx.x)) * 8;
-    if (c >= channels || run > run_rows) return;
+__device__ __forceinline__ void conv_run(const T* __restrict__ x, const T* __restrict__ weight,
+                                         const int32_t* __restrict__ cu, int num_seqs, const T* state_in,
+                                         T* state_out, T* __restrict__ y, int64_t total_tokens, int channels,
+                                         int64_t run_rows, int64_t run, int c) {
+    constexpr int TB = run_tokens<T>();
     const size_t C = static_cast<size_t>(channels);
     constexpr int S = K - 1;  // state length
     auto soff = [&](int n, int m) { return (static_cast<size_t>(n) * S + m) * C + c; };
@@ -148,6 +152,30 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
         uint4 xin[TB];
 #pragma unroll
         for (int u = 0; u < TB; ++u) xin[u] = load_raw8(x + static_cast<size_t>(min(t0 + u, t1 - 1)) * C + c);
+        if (t1 <= end && t0 - S >= start) {
+            // the run and the K - 1 rows before it lie inside one request
+#pragma unroll
+            for (int m = 0; m < S; ++m) win[m] = load_raw8(x + static_cast<size_t>(t0 - 1 - m) * C + c);
+#pragma unroll
+            for (int u = 0; u < TB; ++u) {
+                if (t0 + u >= t1) break;
+                float acc[8];
+                conv8_bf16(xin[u], win[0], win[1], win[2], taps, acc);
+                if constexpr (SILU) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) acc[i] *= gate_sigmoid(acc[i]);
+                }
+                store8c(y + static_cast<size_t>(t0 + u) * C + c, acc);
+#pragma unroll
+                for (int m = S - 1; m > 0; --m) win[m] = win[m - 1];
+                if constexpr (S > 0) win[0] = xin[u];
+            }
+            if (t1 == end && state_out) {
+#pragma unroll
+                for (int m = 0; m < S; ++m) store_raw8(state_out + soff(n, m), win[S - 1 - m]);
+            }
+            return;
+        }
         fill_window(t0);
 #pragma unroll
         for (int u = 0; u < TB; ++u) {
@@ -244,6 +272,22 @@ __global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x
                 for (int m = 0; m < S; ++m) store8c(state_out + soff(n, m), win[S - 1 - m]);
             }
         }
+    }
+}
+
+template <int K, typename T, bool SILU>
+__global__ __launch_bounds__(256) void short_conv_kernel(const T* __restrict__ x, const T* __restrict__ weight,
+                                                         const int32_t* __restrict__ cu, int num_seqs,
+                                                         const T* state_in, T* state_out, T* __restrict__ y,
+                                                         int64_t total_tokens, int channels, int64_t run_rows,
+                                                         int cblocks) {
+    const int64_t pairs = (run_rows + 1) * cblocks;
+    for (int64_t id = blockIdx.x; id < pairs; id += gridDim.x) {
+        const int64_t run = id / cblocks;
+        const int c = (static_cast<int>(id - run * cblocks) * 256 + static_cast<int>(threadIdx.x)) * 8;
+        if (c < channels)
+            conv_run<K, T, SILU>(x, weight, cu, num_seqs, state_in, state_out, y, total_tokens, channels, run_rows,
+                                 run, c);
     }
 }
 
@@ -383,9 +427,11 @@ static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
                 static_cast<T*>(a.y), a.total_tokens, a.channels);
         return hipGetLastError();
     }
+    constexpr int TB = run_tokens<T>();
     const int64_t run_rows = (a.total_tokens + TB - 1) / TB;
-    const int64_t per = (run_rows + 8) / 8;  // runs per XCD: 8 per >= run_rows + 1
-    const dim3 grid(static_cast<unsigned>(8 * per), static_cast<unsigned>((a.channels / 8 + 255) / 256));
+    const int cblocks = (a.channels / 8 + 255) / 256;
+    const int64_t pairs = (run_rows + 1) * cblocks;
+    const unsigned grid = static_cast<unsigned>(pairs < kConvMaxGroups ? pairs : kConvMaxGroups);
     const T* x = static_cast<const T*>(a.x);
     const T* w = static_cast<const T*>(a.weight);
     const T* si = static_cast<const T*>(a.state_in);
@@ -393,10 +439,10 @@ static hipError_t launch_conv_kt(const ConvArgs& a, hipStream_t stream) {
     T* y = static_cast<T*>(a.y);
     if (a.silu)
         short_conv_kernel<K, T, true><<<grid, 256, 0, stream>>>(x, w, a.cu_seqlens, a.num_seqs, si, so, y,
-                                                                 a.total_tokens, a.channels, run_rows);
+                                                                 a.total_tokens, a.channels, run_rows, cblocks);
     else
         short_conv_kernel<K, T, false><<<grid, 256, 0, stream>>>(x, w, a.cu_seqlens, a.num_seqs, si, so, y,
-                                                                  a.total_tokens, a.channels, run_rows);
+                                                                  a.total_tokens, a.channels, run_rows, cblocks);
     return hipGetLastError();
 }
 

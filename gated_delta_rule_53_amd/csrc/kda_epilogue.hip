@@ -28,16 +28,19 @@ __device__ __forceinline__ void load8(float (&x)[8], const T* p) {
     for (int i = 0; i < 8; ++i) x[i] = to_f32(v[i]);
 }
 
+// bf16 rounded by pairs in hardware
 template <typename T>
 __device__ __forceinline__ void store8(T* p, const float (&x)[8]) {
-    T v[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = from_f32<T>(x[i]);
-    constexpr int BYTES = 8 * static_cast<int>(sizeof(T));
     typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+    if constexpr (sizeof(T) == 2) {
+        __builtin_nontemporal_store(u32x4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                                          pack_bf16x2(x[6], x[7])},
+                                    reinterpret_cast<u32x4*>(p));
+    } else {
 #pragma unroll
-    for (int i = 0; i < BYTES / 16; ++i)
-        __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(v)[i], reinterpret_cast<u32x4*>(p) + i);
+        for (int i = 0; i < 2; ++i)
+            __builtin_nontemporal_store(reinterpret_cast<const u32x4*>(x)[i], reinterpret_cast<u32x4*>(p) + i);
+    }
 }
 
 }  // namespace
