@@ -22,7 +22,7 @@
 // of the state is a float4, and a wave touches whole 512-byte rows.
 #include <type_traits>
 
-#include "kda_common.h"
+#include "kda_bf16_mfma.h"
 #include "kda_internal.h"
 
 namespace kda {
@@ -205,6 +205,39 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
     }
 }
 
+// Element loads of 16- or 32-bit values, kept as raw bits until used (a
+// conversion at the load would make the wave wait for it there).
+template <typename T>
+__device__ __forceinline__ uint32_t load_bits(__amdgpu_buffer_rsrc_t r, int off_bytes) {
+    if constexpr (sizeof(T) == 2)
+        return __builtin_amdgcn_raw_buffer_load_b16(r, off_bytes, 0, 0);
+    else
+        return __builtin_amdgcn_raw_buffer_load_b32(r, off_bytes, 0, 0);
+}
+template <typename T>
+__device__ __forceinline__ float bits_f32(uint32_t u) {
+    return sizeof(T) == 2 ? __uint_as_float(u << 16) : __uint_as_float(u);
+}
+
+// Four consecutive outputs at byte offset off of the resource.
+template <typename TOut>
+__device__ __forceinline__ void store4(__amdgpu_buffer_rsrc_t r, int off, const floatx4& x) {
+    typedef int intx4 __attribute__((ext_vector_type(4)));
+    typedef int intx2 __attribute__((ext_vector_type(2)));
+    if constexpr (sizeof(TOut) == 4)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, x), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b64(
+            intx2{static_cast<int>(pack_bf16x2(x[0], x[1])), static_cast<int>(pack_bf16x2(x[2], x[3]))}, r, off, 0, 0);
+}
+template <typename TOut>
+__device__ __forceinline__ void store1(__amdgpu_buffer_rsrc_t r, int off, float x) {
+    if constexpr (sizeof(TOut) == 4)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(x), r, off, 0, 0);
+    else
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(pack_bf16x2(x, 0.f)), r, off, 0, 0);
+}
+
 // Multi-token verify decode with state-slot indirection.  Sequence n has
 // `width` tokens (rows n*width .. n*width+width-1) and one state slot per
 // token, idx = indices[n*width ..]: it starts from the state in slot
@@ -214,14 +247,12 @@ __global__ __launch_bounds__(256) void decode_step_kernel(
 // starting state is read before anything is written, so idx[a-1] may also
 // appear among the destinations.  Each token is the decode step above.
 // NORM: each token's output row gets the gated RMSNorm of decode_step_kernel
-// before it is written, so o itself never reaches HBM.  With S[dk][dv] the
-// row already sits in wave 0's first lanes, which apply it in registers;
-// with S^T it goes through LDS to wave 0 after the token's last barrier,
-// while the other waves load the next token.  The token's output-gate row
-// is loaded with its q and k, and the norm weight once, both into LDS, so
-// no global load is waited for there; the gate row alternates between two
-// buffers, since the next token's is stored while wave 0 may still be
-// reading this one's.
+// before it is written, so o itself never reaches HBM.  With S[dk][dv] every
+// row group holds the whole row and applies it in registers; with S^T the row
+// goes through LDS and every wave applies it after the token's last barrier.
+// The token's output-gate row is loaded with its q and k, and the norm weight
+// once, both into LDS; the gate row alternates between two buffers, since the
+// next token's is stored while this one's may still be read.
 template <int D, typename TIn, typename TOut, bool GATED, bool TRANS, bool NORM>
 __global__ __launch_bounds__(256) void verify_kernel(
     const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -232,11 +263,12 @@ __global__ __launch_bounds__(256) void verify_kernel(
     constexpr int NRG = 256 / NCG;
     constexpr int RPT = D / NRG;
     static_assert(NRG * NCG == 256 && RPT * NRG == D, "tiling");
+    constexpr int kNonTemporal = 2;  // buffer cache policy: the states are not read back here
 
     const int pair = blockIdx.x;  // n * H + h
     const int n = pair / num_heads, h = pair - n * num_heads;
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int cg = tid % NCG, rg = tid / NCG;
     const int32_t* idx = indices + static_cast<size_t>(n) * width;
     const size_t slot_stride = static_cast<size_t>(num_heads) * D * D;
@@ -244,43 +276,82 @@ __global__ __launch_bounds__(256) void verify_kernel(
         return (slot >= 0 && slot < num_slots) ? pool + slot * slot_stride + static_cast<size_t>(h) * D * D
                                                : nullptr;
     };
+    // The state block of a slot as a buffer resource: an invalid slot gets an
+    // empty range, so its stores are dropped and no branch surrounds them.
+    auto slot_rsrc = [&](int slot) {
+        float* S = slot_ptr(slot);
+        return buffer_rsrc(S ? S : pool, S ? D * D * 4 : 0);
+    };
+    // byte offset of this thread's row i of the block
+    auto s_off = [&](int i) { return ((rg + NRG * i) * D + 4 * cg) * 4; };
 
     int a = accepted ? accepted[n] : 1;
     a = a < 1 ? 1 : (a > width ? width : a);
     floatx4 s[RPT];
     {
-        const float* S = slot_ptr(idx[a - 1]);
+        const auto sr = slot_rsrc(idx[a - 1]);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-            s[i] = S ? *reinterpret_cast<const floatx4*>(S + (rg + NRG * i) * D + 4 * cg)
-                     : floatx4{0.f, 0.f, 0.f, 0.f};
+        for (int i = 0; i < RPT; ++i) s[i] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(sr, s_off(i), 0, 0));
     }
 
-    __shared__ float sq[D], sk[D], se[D];
+    // per-token rows, one entry per thread (threads >= D write entries that are never read)
+    __shared__ float sq[256], sk[256], se[256], sv[256];
     __shared__ float red[4][NCG][8];
-    __shared__ float so[NORM ? D : 1];  // the token's output row on its way to the epilogue
-    __shared__ float sog[NORM ? 2 : 1][NORM ? D : 1];  // sigmoid of the output-gate row of token t in [t & 1]
-    __shared__ float snw[NORM ? D : 1];                 // the norm weight
+    __shared__ float so[TRANS ? D : 1];                  // TRANS: the token's output row
+    __shared__ float sog[NORM ? 2 : 1][NORM ? 256 : 1];  // sigmoid of the output-gate row of token t in [t & 1]
+    __shared__ float snw[NORM ? D : 1];                   // the norm weight
     if constexpr (NORM) {
         if (tid < D) snw[tid] = np.weight[tid];
     }
+    // A token's inputs, loaded raw one token ahead (the last token's again
+    // after the last), so their loads fly while the previous token is
+    // computed and its state stored.  Thread c < D takes channel c of q, k, v,
+    // g and the output gate; threads past D read past the row, which gives
+    // zeros; every thread takes beta.  No branch surrounds a load or a store
+    // in the token loop, so the wait for these loads counts exactly the
+    // stores issued after them and never waits for those stores.
+    typedef std::conditional_t<GATED, TIn, float> GIn;
+    typedef std::conditional_t<GATED, TIn, float> BIn;
+    const int ct = tid & (D - 1);  // the channel of this thread's LDS entries
+    const int eo = tid < D ? tid : D;
+    uint32_t nq, nk, nv, ngate = 0, ng, nb;
+    auto fetch = [&](int t) {
+        const size_t tok = (static_cast<size_t>(n) * width + t) * num_heads + h;
+        nq = load_bits<TIn>(buffer_rsrc(q + tok * D, D * sizeof(TIn)), eo * sizeof(TIn));
+        nk = load_bits<TIn>(buffer_rsrc(k + tok * D, D * sizeof(TIn)), eo * sizeof(TIn));
+        nv = load_bits<TIn>(buffer_rsrc(v + tok * D, D * sizeof(TIn)), eo * sizeof(TIn));
+        if constexpr (NORM)
+            ngate = load_bits<TIn>(buffer_rsrc(static_cast<const TIn*>(np.gate) + tok * D, D * sizeof(TIn)),
+                                   eo * sizeof(TIn));
+        const GIn* gb = static_cast<const GIn*>(g) + (gph ? tok : tok * D);
+        ng = load_bits<GIn>(buffer_rsrc(gb, (gph ? 1 : D) * sizeof(GIn)), (gph ? (tid < D ? 0 : 1) : eo) * sizeof(GIn));
+        nb = load_bits<BIn>(buffer_rsrc(static_cast<const BIn*>(beta) + tok, sizeof(BIn)), 0);
+    };
+    fetch(0);
+    // The first token needs the state and its inputs anyway; waiting here also
+    // keeps the compiler's count at the loop head to what the loop issues (it
+    // merges the entry path into every iteration).
+    wait_vmcnt<0>();
     for (int t = 0; t < width; ++t) {
         const size_t row = static_cast<size_t>(n) * width + t;  // token row
         const size_t tok = row * num_heads + h;                  // (token, head)
-        if (tid < D) {
-            const size_t off = tok * D + tid;
-            sq[tid] = to_f32(q[off]);
-            sk[tid] = to_f32(k[off]);
-            if constexpr (NORM) sog[t & 1][tid] = gate_sigmoid(to_f32(static_cast<const TIn*>(np.gate)[off]));
-            const size_t goff = gph ? tok : off;
-            float gv;
-            if constexpr (GATED)
-                gv = gate_g(to_f32(static_cast<const TIn*>(g)[goff]), gp.dt_bias[gph ? h : h * D + tid],
-                            gate_exp(gp.a_log[h]), gp.lower_bound, gp.has_lower_bound);
-            else
-                gv = static_cast<const float*>(g)[goff];
-            se[tid] = fast_exp2(gv * kLog2e);
-        }
+        sq[tid] = bits_f32<TIn>(nq);
+        sk[tid] = bits_f32<TIn>(nk);
+        sv[tid] = bits_f32<TIn>(nv);
+        if constexpr (NORM) sog[t & 1][tid] = gate_sigmoid(bits_f32<TIn>(ngate));
+        float gv;
+        if constexpr (GATED)
+            gv = gate_g(bits_f32<GIn>(ng), gp.dt_bias[gph ? h : h * D + ct], gate_exp(gp.a_log[h]), gp.lower_bound,
+                        gp.has_lower_bound);
+        else
+            gv = bits_f32<GIn>(ng);
+        se[tid] = fast_exp2(gv * kLog2e);
+        float b;
+        if constexpr (GATED)
+            b = gate_sigmoid(bits_f32<BIn>(nb));
+        else
+            b = bits_f32<BIn>(nb);
+        fetch(t + 1 < width ? t + 1 : t);
         __syncthreads();
         float aq = 0.f, ak = 0.f, aqk = 0.f;
 #pragma unroll
@@ -295,17 +366,14 @@ __global__ __launch_bounds__(256) void verify_kernel(
         aqk = wave_sum_from(aqk, 1);
         const float rq = (l2norm ? rsqrtf(aq + kNormEps) : 1.f) * scale;
         const float rk = l2norm ? rsqrtf(ak + kNormEps) : 1.f;
+        const float kq = rk * rq * aqk;
+        const auto sr = slot_rsrc(idx[t]);
+        const auto orr = buffer_rsrc(out + tok * D, D * sizeof(TOut));
         if constexpr (TRANS) {
             const floatx4 e4 = {se[4 * cg], se[4 * cg + 1], se[4 * cg + 2], se[4 * cg + 3]};
             const floatx4 k4 = {sk[4 * cg], sk[4 * cg + 1], sk[4 * cg + 2], sk[4 * cg + 3]};
             const floatx4 q4 = {sq[4 * cg], sq[4 * cg + 1], sq[4 * cg + 2], sq[4 * cg + 3]};
-            float b;
-            if constexpr (GATED)
-                b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
-            else
-                b = static_cast<const float*>(beta)[tok];
-            const float kq = rk * rq * aqk;
-            float* S = slot_ptr(idx[t]);
+            typedef int intx4 __attribute__((ext_vector_type(4)));
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int c = rg + NRG * i;
@@ -314,15 +382,10 @@ __global__ __launch_bounds__(256) void verify_kernel(
                     group_sum(s[i][0] * k4[0] + s[i][1] * k4[1] + s[i][2] * k4[2] + s[i][3] * k4[3], NCG) * rk;
                 const float p =
                     group_sum(s[i][0] * q4[0] + s[i][1] * q4[1] + s[i][2] * q4[2] + s[i][3] * q4[3], NCG) * rq;
-                const float delta = b * (to_f32(v[tok * D + c]) - u);
+                const float delta = b * (sv[c] - u);
                 s[i] += (rk * delta) * k4;
-                if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + c * D + 4 * cg));
-                if (cg == 0) {
-                    if constexpr (NORM)
-                        so[c] = p + kq * delta;
-                    else
-                        out[tok * D + c] = from_f32<TOut>(p + kq * delta);
-                }
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, s[i]), sr, s_off(i), 0, kNonTemporal);
+                if (cg == 0) so[c] = p + kq * delta;
             }
         } else {
             floatx4 pu = {0.f, 0.f, 0.f, 0.f}, pp = {0.f, 0.f, 0.f, 0.f};
@@ -346,69 +409,55 @@ __global__ __launch_bounds__(256) void verify_kernel(
                 }
             }
             __syncthreads();
+            // every thread gets its four columns' u and p (the same in each row group)
             floatx4 u, p;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 u[j] = (red[0][cg][j] + red[1][cg][j] + red[2][cg][j] + red[3][cg][j]) * rk;
                 p[j] = (red[0][cg][4 + j] + red[1][cg][4 + j] + red[2][cg][4 + j] + red[3][cg][4 + j]) * rq;
             }
-            float b;
-            if constexpr (GATED)
-                b = gate_sigmoid(to_f32(static_cast<const TIn*>(beta)[tok]));
-            else
-                b = static_cast<const float*>(beta)[tok];
-            const size_t voff = tok * D + 4 * cg;
             floatx4 delta;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) delta[j] = b * (to_f32(v[voff + j]) - u[j]);
-            float* S = slot_ptr(idx[t]);
+            for (int j = 0; j < 4; ++j) delta[j] = b * (sv[4 * cg + j] - u[j]);
 #pragma unroll
             for (int i = 0; i < RPT; ++i) {
                 const int r = rg + NRG * i;
                 s[i] += (rk * sk[r]) * delta;
-                if (S) __builtin_nontemporal_store(s[i], reinterpret_cast<floatx4*>(S + r * D + 4 * cg));
+                typedef int intx4 __attribute__((ext_vector_type(4)));
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(intx4, s[i]), sr, s_off(i), 0, kNonTemporal);
             }
-            const float kq = rk * rq * aqk;
+            floatx4 ov;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) ov[j] = p[j] + kq * delta[j];
             if constexpr (NORM) {
-                // the whole output row is in wave 0's first NCG lanes (four
-                // columns each; the other lanes of the wave repeat them): the
-                // epilogue runs there, with no exchange
-                if (wave == 0) {
-                    float ov[4], ss = 0.f;
+                // each row group holds the whole output row (four columns per
+                // lane of its NCG lanes): the epilogue runs in registers
+                float ss = ov[0] * ov[0] + ov[1] * ov[1] + ov[2] * ov[2] + ov[3] * ov[3];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        ov[j] = p[j] + kq * delta[j];
-                        ss += ov[j] * ov[j];
-                    }
+                for (int m = 1; m < NCG; m <<= 1) ss += __shfl_xor(ss, m, 64);
+                const float r = rsqrtf(ss * (1.f / D) + np.eps);
 #pragma unroll
-                    for (int m = 1; m < NCG; m <<= 1) ss += __shfl_xor(ss, m, 64);
-                    const float r = rsqrtf(ss * (1.f / D) + np.eps);
-                    if (rg == 0) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j)
-                            out[voff + j] = from_f32<TOut>(ov[j] * r * snw[4 * cg + j] * sog[t & 1][4 * cg + j]);
-                    }
-                }
-            } else if (rg == 0) {
-#pragma unroll
-                for (int j = 0; j < 4; ++j) out[voff + j] = from_f32<TOut>(p[j] + kq * delta[j]);
+                for (int j = 0; j < 4; ++j) ov[j] *= r * snw[4 * cg + j] * sog[t & 1][4 * cg + j];
             }
+            // row group 0 stores the row (the others aim past its end)
+            store4<TOut>(orr, rg == 0 ? 4 * cg * static_cast<int>(sizeof(TOut)) : D * static_cast<int>(sizeof(TOut)),
+                         ov);
         }
-        // sq, sk, se and red are rewritten by the next token
+        // sq, sk, sv, se, red and so are rewritten by the next token
         __syncthreads();
-        if constexpr (NORM && TRANS) {
-            // so is rewritten only after the next token's first barrier, which
-            // wave 0 reaches once it has read it here
-            if (wave == 0) {
+        if constexpr (TRANS) {
+            // the row from LDS, one element per thread c < D (so is rewritten
+            // only after the next token's first barrier, which every wave
+            // reaches after reading it here)
+            float o = so[ct];
+            if constexpr (NORM) {
                 float ss = 0.f;
 #pragma unroll
                 for (int c = lane; c < D; c += 64) ss += so[c] * so[c];
                 ss = wave_sum_from(ss, 1);
-                const float r = rsqrtf(ss * (1.f / D) + np.eps);
-#pragma unroll
-                for (int c = lane; c < D; c += 64)
-                    out[tok * D + c] = from_f32<TOut>(so[c] * r * snw[c] * sog[t & 1][c]);
+                o *= rsqrtf(ss * (1.f / D) + np.eps) * snw[ct] * sog[t & 1][ct];
             }
+            store1<TOut>(orr, eo * static_cast<int>(sizeof(TOut)), o);
         }
     }
 }
