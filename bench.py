@@ -49,7 +49,8 @@ TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
 KERNEL_SOURCES = {
     "prefill": ["gated_delta_rule_53_amd/csrc/kda_prefill_split.hip", "gated_delta_rule_53_amd/csrc/kda_bf16_mfma.h",
                 "gated_delta_rule_53_amd/csrc/kda_common.h"],
-    "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_common.h"],
+    "decode": ["gated_delta_rule_53_amd/csrc/kda_decode.hip", "gated_delta_rule_53_amd/csrc/kda_bf16_mfma.h",
+               "gated_delta_rule_53_amd/csrc/kda_common.h"],
 }
 KERNEL_SOURCES["gated_prefill"] = KERNEL_SOURCES["prefill"]
 KERNEL_SOURCES["prefill_varlen8"] = KERNEL_SOURCES["prefill"]
@@ -219,7 +220,8 @@ def bench_prefill_conv(steps: int, warmup: int):
                        scale=x.scale, qk_l2norm=1, chunk_size=64)
     ws = torch.empty(kda.chunk_fwd_workspace_bytes(prob), dtype=torch.uint8, device=dev)
     y = torch.empty((T, C), dtype=torch.bfloat16, device=dev)
-    qkv = [torch.empty((T, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)]
+    # the convolved q, k, v of each input copy (three copies in turn, as for the fused call)
+    qkv = [[torch.empty((T, H, d), dtype=torch.bfloat16, device=dev) for _ in range(3)] for _ in range(3)]
     stream = torch.cuda.current_stream()
 
     def fused(i):
@@ -234,17 +236,18 @@ def bench_prefill_conv(steps: int, warmup: int):
         kda.short_conv(c["x"].view(T, C), w_, cu, c["cs"], silu=True, out=y, final_state=c["cs_out"])
 
     def core_only(i):
-        c = copies[i % 3]
-        kda.chunk_fwd(qkv[0], qkv[1], qkv[2], c["g"], c["b"], cu, c["s0"], scale=x.scale, out=c["out"],
+        c, q3 = copies[i % 3], qkv[i % 3]
+        kda.chunk_fwd(q3[0], q3[1], q3[2], c["g"], c["b"], cu, c["s0"], scale=x.scale, out=c["out"],
                       final_state=c["fs"], workspace=ws)
 
     for i in range(warmup):
         fused(i)
     wall, per = time_launches(fused, steps, stream)
-    conv_only(0)
     yv = y.view(T, 3, H, d)
-    for j in range(3):
-        qkv[j].copy_(yv[:, j])
+    for i in range(3):
+        conv_only(i)
+        for j in range(3):
+            qkv[i][j].copy_(yv[:, j])
     for i in range(warmup):
         conv_only(i)
         core_only(i)

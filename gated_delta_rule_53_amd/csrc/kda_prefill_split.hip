@@ -291,9 +291,16 @@ __device__ __forceinline__ floatx8 conv8(const uint4& x0, const uint4& x1, const
 }
 
 // One lane's part of a record fragment, as fp16.  A record is written once
-// and read once, by the chain pass: the stores are non-temporal.
+// and read once, by the chain pass.  NT: a non-temporal store (config 2: about
+// 2 % faster); the chain pass with the fused convolution, whose helper waves
+// touch fewer record lines ahead, reads them faster from the last-level cache
+// after ordinary stores (201 against 207 us).
+template <bool NT>
 __device__ __forceinline__ void store_frag(unsigned char* p, const floatx8& x) {
-    __builtin_nontemporal_store(__builtin_convertvector(x, halfx8), reinterpret_cast<halfx8*>(p));
+    if constexpr (NT)
+        __builtin_nontemporal_store(__builtin_convertvector(x, halfx8), reinterpret_cast<halfx8*>(p));
+    else
+        *reinterpret_cast<halfx8*>(p) = __builtin_convertvector(x, halfx8);
 }
 
 // Sequence of chunk cg: the last n with offsets[n] <= cg (empty sequences are skipped).
@@ -504,13 +511,13 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                 const int R = fr >> 2, s = fr & 3, r0 = 32 * s + ka;
                 const floatx8 x = bf8_to_f(col8_tr2(smem, P_PTH, SN, r0, r0 + 16, 16 * R, li)) +
                                   bf8_to_f(col8_tr2(smem, P_PTL, SN, r0, r0 + 16, 16 * R, li));
-                store_frag(rec + REC_NPSI + fr * FRAG + ln * 16, -x);
+                store_frag<!CONV>(rec + REC_NPSI + fr * FRAG + ln * 16, -x);
             } else if (fr < 22) {  // X' diag(rk beta) [tri], fp16: X'^T[32s + k][16R + li]
                 const int b = fr - 16;
                 const int R = tri_R(b), r0 = 32 * tri_s(b) + ka;
                 const floatx8 x = bf8_to_f(col8_tr2(smem, P_XTH, SN, r0, r0 + 16, 16 * R, li)) +
                                   bf8_to_f(col8_tr2(smem, P_XTL, SN, r0, r0 + 16, 16 * R, li));
-                store_frag(rec + REC_X + b * FRAG + ln * 16, x);
+                store_frag<!CONV>(rec + REC_X + b * FRAG + ln * 16, x);
             } else {  // P' [tri], fp16, from the row-major hi/lo planes
                 const int b = fr - 22, R = tri_R(b);
                 const int o = ((16 * R + li) * SN + 32 * tri_s(b) + ka) * 2;
@@ -522,7 +529,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                     x[i] = static_cast<float>(h0[i]) + static_cast<float>(q0[i]);
                     x[4 + i] = static_cast<float>(h1[i]) + static_cast<float>(q1[i]);
                 }
-                store_frag(rec + REC_P + b * FRAG + ln * 16, x);
+                store_frag<!CONV>(rec + REC_P + b * FRAG + ln * 16, x);
             }
         }
     };
@@ -851,7 +858,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                     floatx8 x = bf8_to_f(col8_tr2(smem, P_KIH, SW, r0, r0 + 16, 16 * w, li)) +
                                 bf8_to_f(col8_tr2(smem, P_KIL, SW, r0, r0 + 16, 16 * w, li));
                     x *= sEL[16 * w + li];
-                    store_frag(rec + REC_KE + fr * FRAG + ln * 16, x);
+                    store_frag<!CONV>(rec + REC_KE + fr * FRAG + ln * 16, x);
                 } else {
                     // Qg' [R][s]: rq_r Qg[r][c] e^{G_31}[c] at channels c = 32s + k
                     const int f2 = fr - 16, R = f2 >> 2, s = f2 & 3;
@@ -868,7 +875,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
                         x[i] = (static_cast<float>(h0[i]) + static_cast<float>(q0[i])) * (rq * e0[i]);
                         x[4 + i] = (static_cast<float>(h1[i]) + static_cast<float>(q1[i])) * (rq * e1[i]);
                     }
-                    store_frag(rec + REC_QG + f2 * FRAG + ln * 16, x);
+                    store_frag<!CONV>(rec + REC_QG + f2 * FRAG + ln * 16, x);
                 }
             }
             float* vec = reinterpret_cast<float*>(rec + REC_VEC);
