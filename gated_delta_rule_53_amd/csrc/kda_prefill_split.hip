@@ -1864,24 +1864,32 @@ __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_ker
             vb[s] = __builtin_convertvector(
                 bf8_to_f(col8_tr2(vb_cur, 0, DVT, r0, r0 + 16, 0, l16)), halfx8);
         }
-        // the products of D, each followed by one load of the next chunk (pinned order)
-        floatx4 Dm = mmah(as_halfx8(cur.x[0]), vb[0], floatx4{0.f, 0.f, 0.f, 0.f});
+        // the products of D in two independent accumulators (K blocks 0, 1 and
+        // 2, 3 of S), each product followed by one load of the next chunk
+        // (pinned order)
+        const floatx4 z4 = {0.f, 0.f, 0.f, 0.f};
+        floatx4 Da = mmah(as_halfx8(cur.x[0]), vb[0], z4);
         __builtin_amdgcn_sched_barrier(0);
         load_a(nxt, nrec, nrr, 0, lane);
         __builtin_amdgcn_sched_barrier(0);
-        Dm = mmah(as_halfx8(cur.x[1]), vb[1], Dm);
+        floatx4 Db = mmah(as_halfx8(cur.x[1]), vb[1], z4);
         __builtin_amdgcn_sched_barrier(0);
         load_a(nxt, nrec, nrr, 1, lane);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            Dm = mmah(as_halfx8(cur.np[s]), shs[s], Dm);
+        for (int s = 0; s < 2; ++s) {
+            Da = mmah(as_halfx8(cur.np[s]), shs[s], Da);
+            Db = mmah(as_halfx8(cur.np[2 + s]), shs[2 + s], Db);
             __builtin_amdgcn_sched_barrier(0);
-            load_a(nxt, nrec, nrr, 2 + s, lane);
+            load_a(nxt, nrec, nrr, 2 + 2 * s, lane);
             __builtin_amdgcn_sched_barrier(0);
-            Dm = mmah(as_halfx8(cur.np[s]), sls[s], Dm);
+            Da = mmah(as_halfx8(cur.np[s]), sls[s], Da);
+            Db = mmah(as_halfx8(cur.np[2 + s]), sls[2 + s], Db);
+            __builtin_amdgcn_sched_barrier(0);
+            load_a(nxt, nrec, nrr, 3 + 2 * s, lane);
+            __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
+        const floatx4 Dm = Da + Db;
         // (3) D_m into LDS: rows 16m .. 16m+15 are half (m & 1) of K block m >> 1
         {
             halfx4 dh, dl;
@@ -1890,14 +1898,19 @@ __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_ker
             *reinterpret_cast<halfx4*>(lds_dx + o) = dh;
             *reinterpret_cast<halfx4*>(lds_dx + o + FRAG) = dl;
         }
-        O = floatx4{0.f, 0.f, 0.f, 0.f};
+        floatx4 Oa = z4, Ob = z4;
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            O = mmah(shs[s], as_halfx8(cur.qg[s]), O);
+        for (int s = 0; s < 4; s += 2) {
+            Oa = mmah(shs[s], as_halfx8(cur.qg[s]), Oa);
             __builtin_amdgcn_sched_barrier(0);
             load_b(nxt, nrec, s);
             __builtin_amdgcn_sched_barrier(0);
+            Ob = mmah(shs[s + 1], as_halfx8(cur.qg[s + 1]), Ob);
+            __builtin_amdgcn_sched_barrier(0);
+            load_b(nxt, nrec, s + 1);
+            __builtin_amdgcn_sched_barrier(0);
         }
+        O = Oa + Ob;
         L = len_of(j);
         KDA_PHASE_MARK(19);
         lds_barrier();
