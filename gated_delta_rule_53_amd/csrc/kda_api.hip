@@ -74,7 +74,9 @@ hipError_t scratch_address(void** out) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned_to(const void* p, size_t bytes) { return (reinterpret_cast<uintptr_t>(p) & (bytes - 1)) == 0; }
 
-// Largest token count of kda_short_conv: 256 * ceil(T / 8) + 2048 work-items along x below 2^32.
+// Largest token count of kda_short_conv, as its header states.  (The launch
+// takes (run, channel block) pairs in turn from at most 2^20 workgroups, so
+// the grid fits the hardware's limits for any count up to this one.)
 constexpr int64_t kConvMaxTokens = (int64_t(1) << 27) - 1024;
 
 // Alignment the kernels' vector accesses need: q, k, v, out, the states, the
@@ -528,8 +530,7 @@ kda_status_t kda_short_conv(int32_t num_seqs, int64_t total_tokens, int32_t chan
         return fail(KDA_ERR_UNSUPPORTED, "%s: kernel_size %d (supported: 1 to 4)", what, kernel_size);
     if (dtype != KDA_F32 && dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "%s: dtype %d", what, dtype);
     if (silu != 0 && silu != 1) return fail(KDA_ERR_BAD_SHAPE, "%s: silu must be 0 or 1", what);
-    // grid: one workgroup of 256 threads per 8 tokens (x; in place: per request) and per 2048
-    // channels (y); the launch's work-item count along x must stay below 2^32
+    // in place the grid is one workgroup per request (x) and per 2048 channels (y)
     if (total_tokens > kConvMaxTokens || channels > (1 << 26) || num_seqs > (1 << 23))
         return fail(KDA_ERR_UNSUPPORTED, "%s: problem too large (at most %lld tokens, 2^23 requests, 2^26 "
                     "channels)", what, (long long)kConvMaxTokens);
