@@ -7,7 +7,8 @@ pool slots).  Bars as everywhere: max|gpu - oracle| / max|oracle| <= 2e-3
 slots the call does not name must come back bit for bit.  Cases cover padded
 (-1) and out-of-range indices, both head sizes, the two-pass bf16 d=128 prefill
 with one and with two value tiles per workgroup (40 chains > 32), the on-chip
-prefill, empty sequences and the fused gate.
+prefill, empty sequences, the fused gate and windows of up to 12 tokens; a
+bf16 output must equal the fp32 output rounded to nearest even, bit for bit.
 """
 import numpy as np
 import pytest
@@ -48,6 +49,8 @@ VERIFY_CASES = [
     (6, 1, 3, 128, torch.bfloat16, False, 1, False),
     (4, 5, 2, 64, torch.bfloat16, True, 0, True),
     (3, 2, 2, 128, torch.float32, True, 1, False),
+    (3, 12, 2, 128, torch.bfloat16, True, 2, True),   # wider windows: the loop's one-token-ahead loads
+    (2, 9, 2, 64, torch.float32, True, 1, False),
 ]
 
 
@@ -193,3 +196,34 @@ def test_verify_normed(N, W, H, d, dtype, layout, raw):
     err = rel_err(y, ref)
     print(f"  err {err:.3e}")
     assert err <= tol_for(dtype), err
+
+
+@pytest.mark.parametrize("layout", ["dk_dv", "dv_dk"])
+@pytest.mark.parametrize("normed", [False, True])
+def test_verify_bf16_out_is_rounded_fp32_out(layout, normed):
+    """The bf16 output is the fp32 output rounded to nearest even, bit for bit,
+    and the written pool is the same: the output's dtype changes only its final
+    rounding and store (the bench runs verify with bf16 outputs)."""
+    import gated_delta_rule_53_amd as kda
+    N, W, H, d = 6, 6, 4, 128
+    x = w.make_verify(N, W, H, d, torch.bfloat16, g_mu=2.0, pad=1, seed=61)
+    gen = torch.Generator().manual_seed(62)
+    og = torch.randn((N, W, H, d), generator=gen).to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn((d,), generator=gen)
+    announce(f"verify bf16 vs fp32 output layout={layout} normed={normed}")
+    pool_in = x.pool if layout == "dk_dv" else x.pool.transpose(-1, -2).contiguous()
+    args = (dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta))
+    ys, pools = {}, {}
+    for od in (torch.float32, torch.bfloat16):
+        pool = dev(pool_in.clone())
+        common = dict(scale=x.scale, state_layout=layout, out_dtype=od)
+        if normed:
+            ys[od] = kda.recurrent_verify_normed(*args, pool, dev(x.indices), dev(og), dev(nw), dev(x.accepted),
+                                                 norm_eps=1e-6, **common)
+        else:
+            ys[od] = kda.recurrent_verify(*args, pool, dev(x.indices), dev(x.accepted), **common)
+        pools[od] = pool
+    torch.cuda.synchronize()
+    assert ys[torch.bfloat16].dtype == torch.bfloat16
+    assert torch.equal(pools[torch.float32], pools[torch.bfloat16])
+    assert torch.equal(ys[torch.bfloat16], ys[torch.float32].to(torch.bfloat16))
