@@ -331,6 +331,39 @@ __device__ inline int seq_chunks(const int32_t* __restrict__ cu, int i, int64_t 
     return (a >= 0 && b <= total_tokens && b >= a) ? static_cast<int>((b - a + C - 1) / C) : 0;
 }
 
+// Where prep_kernel and chain_kernel find each sequence's chunks: the chunk
+// map's offsets and order in the workspace, or, with offsets null (at most
+// kLaneMapSeqs sequences, every chain running at once so their order does not
+// matter), offsets each wave computes from cu_seqlens at its start and the
+// sequences in index order.  One kernel launch fewer per call.
+struct ChunkMap {
+    const int32_t* offsets;  // [N + 1], or null
+    const int32_t* order;    // [N], or null
+    int64_t total_tokens;
+    int max_chunks;          // the workspace's record capacity in chunks
+};
+constexpr int kLaneMapSeqs = 63;
+
+// The chunk map's offsets in a wave's lanes: lane n (n <= num_seqs) holds
+// offsets[n], clamped to max_chunks as chunk_map_kernel clamps them.
+__device__ __forceinline__ int lane_offsets(const int32_t* __restrict__ cu, int num_seqs, const ChunkMap& cm,
+                                            int lane) {
+    const int mine = lane < num_seqs ? seq_chunks(cu, lane, cm.total_tokens) : 0;
+    int x = mine;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+        const int y = __shfl_up(x, off, 64);
+        x += lane >= off ? y : 0;
+    }
+    return min(x - mine, cm.max_chunks);
+}
+
+// find_seq over lane-held offsets: the last n < num_seqs with offsets[n] <= cg.
+__device__ __forceinline__ int find_seq_lanes(int lane_off, int lane, int num_seqs, int cg) {
+    const unsigned long long m = __ballot(lane < num_seqs && lane_off <= cg);
+    return m ? 63 - __clzll(static_cast<long long>(m)) : 0;
+}
+
 __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restrict__ cu, int num_seqs,
                                                          int64_t total_tokens, int max_chunks,
                                                          int32_t* __restrict__ offsets, int32_t* __restrict__ order) {
@@ -388,12 +421,13 @@ __global__ __launch_bounds__(1024) void chunk_map_kernel(const int32_t* __restri
 // first chunk) and the head's taps, which waves 0-3 fetched with the item's
 // other inputs; after the first barrier each row is convolved from rows
 // r - 3 .. r.
-template <bool GATED, bool GPH, bool CONV>
+template <bool GATED, bool GPH, bool CONV, bool LMAP>
 __global__ __launch_bounds__(PNT) void prep_kernel(
     const bf16_t* __restrict__ q, const bf16_t* __restrict__ k, const void* __restrict__ g_in,
     const void* __restrict__ beta_in, GateParams gp, const int32_t* __restrict__ cu_seqlens,
     const int32_t* __restrict__ offsets, unsigned char* __restrict__ records, int num_seqs, int num_heads,
-    float scale, int l2norm, int qk_row, ConvParams cv) {
+    float scale, int l2norm, int qk_row, ConvParams cv, int64_t total_tokens, int max_chunks) {
+    const ChunkMap cm{offsets, nullptr, total_tokens, max_chunks};
     const float* __restrict__ g = static_cast<const float*>(g_in);
     const float* __restrict__ beta = static_cast<const float*>(beta_in);
     const bf16_t* __restrict__ graw = static_cast<const bf16_t*>(g_in);
@@ -412,7 +446,16 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
 
     KDA_PHASE_BEGIN
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int n_chunks = offsets[num_seqs];
+    // LMAP: the chunk offsets in the wave's lanes (cm.offsets is null)
+    const int lane_off = LMAP ? lane_offsets(cu_seqlens, num_seqs, cm, static_cast<int>(threadIdx.x) & 63) : 0;
+    // offsets[n] of sequence n (n uniform), from the map or from the lanes
+    auto offset_of = [&](int n) {
+        if constexpr (LMAP)
+            return __builtin_amdgcn_readlane(lane_off, n);
+        else
+            return offsets[n];
+    };
+    const int n_chunks = offset_of(num_seqs);
     const int items = n_chunks * num_heads;
 
     // Prefetch registers: row tid/16, channels 8(tid%16) .. +7 of k, q, g; beta.
@@ -431,8 +474,10 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
     const int qk_bytes = qk_row * 2;          // one token's q or k row
     auto fetch = [&](int item, int tid) {
         const int cg = item / num_heads, h = item - (item / num_heads) * num_heads;
-        const int n = find_seq(offsets, num_seqs, cg);
-        const int64_t start = cu_seqlens[n] + static_cast<int64_t>(C) * (cg - offsets[n]);
+        const int n = LMAP ? find_seq_lanes(lane_off, static_cast<int>(threadIdx.x) & 63, num_seqs, cg)
+                           : find_seq(offsets, num_seqs, cg);
+        const int first_chunk = offset_of(n);
+        const int64_t start = cu_seqlens[n] + static_cast<int64_t>(C) * (cg - first_chunk);
         const int L = max(static_cast<int>(min64(C, cu_seqlens[n + 1] - start)), 0);
         const int r = tid >> 4, cc = tid & 15;
         const size_t head0 = static_cast<size_t>(start) * num_heads + h;  // (first row, head)
@@ -449,7 +494,7 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             // head's k and q channels 8 cc .. 8 cc + 7 (taps padded at the front
             // to four); the other waves read nothing (an empty range)
             const int l4 = r & 3;
-            const bool first = cg == offsets[n];
+            const bool first = cg == first_chunk;
             const int srow_bytes = cv.channels * 2;
             const bool is_k = (wave & 1) == 0;
             const int blk = is_k ? num_heads * D : 0;  // channel block of k or q
@@ -1506,8 +1551,8 @@ constexpr int TOUCH_AHEAD = 6;
 // chunk's V rows instead of copying them (see below).
 template <typename TOut, bool CONV>
 __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_kernel(
-    const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ order, const unsigned char* __restrict__ records, const float* initial_state,
+    const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, ChunkMap cm,
+    const unsigned char* __restrict__ records, const float* initial_state,
     TOut* __restrict__ out, float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs,
     int num_heads, int state_trans, int v_row, ConvParams cv) {
     __shared__ __align__(16) unsigned char lds_sx[CH_SX_BYTES];
@@ -1523,11 +1568,19 @@ __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_ker
     const int crank = (id / 64) * 8 + (id & 7);
     const int unit = (id >> 3) & 7;
     if (crank >= num_seqs * num_heads) return;
-    const int n = order[crank / num_heads], h = crank % num_heads;
+    const int n = cm.order ? cm.order[crank / num_heads] : crank / num_heads, h = crank % num_heads;
     const int m = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     const int lane0 = static_cast<int>(threadIdx.x) & 63;
     const int col0 = unit * DVT;
-    const int c_begin = offsets[n], c_end = offsets[n + 1];
+    int c_begin, c_end;
+    if (cm.offsets) {
+        c_begin = cm.offsets[n];
+        c_end = cm.offsets[n + 1];
+    } else {
+        const int lane_off = lane_offsets(cu_seqlens, num_seqs, cm, lane0);
+        c_begin = __builtin_amdgcn_readlane(lane_off, n);
+        c_end = __builtin_amdgcn_readlane(lane_off, n + 1);
+    }
     const int nc = c_end - c_begin;
     const int64_t t_first = cu_seqlens[n], t_last = cu_seqlens[n + 1];
     const int row_stride = num_heads * D;
@@ -2008,26 +2061,6 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     int32_t* order = offsets + a.num_seqs + 1;
     unsigned char* records = ws + map_bytes(a.num_seqs);
     const size_t max_chunks = static_cast<size_t>((a.total_tokens + C - 1) / C) + static_cast<size_t>(a.num_seqs);
-    chunk_map_kernel<<<1, 1024, 0, stream>>>(a.cu_seqlens, a.num_seqs, a.total_tokens, static_cast<int>(max_chunks),
-                                             offsets, order);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    const size_t max_items = max_chunks * static_cast<size_t>(a.num_heads);
-    const unsigned prep_grid = static_cast<unsigned>(max_items < static_cast<size_t>(device_cu_count()) ? max_items : static_cast<size_t>(device_cu_count()));
-    if (prep_grid > 0) {
-        const bf16_t* q = static_cast<const bf16_t*>(a.q);
-        const bf16_t* k = static_cast<const bf16_t*>(a.k);
-        auto pick = [&](auto conv) {
-            constexpr bool CV = decltype(conv)::value;
-            return a.gate.a_log ? (a.gate_per_head ? prep_kernel<true, true, CV> : prep_kernel<true, false, CV>)
-                                : (a.gate_per_head ? prep_kernel<false, true, CV> : prep_kernel<false, false, CV>);
-        };
-        auto* kern = a.conv.weight ? pick(std::true_type{}) : pick(std::false_type{});
-        kern<<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, offsets, records, a.num_seqs,
-                                            a.num_heads, a.scale, a.l2norm, static_cast<int>(a.qkv_row), a.conv);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
     const unsigned chains = static_cast<unsigned>(a.num_seqs) * static_cast<unsigned>(a.num_heads);
     const unsigned groups = (chains + 7u) & ~7u;
     // While every 16-column tile has a compute unit of its own, the chunk
@@ -2038,16 +2071,46 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
     // With the convolution fused, chain_kernel (whose touch wave convolves
     // V) runs in both cases, without the padding when tiles outnumber CUs.
     const bool pairs = static_cast<size_t>(chains) * (D / DVT) > static_cast<size_t>(device_cu_count());
+    // Every chain running at once and few sequences: the kernels find the
+    // chunks themselves, with no chunk-map launch.
+    const bool lane_map = !pairs && a.num_seqs <= kLaneMapSeqs;
+    const ChunkMap cm{lane_map ? nullptr : offsets, lane_map ? nullptr : order, a.total_tokens,
+                      static_cast<int>(max_chunks)};
+    hipError_t e = hipSuccess;
+    if (!lane_map) {
+        chunk_map_kernel<<<1, 1024, 0, stream>>>(a.cu_seqlens, a.num_seqs, a.total_tokens,
+                                                 static_cast<int>(max_chunks), offsets, order);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t max_items = max_chunks * static_cast<size_t>(a.num_heads);
+    const unsigned prep_grid = static_cast<unsigned>(max_items < static_cast<size_t>(device_cu_count()) ? max_items : static_cast<size_t>(device_cu_count()));
+    if (prep_grid > 0) {
+        const bf16_t* q = static_cast<const bf16_t*>(a.q);
+        const bf16_t* k = static_cast<const bf16_t*>(a.k);
+        auto pick = [&](auto conv, auto lmap) {
+            constexpr bool CV = decltype(conv)::value, LM = decltype(lmap)::value;
+            return a.gate.a_log ? (a.gate_per_head ? prep_kernel<true, true, CV, LM> : prep_kernel<true, false, CV, LM>)
+                                : (a.gate_per_head ? prep_kernel<false, true, CV, LM> : prep_kernel<false, false, CV, LM>);
+        };
+        auto pick_map = [&](auto lmap) { return a.conv.weight ? pick(std::true_type{}, lmap) : pick(std::false_type{}, lmap); };
+        auto* kern = lane_map ? pick_map(std::true_type{}) : pick_map(std::false_type{});
+        kern<<<prep_grid, PNT, 0, stream>>>(q, k, a.g, a.beta, a.gate, a.cu_seqlens, cm.offsets, records,
+                                            a.num_seqs, a.num_heads, a.scale, a.l2norm, static_cast<int>(a.qkv_row),
+                                            a.conv, a.total_tokens, static_cast<int>(max_chunks));
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
     if (a.conv.weight) {
         chain_kernel<TOut, true><<<groups * 8, CH_THREADS_CONV, pairs ? 0 : 64 * 1024, stream>>>(
-            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+            static_cast<const bf16_t*>(a.v), a.cu_seqlens, cm, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
             a.state_trans, static_cast<int>(a.qkv_row), a.conv);
         return hipGetLastError();
     }
     if (!pairs) {
         chain_kernel<TOut, false><<<groups * 8, CH_THREADS, 64 * 1024, stream>>>(
-            static_cast<const bf16_t*>(a.v), a.cu_seqlens, offsets, order, records, a.initial_state,
+            static_cast<const bf16_t*>(a.v), a.cu_seqlens, cm, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
             a.state_trans, static_cast<int>(a.qkv_row), a.conv);
         return hipGetLastError();
