@@ -65,7 +65,9 @@ KERNEL_SOURCES["epilogue"] = ["gated_delta_rule_53_amd/csrc/kda_epilogue.hip", "
 # kernels launched by one kda_chunk_fwd call on the bf16, d=128 path
 # one chain per (sequence, head, 16-column tile): chain_kernel while every tile
 # has a compute unit, scan_kernel (two tiles per workgroup) beyond that
-PREFILL_KERNELS = ["chunk_map_kernel", "prep_kernel", "chain_kernel"]
+# one sequence, every chain on compute units of its own: prep and the chain pass find the
+# chunks themselves (no chunk-map launch)
+PREFILL_KERNELS = ["prep_kernel", "chain_kernel"]
 PREFILL_KERNELS_MANY = ["chunk_map_kernel", "prep_kernel", "scan_kernel"]
 
 
@@ -700,7 +702,7 @@ def main():
                          "tokens_per_s": round(pc["tokens"] * args.steps / pc["wall"], 1),
                          "unfused_us": round(pc["per_launch_unfused"] * 1e6, 2),
                          "unfused_alg_bytes": pc["alg_bytes_unfused"],
-                         "roofline": prefill_roofline("kda_chunk_fwd_conv = chunk_map_kernel + prep_kernel (CONV) + "
+                         "roofline": prefill_roofline("kda_chunk_fwd_conv = prep_kernel (CONV) + "
                                                       "chain_kernel (CONV) + conv_state_kernel", pc, pc_tr)},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
                           "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
