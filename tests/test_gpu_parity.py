@@ -257,3 +257,35 @@ def test_decode_256x64_workload():
     eo, es = rel_err(out, ro), rel_err(st, rs)
     print(f"  err out {eo:.3e} state {es:.3e}")
     assert eo <= 2e-3 and es <= 2e-3
+
+
+@pytest.mark.parametrize("H", [2, 40], ids=["lane_map", "map_kernel"])
+def test_prefill_malformed_cu_seqlens(H):
+    """Entries outside [0, T] and a decreasing pair make their sequences empty:
+    no out-of-bounds access, their final states equal their initial states, no
+    output row outside the well-formed sequences is written, and the
+    well-formed sequences match the oracle.  H=2: the kernels compute the chunk
+    map themselves; H=40: more tiles than CUs, the chunk-map kernel and the
+    two-tile scan."""
+    import gated_delta_rule_53_amd as kda
+    T, d = 300, 128
+    x = w.make_prefill([T], H, d, torch.bfloat16, g_mu=2.0, seed=31, name="malformed_cu")
+    cu = torch.tensor([-10, 100, 160, 250, 400, 300], dtype=torch.int32)
+    N = cu.numel() - 1
+    gen = torch.Generator().manual_seed(32)
+    s0 = torch.randn((N, H, d, d), generator=gen) * 0.01
+    announce(f"prefill malformed cu_seqlens H={H}")
+    out = torch.full((T, H, d), float("nan"), device="cuda:0")
+    out, fs = kda.chunk_fwd(dev(x.q), dev(x.k), dev(x.v), dev(x.g), dev(x.beta), dev(cu), dev(s0),
+                            scale=x.scale, out=out, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o, s = out.cpu(), fs.cpu()
+    for n in (0, 3, 4):
+        assert torch.equal(s[n], s0[n]), n
+    assert torch.isnan(o[:100]).all() and torch.isnan(o[250:]).all()
+    rows = slice(100, 250)
+    ref_o, ref_s = oracle.forward(x.q[rows], x.k[rows], x.v[rows], x.g[rows], x.beta[rows],
+                                  torch.tensor([0, 60, 150], dtype=torch.int32), s0[1:3], scale=x.scale)
+    eo, es = rel_err(out[rows], ref_o), rel_err(fs[1:3], ref_s)
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= 2e-3 and es <= 2e-3, (eo, es)
