@@ -18,7 +18,9 @@ bf16 gate and beta activated in the kernel) is reported under ``gated_prefill``.
 
 Kernel durations come from HIP events recorded around every launch on the
 stream the kernels run on; ``roofline.achieved`` divides the algorithmic bytes
-of one launch by the mean launch duration.
+of one launch by the mean launch duration.  Before its timed launches every leg
+runs its own step untimed for ``settle_s`` seconds, after its W warmup steps:
+the GPU's clocks rise only after some tens of milliseconds of sustained load.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
@@ -89,9 +91,35 @@ def measured_traffic(kind: str):
     return rec.get("bytes_per_launch")
 
 
-def time_launches(fn, n: int, stream):
-    """Run fn() n times; returns (wall seconds, mean per-launch seconds from events)."""
+# The GPU raises its clocks only after some tens of milliseconds of sustained load:
+# on a 4096-token prefill the first ~100 calls after idle ran at 160-180 us, the
+# following ones at ~150 us.  Each leg therefore runs its own step untimed for at
+# least this long before its K timed launches (after its W warmup steps), so that
+# the timed launches see the clocks that a caller issuing work back to back sees.
+SETTLE_S = 0.2
+
+
+def settle(fn, seconds: float = SETTLE_S) -> int:
+    """Call fn(i) untimed until `seconds` of wall time have passed; returns the call count."""
     import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    i = 0
+    while True:
+        for _ in range(8):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+        if time.perf_counter() - t0 >= seconds:
+            return i
+
+
+def time_launches(fn, n: int, stream):
+    """Run fn() n times; returns (wall seconds, mean per-launch seconds from events).
+
+    The leg's step is first run untimed for SETTLE_S seconds (settle())."""
+    import torch
+    settle(fn)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -639,6 +667,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle_s": SETTLE_S,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
