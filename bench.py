@@ -16,9 +16,10 @@ each far larger than the Infinity Cache, so one input copy serves.  The same
 prefill workload through the fused-gate entry point (kda_chunk_fwd_gated: raw
 bf16 gate and beta activated in the kernel) is reported under ``gated_prefill``.
 
-Kernel durations come from HIP events recorded around every launch on the
-stream the kernels run on; ``roofline.achieved`` divides the algorithmic bytes
-of one launch by the mean launch duration.  Before its timed launches every leg
+Kernel durations come from a pair of HIP events around each leg's K back-to-back
+launches, on the stream the kernels run on; ``roofline.achieved`` divides the
+algorithmic bytes of one launch by the mean launch duration (the events'
+interval over K).  Before its timed launches every leg
 runs its own step untimed for ``settle_s`` seconds, after its W warmup steps:
 the GPU's clocks rise only after some tens of milliseconds of sustained load.
 
@@ -115,21 +116,25 @@ def settle(fn, seconds: float = SETTLE_S) -> int:
 
 
 def time_launches(fn, n: int, stream):
-    """Run fn() n times; returns (wall seconds, mean per-launch seconds from events).
+    """Run fn() n times back to back; returns (wall seconds, mean per-launch seconds).
 
-    The leg's step is first run untimed for SETTLE_S seconds (settle())."""
+    The leg's step is first run untimed for SETTLE_S seconds (settle()).  One
+    pair of HIP events on the kernels' stream brackets the n launches, and the
+    mean launch duration is their interval over n: it includes whatever gaps the
+    GPU leaves between launches, and no event markers are placed between them
+    (a marker per launch left the GPU idle about 5 us per launch)."""
     import torch
     settle(fn)
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    start.record(stream)
     for i in range(n):
-        evs[i][0].record(stream)
         fn(i)
-        evs[i][1].record(stream)
+    end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = sum(a.elapsed_time(b) for a, b in evs) / n / 1e3
+    per = start.elapsed_time(end) / n / 1e3
     return wall, per
 
 
