@@ -737,7 +737,7 @@ def main():
                          "unfused_us": round(pc["per_launch_unfused"] * 1e6, 2),
                          "unfused_alg_bytes": pc["alg_bytes_unfused"],
                          "roofline": prefill_roofline("kda_chunk_fwd_conv = prep_kernel (CONV) + "
-                                                      "chain_kernel (CONV) + conv_state_kernel", pc, pc_tr)},
+                                                      "chain_kernel (CONV, writes the conv state)", pc, pc_tr)},
         "gated_prefill": {"workload": gp["x"].name + "_raw_bf16_gate",
                           "tokens_per_s": round(gp["tokens"] * args.steps / gp["wall"], 1),
                           "roofline": {"kernel": "kda_chunk_fwd_gated = " + " + ".join(PREFILL_KERNELS),

@@ -152,7 +152,7 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
                             float* final_state, void* workspace, size_t workspace_bytes, void* stream,
                             const int32_t* slots = nullptr, int num_slots = 0,
                             Workspace ws_kind = Workspace::kCaller, const kda::ConvParams* conv = nullptr,
-                            int64_t qkv_row = 0) {
+                            int64_t qkv_row = 0, void* conv_state_out = nullptr) {
     if (p->chunk_size != 0 && p->chunk_size != 64)
         return fail(KDA_ERR_UNSUPPORTED, "%s: chunk_size %d (supported: 64)", what, p->chunk_size);
     if (p->num_seqs == 0) {
@@ -208,6 +208,7 @@ kda_status_t chunk_fwd_impl(const char* what, const kda_problem_t* p, const kda:
     a.num_slots = num_slots;
     a.qkv_row = qkv_row > 0 ? qkv_row : int64_t(p->num_heads) * p->head_k;
     if (conv) a.conv = *conv;
+    a.conv_state_out = conv ? conv_state_out : nullptr;
     a.total_tokens = p->total_tokens;
     a.num_seqs = p->num_seqs;
     a.num_heads = p->num_heads;
@@ -363,11 +364,14 @@ kda_status_t kda_chunk_fwd_conv(const kda_problem_t* p, const kda_gate_t* gate, 
     cv.K = conv->kernel_size;
     cv.silu = conv->silu;
     cv.channels = static_cast<int>(channels);
+    // The chain pass writes the new conv states (after its own reads of the old
+    // ones); a call that launches nothing (no tokens, no final state) copies
+    // them with a kernel of their own.
+    const bool chain_runs = p->num_seqs > 0 && (p->total_tokens > 0 || final_state);
     st = chunk_fwd_impl(what, p, gp, x, x ? x + hd : nullptr, x ? x + 2 * hd : nullptr, g, beta, cu_seqlens,
                         initial_state, out, final_state, workspace, workspace_bytes, stream, nullptr, 0,
-                        Workspace::kCaller, &cv, channels);
-    if (st != KDA_OK || !conv->state_out || p->num_seqs == 0 || conv->kernel_size < 2) return st;
-    // the new conv states, after every read of the old ones
+                        Workspace::kCaller, &cv, channels, conv->state_out);
+    if (st != KDA_OK || chain_runs || !conv->state_out || p->num_seqs == 0 || conv->kernel_size < 2) return st;
     kda::ConvArgs a{};
     a.x = qkv;
     a.cu_seqlens = cu_seqlens;

@@ -90,6 +90,9 @@ struct PrefillArgs {
     // projection, as with conv).
     int64_t qkv_row;
     ConvParams conv;  // conv.weight null: q, k, v are used as given
+    // With conv: the new conv states [N, K - 1, 3 H d], written by the chain
+    // pass (may be conv.state itself), or null.
+    void* conv_state_out;
     int64_t total_tokens;
     int num_seqs;
     int num_heads;

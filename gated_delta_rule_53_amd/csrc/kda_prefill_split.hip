@@ -1554,7 +1554,7 @@ __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_ker
     const bf16_t* __restrict__ v, const int32_t* __restrict__ cu_seqlens, ChunkMap cm,
     const unsigned char* __restrict__ records, const float* initial_state,
     TOut* __restrict__ out, float* final_state, const int32_t* __restrict__ slots, int num_slots, int num_seqs,
-    int num_heads, int state_trans, int v_row, ConvParams cv) {
+    int num_heads, int state_trans, int v_row, ConvParams cv, bf16_t* conv_state_out) {
     __shared__ __align__(16) unsigned char lds_sx[CH_SX_BYTES];
     __shared__ __align__(16) unsigned char lds_dx[CH_DX_BYTES];
     __shared__ __align__(16) unsigned char lds_vb[3 * CH_VBYTES];  // chunk j's V rows in buffer j mod 3
@@ -1776,6 +1776,30 @@ __global__ __launch_bounds__(CONV ? CH_THREADS_CONV : CH_THREADS) void chain_ker
             wait_vmcnt<0>();
             sum += tka + tkb + tkc;
             reinterpret_cast<uint32_t*>(lds_sink)[hi * 64 + lane] = sum;
+            // The request's new conv state, this unit's 16 channels of its
+            // head's q, k and v blocks: row r is entry len + r of the window
+            // (the input row when that lies past the old state, else the old
+            // state's row, else zero).  Lane: block p = lane / 6, row r = (lane
+            // / 2) % 3, half lane & 1.  Each slice of the old state is read by
+            // this workgroup alone (its v columns above, q and k by the prep
+            // pass before), and every lane's load precedes the stores, so the
+            // new state may overwrite the old.
+            if (hi == 0 && conv_state_out && cv.K > 1) {
+                const int S = cv.K - 1;
+                const int p = lane / 6, r = (lane >> 1) % 3;
+                const int64_t start = t_first, end = t_last;
+                const int64_t len = start < 0 || end > cm.total_tokens || end < start ? 0 : end - start;
+                const size_t Cc = static_cast<size_t>(cv.channels);
+                const size_t c = static_cast<size_t>(p) * num_heads * D + h * D + col0 + 8 * (lane & 1);
+                const bf16_t* x0 = v - 2 * static_cast<size_t>(num_heads) * D;  // the fused projection
+                const bool live = lane < 18 && r < S;
+                const int64_t i = len + r;
+                const bf16_t* src = i >= S ? x0 + static_cast<size_t>(start + i - S) * Cc + c
+                                           : (cv.state ? cv.state + (static_cast<size_t>(n) * S + i) * Cc + c : nullptr);
+                uint4 val = {0u, 0u, 0u, 0u};
+                if (live && src) val = *reinterpret_cast<const uint4*>(src);
+                if (live) *reinterpret_cast<uint4*>(conv_state_out + (static_cast<size_t>(n) * S + r) * Cc + c) = val;
+            }
             return;
         }
         if (nc > 0) {
@@ -2105,14 +2129,14 @@ static hipError_t launch_split_t(const PrefillArgs& a, void* workspace, hipStrea
         chain_kernel<TOut, true><<<groups * 8, CH_THREADS_CONV, pairs ? 0 : 64 * 1024, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, cm, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
-            a.state_trans, static_cast<int>(a.qkv_row), a.conv);
+            a.state_trans, static_cast<int>(a.qkv_row), a.conv, static_cast<bf16_t*>(a.conv_state_out));
         return hipGetLastError();
     }
     if (!pairs) {
         chain_kernel<TOut, false><<<groups * 8, CH_THREADS, 64 * 1024, stream>>>(
             static_cast<const bf16_t*>(a.v), a.cu_seqlens, cm, records, a.initial_state,
             static_cast<TOut*>(a.out), a.final_state, a.slots, a.num_slots, a.num_seqs, a.num_heads,
-            a.state_trans, static_cast<int>(a.qkv_row), a.conv);
+            a.state_trans, static_cast<int>(a.qkv_row), a.conv, nullptr);
         return hipGetLastError();
     }
     scan_kernel<TOut, 2><<<groups * ScanShape<2>::UNITS, ScanShape<2>::THREADS, 0, stream>>>(

@@ -247,9 +247,9 @@ kda_status_t kda_chunk_fwd_gated(const kda_problem_t *problem, const kda_gate_t 
  *                request's last K - 1 inputs before this call, oldest first;
  *                NULL for zeros
  *   state_out    [N, K - 1, 3 H d] bf16 (device, 16-byte aligned), written
- *                after the prefill with each request's last K - 1 inputs (its
- *                old state followed by its inputs when it is shorter); NULL to
- *                skip; may equal state_in
+ *                with each request's last K - 1 inputs (its old state followed
+ *                by its inputs when it is shorter), each slice after the
+ *                call's last read of it; NULL to skip; may equal state_in
  */
 typedef struct kda_conv {
     int32_t kernel_size;

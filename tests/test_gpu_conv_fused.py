@@ -13,10 +13,10 @@ References:
   oracle.forward and oracle.epilogue, within 2e-3 of max|oracle|; a bf16
   output, rounded once, may also differ by half a bf16 ulp of each value
   (2^-9 |ref|).
-Cases: requests shorter than the filter, empty requests, chunk boundaries,
-every filter length, with and without conv state and SiLU, the conv state
-updated in place, raw gates, both output dtypes and state layouts, many
-chains, and the full 4096-token, 32-head workload.
+Cases: requests shorter than the filter, empty requests, a call with no
+tokens, chunk boundaries, every filter length, with and without conv state
+and SiLU, the conv state updated in place, raw gates, both output dtypes and
+state layouts, many chains, and the full 4096-token, 32-head workload.
 """
 import numpy as np
 import pytest
@@ -152,6 +152,37 @@ def test_fused_conv_state_in_place():
     o2, f2, s2 = _fused(x, True, torch.float32, "dk_dv", in_place=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2) and torch.equal(s1, s2)
+
+
+@pytest.mark.parametrize("final_state", [True, False], ids=["final_state", "no_final_state"])
+@pytest.mark.parametrize("in_place", [False, True], ids=["out_of_place", "in_place"])
+def test_fused_conv_state_with_no_tokens(final_state, in_place):
+    """Every request empty (T = 0): each new conv state is its old one, bit for
+    bit; written by the chain pass when the call produces final states (which
+    then equal the initial ones), and by a kernel of its own when it produces
+    nothing else."""
+    import gated_delta_rule_53_amd as kda
+    N, H, d, K = 3, 2, 128, 4
+    C = 3 * H * d
+    gen = torch.Generator().manual_seed(21)
+    cs_host = torch.randn((N, K - 1, C), generator=gen).to(torch.bfloat16)
+    s0_host = torch.randn((N, H, d, d), generator=gen) * 0.1
+    wt = dev(torch.randn((K, C), generator=gen).to(torch.bfloat16))
+    announce(f"conv-fused prefill, no tokens, final_state={final_state} in_place={in_place}")
+    qkv = torch.empty((0, 3, H, d), dtype=torch.bfloat16, device="cuda:0")
+    g = torch.empty((0, H, d), dtype=torch.float32, device="cuda:0")
+    b = torch.empty((0, H), dtype=torch.float32, device="cuda:0")
+    cu = torch.zeros(N + 1, dtype=torch.int32, device="cuda:0")
+    cs = dev(cs_host)
+    cs_out = cs if in_place else torch.full_like(cs, 7.0)
+    _, fs = kda.chunk_fwd_conv(qkv, g, b, wt, cu, dev(s0_host), cs, conv_state_out=cs_out,
+                               output_final_state=final_state)
+    torch.cuda.synchronize()
+    assert torch.equal(cs_out.cpu(), cs_host)
+    if final_state:
+        assert torch.equal(fs.cpu(), s0_host)
+    else:
+        assert fs is None
 
 
 @pytest.mark.parametrize("lb", [None, -5.0])
