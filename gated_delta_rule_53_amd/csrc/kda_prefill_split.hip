@@ -120,10 +120,11 @@ static_assert(P_LDS <= 160 * 1024, "prep LDS budget");
 constexpr int P_WT = P_XDH;                                     // 16 wave totals [16][128] fp32 (phase 1 only)
 static_assert(16 * D * 4 <= 4 * 4 * BLK, "wave totals alias X_RR and X_RR diag(rk^2 beta)");
 // Exact path (a chunk whose decay is too strong for the reference token):
-// raw k, q and e^g of every row, fp32 [64][128], in regions 1-3 before the
-// planes are formed there.
-constexpr int P_GK = 0, P_GQ = C * D * 4, P_GE = 2 * C * D * 4;
-static_assert(P_GE + C * D * 4 <= P_R3_END && P_R3_END <= P_PH, "exact-path arrays fit below P'");
+// raw k and q of every row, bf16 [64][128] (the values are bf16 already), and
+// e^g and G (the cumulative log-decay from the chunk's start), fp32 [64][128],
+// in regions 1-3 before the planes are formed there.
+constexpr int P_GK = 0, P_GQ = C * D * 2, P_GE = 2 * C * D * 2, P_GG = P_GE + C * D * 4;
+static_assert(P_GG + C * D * 4 <= P_R3_END && P_R3_END <= P_PH, "exact-path arrays fit below P'");
 // Fused convolution: the raw k and q rows -4 .. 63 of the chunk (row -4 + i
 // at i * 256 bytes), in region 1 from the top of an item until its planes.
 constexpr int P_CVK = 0, P_CVQ = (C + 4) * D * 2;
@@ -172,50 +173,52 @@ __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* re
     return rec + base + ((unit * ns + s) * 2 + hl) * FRAG + lane * 16;
 }
 
-// Exact A' and P' of one (chunk, head), for chunks whose decay is too strong
-// to factor through the reference token.  Raw k, q and e^g of every row are
-// in LDS (fp32 [64][128]).  For column i the per-channel vector
-// z = k_i e^{G_r - G_i} is carried down the rows by z <- z e^{g_r}, starting
-// from z = k_i at row i: every factor is at most 1, so nothing overflows
-// however strong the decay (tiny products underflow towards zero, as the
-// exact values do).  Then, with the same scalings as the MFMA path,
-//   A'[r][i] = beta_r rk_r^2 (k_r . z)   (i < r),   P'[r][i] = rq_r (q_r . z)   (i <= r),
-// written where that path leaves them: A' diagonal blocks in fp32 and the
-// other A' blocks as bf16 hi/lo (both transposed), P' as bf16 hi/lo
-// row-major.  Entries above the diagonal are not written: the inverses do
-// not read them and the P' planes are cleared beforehand.
-// Lane (l4, l16) takes column i = 4 pw + l4 and channels 8 l16 .. 8 l16 + 7;
-// the 16 lanes of a DPP row reduce the dot products over the channels.
+// A' and P' of a chunk whose decay is too steep for one reference token,
+// exactly (every factor at most 1, so none overflows; the ones that underflow
+// are zero).
+// - The four diagonal 16x16 blocks, elementwise: wave pw takes columns i =
+//   4 pw .. 4 pw + 3 (one per lane group; lane l16 holds 8 channels) and
+//   carries k_i e^{G_r - G_i} down its block's rows r >= i as a running
+//   product of e^{g_r} <= 1, forming k_r . z and q_r . z per row.
+// - The six blocks below the diagonal (R > I), on MFMA: with e the last token
+//   of block I, A'_RI = (k_r e^{G_r - G_e}) (k_i e^{G_e - G_i})^T and P'_RI the
+//   same with q_r, both operands bf16 hi/lo pairs built in registers.  The
+//   waves whose diagonal columns have the fewest rows take them.
+// Results go where the factored path puts its own: A' blocks below the
+// diagonal and P' as bf16 hi/lo planes, the diagonal blocks of L' in fp32.
 __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16, int l4) {
-    const float* gk = reinterpret_cast<const float*>(smem + P_GK);
-    const float* gq = reinterpret_cast<const float*>(smem + P_GQ);
     const float* ge = reinterpret_cast<const float*>(smem + P_GE);
+    const float* gg = reinterpret_cast<const float*>(smem + P_GG);
     const float* srk = reinterpret_cast<const float*>(smem + P_RK);
     const float* srq = reinterpret_cast<const float*>(smem + P_RQ);
     const float* sbeta = reinterpret_cast<const float*>(smem + P_BETA);
-    // Column group pw starts at row 4 pw.  The four waves sharing a SIMD
-    // (wave mod 4) get groups whose row counts add up to the same total.
-    const int pw = ((wave >> 2) & 1) ? (wave ^ 3) : wave;
-    const int r0 = 4 * pw, i = r0 + l4, co = 8 * l16;
-    auto row8 = [&](const float* base, int r) {
-        const floatx4 a = *reinterpret_cast<const floatx4*>(base + r * D + co);
-        const floatx4 b = *reinterpret_cast<const floatx4*>(base + r * D + co + 4);
+    auto f32row8 = [&](const float* base, int r, int c0) {
+        const floatx4 a = *reinterpret_cast<const floatx4*>(base + r * D + c0);
+        const floatx4 b = *reinterpret_cast<const floatx4*>(base + r * D + c0 + 4);
         return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     };
-    const floatx8 ki = row8(gk, i);
+    auto bfrow8 = [&](int plane, int r, int c0) { return bf8_to_f(ld8(smem, plane + (r * D + c0) * 2)); };
+    // ---- diagonal blocks ----
+    // Column group pw starts at row 4 pw and runs to its block's end.  The
+    // four waves sharing a SIMD (wave mod 4) get groups whose row counts add
+    // up to the same total.
+    const int pw = ((wave >> 2) & 1) ? (wave ^ 3) : wave;
+    const int r0 = 4 * pw, i = r0 + l4, co = 8 * l16;
+    const int rend = (r0 | 15) + 1;
+    const floatx8 ki = bfrow8(P_GK, i, co);
     floatx8 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float av = 0.f, pv = 0.f;  // lane l16 keeps the sums of row 16 (r / 16) + l16
     // Row r of the sums: z is born at r == i (the first four rows of the
-    // group), decayed by e^{g_r} afterwards; a 16-row batch ends at r % 16 == 15.
+    // group), decayed by e^{g_r} afterwards; the block ends at r % 16 == 15.
     auto step = [&](int r, bool birth) {
-        const floatx8 er = row8(ge, r);
+        const floatx8 er = f32row8(ge, r, co);
         if (birth) {
 #pragma unroll
             for (int c = 0; c < 8; ++c) z[c] = r == i ? ki[c] : z[c] * er[c];
         } else {
             z *= er;
         }
-        const floatx8 kr = row8(gk, r), qr = row8(gq, r);
+        const floatx8 kr = bfrow8(P_GK, r, co), qr = bfrow8(P_GQ, r, co);
         float a = 0.f, p = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
@@ -235,19 +238,74 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
         *reinterpret_cast<uint16_t*>(smem + P_PL + (rr * SN + i) * 2) = static_cast<uint16_t>(l);
         if (rr == i) return;
         const float rk = srk[rr];
-        const float av_s = sbeta[rr] * rk * rk * av;
-        const int R = rr >> 4, I = i >> 4;
-        if (R == I) {
-            *reinterpret_cast<float*>(smem + P_LDT + ((R * 16 + (i & 15)) * LDS_STR + (rr & 15)) * 4) = av_s;
-        } else {
-            split2(av_s, 0.f, h, l);
-            const int o = ((pair_index(R, I) * 16 + (i & 15)) * WSTR + (rr & 15)) * 2;
-            *reinterpret_cast<uint16_t*>(smem + P_ATH + o) = static_cast<uint16_t>(h);
-            *reinterpret_cast<uint16_t*>(smem + P_ATL + o) = static_cast<uint16_t>(l);
-        }
+        const int R = rr >> 4;
+        *reinterpret_cast<float*>(smem + P_LDT + ((R * 16 + (i & 15)) * LDS_STR + (rr & 15)) * 4) =
+            sbeta[rr] * rk * rk * av;
     };
     for (int r = r0; r < r0 + 4; ++r) step(r, true);
-    for (int r = r0 + 4; r < C; ++r) step(r, false);
+    for (int r = r0 + 4; r < rend; ++r) step(r, false);
+
+    // ---- blocks below the diagonal ----
+    const int b = wave == 3 ? 0 : wave == 11 ? 1 : wave == 4 ? 2 : wave == 12 ? 3 : wave == 2 ? 4 : wave == 13 ? 5 : -1;
+    if (b < 0) return;
+    const int R = b < 1 ? 1 : b < 3 ? 2 : 3;
+    const int I = b < 1 ? 0 : b < 3 ? b - 1 : b - 3;
+    const int rrow = 16 * R + l16, icol = 16 * I + l16, e = 16 * I + 15;
+    floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int s = 0; s < 4; ++s) {
+        const int c0 = 32 * s + 8 * l4;
+        // columns up to e: k_i e^{G_e - G_i}, G_e <= G_i
+        const floatx8 gm = f32row8(gg, e, c0);
+        bf16x8 bh, bl;
+        {
+            const floatx8 gc = f32row8(gg, icol, c0), kc = bfrow8(P_GK, icol, c0);
+            floatx8 xb;
+#pragma unroll
+            for (int c = 0; c < 8; ++c) xb[c] = kc[c] * fast_exp2((gm[c] - gc[c]) * kLog2e);
+            split8(xb, bh, bl);
+        }
+        // rows after e: e^{G_r - G_e}, G_r <= G_e, shared by A' (k_r) and P' (q_r)
+        floatx8 fr;
+        {
+            const floatx8 gr = f32row8(gg, rrow, c0);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) fr[c] = fast_exp2((gr[c] - gm[c]) * kLog2e);
+        }
+        {
+            const floatx8 kr = bfrow8(P_GK, rrow, c0);
+            bf16x8 ah, al;
+            split8(kr * fr, ah, al);
+            accA = mma3(ah, al, bh, bl, accA);
+        }
+        {
+            const floatx8 qr = bfrow8(P_GQ, rrow, c0);
+            bf16x8 ph, pl;
+            split8(qr * fr, ph, pl);
+            accP = mma3(ph, pl, bh, bl, accP);
+        }
+    }
+    // rows 16 R + 4 l4 + j, column 16 I + l16, stored as the factored path stores them
+    floatx4 a, pq;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int r = 16 * R + 4 * l4 + j;
+        const float rk = srk[r];
+        a[j] = sbeta[r] * rk * rk * accA[j];
+        pq[j] = srq[r] * accP[j];
+    }
+    bf16x4 hi, lo;
+    split4(a, hi, lo);
+    const int o = ((pair_index(R, I) * 16 + l16) * WSTR + 4 * l4) * 2;
+    *reinterpret_cast<bf16x4*>(smem + P_ATH + o) = hi;
+    *reinterpret_cast<bf16x4*>(smem + P_ATL + o) = lo;
+    split4(pq, hi, lo);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int o2 = ((16 * R + 4 * l4 + j) * SN + 16 * I + l16) * 2;
+        *reinterpret_cast<__bf16*>(smem + P_PH + o2) = hi[j];
+        *reinterpret_cast<__bf16*>(smem + P_PL + o2) = lo[j];
+    }
 }
 
 // ---- the short convolution fused into the q/k/v loads ----
@@ -746,15 +804,20 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             floatx8 eg;
 #pragma unroll
             for (int i = 0; i < 8; ++i) eg[i] = fast_exp2(gr[i] * kLog2e);
-            float* gk = reinterpret_cast<float*>(smem + P_GK);
-            float* gq = reinterpret_cast<float*>(smem + P_GQ);
+            // G_r (from the chunk's start)
+            const floatx8 dl = offsets8(sWT + wave * D + 8 * cc) + incl + offsets8(sG31 + 8 * cc);
             float* ge = reinterpret_cast<float*>(smem + P_GE);
-            *reinterpret_cast<floatx4*>(gk + o) = floatx4{kf[0], kf[1], kf[2], kf[3]};
-            *reinterpret_cast<floatx4*>(gk + o + 4) = floatx4{kf[4], kf[5], kf[6], kf[7]};
-            *reinterpret_cast<floatx4*>(gq + o) = floatx4{qf[0], qf[1], qf[2], qf[3]};
-            *reinterpret_cast<floatx4*>(gq + o + 4) = floatx4{qf[4], qf[5], qf[6], qf[7]};
+            float* gg = reinterpret_cast<float*>(smem + P_GG);
+            auto pack8 = [](const floatx8& x) {  // exact: the values are bf16 already
+                return uint4{pack_bf16x2(x[0], x[1]), pack_bf16x2(x[2], x[3]), pack_bf16x2(x[4], x[5]),
+                             pack_bf16x2(x[6], x[7])};
+            };
+            *reinterpret_cast<uint4*>(smem + P_GK + o * 2) = pack8(kf);
+            *reinterpret_cast<uint4*>(smem + P_GQ + o * 2) = pack8(qf);
             *reinterpret_cast<floatx4*>(ge + o) = floatx4{eg[0], eg[1], eg[2], eg[3]};
             *reinterpret_cast<floatx4*>(ge + o + 4) = floatx4{eg[4], eg[5], eg[6], eg[7]};
+            *reinterpret_cast<floatx4*>(gg + o) = floatx4{dl[0], dl[1], dl[2], dl[3]};
+            *reinterpret_cast<floatx4*>(gg + o + 4) = floatx4{dl[4], dl[5], dl[6], dl[7]};
             // P' planes (hi and lo, adjacent) cleared: exact_ap writes i <= r only
             static_assert(P_PL == P_PH + PN && 2 * PN % 16 == 0, "P' planes adjacent");
             for (int u = tid; u < 2 * PN / 16; u += PNT)
@@ -765,10 +828,14 @@ __global__ __launch_bounds__(PNT) void prep_kernel(
             }
             lds_barrier();
             exact_ap(smem, wave, l16, l4);
+            // k, q and G of this row back from LDS (nothing is kept live across
+            // exact_ap), before the barrier after which the planes overwrite them
+            kf = bf8_to_f(ld8(smem, P_GK + o * 2));
+            qf = bf8_to_f(ld8(smem, P_GQ + o * 2));
+            const floatx8 dg = offsets8(gg + o);
             lds_barrier();
             // d = G_r (from the chunk's start), dt = G_last - G_r
-            const floatx8 dl = offsets8(sWT + wave * D + 8 * cc) + incl + offsets8(sG31 + 8 * cc);
-            planes(dl * kLog2e, (offsets8(sGLL + 8 * cc) - dl) * kLog2e);
+            planes(dg * kLog2e, (offsets8(sGLL + 8 * cc) - dg) * kLog2e);
         } else {
             const floatx8 d = (offsets8(sWT + wave * D + 8 * cc) + incl) * kLog2e;
             planes(d, -d);
