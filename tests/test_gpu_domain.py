@@ -74,6 +74,24 @@ def test_mixed_heads_fast_and_exact(d, dtype):
 
 
 @pytest.mark.parametrize("d,dtype", PATHS, ids=PATH_IDS)
+def test_reference_span_threshold(d, dtype):
+    """Decays just either side of where the bf16 d=128 path leaves its reference
+    token: a constant g per head makes each 32-token half of a full chunk span
+    32 |g|, and the limit there is 60 (|g| = 1.875).  Heads at |g| = 1.85 and
+    1.87 stay on the factored path with factors near e^60, heads at 1.88 and
+    1.95 take the exact one; the 24-token sequence's chunk spans at most 24 |g|
+    and stays factored in every head.  Every head must meet the bar on both
+    sides."""
+    x = w.make_prefill([128, 24, 64], 4, d, dtype, seed=49)
+    for h, gv in enumerate((-1.85, -1.87, -1.88, -1.95)):
+        x.g[:, h] = gv
+    announce(f"prefill reference-span threshold d={d} {dtype}")
+    out, fs = prefill_on_gpu(x)
+    ro, rs = oracle.forward(x.q, x.k, x.v, x.g, x.beta, x.cu_seqlens, x.initial_state, scale=x.scale)
+    _check(out, fs, ro, rs, dtype)
+
+
+@pytest.mark.parametrize("d,dtype", PATHS, ids=PATH_IDS)
 @pytest.mark.parametrize("a_log_value", [math.log(16.0), None], ids=["A16", "A_U1_16"])
 def test_page_softplus_gate(d, dtype, a_log_value):
     """Softplus gate, A_log = log 16 (or log U(1, 16) per head), dt_bias = 0,
