@@ -37,7 +37,8 @@
 //                     into LDS ahead of them, form Delta0 ahead of them and
 //                     form the output behind them, for all its tiles.
 // Inside prep, operands are bf16 hi/lo pairs (hi*hi + hi*lo + lo*hi), except
-// k.k in A (inverted afterwards); the 16x16 diagonal inverses are fp32.
+// k.k in A (inverted afterwards; pairs too in the blocks that chunks too steep
+// for the reference token form on MFMA); the 16x16 diagonal inverses are fp32.
 #include <type_traits>
 
 #include "kda_bf16_mfma.h"
@@ -184,8 +185,12 @@ __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* re
 //   of block I, A'_RI = (k_r e^{G_r - G_e}) (k_i e^{G_e - G_i})^T and P'_RI the
 //   same with q_r, both operands bf16 hi/lo pairs built in registers.  The
 //   waves whose diagonal columns have the fewest rows take them.
-// Results go where the factored path puts its own: A' blocks below the
-// diagonal and P' as bf16 hi/lo planes, the diagonal blocks of L' in fp32.
+// With the factored path's scalings, A'[r][i] = beta_r rk_r^2 (k_r . z) for
+// i < r and P'[r][i] = rq_r (q_r . z) for i <= r (z = k_i e^{G_r - G_i}), and
+// written where that path puts its own: A' blocks below the diagonal and P' as
+// bf16 hi/lo planes, the diagonal blocks of L' in fp32.  Entries above the
+// diagonal are not written: the inverses do not read them, and the P' planes
+// are cleared beforehand.
 __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16, int l4) {
     const float* ge = reinterpret_cast<const float*>(smem + P_GE);
     const float* gg = reinterpret_cast<const float*>(smem + P_GG);
