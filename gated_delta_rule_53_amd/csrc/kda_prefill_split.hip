@@ -176,15 +176,19 @@ __device__ __forceinline__ const unsigned char* frag_ptr(const unsigned char* re
 
 // A' and P' of a chunk whose decay is too steep for one reference token,
 // exactly (every factor at most 1, so none overflows; the ones that underflow
-// are zero).
-// - The four diagonal 16x16 blocks, elementwise: wave pw takes columns i =
-//   4 pw .. 4 pw + 3 (one per lane group; lane l16 holds 8 channels) and
-//   carries k_i e^{G_r - G_i} down its block's rows r >= i as a running
-//   product of e^{g_r} <= 1, forming k_r . z and q_r . z per row.
-// - The six blocks below the diagonal (R > I), on MFMA: with e the last token
-//   of block I, A'_RI = (k_r e^{G_r - G_e}) (k_i e^{G_e - G_i})^T and P'_RI the
-//   same with q_r, both operands bf16 hi/lo pairs built in registers.  The
-//   waves whose diagonal columns have the fewest rows take them.
+// are zero).  The chunk's 64 rows form eight 8-row groups.
+// - Inside each group, elementwise: wave pw takes columns i = 4 pw .. 4 pw + 3
+//   (one per lane group; lane l16 holds 8 channels) and carries
+//   z = k_i e^{G_r - G_i} down the group's rows r >= i as a running product of
+//   e^{g_r} <= 1, forming k_r . z and q_r . z per row.
+// - Everything else below the diagonal, on MFMA, with both operands referred
+//   to the last token e of the column block (columns k_i e^{G_e - G_i}, rows
+//   k_r e^{G_r - G_e}, q_r for P'), bf16 hi/lo pairs built in registers: the
+//   six 16x16 blocks R > I (e = 16 I + 15), and in each diagonal block the
+//   rows 8 .. 15 against the columns 0 .. 7 (e = 16 R + 7), two diagonal blocks
+//   to one product (its two cross quarters mix references and are dropped;
+//   their factors are at most 1 too).  The waves whose groups have the fewest
+//   rows take these eight products, two per SIMD.
 // With the factored path's scalings, A'[r][i] = beta_r rk_r^2 (k_r . z) for
 // i < r and P'[r][i] = rq_r (q_r . z) for i <= r (z = k_i e^{G_r - G_i}), and
 // written where that path puts its own: A' blocks below the diagonal and P' as
@@ -203,18 +207,18 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
         return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     };
     auto bfrow8 = [&](int plane, int r, int c0) { return bf8_to_f(ld8(smem, plane + (r * D + c0) * 2)); };
-    // ---- diagonal blocks ----
-    // Column group pw starts at row 4 pw and runs to its block's end.  The
-    // four waves sharing a SIMD (wave mod 4) get groups whose row counts add
-    // up to the same total.
+    // ---- inside the 8-row groups ----
+    // Column group pw starts at row 4 pw and runs to its 8-row group's end (8
+    // rows for even pw, 4 for odd).  The four waves sharing a SIMD (wave mod 4)
+    // get two of each.
     const int pw = ((wave >> 2) & 1) ? (wave ^ 3) : wave;
     const int r0 = 4 * pw, i = r0 + l4, co = 8 * l16;
-    const int rend = (r0 | 15) + 1;
+    const int rend = (r0 | 7) + 1;
     const floatx8 ki = bfrow8(P_GK, i, co);
     floatx8 z = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     float av = 0.f, pv = 0.f;  // lane l16 keeps the sums of row 16 (r / 16) + l16
     // Row r of the sums: z is born at r == i (the first four rows of the
-    // group), decayed by e^{g_r} afterwards; the block ends at r % 16 == 15.
+    // group), decayed by e^{g_r} afterwards; the group ends at r % 8 == 7.
     auto step = [&](int r, bool birth) {
         const floatx8 er = f32row8(ge, r, co);
         if (birth) {
@@ -234,9 +238,9 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
         p = row16_sum(p);
         av = l16 == (r & 15) ? a : av;
         pv = l16 == (r & 15) ? p : pv;
-        if ((r & 15) != 15) return;
+        if ((r & 7) != 7) return;
         const int rr = (r & ~15) + l16;
-        if (rr < i) return;
+        if (rr < i || rr > r) return;  // lanes of the group's rows at or below the diagonal
         uint32_t h, l;
         split2(srq[rr] * pv, 0.f, h, l);
         *reinterpret_cast<uint16_t*>(smem + P_PH + (rr * SN + i) * 2) = static_cast<uint16_t>(h);
@@ -250,12 +254,26 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
     for (int r = r0; r < r0 + 4; ++r) step(r, true);
     for (int r = r0 + 4; r < rend; ++r) step(r, false);
 
-    // ---- blocks below the diagonal ----
-    const int b = wave == 3 ? 0 : wave == 11 ? 1 : wave == 4 ? 2 : wave == 12 ? 3 : wave == 2 ? 4 : wave == 13 ? 5 : -1;
+    // ---- the rest below the diagonal, on MFMA ----
+    // jobs 0-5: block (R, I) = (1,0), (2,0), (2,1), (3,0), (3,1), (3,2); jobs 6,
+    // 7: the lower-left quarters of diagonal blocks 0, 1 and 2, 3.  Lane l16 is
+    // the row (A operand) and the column (B operand) of its 16.
+    const int b = wave == 1 ? 0 : wave == 3 ? 1 : wave == 4 ? 2 : wave == 6 ? 3 : wave == 9 ? 4 : wave == 11 ? 5
+                : wave == 12 ? 6 : wave == 14 ? 7 : -1;
     if (b < 0) return;
-    const int R = b < 1 ? 1 : b < 3 ? 2 : 3;
-    const int I = b < 1 ? 0 : b < 3 ? b - 1 : b - 3;
-    const int rrow = 16 * R + l16, icol = 16 * I + l16, e = 16 * I + 15;
+    int rrow, icol, e;
+    if (b < 6) {
+        const int R = b < 1 ? 1 : b < 3 ? 2 : 3;
+        const int I = b < 1 ? 0 : b < 3 ? b - 1 : b - 3;
+        rrow = 16 * R + l16;
+        icol = 16 * I + l16;
+        e = 16 * I + 15;
+    } else {
+        const int Rd = 2 * (b - 6) + (l16 >> 3);  // this lane's diagonal block
+        rrow = 16 * Rd + 8 + (l16 & 7);
+        icol = 16 * Rd + (l16 & 7);
+        e = 16 * Rd + 7;
+    }
     floatx4 accA = {0.f, 0.f, 0.f, 0.f}, accP = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
     for (int s = 0; s < 4; ++s) {
@@ -290,26 +308,46 @@ __device__ __forceinline__ void exact_ap(unsigned char* smem, int wave, int l16,
             accP = mma3(ph, pl, bh, bl, accP);
         }
     }
-    // rows 16 R + 4 l4 + j, column 16 I + l16, stored as the factored path stores them
-    floatx4 a, pq;
+    // accumulator j of lane (l4, l16): A operand row m = 4 l4 + j, B operand
+    // column n = l16, stored as the factored path stores them
+    if (b < 6) {
+        const int R = b < 1 ? 1 : b < 3 ? 2 : 3;
+        const int I = b < 1 ? 0 : b < 3 ? b - 1 : b - 3;
+        floatx4 a, pq;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int r = 16 * R + 4 * l4 + j;
-        const float rk = srk[r];
-        a[j] = sbeta[r] * rk * rk * accA[j];
-        pq[j] = srq[r] * accP[j];
-    }
-    bf16x4 hi, lo;
-    split4(a, hi, lo);
-    const int o = ((pair_index(R, I) * 16 + l16) * WSTR + 4 * l4) * 2;
-    *reinterpret_cast<bf16x4*>(smem + P_ATH + o) = hi;
-    *reinterpret_cast<bf16x4*>(smem + P_ATL + o) = lo;
-    split4(pq, hi, lo);
+        for (int j = 0; j < 4; ++j) {
+            const int r = 16 * R + 4 * l4 + j;
+            const float rk = srk[r];
+            a[j] = sbeta[r] * rk * rk * accA[j];
+            pq[j] = srq[r] * accP[j];
+        }
+        bf16x4 hi, lo;
+        split4(a, hi, lo);
+        const int o = ((pair_index(R, I) * 16 + l16) * WSTR + 4 * l4) * 2;
+        *reinterpret_cast<bf16x4*>(smem + P_ATH + o) = hi;
+        *reinterpret_cast<bf16x4*>(smem + P_ATL + o) = lo;
+        split4(pq, hi, lo);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const int o2 = ((16 * R + 4 * l4 + j) * SN + 16 * I + l16) * 2;
-        *reinterpret_cast<__bf16*>(smem + P_PH + o2) = hi[j];
-        *reinterpret_cast<__bf16*>(smem + P_PL + o2) = lo[j];
+        for (int j = 0; j < 4; ++j) {
+            const int o2 = ((16 * R + 4 * l4 + j) * SN + 16 * I + l16) * 2;
+            *reinterpret_cast<__bf16*>(smem + P_PH + o2) = hi[j];
+            *reinterpret_cast<__bf16*>(smem + P_PL + o2) = lo[j];
+        }
+    } else if ((l4 >> 1) == (l16 >> 3)) {  // rows and column of the same diagonal block
+        const int Rd = 2 * (b - 6) + (l16 >> 3);
+        const int cl = l16 & 7;  // column 16 Rd + cl
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            const int rl = 8 + 4 * (l4 & 1) + j;  // row 16 Rd + rl
+            const int r = 16 * Rd + rl;
+            const float rk = srk[r];
+            *reinterpret_cast<float*>(smem + P_LDT + ((Rd * 16 + cl) * LDS_STR + rl) * 4) =
+                sbeta[r] * rk * rk * accA[j];
+            uint32_t h, l;
+            split2(srq[r] * accP[j], 0.f, h, l);
+            *reinterpret_cast<uint16_t*>(smem + P_PH + (r * SN + 16 * Rd + cl) * 2) = static_cast<uint16_t>(h);
+            *reinterpret_cast<uint16_t*>(smem + P_PL + (r * SN + 16 * Rd + cl) * 2) = static_cast<uint16_t>(l);
+        }
     }
 }
 
