@@ -16,7 +16,8 @@ References:
 Cases: requests shorter than the filter, empty requests, a call with no
 tokens, chunk boundaries, every filter length, with and without conv state
 and SiLU, the conv state updated in place, raw gates, both output dtypes and
-state layouts, many chains, and the full 4096-token, 32-head workload.
+state layouts, steep decays (the exact path), many chains, and the full
+4096-token, 32-head workload.
 """
 import numpy as np
 import pytest
@@ -197,6 +198,29 @@ def test_fused_conv_with_raw_gate(lb):
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
     g, b = ogate.activate(gi.raw_g, gi.raw_beta, gi.a_log, gi.dt_bias, lb)
+    ro, rf, _ = _oracle(x, True, g, b)
+    eo, es = rel_err(o2, ro), rel_err(f2, rf)
+    print(f"  err out {eo:.3e} state {es:.3e}")
+    assert eo <= TOL_BF16 and es <= TOL_BF16, (eo, es)
+
+
+def test_fused_conv_steep_decay():
+    """The page's gate at its initialisation (A_log = log 16, dt_bias = 0, raw
+    gate ~ N(0, 1), about -13 per token): every chunk takes the exact path,
+    which in this mode forms its operands from the convolved k and q."""
+    import math
+    lens, H = [150, 64, 33], 2
+    x = w.make_conv_prefill(lens, H, 128, 4, seed=14)
+    gi = w.make_gate(sum(lens), H, 128, torch.bfloat16, mu=0.0, std=1.0, dt_std=0.0,
+                     a_log_value=math.log(16.0), seed=15)
+    kw = dict(a_log=dev(gi.a_log), dt_bias=dev(gi.dt_bias), lower_bound=None)
+    announce("conv-fused prefill, steep decay (exact path)")
+    o1, f1, _ = _unfused(x, True, torch.float32, "dk_dv", kw, gi.raw_g, gi.raw_beta)
+    o2, f2, _ = _fused(x, True, torch.float32, "dk_dv", kw, gi.raw_g, gi.raw_beta)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    g, b = ogate.activate(gi.raw_g, gi.raw_beta, gi.a_log, gi.dt_bias)
+    assert float(g.mean()) < -5.0
     ro, rf, _ = _oracle(x, True, g, b)
     eo, es = rel_err(o2, ro), rel_err(f2, rf)
     print(f"  err out {eo:.3e} state {es:.3e}")
